@@ -1,0 +1,202 @@
+"""Seeded synthetic weights and inputs for the FlashHead Lite DiT slice denoiser.
+
+This module is the one place both sides of a parity check draw their data from:
+the CPU oracle (``oracle/``) and the HIP library (``audio_driven_talking_amd``).
+It holds workload sizes, tensor names/shapes/dtypes and seeded random numbers,
+and nothing of the method's arithmetic (no norms, no attention, no sampler).
+
+Workloads follow the gizai:flashhead reference page (overview paragraph): a
+512x512 picture coded to a latent of 5 frames of 16x16, 5 latent frames of 32
+audio tokens, 30 blocks of width 1536 with 12 heads, 4 flow-matching steps.
+The SoulX-FlashHead audio-cpp page (section "Generate") fixes 4 steps and seed
+42 as defaults; its "Variant boundaries" section says the transformer's
+dimensions come from an embedded configuration, hence every size below is a
+plain runtime value.
+
+Distributions (none is on the pages; they are stated here once):
+  * matrices: N(0, 0.02) drawn in float32, rounded to bfloat16 (round to
+    nearest even); both sides use exactly these values;
+  * biases, modulation tables: N(0, 0.02), float32;
+  * norm gains: 1 + N(0, 0.02), float32;
+  * latent noise, motion latent, audio tokens, residual stream, time
+    embedding: N(0, 1), float32.
+Every tensor has its own generator, keyed by (seed, crc32(name)), so a subset
+of blocks can be drawn without drawing the rest.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import hashlib
+import os
+import zlib
+
+import numpy as np
+
+WEIGHT_SEED = 1234
+NOISE_SEED = 42
+MOTION_SEED = 43
+AUDIO_SEED = 44
+RESID_SEED = 41
+TEMB_SEED = 45
+LANE_SEED_STRIDE = 100
+
+
+@dataclasses.dataclass(frozen=True)
+class DiTConfig:
+    """Sizes of one DiT and its slice latent (all plain values)."""
+    n_blocks: int = 30
+    dim: int = 1536
+    n_heads: int = 12
+    head_dim: int = 128
+    ffn_dim: int = 8960
+    in_ch: int = 16
+    out_ch: int = 16
+    frames: int = 5
+    height: int = 16
+    width: int = 16
+    motion_frames: int = 2
+    audio_per_frame: int = 32
+    freq_dim: int = 256
+    cross_full: bool = False   # False: frame-local audio attention; True: all audio tokens
+    eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    @property
+    def tokens(self) -> int:
+        return self.frames * self.height * self.width
+
+    @property
+    def audio_tokens(self) -> int:
+        return self.frames * self.audio_per_frame
+
+    def replace(self, **kw) -> "DiTConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads. Sizes only; seeds are the module constants above.
+CONFIGS = {
+    # 2 blocks, width 256, 2 heads x 128, FFN 1024; latent 2x8x8; 64 audio tokens; 1 step.
+    "toy": DiTConfig(n_blocks=2, dim=256, n_heads=2, head_dim=128, ffn_dim=1024,
+                     frames=2, height=8, width=8, motion_frames=1),
+    # one real-shape block: 1280 tokens, width 1536, 12 heads, FFN 8960, 160 audio tokens
+    "block": DiTConfig(n_blocks=1),
+    # full Lite slice: 30 blocks, 5x16x16 latent, 2 motion frames, 4 steps
+    "slice": DiTConfig(),
+    # 768x768 output: latent 5x24x24 (2880 tokens)
+    "slice768": DiTConfig(height=24, width=24),
+}
+TOY_SIGMAS = (1.0, 0.0)
+SLICE_SIGMAS = (1.0, 0.75, 0.5, 0.25, 0.0)
+
+
+def param_specs(cfg: DiTConfig, blocks=None):
+    """(name, shape, kind) of every tensor, in blob order.
+
+    kind is 'matrix' (bf16, stored [out, in]), 'vector' (f32) or 'gain' (f32).
+    ``qkv.w`` stacks the q, k and v projections ([3D, D], rows q then k then v);
+    ``ckv.w`` stacks the audio k and v projections ([2D, D]).
+    ``mod`` is a block's modulation table [6, D]: rows shift, scale, gate of the
+    self-attention branch, then shift, scale, gate of the FFN branch.
+    ``head.mod`` is the output norm's table [2, D]: rows shift, scale.
+    """
+    D, Fd, C, Co, Fq = cfg.dim, cfg.ffn_dim, cfg.in_ch, cfg.out_ch, cfg.freq_dim
+    specs = [
+        ("time_in.w", (D, Fq), "matrix"), ("time_in.b", (D,), "vector"),
+        ("time_out.w", (D, D), "matrix"), ("time_out.b", (D,), "vector"),
+        ("time_proj.w", (6 * D, D), "matrix"), ("time_proj.b", (6 * D,), "vector"),
+        ("patch.w", (D, C), "matrix"), ("patch.b", (D,), "vector"),
+        ("head.w", (Co, D), "matrix"), ("head.b", (Co,), "vector"),
+        ("head.mod", (2, D), "vector"),
+    ]
+    ids = range(cfg.n_blocks) if blocks is None else blocks
+    for i in ids:
+        p = f"blocks.{i}."
+        specs += [
+            (p + "mod", (6, D), "vector"),
+            (p + "qkv.w", (3 * D, D), "matrix"), (p + "qkv.b", (3 * D,), "vector"),
+            (p + "norm_q.g", (D,), "gain"), (p + "norm_k.g", (D,), "gain"),
+            (p + "o.w", (D, D), "matrix"), (p + "o.b", (D,), "vector"),
+            (p + "norm3.g", (D,), "gain"), (p + "norm3.b", (D,), "vector"),
+            (p + "cq.w", (D, D), "matrix"), (p + "cq.b", (D,), "vector"),
+            (p + "ckv.w", (2 * D, D), "matrix"), (p + "ckv.b", (2 * D,), "vector"),
+            (p + "norm_cq.g", (D,), "gain"), (p + "norm_ck.g", (D,), "gain"),
+            (p + "co.w", (D, D), "matrix"), (p + "co.b", (D,), "vector"),
+            (p + "ffn1.w", (Fd, D), "matrix"), (p + "ffn1.b", (Fd,), "vector"),
+            (p + "ffn2.w", (D, Fd), "matrix"), (p + "ffn2.b", (D,), "vector"),
+        ]
+    return specs
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    return np.random.default_rng([seed, zlib.crc32(name.encode())])
+
+
+def _draw(seed, name, shape, kind):
+    g = _rng(seed, name)
+    x = g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+    if kind == "matrix":
+        return bf16_bits(x)                      # uint16 bf16 bits
+    if kind == "gain":
+        return (x + np.float32(1.0)).astype(np.float32)
+    return x.astype(np.float32)
+
+
+def make_weights(cfg: DiTConfig, seed: int = WEIGHT_SEED, blocks=None, threads=None):
+    """dict name -> array. Matrices come as uint16 bf16 bits, the rest as float32."""
+    specs = param_specs(cfg, blocks)
+    threads = threads or min(16, os.cpu_count() or 1)
+    with _cf.ThreadPoolExecutor(threads) as ex:
+        arrs = list(ex.map(lambda s: _draw(seed, *s), specs))
+    return {s[0]: a for s, a in zip(specs, arrs)}
+
+
+def weights_f32(weights: dict) -> dict:
+    """The same weights with every matrix widened to float32 values (exact)."""
+    return {k: (bf16_to_f32(v) if v.dtype == np.uint16 else v) for k, v in weights.items()}
+
+
+def weights_digest(weights: dict) -> str:
+    h = hashlib.sha256()
+    for k in sorted(weights):
+        h.update(k.encode())
+        h.update(np.ascontiguousarray(weights[k]).tobytes())
+    return h.hexdigest()
+
+
+def normal(shape, seed: int) -> np.ndarray:
+    return np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+
+
+def slice_inputs(cfg: DiTConfig, batch: int = 1):
+    """Noise latent [B,C,F,H,W], motion latent [B,C,Fm,H,W], audio tokens [B,La,D].
+
+    Lane b draws from seeds (42, 43, 44) + 100*b, so lane b of a batch equals
+    the single-lane inputs of that lane.
+    """
+    C, F, H, W, Fm = cfg.in_ch, cfg.frames, cfg.height, cfg.width, cfg.motion_frames
+    lat = np.stack([normal((C, F, H, W), NOISE_SEED + LANE_SEED_STRIDE * b) for b in range(batch)])
+    mot = np.stack([normal((C, Fm, H, W), MOTION_SEED + LANE_SEED_STRIDE * b) for b in range(batch)])
+    aud = np.stack([normal((cfg.audio_tokens, cfg.dim), AUDIO_SEED + LANE_SEED_STRIDE * b)
+                    for b in range(batch)])
+    return lat, mot, aud
+
+
+def block_inputs(cfg: DiTConfig, batch: int = 1):
+    """Residual stream x [B,N,D], time embedding e [B,D], audio tokens [B,La,D]."""
+    x = np.stack([normal((cfg.tokens, cfg.dim), RESID_SEED + LANE_SEED_STRIDE * b) for b in range(batch)])
+    e = np.stack([normal((cfg.dim,), TEMB_SEED + LANE_SEED_STRIDE * b) for b in range(batch)])
+    a = np.stack([normal((cfg.audio_tokens, cfg.dim), AUDIO_SEED + LANE_SEED_STRIDE * b)
+                  for b in range(batch)])
+    return x, e, a
