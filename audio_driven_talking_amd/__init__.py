@@ -1,0 +1,282 @@
+"""Python binding of libfh, the MI355X slice denoiser of SoulX-FlashHead Lite.
+
+Thin ctypes marshalling over the C ABI declared in ``include/fh.h``: the
+functions here carry the C names and pass torch tensor pointers, sizes and
+the current HIP stream through; every step of the computation runs in the
+library's HIP kernels. PyTorch supplies device memory and streams only.
+
+The library must have been built (``python -m audio_driven_talking_amd.build``);
+importing this package without ``libfh.so`` raises ImportError -- there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfh.so")
+
+FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHTS = range(7)
+FH_DTYPE_BF16, FH_DTYPE_F32 = 1, 2
+FH_OPT_GRAPH, FH_OPT_TIME_KERNEL = 1, 2
+KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn",
+                  "cross_attn", "layernorm", "rmsnorm_rope"]
+FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
+
+# every symbol include/fh.h declares
+EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_weights_bind",
+           "fh_weights_release", "fh_workspace_bytes", "fh_dit_block_forward",
+           "fh_dit_denoise_slice", "fh_set_option", "fh_kernel_time", "fh_last_error",
+           "fh_status_str"]
+
+
+class fh_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_blocks", "dim", "n_heads", "head_dim", "ffn_dim", "in_ch", "out_ch", "frames", "height",
+        "width", "motion_frames", "audio_per_frame", "freq_dim", "cross_full")] + [
+        ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class fh_tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("offset", ctypes.c_uint64)]
+
+
+class FHError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    # torch first: libfh must bind to the HIP runtime torch already loaded
+    # (same soname), since it receives torch's device pointers and streams.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m audio_driven_talking_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "fh_create": (i32, [ctypes.POINTER(fh_config), ctypes.POINTER(vp)]),
+        "fh_destroy": (None, [vp]),
+        "fh_weight_count": (i32, [vp]),
+        "fh_weight_spec": (i32, [vp, i32, ctypes.POINTER(fh_tensor)]),
+        "fh_weights_bind": (i32, [vp, vp, sz, ctypes.POINTER(fh_tensor), i32, ctypes.POINTER(vp)]),
+        "fh_weights_release": (None, [vp]),
+        "fh_workspace_bytes": (sz, [vp, i32]),
+        "fh_dit_block_forward": (i32, [vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "fh_dit_denoise_slice": (i32, [vp, vp, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_float), i32,
+                                       vp, vp, sz, vp]),
+        "fh_set_option": (i32, [vp, i32, i32]),
+        "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+        "fh_last_error": (ctypes.c_char_p, [vp]),
+        "fh_status_str": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def _check(ctx, status):
+    if status != FH_OK:
+        msg = lib.fh_last_error(ctx).decode() if ctx else lib.fh_status_str(status).decode()
+        raise FHError(status, msg or lib.fh_status_str(status).decode())
+
+
+def _cfg_struct(cfg) -> fh_config:
+    get = (lambda k: cfg[k]) if isinstance(cfg, dict) else (lambda k: getattr(cfg, k))
+    s = fh_config()
+    for n, _ in fh_config._fields_:
+        v = get(n)
+        setattr(s, n, float(v) if n in ("eps", "rope_theta") else int(v))
+    return s
+
+
+class Context:
+    """An fh_ctx*. Destroyed with the object."""
+
+    def __init__(self, handle, cfg):
+        self.handle = handle
+        self.cfg = cfg
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.fh_destroy(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+class Weights:
+    """An fh_weights* plus the device blob it points into (kept alive here)."""
+
+    def __init__(self, handle, blob, ctx):
+        self.handle, self.blob, self.ctx = handle, blob, ctx
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.fh_weights_release(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+def fh_create(cfg) -> Context:
+    """cfg: a mapping or object with the fh_config field names."""
+    h = ctypes.c_void_p()
+    st = lib.fh_create(ctypes.byref(_cfg_struct(cfg)), ctypes.byref(h))
+    if st != FH_OK:
+        raise FHError(st, lib.fh_status_str(st).decode())
+    return Context(h, cfg)
+
+
+def fh_weight_specs(ctx: Context):
+    """[(name, dtype, shape)] the context needs, in its order."""
+    out = []
+    t = fh_tensor()
+    for i in range(lib.fh_weight_count(ctx)):
+        _check(ctx, lib.fh_weight_spec(ctx, i, ctypes.byref(t)))
+        out.append((t.name.decode(), t.dtype, tuple(t.shape[:t.ndim])))
+    return out
+
+
+def _host_bytes(a):
+    """numpy uint16 (bf16 bits) / float32 array, or a torch tensor, as (bytes view, dtype code)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            t = a.detach().contiguous().cpu()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint8), FH_DTYPE_BF16
+            if t.dtype == torch.float32:
+                return t.numpy().view(np.uint8), FH_DTYPE_F32
+            raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a.view(np.uint8).reshape(-1), FH_DTYPE_BF16
+    if a.dtype == np.float32:
+        return a.view(np.uint8).reshape(-1), FH_DTYPE_F32
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def fh_weights_bind(ctx: Context, tensors: dict, device="cuda") -> Weights:
+    """Pack `tensors` (name -> bf16-bits uint16 / float32 arrays or tensors) into
+    one device blob at 256-byte aligned offsets and bind it."""
+    import torch
+    specs = fh_weight_specs(ctx)
+    entries, off = [], 0
+    for name, _, shape in specs:
+        if name not in tensors:
+            raise KeyError(f"weight {name!r} missing")
+        buf, code = _host_bytes(tensors[name])
+        entries.append((name, code, shape, off, buf))
+        off = (off + buf.size + 255) & ~255
+    host = np.zeros(max(off, 256), dtype=np.uint8)
+    for _, _, _, o, buf in entries:
+        host[o:o + buf.size] = buf
+    blob = torch.from_numpy(host).to(device)
+    index = (fh_tensor * len(entries))()
+    names = []
+    for i, (name, code, shape, o, _) in enumerate(entries):
+        nb = name.encode()
+        names.append(nb)
+        index[i].name = nb
+        index[i].dtype = code
+        index[i].ndim = len(shape)
+        for j, s in enumerate(shape):
+            index[i].shape[j] = s
+        index[i].offset = o
+    h = ctypes.c_void_p()
+    _check(ctx, lib.fh_weights_bind(ctx, ctypes.c_void_p(blob.data_ptr()), blob.numel(), index,
+                                    len(entries), ctypes.byref(h)))
+    return Weights(h, blob, ctx)
+
+
+def fh_workspace_bytes(ctx: Context, batch: int) -> int:
+    return int(lib.fh_workspace_bytes(ctx, int(batch)))
+
+
+def workspace(ctx: Context, batch: int, device="cuda"):
+    """A device byte tensor of fh_workspace_bytes(ctx, batch)."""
+    import torch
+    return torch.empty(fh_workspace_bytes(ctx, batch), dtype=torch.uint8, device=device)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+
+
+def _dev_f32(t, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 \
+            or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(ctx):
+    c = ctx.cfg
+    get = (lambda k: c[k]) if isinstance(c, dict) else (lambda k: getattr(c, k))
+    return {k: int(get(k)) for k in ("dim", "in_ch", "frames", "height", "width", "motion_frames",
+                                     "audio_per_frame")}
+
+
+def fh_dit_block_forward(ctx, w, block, x, temb, audio, ws, stream=None):
+    """One DiT block in place on x [B, N, D] (device f32)."""
+    d = _dims(ctx)
+    B = x.shape[0]
+    N, D = d["frames"] * d["height"] * d["width"], d["dim"]
+    _check(ctx, lib.fh_dit_block_forward(
+        ctx, w, int(block), B, _dev_f32(x, (B, N, D), "x"), _dev_f32(temb, (B, D), "temb"),
+        _dev_f32(audio, (B, d["frames"] * d["audio_per_frame"], D), "audio"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+def fh_dit_denoise_slice(ctx, w, latent, motion_latent, audio_tokens, sigmas, latent_out, ws,
+                         stream=None):
+    """Denoise [B, C, F, H, W] latents with len(sigmas)-1 Euler steps (host sigmas)."""
+    d = _dims(ctx)
+    B = latent.shape[0]
+    C, F, H, W = d["in_ch"], d["frames"], d["height"], d["width"]
+    sig = (ctypes.c_float * max(len(sigmas), 1))(*[float(s) for s in sigmas])
+    _check(ctx, lib.fh_dit_denoise_slice(
+        ctx, w, B, _dev_f32(latent, (B, C, F, H, W), "latent"),
+        _dev_f32(motion_latent, (B, C, d["motion_frames"], H, W), "motion_latent"),
+        _dev_f32(audio_tokens, (B, F * d["audio_per_frame"], d["dim"]), "audio_tokens"),
+        sig, len(sigmas) - 1, _dev_f32(latent_out, (B, C, F, H, W), "latent_out"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+def fh_set_option(ctx, option, value):
+    _check(ctx, lib.fh_set_option(ctx, int(option), int(value)))
+
+
+def fh_kernel_time(ctx):
+    """(total ms, launches) of the timed kernel class since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(ctx, lib.fh_kernel_time(ctx, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def fh_last_error(ctx):
+    return lib.fh_last_error(ctx).decode()
+
+
+def fh_status_str(status):
+    return lib.fh_status_str(int(status)).decode()

@@ -1,0 +1,602 @@
+// libfh host runtime: configuration checks, weight binding, workspace carving,
+// the block / slice schedules, HIP graph capture and replay, kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "fh.h"
+#include "fh_kernels.h"
+
+namespace {
+
+struct Spec {
+  std::string name;
+  int dtype;
+  int ndim;
+  int64_t shape[2];
+};
+
+struct WBlock {
+  const bf16_t *qkv_w, *o_w, *cq_w, *ckv_w, *co_w, *ffn1_w, *ffn2_w;
+  const float *mod, *qkv_b, *norm_q, *norm_k, *o_b, *norm3_g, *norm3_b, *cq_b, *ckv_b, *norm_cq,
+      *norm_ck, *co_b, *ffn1_b, *ffn2_b;
+};
+
+struct GraphEntry {
+  std::vector<uint64_t> key;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+struct WS {
+  float* x;
+  bf16_t *h, *qk, *vt, *ao, *qc, *u, *aud, *kc, *vct;
+  float *emb, *t1, *e, *e0, *rcos, *rsin;
+  size_t total;
+};
+
+constexpr int MAX_GRAPHS = 8;
+constexpr int GEMV_ROWS = 8;
+
+}  // namespace
+
+struct fh_weights {
+  fh_ctx* ctx;
+  const bf16_t *time_in_w, *time_out_w, *time_proj_w, *patch_w, *head_w;
+  const float *time_in_b, *time_out_b, *time_proj_b, *patch_b, *head_b, *head_mod;
+  std::vector<WBlock> blk;
+};
+
+struct fh_ctx {
+  fh_config cfg;
+  int N, HW, La;
+  std::vector<Spec> specs;
+  std::string err;
+  bool use_graph = true;
+  int time_class = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_free, ev_pending;
+  double time_ms = 0.0;
+  int64_t time_count = 0;
+  hipStream_t cap_stream = nullptr;
+  std::vector<GraphEntry> graphs;
+};
+
+namespace {
+
+int fail(fh_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return code;
+}
+
+#define FH_HIP(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(c, FH_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+std::vector<Spec> make_specs(const fh_config& g) {
+  const int64_t D = g.dim, Fd = g.ffn_dim, C = g.in_ch, Co = g.out_ch, Fq = g.freq_dim;
+  std::vector<Spec> s;
+  auto mat = [&](const std::string& n, int64_t a, int64_t b) { s.push_back({n, FH_DTYPE_BF16, 2, {a, b}}); };
+  auto vec = [&](const std::string& n, int64_t a) { s.push_back({n, FH_DTYPE_F32, 1, {a, 0}}); };
+  auto tab = [&](const std::string& n, int64_t a, int64_t b) { s.push_back({n, FH_DTYPE_F32, 2, {a, b}}); };
+  mat("time_in.w", D, Fq); vec("time_in.b", D);
+  mat("time_out.w", D, D); vec("time_out.b", D);
+  mat("time_proj.w", 6 * D, D); vec("time_proj.b", 6 * D);
+  mat("patch.w", D, C); vec("patch.b", D);
+  mat("head.w", Co, D); vec("head.b", Co);
+  tab("head.mod", 2, D);
+  for (int i = 0; i < g.n_blocks; ++i) {
+    const std::string p = "blocks." + std::to_string(i) + ".";
+    tab(p + "mod", 6, D);
+    mat(p + "qkv.w", 3 * D, D); vec(p + "qkv.b", 3 * D);
+    vec(p + "norm_q.g", D); vec(p + "norm_k.g", D);
+    mat(p + "o.w", D, D); vec(p + "o.b", D);
+    vec(p + "norm3.g", D); vec(p + "norm3.b", D);
+    mat(p + "cq.w", D, D); vec(p + "cq.b", D);
+    mat(p + "ckv.w", 2 * D, D); vec(p + "ckv.b", 2 * D);
+    vec(p + "norm_cq.g", D); vec(p + "norm_ck.g", D);
+    mat(p + "co.w", D, D); vec(p + "co.b", D);
+    mat(p + "ffn1.w", Fd, D); vec(p + "ffn1.b", Fd);
+    mat(p + "ffn2.w", D, Fd); vec(p + "ffn2.b", D);
+  }
+  return s;
+}
+
+WS carve(const fh_ctx* c, int B, char* base) {
+  const fh_config& g = c->cfg;
+  const size_t N = c->N, D = g.dim, La = c->La, Fd = g.ffn_dim, nb = g.n_blocks;
+  const size_t R = (size_t)(B > 1 ? B : 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  WS w;
+  w.x = (float*)take(B * N * D * 4);
+  w.h = (bf16_t*)take(B * N * D * 2);
+  w.qk = (bf16_t*)take(B * N * 2 * D * 2);
+  w.vt = (bf16_t*)take(B * N * D * 2);
+  w.ao = (bf16_t*)take(B * N * D * 2);
+  w.qc = (bf16_t*)take(B * N * D * 2);
+  w.u = (bf16_t*)take(B * N * Fd * 2);
+  w.aud = (bf16_t*)take(B * La * D * 2);
+  w.kc = (bf16_t*)take(nb * B * La * D * 2);
+  w.vct = (bf16_t*)take(nb * B * La * D * 2);
+  w.emb = (float*)take(R * g.freq_dim * 4);
+  w.t1 = (float*)take(R * D * 4);
+  w.e = (float*)take(R * D * 4);
+  w.e0 = (float*)take(R * 6 * D * 4);
+  w.rcos = (float*)take(N * (g.head_dim / 2) * 4);
+  w.rsin = (float*)take(N * (g.head_dim / 2) * 4);
+  w.total = off;
+  return w;
+}
+
+// -------- kernel timing (events around the launches of one kernel class)
+struct Timed {
+  fh_ctx* c;
+  int cls;
+  hipStream_t s;
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  Timed(fh_ctx* c_, int cls_, hipStream_t s_) : c(c_), cls(cls_), s(s_) {
+    if (c->time_class != cls) return;
+    if (!c->ev_free.empty()) {
+      ev = c->ev_free.back();
+      c->ev_free.pop_back();
+    } else {
+      if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess) {
+        ev = {nullptr, nullptr};
+        return;
+      }
+    }
+    hipEventRecord(ev.first, s);
+  }
+  ~Timed() {
+    if (!ev.first) return;
+    hipEventRecord(ev.second, s);
+    c->ev_pending.push_back(ev);
+  }
+};
+
+size_t slot_elems(const fh_ctx* c, int B) { return (size_t)B * c->La * c->cfg.dim; }
+
+int audio_kv(fh_ctx* c, const WBlock& wb, int B, bf16_t* kc, bf16_t* vct, const WS& ws, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int D = g.dim;
+  fh::EpiArgs ep;
+  ep.bias = wb.ckv_b;
+  ep.out_bf = kc;
+  ep.ldo = D;
+  ep.split = D;
+  ep.out_t = vct;
+  ep.t_cols = D;
+  ep.rows_per_lane = c->La;
+  FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.aud, D, wb.ckv_w, D, B * c->La, 2 * D, D, ep, s));
+  FH_HIP(fh::rmsnorm_rope_bf16(kc, D, B * c->La, D, 1, wb.norm_ck, nullptr, nullptr, nullptr, c->La,
+                               g.head_dim, g.eps, s));
+  return FH_OK;
+}
+
+int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int e0_stride,
+              const bf16_t* kc, const bf16_t* vct, const WS& ws, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int N = c->N, D = g.dim, M = B * N, Fd = g.ffn_dim;
+  const float scale = 1.0f / std::sqrt((float)g.head_dim);
+  {
+    Timed t(c, FH_K_LAYERNORM, s);
+    FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
+                              nullptr, nullptr, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_QKV, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.qkv_b;
+    ep.out_bf = ws.qk;
+    ep.ldo = 2 * D;
+    ep.split = 2 * D;
+    ep.out_t = ws.vt;
+    ep.t_cols = D;
+    ep.rows_per_lane = N;
+    FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
+  }
+  {
+    Timed t(c, FH_K_RMSNORM_ROPE, s);
+    FH_HIP(fh::rmsnorm_rope_bf16(ws.qk, 2 * D, M, D, 2, wb.norm_q, wb.norm_k, ws.rcos, ws.rsin, N,
+                                 g.head_dim, g.eps, s));
+  }
+  {
+    Timed t(c, FH_K_ATTN, s);
+    FH_HIP(fh::flash_attn(ws.qk, 2 * D, ws.qk + D, 2 * D, ws.vt, ws.ao, D, B, N, g.n_heads, scale, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_O, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.o_b;
+    ep.x = x;
+    ep.ldx = D;
+    ep.gate_tab = wb.mod + 2 * D;
+    ep.gate_e0 = e0 + 2 * D;
+    ep.gate_stride = e0_stride;
+    ep.rows_per_lane = N;
+    FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.ao, D, wb.o_w, D, M, D, D, ep, s));
+  }
+  {
+    Timed t(c, FH_K_LAYERNORM, s);
+    FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, nullptr, nullptr, nullptr, nullptr, 0, wb.norm3_g,
+                              wb.norm3_b, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_CQ, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.cq_b;
+    ep.out_bf = ws.qc;
+    ep.ldo = D;
+    FH_HIP(fh::gemm_bf16(fh::EPI_BF16, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
+  }
+  {
+    Timed t(c, FH_K_RMSNORM_ROPE, s);
+    FH_HIP(fh::rmsnorm_rope_bf16(ws.qc, D, M, D, 1, wb.norm_cq, nullptr, nullptr, nullptr, N, g.head_dim,
+                                 g.eps, s));
+  }
+  {
+    Timed t(c, FH_K_CROSS_ATTN, s);
+    FH_HIP(fh::cross_attn(ws.qc, D, kc, D, vct, ws.ao, D, B, N, c->La, c->HW, g.audio_per_frame,
+                          g.cross_full, g.n_heads, scale, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_CO, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.co_b;
+    ep.x = x;
+    ep.ldx = D;
+    FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
+  }
+  {
+    Timed t(c, FH_K_LAYERNORM, s);
+    FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D,
+                              e0 + 4 * D, e0_stride, nullptr, nullptr, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_FFN1, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.ffn1_b;
+    ep.out_bf = ws.u;
+    ep.ldo = Fd;
+    FH_HIP(fh::gemm_bf16(fh::EPI_GELU_BF16, ws.h, D, wb.ffn1_w, D, M, Fd, D, ep, s));
+  }
+  {
+    Timed t(c, FH_K_GEMM_FFN2, s);
+    fh::EpiArgs ep;
+    ep.bias = wb.ffn2_b;
+    ep.x = x;
+    ep.ldx = D;
+    ep.gate_tab = wb.mod + 5 * D;
+    ep.gate_e0 = e0 + 5 * D;
+    ep.gate_stride = e0_stride;
+    ep.rows_per_lane = N;
+    FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ep, s));
+  }
+  return FH_OK;
+}
+
+// The whole slice: audio K/V of every block, motion pin, then per step the
+// time embedding, patch embedding, all blocks and the head + Euler update.
+int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, const float* motion,
+                  const float* audio, const float* sigmas, int n_steps, float* out, const WS& ws,
+                  hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int N = c->N, D = g.dim, C = g.in_ch;
+  const int nmt = g.motion_frames * c->HW;
+  FH_HIP(fh::pin_motion(latent, motion, out, B * C, N, nmt, s));
+  if (n_steps == 0) return FH_OK;
+  FH_HIP(fh::rope_table(ws.rcos, ws.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
+  FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
+  for (int i = 0; i < g.n_blocks; ++i) {
+    int rc = audio_kv(c, w->blk[i], B, ws.kc + i * slot_elems(c, B), ws.vct + i * slot_elems(c, B), ws, s);
+    if (rc) return rc;
+  }
+  for (int st = 0; st < n_steps; ++st) {
+    const float t = 1000.0f * sigmas[st];
+    FH_HIP(fh::sinusoid(ws.emb, &t, 1, g.freq_dim, s));
+    FH_HIP(fh::gemv_bf16(ws.emb, 1, g.freq_dim, w->time_in_w, w->time_in_b, ws.t1, D, 0, 1, s));
+    FH_HIP(fh::gemv_bf16(ws.t1, 1, D, w->time_out_w, w->time_out_b, ws.e, D, 0, 0, s));
+    FH_HIP(fh::gemv_bf16(ws.e, 1, D, w->time_proj_w, w->time_proj_b, ws.e0, 6 * D, 1, 0, s));
+    FH_HIP(fh::patch_embed(out, B, C, N, w->patch_w, w->patch_b, ws.x, D, s));
+    for (int i = 0; i < g.n_blocks; ++i) {
+      int rc = run_block(c, w->blk[i], B, ws.x, ws.e0, 0, ws.kc + i * slot_elems(c, B),
+                         ws.vct + i * slot_elems(c, B), ws, s);
+      if (rc) return rc;
+    }
+    FH_HIP(fh::head_euler(ws.x, B, N, D, g.eps, w->head_mod, ws.e, 0, w->head_w, w->head_b, g.out_ch, out,
+                          out, motion, nmt, sigmas[st + 1] - sigmas[st], s));
+  }
+  return FH_OK;
+}
+
+bool check_ws(fh_ctx* c, int B, void* ws, size_t ws_bytes, int* rc) {
+  const size_t need = carve(c, B, nullptr).total;
+  if (!ws || ((uintptr_t)ws & 255)) {
+    *rc = fail(c, FH_EWORKSPACE, "workspace must be a non-null 256-byte aligned device pointer");
+    return false;
+  }
+  if (ws_bytes < need) {
+    *rc = fail(c, FH_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes batch %d needs",
+               ws_bytes, need, B);
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fh_create(const fh_config* cfg, fh_ctx** out) {
+  if (!out) return FH_EINVAL;
+  *out = nullptr;
+  if (!cfg) return FH_EINVAL;
+  const fh_config& g = *cfg;
+  if (g.n_blocks <= 0 || g.dim <= 0 || g.n_heads <= 0 || g.head_dim <= 0 || g.ffn_dim <= 0 ||
+      g.in_ch <= 0 || g.out_ch <= 0 || g.frames <= 0 || g.height <= 0 || g.width <= 0 ||
+      g.motion_frames < 0 || g.audio_per_frame <= 0 || g.freq_dim <= 0 ||
+      (g.cross_full != 0 && g.cross_full != 1) || !(g.eps > 0.f) || !std::isfinite(g.eps) ||
+      !(g.rope_theta > 1.f) || !std::isfinite(g.rope_theta))
+    return FH_ESHAPE;
+  if (g.dim != g.n_heads * g.head_dim || g.in_ch != g.out_ch || g.motion_frames >= g.frames)
+    return FH_ESHAPE;
+  if (g.head_dim != 128 || g.dim % 128 || g.ffn_dim % 128 || g.dim > 2048 || g.in_ch > 64 ||
+      g.freq_dim % 8 || g.freq_dim * 4 > 65536 || (g.height * g.width) % 32 || g.audio_per_frame % 32)
+    return FH_EUNSUPPORTED;
+  fh_ctx* ctx = new fh_ctx();
+  ctx->cfg = g;
+  ctx->HW = g.height * g.width;
+  ctx->N = g.frames * ctx->HW;
+  ctx->La = g.frames * g.audio_per_frame;
+  ctx->specs = make_specs(g);
+  *out = ctx;
+  return FH_OK;
+}
+
+void fh_destroy(fh_ctx* c) {
+  if (!c) return;
+  for (auto& ge : c->graphs) {
+    if (ge.exec) hipGraphExecDestroy(ge.exec);
+    if (ge.graph) hipGraphDestroy(ge.graph);
+  }
+  for (auto& e : c->ev_free) { hipEventDestroy(e.first); hipEventDestroy(e.second); }
+  for (auto& e : c->ev_pending) { hipEventDestroy(e.first); hipEventDestroy(e.second); }
+  if (c->cap_stream) hipStreamDestroy(c->cap_stream);
+  delete c;
+}
+
+int fh_weight_count(const fh_ctx* c) { return c ? (int)c->specs.size() : 0; }
+
+int fh_weight_spec(const fh_ctx* c, int i, fh_tensor* out) {
+  if (!c || !out || i < 0 || i >= (int)c->specs.size()) return FH_EINVAL;
+  const Spec& s = c->specs[i];
+  std::memset(out, 0, sizeof *out);
+  out->name = s.name.c_str();
+  out->dtype = s.dtype;
+  out->ndim = s.ndim;
+  out->shape[0] = s.shape[0];
+  out->shape[1] = s.shape[1];
+  return FH_OK;
+}
+
+int fh_weights_bind(fh_ctx* c, const void* blob, size_t blob_bytes, const fh_tensor* index, int n_index,
+                    fh_weights** out) {
+  if (!c) return FH_EINVAL;
+  if (!out) return fail(c, FH_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!blob || !index || n_index <= 0) return fail(c, FH_EINVAL, "null blob or empty index");
+  if ((uintptr_t)blob & 15) return fail(c, FH_EWEIGHTS, "blob must be 16-byte aligned");
+  std::unordered_map<std::string, const fh_tensor*> by_name;
+  for (int i = 0; i < n_index; ++i) {
+    if (!index[i].name) return fail(c, FH_EINVAL, "index entry %d has no name", i);
+    by_name[index[i].name] = &index[i];
+  }
+  std::unordered_map<std::string, const void*> ptr;
+  for (const Spec& s : c->specs) {
+    auto it = by_name.find(s.name);
+    if (it == by_name.end()) return fail(c, FH_EWEIGHTS, "weight '%s' missing from the index", s.name.c_str());
+    const fh_tensor& t = *it->second;
+    if (t.dtype != s.dtype)
+      return fail(c, FH_EWEIGHTS, "weight '%s' has dtype %d, expected %d", s.name.c_str(), t.dtype, s.dtype);
+    if (t.ndim != s.ndim || t.shape[0] != s.shape[0] || (s.ndim == 2 && t.shape[1] != s.shape[1]))
+      return fail(c, FH_EWEIGHTS, "weight '%s' has the wrong shape", s.name.c_str());
+    const size_t elems = (size_t)s.shape[0] * (s.ndim == 2 ? (size_t)s.shape[1] : 1);
+    const size_t bytes = elems * (s.dtype == FH_DTYPE_BF16 ? 2 : 4);
+    if (t.offset % 16) return fail(c, FH_EWEIGHTS, "weight '%s' offset is not 16-byte aligned", s.name.c_str());
+    if (t.offset > blob_bytes || bytes > blob_bytes - t.offset)
+      return fail(c, FH_EWEIGHTS, "weight '%s' lies outside the blob", s.name.c_str());
+    ptr[s.name] = (const char*)blob + t.offset;
+  }
+  fh_weights* w = new fh_weights();
+  w->ctx = c;
+  auto M = [&](const std::string& n) { return (const bf16_t*)ptr[n]; };
+  auto V = [&](const std::string& n) { return (const float*)ptr[n]; };
+  w->time_in_w = M("time_in.w"); w->time_in_b = V("time_in.b");
+  w->time_out_w = M("time_out.w"); w->time_out_b = V("time_out.b");
+  w->time_proj_w = M("time_proj.w"); w->time_proj_b = V("time_proj.b");
+  w->patch_w = M("patch.w"); w->patch_b = V("patch.b");
+  w->head_w = M("head.w"); w->head_b = V("head.b"); w->head_mod = V("head.mod");
+  for (int i = 0; i < c->cfg.n_blocks; ++i) {
+    const std::string p = "blocks." + std::to_string(i) + ".";
+    WBlock b;
+    b.mod = V(p + "mod");
+    b.qkv_w = M(p + "qkv.w"); b.qkv_b = V(p + "qkv.b");
+    b.norm_q = V(p + "norm_q.g"); b.norm_k = V(p + "norm_k.g");
+    b.o_w = M(p + "o.w"); b.o_b = V(p + "o.b");
+    b.norm3_g = V(p + "norm3.g"); b.norm3_b = V(p + "norm3.b");
+    b.cq_w = M(p + "cq.w"); b.cq_b = V(p + "cq.b");
+    b.ckv_w = M(p + "ckv.w"); b.ckv_b = V(p + "ckv.b");
+    b.norm_cq = V(p + "norm_cq.g"); b.norm_ck = V(p + "norm_ck.g");
+    b.co_w = M(p + "co.w"); b.co_b = V(p + "co.b");
+    b.ffn1_w = M(p + "ffn1.w"); b.ffn1_b = V(p + "ffn1.b");
+    b.ffn2_w = M(p + "ffn2.w"); b.ffn2_b = V(p + "ffn2.b");
+    w->blk.push_back(b);
+  }
+  *out = w;
+  return FH_OK;
+}
+
+void fh_weights_release(fh_weights* w) { delete w; }
+
+size_t fh_workspace_bytes(const fh_ctx* c, int batch) {
+  if (!c || batch <= 0) return 0;
+  return carve(c, batch, nullptr).total;
+}
+
+int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, float* x, const float* temb,
+                         const float* audio, void* ws, size_t ws_bytes, void* stream) {
+  if (!c) return FH_EINVAL;
+  if (!w || w->ctx != c) return fail(c, FH_EINVAL, "weights are null or bound to another context");
+  if (batch <= 0) return fail(c, FH_EINVAL, "batch must be positive, got %d", batch);
+  if (block < 0 || block >= c->cfg.n_blocks)
+    return fail(c, FH_EINVAL, "block %d outside [0, %d)", block, c->cfg.n_blocks);
+  if (!x || !temb || !audio) return fail(c, FH_EINVAL, "null x, temb or audio");
+  int rc = FH_OK;
+  if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const fh_config& g = c->cfg;
+  const int D = g.dim;
+  WS wsp = carve(c, batch, (char*)ws);
+  FH_HIP(fh::rope_table(wsp.rcos, wsp.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
+  FH_HIP(fh::f32_to_bf16(audio, wsp.aud, (int64_t)batch * c->La * D, s));
+  rc = audio_kv(c, w->blk[block], batch, wsp.kc, wsp.vct, wsp, s);
+  if (rc) return rc;
+  for (int r0 = 0; r0 < batch; r0 += GEMV_ROWS) {
+    const int R = batch - r0 < GEMV_ROWS ? batch - r0 : GEMV_ROWS;
+    FH_HIP(fh::gemv_bf16(temb + (size_t)r0 * D, R, D, w->time_proj_w, w->time_proj_b,
+                         wsp.e0 + (size_t)r0 * 6 * D, 6 * D, 1, 0, s));
+  }
+  return run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s);
+}
+
+int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float* latent,
+                         const float* motion_latent, const float* audio_tokens, const float* sigmas,
+                         int n_steps, float* latent_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!c) return FH_EINVAL;
+  if (!w || w->ctx != c) return fail(c, FH_EINVAL, "weights are null or bound to another context");
+  if (batch <= 0) return fail(c, FH_EINVAL, "batch must be positive, got %d", batch);
+  if (n_steps < 0) return fail(c, FH_EINVAL, "n_steps must be >= 0, got %d", n_steps);
+  if (!latent || !latent_out || (!motion_latent && c->cfg.motion_frames > 0) || !audio_tokens ||
+      (!sigmas && n_steps > 0))
+    return fail(c, FH_EINVAL, "null latent, motion, audio, sigmas or output pointer");
+  for (int i = 0; i <= n_steps && n_steps > 0; ++i)
+    if (!std::isfinite(sigmas[i])) return fail(c, FH_EINVAL, "sigma[%d] is not finite", i);
+  int rc = FH_OK;
+  if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  WS wsp = carve(c, batch, (char*)ws);
+
+  if (!c->use_graph || c->time_class >= 0)
+    return enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, sigmas, n_steps, latent_out, wsp, s);
+
+  std::vector<uint64_t> key = {(uint64_t)(uintptr_t)w, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
+                               (uint64_t)(uintptr_t)motion_latent, (uint64_t)(uintptr_t)audio_tokens,
+                               (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
+                               (uint64_t)n_steps};
+  for (int i = 0; i <= n_steps && n_steps > 0; ++i) {
+    uint32_t b;
+    std::memcpy(&b, &sigmas[i], 4);
+    key.push_back(b);
+  }
+  for (auto& ge : c->graphs)
+    if (ge.key == key) {
+      FH_HIP(hipGraphLaunch(ge.exec, s));
+      return FH_OK;
+    }
+  if (!c->cap_stream) FH_HIP(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+  FH_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+  rc = enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, sigmas, n_steps, latent_out, wsp,
+                     c->cap_stream);
+  hipGraph_t graph = nullptr;
+  hipError_t ce = hipStreamEndCapture(c->cap_stream, &graph);
+  if (rc != FH_OK) {
+    if (graph) hipGraphDestroy(graph);
+    return rc;
+  }
+  if (ce != hipSuccess) return fail(c, FH_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(ce));
+  hipGraphExec_t exec = nullptr;
+  hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (ie != hipSuccess) {
+    hipGraphDestroy(graph);
+    return fail(c, FH_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(ie));
+  }
+  if ((int)c->graphs.size() >= MAX_GRAPHS) {
+    hipGraphExecDestroy(c->graphs.front().exec);
+    hipGraphDestroy(c->graphs.front().graph);
+    c->graphs.erase(c->graphs.begin());
+  }
+  c->graphs.push_back({key, graph, exec});
+  FH_HIP(hipGraphLaunch(exec, s));
+  return FH_OK;
+}
+
+int fh_set_option(fh_ctx* c, int option, int value) {
+  if (!c) return FH_EINVAL;
+  if (option == FH_OPT_GRAPH) {
+    c->use_graph = value != 0;
+    return FH_OK;
+  }
+  if (option == FH_OPT_TIME_KERNEL) {
+    if (value < -1 || value >= FH_K_COUNT) return fail(c, FH_EINVAL, "unknown kernel class %d", value);
+    c->time_class = value;
+    return FH_OK;
+  }
+  return fail(c, FH_EINVAL, "unknown option %d", option);
+}
+
+int fh_kernel_time(fh_ctx* c, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return FH_EINVAL;
+  for (auto& e : c->ev_pending) {
+    FH_HIP(hipEventSynchronize(e.second));
+    float ms = 0.f;
+    FH_HIP(hipEventElapsedTime(&ms, e.first, e.second));
+    c->time_ms += ms;
+    c->time_count += 1;
+    c->ev_free.push_back(e);
+  }
+  c->ev_pending.clear();
+  *total_ms = c->time_ms;
+  *launches = c->time_count;
+  c->time_ms = 0.0;
+  c->time_count = 0;
+  return FH_OK;
+}
+
+const char* fh_last_error(const fh_ctx* c) {
+  if (!c) return "null context";
+  return c->err.c_str();
+}
+
+const char* fh_status_str(int st) {
+  switch (st) {
+    case FH_OK: return "ok";
+    case FH_EINVAL: return "invalid argument";
+    case FH_ESHAPE: return "shape does not match the configuration";
+    case FH_EUNSUPPORTED: return "configuration not implemented by the kernels";
+    case FH_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case FH_EHIP: return "HIP runtime error";
+    case FH_EWEIGHTS: return "weight tensor missing, misaligned or of the wrong dtype/shape";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

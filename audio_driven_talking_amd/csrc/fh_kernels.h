@@ -1,0 +1,94 @@
+// Host-side launchers of the libfh HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+
+namespace fh {
+
+// Epilogues of the bf16 GEMM C[M,N] = A[M,K] * W[N,K]^T (+ bias[N]).
+enum Epi {
+  EPI_BF16 = 0,       // out_bf[m, n] = bf16(C + bias)
+  EPI_GELU_BF16 = 1,  // out_bf[m, n] = bf16(gelu_tanh(C + bias))
+  EPI_GATED_RES = 2,  // x[m, n] += gate[lane(m), n] * (C + bias)
+  EPI_RES = 3,        // x[m, n] += C + bias
+  EPI_SPLIT_T = 4,    // n < split: out_bf[m, n] = bf16(C + bias);
+                      // n >= split: out_t[lane][n - split][m mod rows] = bf16(C + bias)
+};
+
+struct EpiArgs {
+  const float* bias = nullptr;
+  bf16_t* out_bf = nullptr;
+  int ldo = 0;
+  float* x = nullptr;
+  int ldx = 0;
+  const float* gate_tab = nullptr;  // [N] table row
+  const float* gate_e0 = nullptr;   // [lanes, gate_stride] adds (row offset applied by caller)
+  int gate_stride = 0;
+  int rows_per_lane = 1;            // rows of one batch lane (tokens)
+  bf16_t* out_t = nullptr;         // [lanes, t_cols, rows_per_lane]
+  int split = 0;
+  int t_cols = 0;                   // N - split
+};
+
+hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                     const EpiArgs& ep, hipStream_t s);
+
+// LayerNorm of fp32 rows (width D) to bf16. Modulated form (g == nullptr):
+//   out = LN(x) * (1 + tab_scale + e_scale[lane]) + tab_shift + e_shift[lane]
+// Affine form: out = LN(x) * g + b.
+hipError_t layernorm_bf16(const float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
+                          const float* tab_shift, const float* tab_scale, const float* e_shift,
+                          const float* e_scale, int e_stride, const float* g, const float* b,
+                          hipStream_t s);
+
+// In-place RMSNorm over the first D columns of bf16 rows (stride ld), gain g0;
+// with nparts == 2 also columns [D, 2D) with gain g1. If cos_t != nullptr the
+// normalised values are rotated pairwise: pair j of a head (adjacent dims)
+// turns by the angle table [tokens, head_dim/2] row (row mod rows_per_lane).
+hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, const float* g0,
+                             const float* g1, const float* cos_t, const float* sin_t,
+                             int rows_per_lane, int head_dim, float eps, hipStream_t s);
+
+// softmax(q k^T * scale) v over all N keys of the same lane; q/k rows of
+// stride ldq/ldk (head h at column h*128), values transposed vt[lane][D][N].
+hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const bf16_t* vt,
+                      bf16_t* o, int ldo, int B, int N, int n_heads, float scale, hipStream_t s);
+
+// Audio cross-attention with short key ranges: queries of latent frame f =
+// row / hw see keys [f*apf, f*apf + apf) (full != 0: all La keys).
+hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const bf16_t* vct,
+                      bf16_t* o, int ldo, int B, int N, int La, int hw, int apf, int full,
+                      int n_heads, float scale, hipStream_t s);
+
+// Rotary angle tables [N, head_dim/2] (cos, sin), computed in float64.
+hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,
+                      hipStream_t s);
+
+// Sinusoidal timestep embedding of R timesteps t[r] ([R, dim]).
+hipError_t sinusoid(float* out, const float* t_host, int R, int dim, hipStream_t s);
+
+// y[r, n] = act_out(sum_k act_in(x[r, k]) W[n, k] + b[n]); act: 0 none, 1 SiLU.
+hipError_t gemv_bf16(const float* x, int R, int K, const bf16_t* W, const float* b, float* y, int N,
+                     int act_in, int act_out, hipStream_t s);
+
+// x[lane, n, :] = W_p latent[lane, :, n] + b_p  (latent [B, C, N] fp32).
+hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, const float* bp,
+                       float* x, int D, hipStream_t s);
+
+// Output head and Euler update, one token per wave:
+//   v = (LN(x)(1 + head_mod[1] + e) + head_mod[0] + e) W_h^T + b_h
+//   lat_next = token in a motion frame ? motion : lat_cur + dsig * v
+hipError_t head_euler(const float* x, int B, int N, int D, float eps, const float* head_mod,
+                      const float* e, int e_stride, const bf16_t* Wh, const float* bh, int Co,
+                      const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
+                      float dsig, hipStream_t s);
+
+// out = latent with the first n_motion_tok tokens of every (lane, channel) from motion.
+hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC, int N,
+                      int n_motion_tok, hipStream_t s);
+
+hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s);
+
+}  // namespace fh

@@ -1,0 +1,252 @@
+// Small kernels of the slice denoiser: rotary angle tables, timestep
+// sinusoid, the time-MLP GEMVs, patch embedding, the fused output head +
+// Euler update + motion pin, and conversions. All are HBM- or launch-bound.
+#include "fh_common.h"
+#include "fh_kernels.h"
+
+namespace fh {
+namespace {
+
+__global__ void rope_table_kernel(float* __restrict__ cos_t, float* __restrict__ sin_t, int F, int H,
+                                  int W, int half, int nf, int nr, double theta) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_tok = (int64_t)F * H * W;
+  if (i >= n_tok * half) return;
+  const int tok = (int)(i / half), j = (int)(i % half);
+  const int f = tok / (H * W), r = (tok / W) % H, c = tok % W;
+  int pos, jl, n;
+  if (j < nf) {
+    pos = f; jl = j; n = nf;
+  } else if (j < nf + nr) {
+    pos = r; jl = j - nf; n = nr;
+  } else {
+    pos = c; jl = j - nf - nr; n = half - nf - nr;
+  }
+  const double a = (double)pos * pow(theta, -(double)jl / (double)n);
+  cos_t[i] = (float)cos(a);
+  sin_t[i] = (float)sin(a);
+}
+
+constexpr int MAXR = 8;
+struct Times {
+  float t[MAXR];
+};
+
+__global__ void sinusoid_kernel(float* __restrict__ out, Times ts, int R, int dim) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= R * dim) return;
+  const int r = i / dim, k = i % dim, half = dim / 2;
+  const int kk = k < half ? k : k - half;
+  const double a = (double)ts.t[r] * pow(10000.0, -(double)kk / (double)half);
+  out[i] = (float)(k < half ? cos(a) : sin(a));
+}
+
+// 16 outputs per 256-thread workgroup (4 per wave); the R input rows sit in LDS.
+__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int R, int K,
+                                                   const bf16_t* __restrict__ W,
+                                                   const float* __restrict__ b, float* __restrict__ y,
+                                                   int N, int act_in, int act_out) {
+  extern __shared__ float sx[];
+  for (int i = threadIdx.x; i < R * K; i += 256) {
+    float v = x[i];
+    sx[i] = act_in ? silu(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 0; o < 4; ++o) {
+    const int n = blockIdx.x * 16 + wave * 4 + o;
+    if (n >= N) break;
+    float acc[MAXR];
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) acc[r] = 0.f;
+    const u16x8* wr = reinterpret_cast<const u16x8*>(W + (int64_t)n * K);
+    for (int kc = lane; kc < K / 8; kc += 64) {
+      const u16x8 w = wr[kc];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wf = bf2f(w[e]);
+#pragma unroll
+        for (int r = 0; r < MAXR; ++r)
+          if (r < R) acc[r] += wf * sx[r * K + kc * 8 + e];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r)
+      if (r < R) {
+        const float s = wave_sum(acc[r]);
+        if (lane == 0) {
+          const float v = s + b[n];
+          y[(int64_t)r * N + n] = act_out ? silu(v) : v;
+        }
+      }
+  }
+}
+
+constexpr int PT = 16;  // tokens per patch-embed workgroup
+constexpr int MAXC = 64;
+
+__global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restrict__ lat, int C, int N,
+                                                          const bf16_t* __restrict__ Wp,
+                                                          const float* __restrict__ bp,
+                                                          float* __restrict__ x, int D) {
+  __shared__ float sl[MAXC * PT];
+  const int b = blockIdx.y, t0 = blockIdx.x * PT;
+  for (int i = threadIdx.x; i < C * PT; i += 256) {
+    const int c = i / PT, tt = i % PT;
+    sl[i] = t0 + tt < N ? lat[((int64_t)b * C + c) * N + t0 + tt] : 0.f;
+  }
+  __syncthreads();
+  const int d4n = D / 4;
+  for (int item = threadIdx.x; item < PT * d4n; item += 256) {
+    const int tt = item / d4n, d = (item % d4n) * 4;
+    if (t0 + tt >= N) continue;
+    float4 acc = *reinterpret_cast<const float4*>(bp + d);
+    for (int c = 0; c < C; ++c) {
+      const float l = sl[c * PT + tt];
+      acc.x += bf2f(Wp[(d + 0) * C + c]) * l;
+      acc.y += bf2f(Wp[(d + 1) * C + c]) * l;
+      acc.z += bf2f(Wp[(d + 2) * C + c]) * l;
+      acc.w += bf2f(Wp[(d + 3) * C + c]) * l;
+    }
+    *reinterpret_cast<float4*>(x + ((int64_t)b * N + t0 + tt) * D + d) = acc;
+  }
+}
+
+constexpr int MAXV4 = 8;
+
+__global__ __launch_bounds__(256) void head_euler_kernel(
+    const float* __restrict__ x, int B, int N, int D, float eps, const float* __restrict__ hmod,
+    const float* __restrict__ e, int e_stride, const bf16_t* __restrict__ Wh,
+    const float* __restrict__ bh, int Co, const float* lat_cur, float* lat_next,
+    const float* __restrict__ motion, int nmt, float dsig) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= B * N) return;
+  const int b = row / N, tok = row % N;
+  const int nv = D >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * D);
+  float4 v[MAXV4];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV4; ++i)
+    if (i * 64 + lane < nv) {
+      v[i] = xr[i * 64 + lane];
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV4; ++i)
+    if (i * 64 + lane < nv) {
+      float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + bb * bb) + (c * c + d * d);
+    }
+  const float rstd = rsqrtf(wave_sum(q) / (float)D + eps);
+  const float* eb = e + (int64_t)b * e_stride;
+#pragma unroll
+  for (int i = 0; i < MAXV4; ++i)
+    if (i * 64 + lane < nv) {
+      const int col = (i * 64 + lane) * 4;
+      const float4 sh = *reinterpret_cast<const float4*>(hmod + col);
+      const float4 sc = *reinterpret_cast<const float4*>(hmod + D + col);
+      const float4 ee = *reinterpret_cast<const float4*>(eb + col);
+      v[i].x = (v[i].x - mean) * rstd * (1.f + sc.x + ee.x) + sh.x + ee.x;
+      v[i].y = (v[i].y - mean) * rstd * (1.f + sc.y + ee.y) + sh.y + ee.y;
+      v[i].z = (v[i].z - mean) * rstd * (1.f + sc.z + ee.z) + sh.z + ee.z;
+      v[i].w = (v[i].w - mean) * rstd * (1.f + sc.w + ee.w) + sh.w + ee.w;
+    }
+  float mine = 0.f;
+  for (int co = 0; co < Co; ++co) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV4; ++i)
+      if (i * 64 + lane < nv) {
+        const int col = (i * 64 + lane) * 4;
+        const u16x4 w = *reinterpret_cast<const u16x4*>(Wh + (int64_t)co * D + col);
+        p += v[i].x * bf2f(w[0]) + v[i].y * bf2f(w[1]) + v[i].z * bf2f(w[2]) + v[i].w * bf2f(w[3]);
+      }
+    p = wave_sum(p);
+    if (lane == co) mine = p;
+  }
+  if (lane < Co) {
+    const int64_t idx = ((int64_t)b * Co + lane) * N + tok;
+    if (tok < nmt)
+      lat_next[idx] = motion[((int64_t)b * Co + lane) * nmt + tok];
+    else
+      lat_next[idx] = lat_cur[idx] + dsig * (mine + bh[lane]);
+  }
+}
+
+__global__ void pin_motion_kernel(const float* __restrict__ lat, const float* __restrict__ motion,
+                                  float* __restrict__ out, int64_t total, int N, int nmt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t bc = i / N;
+  const int t = (int)(i % N);
+  out[i] = t < nmt ? motion[bc * nmt + t] : lat[i];
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ in, bf16_t* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f2bf(in[i]);
+}
+
+}  // namespace
+
+hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,
+                      hipStream_t s) {
+  const int half = head_dim / 2, nr = head_dim / 6, nf = half - 2 * nr;
+  const int64_t total = (int64_t)F * H * W * half;
+  rope_table_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(cos_t, sin_t, F, H, W, half, nf, nr,
+                                                                   theta);
+  return hipGetLastError();
+}
+
+hipError_t sinusoid(float* out, const float* t_host, int R, int dim, hipStream_t s) {
+  if (R <= 0 || R > MAXR || dim % 2) return hipErrorInvalidValue;
+  Times ts{};
+  for (int r = 0; r < R; ++r) ts.t[r] = t_host[r];
+  sinusoid_kernel<<<(R * dim + 255) / 256, 256, 0, s>>>(out, ts, R, dim);
+  return hipGetLastError();
+}
+
+hipError_t gemv_bf16(const float* x, int R, int K, const bf16_t* W, const float* b, float* y, int N,
+                     int act_in, int act_out, hipStream_t s) {
+  if (R <= 0 || R > MAXR || K % 8 || (size_t)R * K * 4 > 65536) return hipErrorInvalidValue;
+  gemv_kernel<<<(N + 15) / 16, 256, (size_t)R * K * 4, s>>>(x, R, K, W, b, y, N, act_in, act_out);
+  return hipGetLastError();
+}
+
+hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, const float* bp,
+                       float* x, int D, hipStream_t s) {
+  if (C > MAXC || D % 4) return hipErrorInvalidValue;
+  dim3 grid((N + PT - 1) / PT, B);
+  patch_embed_kernel<<<grid, 256, 0, s>>>(lat, C, N, Wp, bp, x, D);
+  return hipGetLastError();
+}
+
+hipError_t head_euler(const float* x, int B, int N, int D, float eps, const float* head_mod,
+                      const float* e, int e_stride, const bf16_t* Wh, const float* bh, int Co,
+                      const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
+                      float dsig, hipStream_t s) {
+  if (D % 4 || D > 256 * MAXV4 || Co > 64) return hipErrorInvalidValue;
+  head_euler_kernel<<<(B * N + 3) / 4, 256, 0, s>>>(x, B, N, D, eps, head_mod, e, e_stride, Wh, bh, Co,
+                                                    lat_cur, lat_next, motion, n_motion_tok, dsig);
+  return hipGetLastError();
+}
+
+hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC, int N,
+                      int n_motion_tok, hipStream_t s) {
+  const int64_t total = (int64_t)BC * N;
+  pin_motion_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(lat, motion, out, total, N,
+                                                                   n_motion_tok);
+  return hipGetLastError();
+}
+
+hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  f32_to_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace fh

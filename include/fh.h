@@ -1,0 +1,177 @@
+/*
+ * fh.h -- C ABI of libfh, the MI355X (gfx950) slice denoiser of SoulX-FlashHead Lite.
+ *
+ * What it computes (gizai:flashhead reference page, overview paragraph): a
+ * Wan-style transformer -- 30 blocks of width 1536, 12 heads, rotary over
+ * frame, row and column -- predicts the flow of one slice's noisy video latent
+ * (5 latent frames of 16x16), whose first latent frames are the motion of the
+ * previous slice, in 4 steps, conditioned on 5 latent frames of 32 audio
+ * tokens. The same page's FlashHead type lists the parameters the library
+ * binds: per-block weights, the `patch` and `head` Linear layers, the output
+ * norm's per-step shift/scale (`headMods`) and the rotary tables (`cos`,
+ * `sin`). The audio-cpp page "SoulX-FlashHead", section "Generate", gives the
+ * 4 denoising steps; its section "Variant boundaries" says the transformer
+ * dimensions come from a configuration (here fh_config) and that an
+ * unavailable implementation is rejected rather than substituted (here:
+ * unsupported sizes return FH_EUNSUPPORTED, never a fallback).
+ *
+ * Conventions for every call:
+ *  - All device pointers are caller-owned HIP device memory (inputs, outputs,
+ *    weights, workspace). The library never allocates device memory.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Calls
+ *    enqueue work on it and return; kernel faults surface at the caller's
+ *    next synchronisation.
+ *  - A context is not thread-safe: use one per host thread / stream.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - On error a call returns an FH_E* code, enqueues nothing, and
+ *    fh_last_error() describes the problem.
+ */
+#ifndef FH_H
+#define FH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FH_OK = 0,
+  FH_EINVAL = 1,        /* null pointer, batch <= 0, n_steps < 0, non-finite sigma, bad block index */
+  FH_ESHAPE = 2,        /* a size or weight shape that does not match the configuration */
+  FH_EUNSUPPORTED = 3,  /* a configuration the kernels do not implement (e.g. head_dim != 128) */
+  FH_EWORKSPACE = 4,    /* workspace pointer null/misaligned or smaller than fh_workspace_bytes() */
+  FH_EHIP = 5,          /* a HIP runtime error; its text is kept in fh_last_error() */
+  FH_EWEIGHTS = 6       /* a required weight tensor is missing, misaligned or of the wrong dtype */
+};
+
+enum { FH_DTYPE_BF16 = 1, FH_DTYPE_F32 = 2 };
+
+/* Sizes of the DiT and of one slice latent. Every dimension is a runtime value
+ * (audio-cpp page, "Variant boundaries"). The kernels implement:
+ *   head_dim == 128, dim == n_heads * 128, dim % 128 == 0, ffn_dim % 128 == 0,
+ *   dim <= 2048, in_ch == out_ch <= 64, freq_dim % 8 == 0, frames*height*width
+ *   a multiple of 32, height*width a multiple of 32, audio_per_frame a
+ *   multiple of 32, 0 <= motion_frames < frames.                                */
+typedef struct fh_config {
+  int32_t n_blocks;         /* 30 for Lite */
+  int32_t dim;              /* model width D, 1536 */
+  int32_t n_heads;          /* 12 */
+  int32_t head_dim;         /* 128 */
+  int32_t ffn_dim;          /* 8960 */
+  int32_t in_ch, out_ch;    /* latent channels C, 16 */
+  int32_t frames;           /* latent frames F, 5 */
+  int32_t height, width;    /* latent rows and columns, 16 x 16 at 512 x 512 */
+  int32_t motion_frames;    /* latent frames pinned to the previous slice's motion, 2 */
+  int32_t audio_per_frame;  /* audio tokens per latent frame, 32 */
+  int32_t freq_dim;         /* sinusoidal timestep embedding width, 256 */
+  int32_t cross_full;       /* 0: a token attends to its latent frame's audio tokens; 1: to all */
+  float eps;                /* LayerNorm / RMSNorm epsilon, 1e-6 */
+  float rope_theta;         /* rotary base, 1e4 */
+} fh_config;
+
+/* One entry of a weight index: a tensor inside the caller's device blob. */
+typedef struct fh_tensor {
+  const char* name;   /* e.g. "blocks.3.qkv.w" (see fh_weight_spec) */
+  int32_t dtype;      /* FH_DTYPE_BF16 for matrices, FH_DTYPE_F32 for the rest */
+  int32_t ndim;       /* 1 or 2 */
+  int64_t shape[4];
+  uint64_t offset;    /* bytes from the blob start; multiple of 16 */
+} fh_tensor;
+
+typedef struct fh_ctx fh_ctx;
+typedef struct fh_weights fh_weights;
+
+/* Validate cfg and make a context. Builds no device state and allocates no
+ * device memory. Returns FH_EINVAL (null), FH_ESHAPE (inconsistent sizes) or
+ * FH_EUNSUPPORTED (sizes the kernels do not implement); *out is NULL then.  */
+int fh_create(const fh_config* cfg, fh_ctx** out);
+
+/* Free the context and everything it caches (captured graphs). */
+void fh_destroy(fh_ctx* ctx);
+
+/* Number of weight tensors the configuration needs, and the i-th one's name,
+ * dtype and shape (offset 0). Matrices are stored [out, in] row-major bf16;
+ * biases, gains and modulation tables are f32. Returns FH_EINVAL for a bad i.
+ * Names: time_in.{w,b} [D,freq_dim], time_out.{w,b} [D,D], time_proj.{w,b}
+ * [6D,D], patch.{w,b} [D,C], head.{w,b} [C,D], head.mod [2,D] (shift, scale),
+ * and per block i "blocks.i.": mod [6,D] (shift, scale, gate of the
+ * self-attention branch, then of the FFN branch), qkv.{w,b} [3D,D] (rows q,
+ * k, v), norm_q.g, norm_k.g [D], o.{w,b} [D,D], norm3.{g,b} [D], cq.{w,b}
+ * [D,D], ckv.{w,b} [2D,D] (rows audio k, then v), norm_cq.g, norm_ck.g [D],
+ * co.{w,b} [D,D], ffn1.{w,b} [ffn_dim,D], ffn2.{w,b} [D,ffn_dim].            */
+int fh_weight_count(const fh_ctx* ctx);
+int fh_weight_spec(const fh_ctx* ctx, int i, fh_tensor* out);
+
+/* Bind a caller-owned device blob holding every tensor of fh_weight_spec at
+ * the offsets given by `index` (n_index entries, any order). No copy is made:
+ * the blob must outlive the returned handle. Every tensor is checked for
+ * presence, dtype, shape, 16-byte alignment and bounds (FH_EWEIGHTS).       */
+int fh_weights_bind(fh_ctx* ctx, const void* dev_blob, size_t blob_bytes, const fh_tensor* index,
+                    int n_index, fh_weights** out);
+void fh_weights_release(fh_weights* w);
+
+/* Device workspace (bytes, 256-byte aligned start required) for a batch of
+ * `batch` independent lanes: activations, the audio keys/values of every
+ * block, the rotary tables and the time embedding (the FlashHead type's
+ * `work` scratch). 0 for batch <= 0 or a null ctx.                           */
+size_t fh_workspace_bytes(const fh_ctx* ctx, int batch);
+
+/* One DiT block (block index `block`) on the residual stream, in place.
+ *   x      device f32 [batch, N, D], N = frames*height*width, tokens in
+ *          (frame, row, column) order; read and overwritten.
+ *   temb   device f32 [batch, D]: the time embedding e; the block's
+ *          modulation is its table + time_proj(SiLU(e)) split in six rows.
+ *   audio  device f32 [batch, frames*audio_per_frame, D], frame-major.
+ * Computes: x += gate_sa * O(SelfAttn(RoPE(RMSNorm q/k), LN(x) modulated));
+ *           x += CrossO(CrossAttn(LN_affine(x), audio));
+ *           x += gate_ff * FFN_gelu_tanh(LN(x) modulated).
+ * Errors: FH_EINVAL, FH_EWORKSPACE, FH_EHIP.                                 */
+int fh_dit_block_forward(fh_ctx* ctx, const fh_weights* w, int block, int batch, float* x,
+                         const float* temb, const float* audio, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Denoise one slice of each of `batch` lanes with n_steps flow-matching Euler
+ * steps (gizai:flashhead page, overview; audio-cpp page "Generate": 4 steps).
+ *   latent         device f32 [batch, C, F, H, W]: the noisy latent.
+ *   motion_latent  device f32 [batch, C, motion_frames, H, W]: the previous
+ *                  slice's motion; written into latent frames [0, motion_frames)
+ *                  before the first step and after every step (bitwise).
+ *   audio_tokens   device f32 [batch, F*audio_per_frame, D].
+ *   sigmas         HOST f32 [n_steps + 1], finite; step i uses timestep
+ *                  1000*sigmas[i] and moves the latent by
+ *                  (sigmas[i+1] - sigmas[i]) * flow.
+ *   latent_out     device f32 [batch, C, F, H, W]; may alias `latent`.
+ * n_steps == 0 returns the motion-pinned input. The call enqueues the whole
+ * denoise (a captured HIP graph is replayed when graphs are enabled).
+ * Errors: FH_EINVAL, FH_EWORKSPACE, FH_EHIP.                                 */
+int fh_dit_denoise_slice(fh_ctx* ctx, const fh_weights* w, int batch, const float* latent,
+                         const float* motion_latent, const float* audio_tokens, const float* sigmas,
+                         int n_steps, float* latent_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Execution options of a context.
+ *   FH_OPT_GRAPH: 1 (default) capture fh_dit_denoise_slice into a HIP graph
+ *     per (batch, pointers, sigmas) and replay it; 0 launch kernels directly.
+ *   FH_OPT_TIME_KERNEL: a kernel class (FH_K_*) to time with HIP events on the
+ *     call's stream around each of its launches (forces direct launches);
+ *     -1 (default) times nothing. fh_kernel_time reads and resets the sums. */
+enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2 };
+enum {
+  FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
+  FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,
+  FH_K_COUNT = 10
+};
+int fh_set_option(fh_ctx* ctx, int option, int value);
+/* Total milliseconds and number of timed launches since the last read.      */
+int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
+
+/* Human-readable text of the last error on ctx (never NULL), and of a code.  */
+const char* fh_last_error(const fh_ctx* ctx);
+const char* fh_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FH_H */

@@ -1,0 +1,157 @@
+"""The C ABI on the host: exports, configuration checks, weight index checks and
+argument validation. Nothing here launches a kernel, so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+fh = pytest.importorskip("audio_driven_talking_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "fh.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fh_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 13
+    assert sorted(fh.EXPORTS) == names
+    lib = ctypes.CDLL(fh.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg_dict(name="slice", **kw):
+    c = synth.CONFIGS[name]
+    d = {f: getattr(c, f) for f in ("n_blocks", "dim", "n_heads", "head_dim", "ffn_dim", "in_ch",
+                                    "out_ch", "frames", "height", "width", "motion_frames",
+                                    "audio_per_frame", "freq_dim", "eps", "rope_theta")}
+    d["cross_full"] = int(c.cross_full)
+    d.update(kw)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64, n_heads=24), fh.FH_EUNSUPPORTED),
+    (dict(n_heads=11), fh.FH_ESHAPE),
+    (dict(motion_frames=5), fh.FH_ESHAPE),
+    (dict(out_ch=8), fh.FH_ESHAPE),
+    (dict(height=15), fh.FH_EUNSUPPORTED),
+    (dict(audio_per_frame=20), fh.FH_EUNSUPPORTED),
+    (dict(ffn_dim=9000), fh.FH_EUNSUPPORTED),
+    (dict(n_blocks=0), fh.FH_ESHAPE),
+    (dict(eps=float("nan")), fh.FH_ESHAPE),
+    (dict(cross_full=2), fh.FH_ESHAPE),
+])
+def test_create_rejects(kw, status):
+    with pytest.raises(fh.FHError) as e:
+        fh.fh_create(cfg_dict(**kw))
+    assert e.value.status == status
+
+
+def test_create_accepts_workloads():
+    for name in synth.CONFIGS:
+        fh.fh_create(synth.CONFIGS[name])
+    fh.fh_create(synth.CONFIGS["slice"].replace(cross_full=True))
+
+
+def test_weight_specs_match_generator():
+    for name in ("toy", "slice"):
+        cfg = synth.CONFIGS[name]
+        ctx = fh.fh_create(cfg)
+        got = [(n, s) for n, _, s in fh.fh_weight_specs(ctx)]
+        exp = [(n, tuple(s)) for n, s, _ in synth.param_specs(cfg)]
+        assert sorted(got) == sorted(exp)
+        kinds = {n: k for n, _, k in synth.param_specs(cfg)}
+        for n, dt, _ in fh.fh_weight_specs(ctx):
+            assert dt == (fh.FH_DTYPE_BF16 if kinds[n] == "matrix" else fh.FH_DTYPE_F32), n
+
+
+def test_workspace_bytes():
+    ctx = fh.fh_create(synth.CONFIGS["slice"])
+    b1, b3 = fh.fh_workspace_bytes(ctx, 1), fh.fh_workspace_bytes(ctx, 3)
+    assert b1 > 50e6 and b3 > 2.5 * b1
+    assert fh.fh_workspace_bytes(ctx, 0) == 0
+
+
+def _index(ctx, base_off=0, drop=None, bad_shape=None, misalign=None):
+    specs = fh.fh_weight_specs(ctx)
+    arr = (fh.fh_tensor * len(specs))()
+    keep, off = [], base_off
+    for i, (n, dt, shape) in enumerate(specs):
+        nb = n.encode()
+        keep.append(nb)
+        arr[i].name = nb
+        arr[i].dtype = dt
+        arr[i].ndim = len(shape)
+        for j, s in enumerate(shape):
+            arr[i].shape[j] = s + (1 if n == bad_shape and j == 0 else 0)
+        arr[i].offset = off + (8 if n == misalign else 0)
+        off += (int(np.prod(shape)) * (2 if dt == fh.FH_DTYPE_BF16 else 4) + 255) & ~255
+    n = len(specs)
+    if drop is not None:
+        names = [s[0] for s in specs]
+        k = names.index(drop)
+        arr2 = (fh.fh_tensor * (n - 1))()
+        j = 0
+        for i in range(n):
+            if i != k:
+                arr2[j] = arr[i]
+                j += 1
+        arr, n = arr2, n - 1
+    return arr, n, off, keep
+
+
+def _bind(ctx, **kw):
+    arr, n, size, keep = _index(ctx, **kw)
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 40)   # never dereferenced: binding is pointer arithmetic only
+    return fh.lib.fh_weights_bind(ctx, fake, size, arr, n, ctypes.byref(h)), h
+
+
+def test_weights_bind_checks_index():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    st, h = _bind(ctx)
+    assert st == fh.FH_OK and h.value
+    fh.lib.fh_weights_release(h)
+    st, _ = _bind(ctx, drop="blocks.1.ffn2.w")
+    assert st == fh.FH_EWEIGHTS and "blocks.1.ffn2.w" in fh.fh_last_error(ctx)
+    st, _ = _bind(ctx, bad_shape="blocks.0.qkv.w")
+    assert st == fh.FH_EWEIGHTS and "shape" in fh.fh_last_error(ctx)
+    st, _ = _bind(ctx, misalign="head.b")
+    assert st == fh.FH_EWEIGHTS and "aligned" in fh.fh_last_error(ctx)
+
+
+def test_call_argument_errors_before_any_launch():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    st, w = _bind(ctx)
+    assert st == fh.FH_OK
+    fake = ctypes.c_void_p(1 << 40)
+    need = fh.fh_workspace_bytes(ctx, 1)
+    sig = (ctypes.c_float * 2)(1.0, 0.0)
+    L = fh.lib
+    # batch 0, negative steps, non-finite sigma, null pointers, small or misaligned workspace
+    assert L.fh_dit_denoise_slice(ctx, w, 0, fake, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, -1, fake, fake, need, None) == fh.FH_EINVAL
+    bad = (ctypes.c_float * 2)(1.0, float("inf"))
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, bad, 1, fake, fake, need, None) == fh.FH_EINVAL
+    assert "sigma" in fh.fh_last_error(ctx)
+    assert L.fh_dit_denoise_slice(ctx, w, 1, None, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake, fake, need - 1, None) == fh.FH_EWORKSPACE
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake,
+                                  ctypes.c_void_p((1 << 40) + 64), need, None) == fh.FH_EWORKSPACE
+    assert L.fh_dit_block_forward(ctx, w, 2, 1, fake, fake, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_dit_block_forward(ctx, w, 0, 1, fake, None, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_dit_block_forward(ctx, None, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, 99, 0) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, fh.FH_K["attn"]) == fh.FH_OK
+    assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, 10) == fh.FH_EINVAL
+    fh.lib.fh_weights_release(w)
+    assert fh.fh_status_str(fh.FH_EWORKSPACE).startswith("workspace")

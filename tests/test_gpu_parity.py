@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library through its C ABI against the float64 CPU oracle.
+
+Bar (stated for bf16 storage with fp32 accumulation): max|g - r| / max|r| <= 2e-2,
+over the non-motion latent frames for slices and over the residual update
+x_out - x_in for single blocks (so the large residual cannot hide block error).
+Motion frames must equal the input motion bitwise.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+class Model:
+    """Context + bound weights + workspace for one configuration."""
+
+    def __init__(self, fh, cfg, W, batch):
+        self.fh, self.cfg, self.W = fh, cfg, W
+        self.ctx = fh.fh_create(cfg)
+        self.w = fh.fh_weights_bind(self.ctx, W)
+        self.ws = fh.workspace(self.ctx, batch)
+
+    def slice(self, lat, mot, aud, sig, graph=True, out=None):
+        self.fh.fh_set_option(self.ctx, self.fh.FH_OPT_GRAPH, int(graph))
+        L = dev(lat)
+        o = torch.empty_like(L) if out is None else out
+        self.fh.fh_dit_denoise_slice(self.ctx, self.w, L, dev(mot), dev(aud), sig, o, self.ws)
+        torch.cuda.synchronize()
+        return o.cpu().numpy()
+
+    def block(self, i, x, e, a):
+        X = dev(x)
+        self.fh.fh_dit_block_forward(self.ctx, self.w, i, X, dev(e), dev(a), self.ws)
+        torch.cuda.synchronize()
+        return X.cpu().numpy()
+
+
+def delta_err(x_gpu, x_ref, x_in):
+    return O.rel_err(x_gpu - x_in, x_ref - x_in)
+
+
+# ------------------------------------------------------------------ toy
+def test_toy_slice(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.TOY_SIGMAS)
+    say("toy slice, graph")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"toy slice rel err {err:.3e}")
+    assert err <= TOL
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    say("toy slice, direct launches")
+    got2 = m.slice(lat, mot, aud, sig, graph=False)
+    np.testing.assert_array_equal(got2, got)          # graph replay == direct, bitwise
+    got3 = m.slice(lat, mot, aud, sig)
+    np.testing.assert_array_equal(got3, got)          # deterministic
+
+
+def test_toy_multi_step_and_edge_cases(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    Wf = synth.weights_f32(W)
+    m = Model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.6, 0.3, 0.0]
+    say("toy B=2, 3 steps")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"toy B=2 3-step rel err {err:.3e}")
+    assert err <= TOL
+    # zero steps: the motion-pinned input, bitwise
+    say("toy zero steps")
+    got0 = m.slice(lat, mot, aud, [0.7])
+    np.testing.assert_array_equal(got0, O.pin_motion(lat, mot).astype(np.float32))
+    # a zero-size step leaves the latent unchanged
+    say("toy zero-size step")
+    gotz = m.slice(lat, mot, aud, [0.5, 0.5])
+    np.testing.assert_array_equal(gotz, O.pin_motion(lat, mot).astype(np.float32))
+    # output aliasing the input
+    say("toy in-place")
+    L = dev(lat)
+    fh.fh_dit_denoise_slice(m.ctx, m.w, L, dev(mot), dev(aud), sig, L, m.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(L.cpu().numpy(), got)
+
+
+def test_toy_full_cross_attention(fh):
+    cfg = synth.CONFIGS["toy"].replace(cross_full=True)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.TOY_SIGMAS)
+    say("toy slice, full cross-attention")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"toy full-cross rel err {err:.3e}")
+    assert err <= TOL
+
+
+# ------------------------------------------------------------------ one real block
+@pytest.fixture(scope="module")
+def block_model(fh):
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    return Model(fh, cfg, W, 3), synth.weights_f32(W)
+
+
+def _block_case(m, Wf, B, W_override=None):
+    cfg = m.cfg
+    x, e, a = synth.block_inputs(cfg, B)
+    got = m.block(0, x, e, a)
+    ref = O.dit_block_from_temb(x, e, a, Wf if W_override is None else W_override, 0, cfg)
+    return delta_err(got, ref, x)
+
+
+def test_block_parity(block_model):
+    m, Wf = block_model
+    say("real-shape block B=1")
+    err = _block_case(m, Wf, 1)
+    say(f"block rel err (residual update) {err:.3e}")
+    assert err <= TOL
+
+
+def test_block_batch3_lanes_independent(block_model):
+    m, Wf = block_model
+    say("real-shape block B=3")
+    x, e, a = synth.block_inputs(m.cfg, 3)
+    got = m.block(0, x, e, a)
+    for b in range(3):
+        ref = O.dit_block_from_temb(x[b:b + 1], e[b:b + 1], a[b:b + 1], Wf, 0, m.cfg)
+        err = delta_err(got[b:b + 1], ref, x[b:b + 1])
+        say(f"  lane {b} rel err {err:.3e}")
+        assert err <= TOL
+
+
+@pytest.mark.parametrize("keep", ["self_attn", "cross_attn", "ffn"])
+def test_block_single_branch(fh, keep):
+    """Zero the other branches' output projections so one branch's kernels
+    (norms, projections, attention or FFN, epilogues) are checked alone."""
+    cfg = synth.CONFIGS["block"]
+    W = dict(synth.make_weights(cfg))
+    off = {"self_attn": ["co", "ffn2"], "cross_attn": ["o", "ffn2"], "ffn": ["o", "co"]}[keep]
+    for n in off:
+        W[f"blocks.0.{n}.w"] = np.zeros_like(W[f"blocks.0.{n}.w"])
+        W[f"blocks.0.{n}.b"] = np.zeros_like(W[f"blocks.0.{n}.b"])
+    m = Model(fh, cfg, W, 1)
+    say(f"real-shape block, {keep} only")
+    err = _block_case(m, synth.weights_f32(W), 1)
+    say(f"  {keep} rel err {err:.3e}")
+    assert err <= TOL
+
+
+# ------------------------------------------------------------------ slices
+def test_slice_two_blocks_full_width(fh):
+    cfg = synth.CONFIGS["slice"].replace(n_blocks=2)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = [1.0, 0.5, 0.0]
+    say("full-width slice, 2 blocks, 2 steps")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+
+
+def test_slice_ragged_tiles(fh):
+    """800 tokens (5 x 16 x 10): the GEMM M tail, the attention query tail and a
+    half key block; one block, one step."""
+    cfg = synth.CONFIGS["slice"].replace(n_blocks=1, width=10)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [0.8, 0.3]
+    say("ragged slice 5x16x10, B=2")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("case", ["slice_b1", "slice_b3", "slice768"])
+def test_full_slice_against_stored_oracle(fh, case):
+    """The full 30-block, 4-step workloads against oracle outputs written by
+    tests/golden/make_golden.py (float64 oracle, same seeded weights)."""
+    path = os.path.join(GOLDEN, case + ".npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path, allow_pickle=False)
+    cfg = synth.CONFIGS[str(g["config"])]
+    B = int(g["batch"])
+    W = synth.make_weights(cfg)
+    assert synth.weights_digest(W) == str(g["digest"]), "weights differ from the stored oracle's"
+    m = Model(fh, cfg, W, B)
+    lat, mot, aud = synth.slice_inputs(cfg, B)
+    say(f"{case}: full slice B={B}")
+    got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
+    ref = g["out"]
+    for b in range(B):
+        err = O.rel_err(got[b:b + 1], ref[b:b + 1], cfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e}")
+        assert err <= TOL
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
