@@ -9,9 +9,9 @@
 // sum does not see. Values arrive transposed ([dim, keys]) from the
 // projection epilogue, so V^T tiles are plain row copies.
 //
-// flash_attn: 128 queries (4 waves) per workgroup; K and V^T blocks of 64
-// keys are staged in padded LDS, double-buffered, the next block fetched to
-// registers during the current one.
+// flash_attn: 64 queries per workgroup, the 4 waves split as 2 query groups x
+// 2 key halves (so a 1280-token slice gives 240 workgroups per lane); K and
+// V^T blocks are DMA'd into XOR-swizzled LDS, double-buffered.
 // cross_attn: short key ranges (32 audio tokens per latent frame, or all of
 // them), fragments loaded straight from global memory, no LDS.
 #include "fh_common.h"
@@ -23,8 +23,6 @@ namespace {
 constexpr int HD = 128;
 constexpr int QT = 128;
 constexpr int KB = 64;
-constexpr int KR = HD + 8;  // padded K row in LDS (bf16): 272 bytes
-constexpr int VR = KB + 4;  // padded V^T row in LDS (bf16): 136 bytes
 
 __device__ __forceinline__ bf16x8 load_v_frag(const bf16_t* p) {
   // keys {0..3} and {8..11} relative to p (see the key permutation above)
@@ -53,16 +51,26 @@ __device__ __forceinline__ void store_o(bf16_t* orow, const f32x16 (&acc)[4], fl
     }
 }
 
+// Self-attention workgroup: 64 queries of one (lane, head); wave w takes
+// query group w & 1 (32 queries) and key half w >> 1. Each step stages one
+// 64-key block of each half (K [64 x 128] and V^T [128 x 64], bf16) into LDS
+// by DMA, XOR-swizzled by (row & 7) on 16-byte chunks, double-buffered; the
+// two halves' online-softmax states are merged through LDS at the end.
+constexpr int AQ = 64;                 // queries per workgroup
+constexpr int KBLK = KB * HD * 2;      // bytes of one K (or V^T) block
+constexpr int ASTAGE = 4 * KBLK;       // K and V^T of both halves
+
 __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
     const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ k, int ldk,
     const bf16_t* __restrict__ vt, bf16_t* __restrict__ o, int ldo, int N, int D,
     float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KB * KR];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * VR];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * ASTAGE];
   const int b = blockIdx.z, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 1, kh = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
-  const int q0 = blockIdx.x * QT + wave * 32;
+  const int q0 = blockIdx.x * AQ + qg * 32;
 
   bf16x8 qf[8];
   {
@@ -72,33 +80,30 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  // staging: K block 64 rows x 16 chunks, V^T block 128 rows x 8 chunks
-  const int kc = tid & 15, kr = tid >> 4;
-  const int vc = tid & 7, vr = tid >> 3;
-  const bf16_t* kbase = k + (int64_t)b * N * ldk + h * HD + kc * 8;
-  const bf16_t* vbase = vt + ((int64_t)b * D + h * HD) * N + vc * 8;
-  u32x4 gk[4], gv[4];
-  auto gload = [&](int kb0) {
+  const int nkb = (N + KB - 1) / KB;
+  const int nh0 = (nkb + 1) / 2;  // key blocks of half 0; half 1 has nkb - nh0
+
+  // DMA roles of this lane: K rows 4g + lane/16 (16 chunks of 16 B per row),
+  // V^T rows 8g + lane/8 (8 chunks per row), g = 4 wave + i
+  const bf16_t* kbase = k + (int64_t)b * N * ldk + h * HD;
+  const bf16_t* vbase = vt + ((int64_t)b * D + h * HD) * N;
+  auto issue = [&](int buf, int j) {
+    char* st = smem + buf * ASTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(kb0 + kr + 16 * i, N - 1);
-      gk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * ldk);
-    }
-    const bool in = kb0 + vc * 8 < N;
+    for (int c = 0; c < 2; ++c) {
+      const int kb = min(c == 0 ? j : nh0 + j, nkb - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      gv[i] = in ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)(vr + 32 * i) * N + kb0)
-                 : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sK[buf][(kr + 16 * i) * KR + kc * 8]) = gk[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16_t* p = &sV[buf][(vr + 32 * i) * VR + vc * 8];
-      reinterpret_cast<u32x2*>(p)[0] = u32x2{gv[i].x, gv[i].y};
-      reinterpret_cast<u32x2*>(p)[1] = u32x2{gv[i].z, gv[i].w};
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * wave + i;
+        const int krow = 4 * g + (lane >> 4);
+        const int kch = (lane & 15) ^ (krow & 7);
+        const int key = min(kb * KB + krow, N - 1);
+        dma16(kbase + (int64_t)key * ldk + kch * 8, st + c * 2 * KBLK + g * 1024);
+        const int vrow = 8 * g + (lane >> 3);
+        const int vch = (lane & 7) ^ (vrow & 7);
+        const int vkey = min(kb * KB + vch * 8, N - 8);
+        dma16(vbase + (int64_t)vrow * N + vkey, st + c * 2 * KBLK + KBLK + g * 1024);
+      }
     }
   };
 
@@ -108,25 +113,28 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const int xr = lr & 7;
 
-  const int nkb = (N + KB - 1) / KB;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) gload((kb + 1) * KB);
+  issue(0, 0);
+  for (int j = 0; j < nh0; ++j) {
+    wait_vm<0>();
+    barrier();
+    if (j + 1 < nh0) issue((j + 1) & 1, j + 1);
+    const int kb = kh == 0 ? j : nh0 + j;
+    if (kb >= nkb) continue;
+    const char* kp = smem + (j & 1) * ASTAGE + kh * 2 * KBLK;
+    const char* vp = kp + KBLK;
 
     f32x16 st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
-      const bf16_t* kp = &sK[cur][(32 * t + lr) * KR + 8 * lh];
+      const char* krow = kp + (32 * t + lr) * (HD * 2);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * s),
-                                                        qf[s], st[t], 0, 0, 0);
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(krow + (((2 * s + lh) ^ xr) << 4)), qf[s], st[t], 0, 0, 0);
     }
     float mx = -INFINITY;
     const bool tail = (kb + 1) * KB > N;
@@ -165,17 +173,42 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8 pf = p_frag(st[t], u);
+        const int c0 = 4 * t + 2 * u;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 vf = load_v_frag(&sV[cur][(32 * dt + lr) * VR + 32 * t + 16 * u + 4 * lh]);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
+          const char* vrow = vp + (32 * dt + lr) * (KB * 2) + lh * 8;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((c0 ^ xr) << 4));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (((c0 + 1) ^ xr) << 4));
+          const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[dt], 0, 0, 0);
         }
       }
-    if (kb + 1 < nkb) sstore(cur ^ 1);
-    __syncthreads();
   }
   l_run += __shfl_xor(l_run, 32, 64);
-  if (q0 + lr < N) store_o(o + ((int64_t)b * N + q0 + lr) * ldo + h * HD, acc, 1.f / l_run, lh);
+
+  // merge the key halves: wave (qg, 1) hands (m, l, acc) to wave (qg, 0)
+  barrier();
+  float* mg = reinterpret_cast<float*>(smem) + qg * (66 * 64);
+  if (kh == 1) {
+    mg[lane] = m_run;
+    mg[64 + lane] = l_run;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mg[(2 + dt * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = mg[lane], l1 = mg[64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = exp2f(m_run - m), a1 = exp2f(m1 - m);
+    const float inv = 1.f / (l_run * a0 + l1 * a1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * a0 + mg[(2 + dt * 16 + r) * 64 + lane] * a1;
+    if (q0 + lr < N) store_o(o + ((int64_t)b * N + q0 + lr) * ldo + h * HD, acc, inv, lh);
+  }
 }
 
 __global__ __launch_bounds__(256) void cross_attn_kernel(
@@ -255,9 +288,9 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(
 hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const bf16_t* vt,
                       bf16_t* o, int ldo, int B, int N, int n_heads, float scale, hipStream_t s) {
   if (B <= 0 || N <= 0) return hipSuccess;
-  if (N % 8 || ldq % 8 || ldk % 8 || ldo % 4) return hipErrorInvalidValue;
+  if (N % 32 || ldq % 8 || ldk % 8 || ldo % 4) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid((N + QT - 1) / QT, n_heads, B);
+  dim3 grid((N + AQ - 1) / AQ, n_heads, B);
   flash_attn_kernel<<<grid, 256, 0, s>>>(q, ldq, k, ldk, vt, o, ldo, N, n_heads * HD, scale_log2);
   return hipGetLastError();
 }

@@ -42,7 +42,7 @@ struct WS {
 };
 
 constexpr int MAX_GRAPHS = 8;
-constexpr int GEMV_ROWS = 8;
+constexpr int GEMV_ROWS = 8;   // time-MLP rows per GEMV launch (steps of a slice, or lanes)
 
 }  // namespace
 
@@ -119,7 +119,7 @@ std::vector<Spec> make_specs(const fh_config& g) {
 WS carve(const fh_ctx* c, int B, char* base) {
   const fh_config& g = c->cfg;
   const size_t N = c->N, D = g.dim, La = c->La, Fd = g.ffn_dim, nb = g.n_blocks;
-  const size_t R = (size_t)(B > 1 ? B : 1);
+  const size_t R = (size_t)(B > GEMV_ROWS ? B : GEMV_ROWS);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -310,20 +310,30 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
     int rc = audio_kv(c, w->blk[i], B, ws.kc + i * slot_elems(c, B), ws.vct + i * slot_elems(c, B), ws, s);
     if (rc) return rc;
   }
-  for (int st = 0; st < n_steps; ++st) {
-    const float t = 1000.0f * sigmas[st];
-    FH_HIP(fh::sinusoid(ws.emb, &t, 1, g.freq_dim, s));
-    FH_HIP(fh::gemv_bf16(ws.emb, 1, g.freq_dim, w->time_in_w, w->time_in_b, ws.t1, D, 0, 1, s));
-    FH_HIP(fh::gemv_bf16(ws.t1, 1, D, w->time_out_w, w->time_out_b, ws.e, D, 0, 0, s));
-    FH_HIP(fh::gemv_bf16(ws.e, 1, D, w->time_proj_w, w->time_proj_b, ws.e0, 6 * D, 1, 0, s));
-    FH_HIP(fh::patch_embed(out, B, C, N, w->patch_w, w->patch_b, ws.x, D, s));
-    for (int i = 0; i < g.n_blocks; ++i) {
-      int rc = run_block(c, w->blk[i], B, ws.x, ws.e0, 0, ws.kc + i * slot_elems(c, B),
-                         ws.vct + i * slot_elems(c, B), ws, s);
-      if (rc) return rc;
+  for (int c0 = 0; c0 < n_steps; c0 += GEMV_ROWS) {
+    // time embedding of up to GEMV_ROWS steps at once (the weights are read once)
+    const int R = n_steps - c0 < GEMV_ROWS ? n_steps - c0 : GEMV_ROWS;
+    float tv[GEMV_ROWS];
+    for (int r = 0; r < R; ++r) tv[r] = 1000.0f * sigmas[c0 + r];
+    FH_HIP(fh::sinusoid(ws.emb, tv, R, g.freq_dim, s));
+    FH_HIP(fh::gemv_bf16(ws.emb, R, g.freq_dim, w->time_in_w, w->time_in_b, ws.t1, D, 0, 1, s));
+    FH_HIP(fh::gemv_bf16(ws.t1, R, D, w->time_out_w, w->time_out_b, ws.e, D, 0, 0, s));
+    FH_HIP(fh::gemv_bf16(ws.e, R, D, w->time_proj_w, w->time_proj_b, ws.e0, 6 * D, 1, 0, s));
+    for (int st = c0; st < c0 + R; ++st) {
+      const float* e = ws.e + (size_t)(st - c0) * D;
+      const float* e0 = ws.e0 + (size_t)(st - c0) * 6 * D;
+      FH_HIP(fh::patch_embed(out, B, C, N, w->patch_w, w->patch_b, ws.x, D, s));
+      for (int i = 0; i < g.n_blocks; ++i) {
+        int rc = run_block(c, w->blk[i], B, ws.x, e0, 0, ws.kc + i * slot_elems(c, B),
+                           ws.vct + i * slot_elems(c, B), ws, s);
+        if (rc) return rc;
+      }
+      // head: LN modulated by (head.mod + e), then W_h, Euler step and motion pin
+      FH_HIP(fh::layernorm_bf16(ws.x, ws.h, B * N, D, N, g.eps, w->head_mod, w->head_mod + D, e, e, 0,
+                                nullptr, nullptr, s));
+      FH_HIP(fh::head_euler(ws.h, B, N, D, w->head_w, w->head_b, g.out_ch, out, out, motion, nmt,
+                            sigmas[st + 1] - sigmas[st], s));
     }
-    FH_HIP(fh::head_euler(ws.x, B, N, D, g.eps, w->head_mod, ws.e, 0, w->head_w, w->head_b, g.out_ch, out,
-                          out, motion, nmt, sigmas[st + 1] - sigmas[st], s));
   }
   return FH_OK;
 }
@@ -360,6 +370,7 @@ int fh_create(const fh_config* cfg, fh_ctx** out) {
   if (g.dim != g.n_heads * g.head_dim || g.in_ch != g.out_ch || g.motion_frames >= g.frames)
     return FH_ESHAPE;
   if (g.head_dim != 128 || g.dim % 128 || g.ffn_dim % 128 || g.dim > 2048 || g.in_ch > 64 ||
+      g.in_ch % 16 ||
       g.freq_dim % 8 || g.freq_dim * 4 > 65536 || (g.height * g.width) % 32 || g.audio_per_frame % 32)
     return FH_EUNSUPPORTED;
   fh_ctx* ctx = new fh_ctx();

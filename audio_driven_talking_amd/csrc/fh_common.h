@@ -42,10 +42,50 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// tanh-approximated GELU, 0.5 z (1 + tanh(u)) with u = sqrt(2/pi)(z + 0.044715 z^3),
+// evaluated as z * sigmoid(2u) = z / (1 + exp(-2u)) (the same function) with the
+// hardware exp2 and reciprocal; large |u| saturates to z or -0 correctly.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float u = c * (z + 0.044715f * z * z * z);
-  return 0.5f * z * (1.0f + tanhf(u));
+  const float c2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float t = c2 * (z + 0.044715f * z * z * z);
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---- LDS DMA (global_load_lds_dwordx4) and explicit waits -------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane;
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding LDS DMA); callers order DMAs with wait_vm.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait states between the last MFMA of a loop and the first read of its
+// accumulator after the loop exit. The compiler's hazard padding does not
+// always cover this cross-block case on gfx950 (a 16x16x32 bf16 result was
+// read stale without it). The accumulator is an operand of the padding, so its
+// reads cannot be scheduled above it; 32 wait states exceed the longest MFMA.
+template <typename T>
+__device__ __forceinline__ void mfma_drain(T& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}

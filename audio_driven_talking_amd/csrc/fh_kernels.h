@@ -77,11 +77,11 @@ hipError_t gemv_bf16(const float* x, int R, int K, const bf16_t* W, const float*
 hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, const float* bp,
                        float* x, int D, hipStream_t s);
 
-// Output head and Euler update, one token per wave:
-//   v = (LN(x)(1 + head_mod[1] + e) + head_mod[0] + e) W_h^T + b_h
-//   lat_next = token in a motion frame ? motion : lat_cur + dsig * v
-hipError_t head_euler(const float* x, int B, int N, int D, float eps, const float* head_mod,
-                      const float* e, int e_stride, const bf16_t* Wh, const float* bh, int Co,
+// Output head and Euler update on the modulated, normalised rows h [B*N, D]
+// (bf16, from layernorm_bf16 with the head's shift/scale):
+//   v = h W_h^T + b_h;  lat_next = token in a motion frame ? motion : lat_cur + dsig * v
+// (latents [B, Co, N]; lat_next may alias lat_cur). Co must be a multiple of 16.
+hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
                       float dsig, hipStream_t s);
 

@@ -3,54 +3,55 @@
 // row-major / transposed store).
 //
 // Both operands are K-contiguous (activations [tokens, K], weights [out, in]).
-// The MFMA is issued as W-fragment x A-fragment so that each lane of the
-// 32x32 result holds 4 consecutive output columns of one row: the epilogue
-// then reads/writes 16-byte fp32 vectors (or 8-byte bf16 vectors).
+// The MFMA is issued as W-fragment x A-fragment so that each lane of a 32x32
+// result holds 4 consecutive output columns of one row: the epilogue then
+// reads/writes 16-byte fp32 vectors (or 8-byte bf16 vectors).
 //
-// Tile: 128 (M) x 128 (N) x 64 (K), 256 threads = 4 waves in 2x2, each wave
-// 64x64 = 2x2 MFMA 32x32x16 tiles. LDS is double-buffered, rows padded to
-// 144 bytes so the fragment reads of 32 consecutive rows spread over all banks;
-// the next K-slab is fetched into registers while the current one is used.
+// Workgroup tile BM x BN, K-slabs of 64, 256 threads = 4 waves in 2x2, each
+// wave (BM/2) x (BN/2) of MFMA 32x32x16 blocks.
+// Operand slabs go global -> LDS directly (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB = 8 rows x 128 B), NS slabs deep, so NS-1 slabs are
+// in flight while one is multiplied; one barrier per slab. Inside a 128-byte
+// row the 16-byte chunks are XOR-swizzled by (row & 7), which makes the
+// fragment reads of 8 consecutive rows hit 8 different bank groups.
+// Tile order is XCD-aware: the grid is padded to a multiple of the 8 XCDs and
+// each XCD gets a contiguous run of tiles, M fastest, so the tiles sharing a
+// weight slab share an L2.
 #include "fh_common.h"
 #include "fh_kernels.h"
 
 namespace fh {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDR = BK + 8;  // padded LDS row, in bf16 elements
+constexpr int KALIGN = 64;  // K must be a multiple of this (either slab depth divides it)
 
 template <int EPI>
-__device__ __forceinline__ void epilogue4(const EpiArgs ep, int m, int n, f32x4 v) {
-  float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
+__device__ __forceinline__ void epilogue4(const EpiArgs& ep, int m, int n, f32x4 v) {
+  const float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
   float c0 = v[0] + b.x, c1 = v[1] + b.y, c2 = v[2] + b.z, c3 = v[3] + b.w;
   if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16) {
     if constexpr (EPI == EPI_GELU_BF16) {
       c0 = gelu_tanh(c0); c1 = gelu_tanh(c1); c2 = gelu_tanh(c2); c3 = gelu_tanh(c3);
     }
-    uint2 w;
-    w.x = pack2bf(c0, c1);
-    w.y = pack2bf(c2, c3);
-    *reinterpret_cast<uint2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
+    const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
+    *reinterpret_cast<u32x2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
   } else if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES) {
-    float4* xp = reinterpret_cast<float4*>(ep.x + (int64_t)m * ep.ldx + n);
-    float4 x = *xp;
+    f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
+    f32x4 x = *xp;
     if constexpr (EPI == EPI_GATED_RES) {
-      int lane = m / ep.rows_per_lane;
-      float4 gt = *reinterpret_cast<const float4*>(ep.gate_tab + n);
-      float4 ge = *reinterpret_cast<const float4*>(ep.gate_e0 + (int64_t)lane * ep.gate_stride + n);
+      const int lane = m / ep.rows_per_lane;
+      const float4 gt = *reinterpret_cast<const float4*>(ep.gate_tab + n);
+      const float4 ge = *reinterpret_cast<const float4*>(ep.gate_e0 + (int64_t)lane * ep.gate_stride + n);
       c0 *= gt.x + ge.x; c1 *= gt.y + ge.y; c2 *= gt.z + ge.z; c3 *= gt.w + ge.w;
     }
-    x.x += c0; x.y += c1; x.z += c2; x.w += c3;
+    x[0] += c0; x[1] += c1; x[2] += c2; x[3] += c3;
     *xp = x;
   } else {  // EPI_SPLIT_T
     if (n < ep.split) {
-      uint2 w;
-      w.x = pack2bf(c0, c1);
-      w.y = pack2bf(c2, c3);
-      *reinterpret_cast<uint2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
+      const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
+      *reinterpret_cast<u32x2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
     } else {
-      int lane = m / ep.rows_per_lane, t = m - lane * ep.rows_per_lane;
+      const int lane = m / ep.rows_per_lane, t = m - lane * ep.rows_per_lane;
       bf16_t* o = ep.out_t + ((int64_t)lane * ep.t_cols + (n - ep.split)) * ep.rows_per_lane + t;
       o[0] = f2bf(c0);
       o[ep.rows_per_lane] = f2bf(c1);
@@ -60,119 +61,176 @@ __device__ __forceinline__ void epilogue4(const EpiArgs ep, int m, int n, f32x4 
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda,
-                                                        const bf16_t* __restrict__ W, int ldw, int M,
-                                                        int N, int K, int tiles_m, EpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDR];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[2][BN * LDR];
+template <int BM, int BN, int BK, int NS>
+constexpr int smem_bytes() { return NS * (BM + BN) * BK * 2; }
 
-  // Tile order: workgroups are dealt round-robin to the 8 XCDs; give each XCD
-  // a contiguous run of tiles, M fastest, so tiles sharing a weight slab sit
-  // in the same L2.
+// XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that 8
+// consecutive rows read at one logical chunk land on 8 different 16-byte bank
+// groups: rows of 128 B (BK 64) use row & 7; rows of 64 B (BK 32) pair up
+// into 128 B and use (row >> 1) & 3.
+template <int BK>
+__device__ __forceinline__ int swz(int row) { return BK == 64 ? (row & 7) : ((row >> 1) & 3); }
+
+template <int EPI, int BM, int BN, int BK, int NS>
+__global__ __launch_bounds__(256, (smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
+void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
+                  int M, int N, int K, int tiles_m, int tiles, EpiArgs ep) {
+  constexpr int ROWB = BK * 2;         // bytes per LDS row of a slab
+  constexpr int CH = BK / 8;           // 16-byte chunks per row
+  constexpr int RG = 64 / CH;          // rows per 1 KB DMA group
+  constexpr int MI = BM / 64;          // 32-row activation blocks per wave
+  constexpr int NI = BN / 64;          // 32-row weight blocks per wave
+  constexpr int GA = BM / RG / 4;      // 1 KB DMA groups per wave per slab, activations
+  constexpr int GW = BN / RG / 4;      // ... weights
+  constexpr int SLAB = (BM + BN) * ROWB;
+  constexpr int INFLIGHT = (NS - 2) * (GA + GW);  // DMAs of younger slabs allowed in flight
+  static_assert(GA >= 1 && GW >= 1 && INFLIGHT < 64, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
+
   int bid = blockIdx.x;
-  const int nt = gridDim.x;
-  if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);
+  const int per_xcd = gridDim.x >> 3;
+  bid = (bid & 7) * per_xcd + (bid >> 3);
+  if (bid >= tiles) return;
   const int tm = bid % tiles_m, tn = bid / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // global -> register staging: thread covers chunk c (8 bf16) of rows r0 + 32 i
-  const int c = tid & 7, r0 = tid >> 3;
-  const bf16_t* pa[4];
-  const bf16_t* pw[4];
+  // DMA: lane fills LDS row (RG g + lane/CH), physical chunk lane%CH, which
+  // holds logical chunk (lane%CH) ^ swz(row)
+  const int drow = lane / CH, dchunk = (lane % CH) ^ swz<BK>(drow);
+  const bf16_t* ga[GA];
+  const bf16_t* gw[GW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int ra = min(m0 + r0 + 32 * i, M - 1);
-    pa[i] = A + (int64_t)ra * lda + c * 8;
-    pw[i] = W + (int64_t)(n0 + r0 + 32 * i) * ldw + c * 8;
-  }
-  u32x4 ga[4], gw[4];
-#define GEMM_GLOAD1(i, k0)                                      \
-  ga[i] = *reinterpret_cast<const u32x4*>(pa[i] + (k0));        \
-  gw[i] = *reinterpret_cast<const u32x4*>(pw[i] + (k0));
-#define GEMM_GLOAD(k0) \
-  GEMM_GLOAD1(0, k0) GEMM_GLOAD1(1, k0) GEMM_GLOAD1(2, k0) GEMM_GLOAD1(3, k0)
-#define GEMM_SSTORE1(i, buf)                                                    \
-  *reinterpret_cast<u32x4*>(&sA[buf][(r0 + 32 * i) * LDR + c * 8]) = ga[i];     \
-  *reinterpret_cast<u32x4*>(&sW[buf][(r0 + 32 * i) * LDR + c * 8]) = gw[i];
-#define GEMM_SSTORE(buf) \
-  GEMM_SSTORE1(0, buf) GEMM_SSTORE1(1, buf) GEMM_SSTORE1(2, buf) GEMM_SSTORE1(3, buf)
+  for (int i = 0; i < GA; ++i)
+    ga[i] = A + (int64_t)min(m0 + RG * (wave + 4 * i) + drow, M - 1) * lda + dchunk * 8;
+#pragma unroll
+  for (int i = 0; i < GW; ++i) gw[i] = W + (int64_t)(n0 + RG * (wave + 4 * i) + drow) * ldw + dchunk * 8;
 
-  f32x16 acc[2][2];
+  auto issue = [&](int buf, int k0) {
+    char* sa = smem + buf * SLAB;
+    char* sw = sa + BM * ROWB;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < GA; ++i) dma16(ga[i] + k0, sa + (wave + 4 * i) * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < GW; ++i) dma16(gw[i] + k0, sw + (wave + 4 * i) * 1024);
+  };
+
+  f32x16 acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / BK;
-  GEMM_GLOAD(0);
-  GEMM_SSTORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) { GEMM_GLOAD((kt + 1) * BK); }
-    const bf16_t* a_base = &sA[cur][(wm * 64 + lr) * LDR + lh * 8];
-    const bf16_t* w_base = &sW[cur][(wn * 64 + lr) * LDR + lh * 8];
+  // fragment rows: activations wm*BM/2 + 32 j + lr, weights wn*BN/2 + 32 i + lr
+  const int xr = swz<BK>(lr);
+  auto compute = [&](int buf) {
+    const char* sa = smem + buf * SLAB + (wm * (BM / 2) + lr) * ROWB;
+    const char* sw = smem + buf * SLAB + BM * ROWB + (wn * (BN / 2) + lr) * ROWB;
+    // fragments of k-step kk+1 are read while the MFMAs of k-step kk run
+    bf16x8 wf[2][NI], af[2][MI];
+    auto read = [&](int set, int kk) {
+      const int off = ((2 * kk + lh) ^ xr) * 16;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) wf[set][i] = *reinterpret_cast<const bf16x8*>(sw + i * 32 * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < MI; ++j) af[set][j] = *reinterpret_cast<const bf16x8*>(sa + j * 32 * ROWB + off);
+    };
+    read(0, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 wf[2], af[2];
+      if (kk + 1 < BK / 16) read((kk + 1) & 1, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next reads ahead of these MFMAs
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        wf[i] = *reinterpret_cast<const bf16x8*>(w_base + i * 32 * LDR + kk * 16);
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        af[j] = *reinterpret_cast<const bf16x8*>(a_base + j * 32 * LDR + kk * 16);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < MI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][i], af[kk & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < KT) { GEMM_SSTORE(cur ^ 1); }
-    __syncthreads();
-  }
+  };
 
-  // result (i, j): lane holds row m = m0 + wm*64 + j*32 + lr and columns
-  // n = n0 + wn*64 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]
+  const int KT = K / BK;
+  // prologue: slabs 0 .. NS-2 in flight (slabs past the end re-fetch the last
+  // one into buffers nobody reads, keeping the wait count uniform)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + wm * 64 + j * 32 + lr;
+  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, KT - 1) * BK);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vm<INFLIGHT>();   // this wave's DMAs of slab kt have landed
+    barrier();             // everyone's have; everyone is done with slab kt-1
+    issue((kt + NS - 1) % NS, min(kt + NS - 1, KT - 1) * BK);
+    compute(kt % NS);
+  }
+  wait_vm<0>();
+
+  // result (i, j): lane holds row m = m0 + wm*BM/2 + j*32 + lr and columns
+  // n = n0 + wn*BN/2 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int m = m0 + wm * (BM / 2) + j * 32 + lr;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * lh;
-        f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        const int n = n0 + wn * (BN / 2) + i * 32 + 8 * g + 4 * lh;
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         epilogue4<EPI>(ep, m, n, v);
       }
   }
 }
 
+template <int BM, int BN, int BK, int NS>
+hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                  const EpiArgs& ep, hipStream_t s) {
+  if (N % BN) return hipErrorInvalidValue;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = tiles_m * (N / BN);
+  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  switch (epi) {
+    case EPI_BF16: gemm_bf16_nt<EPI_BF16, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    case EPI_GELU_BF16: gemm_bf16_nt<EPI_GELU_BF16, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    case EPI_GATED_RES: gemm_bf16_nt<EPI_GATED_RES, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    case EPI_RES: gemm_bf16_nt<EPI_RES, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    case EPI_SPLIT_T: gemm_bf16_nt<EPI_SPLIT_T, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Tile choice from measurements of the slice shapes on MI355X with weights
+// cold in HBM (as in a 30-block slice): big tiles (less L2->LDS traffic per
+// FLOP) where they still give enough workgroups, smaller ones otherwise.
+int gemm_tile_choice(int M, int N, int K) {
+  const int64_t t256 = (int64_t)((M + 255) / 256) * (N / 256);
+  if (N % 256 == 0 && N >= 8192 && t256 >= 170) return 0;  // 256x256, K-slab 64, 2 stages
+  if (N <= 2048) {
+    if (K >= 4096) return M <= 1536 ? 4 : 5;  // 128x64 k64 s4 | 256x128 k32 s4
+    return M <= 1536 ? 3 : 2;                 // 64x64 k64 s4 | 64x128 k64 s3
+  }
+  return M <= 1536 ? 1 : 2;                   // 128x128 k32 s4 | 64x128 k64 s3
+}
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (N % BN || K % BK || lda % 8 || ldw % 8) return hipErrorInvalidValue;
-  const int tiles_m = (M + BM - 1) / BM;
-  dim3 grid(tiles_m * (N / BN)), block(256);
-  switch (epi) {
-    case EPI_BF16: gemm_bf16_nt<EPI_BF16><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, ep); break;
-    case EPI_GELU_BF16: gemm_bf16_nt<EPI_GELU_BF16><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, ep); break;
-    case EPI_GATED_RES: gemm_bf16_nt<EPI_GATED_RES><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, ep); break;
-    case EPI_RES: gemm_bf16_nt<EPI_RES><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, ep); break;
-    case EPI_SPLIT_T: gemm_bf16_nt<EPI_SPLIT_T><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, ep); break;
-    default: return hipErrorInvalidValue;
+  if (N % 128 || K % KALIGN || lda % 8 || ldw % 8) return hipErrorInvalidValue;
+  switch (gemm_tile_choice(M, N, K)) {
+    case 0: return launch<256, 256, 64, 2>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 1: return launch<128, 128, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 2: return launch<64, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 3: return launch<64, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 4: return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    default: return launch<256, 128, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace fh

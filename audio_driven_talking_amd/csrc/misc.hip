@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
   }
 }
 
-constexpr int PT = 16;  // tokens per patch-embed workgroup
+constexpr int PT = 8;   // tokens per patch-embed workgroup
 constexpr int MAXC = 64;
 
+// Each thread owns 4 output columns and produces them for the workgroup's 8
+// tokens, so a weight row group is read once per 8 tokens.
 __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restrict__ lat, int C, int N,
                                                           const bf16_t* __restrict__ Wp,
                                                           const float* __restrict__ bp,
@@ -96,84 +98,65 @@ __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restric
     sl[i] = t0 + tt < N ? lat[((int64_t)b * C + c) * N + t0 + tt] : 0.f;
   }
   __syncthreads();
-  const int d4n = D / 4;
-  for (int item = threadIdx.x; item < PT * d4n; item += 256) {
-    const int tt = item / d4n, d = (item % d4n) * 4;
-    if (t0 + tt >= N) continue;
-    float4 acc = *reinterpret_cast<const float4*>(bp + d);
-    for (int c = 0; c < C; ++c) {
-      const float l = sl[c * PT + tt];
-      acc.x += bf2f(Wp[(d + 0) * C + c]) * l;
-      acc.y += bf2f(Wp[(d + 1) * C + c]) * l;
-      acc.z += bf2f(Wp[(d + 2) * C + c]) * l;
-      acc.w += bf2f(Wp[(d + 3) * C + c]) * l;
+  for (int d = threadIdx.x * 4; d < D; d += 1024) {
+    float acc[PT][4];
+    const float4 bias = *reinterpret_cast<const float4*>(bp + d);
+#pragma unroll
+    for (int tt = 0; tt < PT; ++tt) {
+      acc[tt][0] = bias.x; acc[tt][1] = bias.y; acc[tt][2] = bias.z; acc[tt][3] = bias.w;
     }
-    *reinterpret_cast<float4*>(x + ((int64_t)b * N + t0 + tt) * D + d) = acc;
+    for (int c = 0; c < C; ++c) {
+      float w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = bf2f(Wp[(int64_t)(d + e) * C + c]);
+#pragma unroll
+      for (int tt = 0; tt < PT; ++tt) {
+        const float l = sl[c * PT + tt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tt][e] += w[e] * l;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < PT; ++tt)
+      if (t0 + tt < N)
+        *reinterpret_cast<float4*>(x + ((int64_t)b * N + t0 + tt) * D + d) =
+            make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
   }
 }
 
-constexpr int MAXV4 = 8;
-
+// Output head on the modulated, normalised rows h (bf16 [B*N, D]) fused with
+// the Euler update: MFMA 16x16x32, one wave per 16 tokens and 16 channels;
+// lane l holds token (l % 16) and channels 4 (l / 16) + {0..3} of its group.
 __global__ __launch_bounds__(256) void head_euler_kernel(
-    const float* __restrict__ x, int B, int N, int D, float eps, const float* __restrict__ hmod,
-    const float* __restrict__ e, int e_stride, const bf16_t* __restrict__ Wh,
+    const bf16_t* __restrict__ h, int B, int N, int D, const bf16_t* __restrict__ Wh,
     const float* __restrict__ bh, int Co, const float* lat_cur, float* lat_next,
     const float* __restrict__ motion, int nmt, float dsig) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= B * N) return;
-  const int b = row / N, tok = row % N;
-  const int nv = D >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * D);
-  float4 v[MAXV4];
-  float s = 0.f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * 4 + wave) * 16;
+  if (t0 >= B * N) return;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int row = min(t0 + lr, B * N - 1);
+  const bf16_t* hp = h + (int64_t)row * D + 8 * lq;
+  for (int cg = 0; cg < Co; cg += 16) {
+    const bf16_t* wp = Wh + (int64_t)(cg + lr) * D + 8 * lq;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 32)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(wp + k0),
+                                                    *reinterpret_cast<const bf16x8*>(hp + k0), acc, 0, 0, 0);
+    mfma_drain(acc);
+    if (t0 + lr < B * N) {
+      const int b = (t0 + lr) / N, tok = (t0 + lr) % N;
 #pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      v[i] = xr[i * 64 + lane];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
-  const float mean = wave_sum(s) / (float)D;
-  float q = 0.f;
-#pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
-      q += (a * a + bb * bb) + (c * c + d * d);
-    }
-  const float rstd = rsqrtf(wave_sum(q) / (float)D + eps);
-  const float* eb = e + (int64_t)b * e_stride;
-#pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      const int col = (i * 64 + lane) * 4;
-      const float4 sh = *reinterpret_cast<const float4*>(hmod + col);
-      const float4 sc = *reinterpret_cast<const float4*>(hmod + D + col);
-      const float4 ee = *reinterpret_cast<const float4*>(eb + col);
-      v[i].x = (v[i].x - mean) * rstd * (1.f + sc.x + ee.x) + sh.x + ee.x;
-      v[i].y = (v[i].y - mean) * rstd * (1.f + sc.y + ee.y) + sh.y + ee.y;
-      v[i].z = (v[i].z - mean) * rstd * (1.f + sc.z + ee.z) + sh.z + ee.z;
-      v[i].w = (v[i].w - mean) * rstd * (1.f + sc.w + ee.w) + sh.w + ee.w;
-    }
-  float mine = 0.f;
-  for (int co = 0; co < Co; ++co) {
-    float p = 0.f;
-#pragma unroll
-    for (int i = 0; i < MAXV4; ++i)
-      if (i * 64 + lane < nv) {
-        const int col = (i * 64 + lane) * 4;
-        const u16x4 w = *reinterpret_cast<const u16x4*>(Wh + (int64_t)co * D + col);
-        p += v[i].x * bf2f(w[0]) + v[i].y * bf2f(w[1]) + v[i].z * bf2f(w[2]) + v[i].w * bf2f(w[3]);
+      for (int i = 0; i < 4; ++i) {
+        const int co = cg + 4 * lq + i;
+        const int64_t idx = ((int64_t)b * Co + co) * N + tok;
+        if (tok < nmt)
+          lat_next[idx] = motion[((int64_t)b * Co + co) * nmt + tok];
+        else
+          lat_next[idx] = lat_cur[idx] + dsig * (acc[i] + bh[co]);
       }
-    p = wave_sum(p);
-    if (lane == co) mine = p;
-  }
-  if (lane < Co) {
-    const int64_t idx = ((int64_t)b * Co + lane) * N + tok;
-    if (tok < nmt)
-      lat_next[idx] = motion[((int64_t)b * Co + lane) * nmt + tok];
-    else
-      lat_next[idx] = lat_cur[idx] + dsig * (mine + bh[lane]);
+    }
   }
 }
 
@@ -225,13 +208,12 @@ hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, 
   return hipGetLastError();
 }
 
-hipError_t head_euler(const float* x, int B, int N, int D, float eps, const float* head_mod,
-                      const float* e, int e_stride, const bf16_t* Wh, const float* bh, int Co,
+hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
                       float dsig, hipStream_t s) {
-  if (D % 4 || D > 256 * MAXV4 || Co > 64) return hipErrorInvalidValue;
-  head_euler_kernel<<<(B * N + 3) / 4, 256, 0, s>>>(x, B, N, D, eps, head_mod, e, e_stride, Wh, bh, Co,
-                                                    lat_cur, lat_next, motion, n_motion_tok, dsig);
+  if (D % 32 || Co % 16) return hipErrorInvalidValue;
+  head_euler_kernel<<<(B * N + 63) / 64, 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
+                                                      n_motion_tok, dsig);
   return hipGetLastError();
 }
 

@@ -1,124 +1,130 @@
 // Row-norm kernels: LayerNorm (+adaLN modulate or +affine) fp32 -> bf16, and
 // in-place q/k RMSNorm over the full width fused with the 3-D rotary.
-// One wave per row, 4 rows per 256-thread workgroup; the row stays in
-// registers between the statistics pass and the write pass. HBM-bound.
+// One workgroup per row, each thread owning 8 consecutive columns (two float4
+// or one 16-byte bf16 chunk), so a 1280-token slice launches 1280 workgroups
+// and every load is in flight at once; block reductions go through LDS.
+// Both kernels are HBM/L2-bound.
 #include "fh_common.h"
 #include "fh_kernels.h"
 
 namespace fh {
 namespace {
 
-constexpr int MAXV4 = 8;  // float4 per lane: rows up to 64*4*8 = 2048 wide
+// sum of v over the waves [w0, w0 + nw) of the workgroup (all threads get it)
+__device__ __forceinline__ float group_sum(float v, float* red, int w0, int nw) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < nw; ++w) s += red[w0 + w];
+  __syncthreads();
+  return s;
+}
 
 __global__ __launch_bounds__(256) void layernorm_kernel(
-    const float* __restrict__ x, bf16_t* __restrict__ out, int rows, int D, int rows_per_lane,
-    float eps, const float* __restrict__ tab_shift, const float* __restrict__ tab_scale,
+    const float* __restrict__ x, bf16_t* __restrict__ out, int D, int rows_per_lane, float eps,
+    const float* __restrict__ tab_shift, const float* __restrict__ tab_scale,
     const float* __restrict__ e_shift, const float* __restrict__ e_scale, int e_stride,
     const float* __restrict__ g, const float* __restrict__ b) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int nv = D >> 2;  // float4 chunks in the row; lane takes chunks lane + 64 i
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * D);
-  float4 v[MAXV4];
+  __shared__ float red[8];
+  const int row = blockIdx.x;
+  const int c = threadIdx.x * 8;
+  const bool on = c < D;
+  const float* xr = x + (int64_t)row * D + c;
+  float v[8];
+  if (on) {
+    const float4 a0 = reinterpret_cast<const float4*>(xr)[0];
+    const float4 a1 = reinterpret_cast<const float4*>(xr)[1];
+    v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+    v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  const int nw = blockDim.x >> 6;
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      v[i] = xr[i * 64 + lane];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
-  const float mean = wave_sum(s) / (float)D;
+  for (int e = 0; e < 8; ++e) s += v[e];
+  const float mean = group_sum(s, red, 0, nw) / (float)D;
   float q = 0.f;
+  if (on) {
 #pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
-      q += (a * a + bb * bb) + (c * c + d * d);
-    }
-  const float rstd = rsqrtf(wave_sum(q) / (float)D + eps);
-  const int ln = row / rows_per_lane;
-  uint2* orow = reinterpret_cast<uint2*>(out + (int64_t)row * D);
+    for (int e = 0; e < 8; ++e) q += (v[e] - mean) * (v[e] - mean);
+  }
+  const float rstd = rsqrtf(group_sum(q, red, 0, nw) / (float)D + eps);
+  if (!on) return;
+  float mul[8], add[8];
+  if (g) {
 #pragma unroll
-  for (int i = 0; i < MAXV4; ++i)
-    if (i * 64 + lane < nv) {
-      const int col = (i * 64 + lane) * 4;
-      float4 mul, add;
-      if (g) {
-        mul = *reinterpret_cast<const float4*>(g + col);
-        add = *reinterpret_cast<const float4*>(b + col);
-      } else {
-        float4 ts = *reinterpret_cast<const float4*>(tab_scale + col);
-        float4 th = *reinterpret_cast<const float4*>(tab_shift + col);
-        float4 es = *reinterpret_cast<const float4*>(e_scale + (int64_t)ln * e_stride + col);
-        float4 eh = *reinterpret_cast<const float4*>(e_shift + (int64_t)ln * e_stride + col);
-        mul = make_float4(1.f + ts.x + es.x, 1.f + ts.y + es.y, 1.f + ts.z + es.z, 1.f + ts.w + es.w);
-        add = make_float4(th.x + eh.x, th.y + eh.y, th.z + eh.z, th.w + eh.w);
-      }
-      float y0 = (v[i].x - mean) * rstd * mul.x + add.x;
-      float y1 = (v[i].y - mean) * rstd * mul.y + add.y;
-      float y2 = (v[i].z - mean) * rstd * mul.z + add.z;
-      float y3 = (v[i].w - mean) * rstd * mul.w + add.w;
-      uint2 w;
-      w.x = pack2bf(y0, y1);
-      w.y = pack2bf(y2, y3);
-      orow[i * 64 + lane] = w;
+    for (int e = 0; e < 8; ++e) { mul[e] = g[c + e]; add[e] = b[c + e]; }
+  } else {
+    const int ln = row / rows_per_lane;
+    const float* es = e_scale + (int64_t)ln * e_stride;
+    const float* eh = e_shift + (int64_t)ln * e_stride;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mul[e] = 1.f + tab_scale[c + e] + es[c + e];
+      add[e] = tab_shift[c + e] + eh[c + e];
     }
+  }
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = pack2bf((v[2 * e] - mean) * rstd * mul[2 * e] + add[2 * e],
+                   (v[2 * e + 1] - mean) * rstd * mul[2 * e + 1] + add[2 * e + 1]);
+  *reinterpret_cast<u32x4*>(out + (int64_t)row * D + c) = w;
 }
 
-constexpr int MAXC8 = 4;  // 8-element chunks per lane per part: width up to 64*8*4 = 2048
-
-__global__ __launch_bounds__(256) void rmsnorm_rope_kernel(
-    bf16_t* __restrict__ p, int ld, int rows, int D, int nparts, const float* __restrict__ g0,
+// nparts groups of threads, one per part of the row (q, then k); each thread
+// owns one 8-element chunk; pair j of a head is (dims 2j, 2j+1).
+__global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
+    bf16_t* __restrict__ p, int ld, int D, int tpp, const float* __restrict__ g0,
     const float* __restrict__ g1, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     int rows_per_lane, int head_dim, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int nc = D >> 3;  // 8-element chunks in the row; lane takes chunks lane + 64 i
-  const int half = head_dim >> 1;
-  const int tok = row % rows_per_lane;
-  for (int part = 0; part < nparts; ++part) {
-    u16x8* pr = reinterpret_cast<u16x8*>(p + (int64_t)row * ld + part * D);
-    const float* g = part ? g1 : g0;
-    u16x8 v[MAXC8];
-    float ss = 0.f;
+  __shared__ float red[8];
+  const int row = blockIdx.x;
+  const int part = threadIdx.x / tpp, tp = threadIdx.x % tpp;
+  const int c = tp * 8;
+  const bool on = c < D;
+  bf16_t* pr = p + (int64_t)row * ld + part * D + c;
+  u16x8 raw;
+  if (on) raw = *reinterpret_cast<const u16x8*>(pr);
+  float y[8];
+  float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXC8; ++i)
-      if (i * 64 + lane < nc) {
-        v[i] = pr[i * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float f = bf2f(v[i][e]);
-          ss += f * f;
-        }
-      }
-    const float rs = rsqrtf(wave_sum(ss) / (float)D + eps);
-#pragma unroll
-    for (int i = 0; i < MAXC8; ++i)
-      if (i * 64 + lane < nc) {
-        const int col = (i * 64 + lane) * 8;
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = bf2f(v[i][e]) * rs * g[col + e];
-        if (cos_t) {
-          const int j0 = (col % head_dim) >> 1;  // first pair of this chunk within its head
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float c = cos_t[(int64_t)tok * half + j0 + e];
-            const float s = sin_t[(int64_t)tok * half + j0 + e];
-            const float a = y[2 * e], bb = y[2 * e + 1];
-            y[2 * e] = a * c - bb * s;
-            y[2 * e + 1] = a * s + bb * c;
-          }
-        }
-        u16x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f2bf(y[e]);
-        pr[i * 64 + lane] = o;
-      }
+  for (int e = 0; e < 8; ++e) {
+    y[e] = on ? bf2f(raw[e]) : 0.f;
+    ss += y[e] * y[e];
   }
+  const int wpp = tpp >> 6;
+  // reduce per part: waves [part * wpp, (part + 1) * wpp)
+  const float tot = group_sum(ss, red, part * wpp, wpp);
+  if (!on) return;
+  const float rs = rsqrtf(tot / (float)D + eps);
+  const float* g = part ? g1 : g0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] *= rs * g[c + e];
+  if (cos_t) {
+    const int half = head_dim >> 1;
+    const int tok = row % rows_per_lane;
+    const int j0 = (c % head_dim) >> 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float cs = cos_t[(int64_t)tok * half + j0 + e];
+      const float sn = sin_t[(int64_t)tok * half + j0 + e];
+      const float a = y[2 * e], bb = y[2 * e + 1];
+      y[2 * e] = a * cs - bb * sn;
+      y[2 * e + 1] = a * sn + bb * cs;
+    }
+  }
+  u16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f2bf(y[e]);
+  *reinterpret_cast<u16x8*>(pr) = o;
 }
+
+int threads_for(int D) { return ((D / 8 + 63) / 64) * 64; }
 
 }  // namespace
 
@@ -127,9 +133,9 @@ hipError_t layernorm_bf16(const float* x, bf16_t* out, int rows, int D, int rows
                           const float* e_scale, int e_stride, const float* g, const float* b,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (D % 4 || D > 256 * MAXV4) return hipErrorInvalidValue;
-  layernorm_kernel<<<(rows + 3) / 4, 256, 0, s>>>(x, out, rows, D, rows_per_lane, eps, tab_shift,
-                                                  tab_scale, e_shift, e_scale, e_stride, g, b);
+  if (D % 8 || threads_for(D) > 256) return hipErrorInvalidValue;
+  layernorm_kernel<<<rows, threads_for(D), 0, s>>>(x, out, D, rows_per_lane, eps, tab_shift, tab_scale,
+                                                   e_shift, e_scale, e_stride, g, b);
   return hipGetLastError();
 }
 
@@ -137,9 +143,11 @@ hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, con
                              const float* g1, const float* cos_t, const float* sin_t,
                              int rows_per_lane, int head_dim, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (D % 8 || D > 512 * MAXC8 || ld % 8 || head_dim % 8) return hipErrorInvalidValue;
-  rmsnorm_rope_kernel<<<(rows + 3) / 4, 256, 0, s>>>(p, ld, rows, D, nparts, g0, g1, cos_t, sin_t,
-                                                     rows_per_lane, head_dim, eps);
+  const int tpp = threads_for(D);
+  if (D % 8 || ld % 8 || head_dim % 8 || nparts < 1 || nparts > 2 || tpp * nparts > 512)
+    return hipErrorInvalidValue;
+  rmsnorm_rope_kernel<<<rows, tpp * nparts, 0, s>>>(p, ld, D, tpp, g0, g1, cos_t, sin_t, rows_per_lane,
+                                                     head_dim, eps);
   return hipGetLastError();
 }
 

@@ -1,0 +1,213 @@
+"""Throughput of the FlashHead Lite slice denoiser on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload slice|slice_b3|slice768]
+
+A step is one full slice denoise (30 blocks x 4 Euler steps, audio K/V, time
+embedding, head and motion pin) of a batch of synthetic inputs already in
+HBM. Prints ONE JSON line. Only one GPU is used; --gpus > 1 exits.
+
+Extra objects on the line:
+  roofline      the FFN up-projection GEMM (the largest kernel): algorithmic
+                FLOPs per launch / its mean duration, timed with HIP events on
+                the launch stream over a second pass of the same K steps.
+  cpu_baseline  the float64 numpy oracle timed on this host on a bounded
+                sample of the same workload (some of the slice's block-steps),
+                scaled to frames/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+FRAMES_PER_SLICE = 24         # each slice emits its last 24 frames
+METRIC = "DiT slice denoise video frames/s (30 blk×4 steps) + % bf16 MFMA peak"
+WORKLOADS = {
+    "slice": ("slice", 1, "full Lite slice denoise, batch 1: 30 blocks x 4 Euler steps, latent "
+                          "16x5x16x16 (1280 tokens, 2 motion frames), 160 audio tokens, width 1536"),
+    "slice_b3": ("slice", 3, "full Lite slice denoise, batch 3 (three independent streams)"),
+    "slice768": ("slice768", 1, "full slice denoise at 768x768, latent 16x5x24x24 (2880 tokens), batch 1"),
+}
+ROOF_KERNEL = "gemm_ffn1"
+
+
+def flops_per_slice(cfg, B, n_steps):
+    """Algorithmic FLOPs of one slice call (multiply-add = 2)."""
+    N, D, Fd, La = cfg.tokens, cfg.dim, cfg.ffn_dim, cfg.audio_tokens
+    M = B * N
+    gemm = 2 * M * D * (3 * D + D + D + D) + 2 * 2 * M * D * Fd
+    attn = 4 * B * N * N * D
+    keys = La if cfg.cross_full else cfg.audio_per_frame
+    cross = 4 * B * N * keys * D
+    per_step_blocks = cfg.n_blocks * (gemm + attn + cross)
+    audio_kv = cfg.n_blocks * 2 * B * La * 2 * D * D
+    time_mlp = 2 * (cfg.freq_dim * D + D * D + 6 * D * D)
+    patch_head = 2 * M * cfg.in_ch * D + 2 * M * D * cfg.out_ch
+    return n_steps * (per_step_blocks + time_mlp + patch_head) + audio_kv, \
+        n_steps * cfg.n_blocks * (gemm + attn)
+
+
+def cpu_baseline(cfg, sigmas, budget_s=15.0):
+    """Time the float64 oracle on block-steps of the first step, scale to a slice."""
+    import threadpoolctl
+    import oracle
+    import synth
+    W = synth.weights_f32(synth.make_weights(cfg, blocks=list(range(min(cfg.n_blocks, 8)))))
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    x0 = oracle.pin_motion(lat, mot)
+    e, e0 = oracle.time_embedding(np.array([sigmas[0]]), W, cfg)
+    ang = oracle.rope_angles(cfg)
+    x = oracle.linear(oracle.patchify(x0), W["patch.w"], W["patch.b"])
+    t0 = time.perf_counter()
+    k = 0
+    while k < min(cfg.n_blocks, 8):
+        x = oracle.dit_block(x, e0, aud, oracle.block_weights(W, k), cfg, ang)
+        k += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_block = (time.perf_counter() - t0) / k
+    t_slice = t_block * cfg.n_blocks * (len(sigmas) - 1)
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    return {"value": FRAMES_PER_SLICE / t_slice, "unit": "frames/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{k} of the {cfg.n_blocks * (len(sigmas) - 1)} block-steps of one batch-1 "
+                      f"slice (float64 numpy oracle, {t_block:.3f} s per block-step), scaled to the "
+                      f"whole slice"}
+
+
+def traffic_from_profile(kernel_src_hash, launches_bytes=None):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_ffn1_slice_b1_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_sha256") != kernel_src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="slice", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the slice denoiser has no "
+              "multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import audio_driven_talking_amd as fh
+    import synth
+
+    cfg_name, B, desc = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[cfg_name]
+    sig = list(synth.SLICE_SIGMAS)
+    n_steps = len(sig) - 1
+    W = synth.make_weights(cfg)
+    ctx = fh.fh_create(cfg)
+    w = fh.fh_weights_bind(ctx, W)
+    del W
+    ws = fh.workspace(ctx, B)
+    lat, mot, aud = synth.slice_inputs(cfg, B)
+    L, Mo, A = (torch.from_numpy(a).cuda() for a in (lat, mot, aud))
+    out = torch.empty_like(L)
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0 if args.no_graph else 1)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fh.fh_dit_denoise_slice(ctx, w, L, Mo, A, sig, out, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    T = time.perf_counter() - t0
+    ms = 1e3 * T / args.steps
+
+    total_flops, hot_flops = flops_per_slice(cfg, B, n_steps)
+    value = FRAMES_PER_SLICE * B * args.steps / T
+
+    # roofline kernel: HIP events around each FFN-up launch, same K steps, direct launches
+    fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, fh.FH_K[ROOF_KERNEL])
+    step()
+    torch.cuda.synchronize()
+    fh.fh_kernel_time(ctx)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kms, kn = fh.fh_kernel_time(ctx)
+    fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, -1)
+    M = B * cfg.tokens
+    k_flops = 2.0 * M * cfg.ffn_dim * cfg.dim
+    k_avg_s = kms / 1e3 / max(kn, 1)
+    achieved = k_flops / k_avg_s / 1e12
+    src = open(os.path.join(ROOT, "audio_driven_talking_amd", "csrc", "gemm.hip"), "rb").read()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profile(hashlib.sha256(src).hexdigest()),
+                "kernel": f"{ROOF_KERNEL} (M={M}, N={cfg.ffn_dim}, K={cfg.dim}, "
+                          f"{k_flops / 1e9:.2f} GFLOP per launch)",
+                "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
+
+    breakdown = None
+    if args.breakdown:
+        breakdown = {}
+        for name, k in fh.FH_K.items():
+            fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, k)
+            fh.fh_kernel_time(ctx)
+            for _ in range(3):
+                step()
+            torch.cuda.synchronize()
+            t, n = fh.fh_kernel_time(ctx)
+            breakdown[name] = {"ms_per_slice": round(t / 3, 4), "launches_per_slice": n // 3}
+        fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, -1)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) latent/motion/audio)",
+        "config": {"workload": desc, "batch": B, "tokens": cfg.tokens, "blocks": cfg.n_blocks,
+                   "euler_steps": n_steps, "dim": cfg.dim, "heads": cfg.n_heads,
+                   "ffn": cfg.ffn_dim, "audio_tokens": cfg.audio_tokens,
+                   "cross_attention": "full" if cfg.cross_full else "frame-local",
+                   "graph": not args.no_graph},
+        "latent_token_steps_per_s": round(B * cfg.tokens * n_steps * args.steps / T, 1),
+        "mfma_frac_end_to_end": round(total_flops / (T / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),
+        "roofline": roofline,
+    }
+    if breakdown is not None:
+        line["kernel_ms_per_slice"] = breakdown
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, sig)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

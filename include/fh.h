@@ -52,7 +52,7 @@ enum { FH_DTYPE_BF16 = 1, FH_DTYPE_F32 = 2 };
  * (audio-cpp page, "Variant boundaries"). The kernels implement:
  *   head_dim == 128, dim == n_heads * 128, dim % 128 == 0, ffn_dim % 128 == 0,
  *   dim <= 2048, in_ch == out_ch <= 64, freq_dim % 8 == 0, frames*height*width
- *   a multiple of 32, height*width a multiple of 32, audio_per_frame a
+ *   a multiple of 32, height*width a multiple of 32, in_ch a multiple of 16, audio_per_frame a
  *   multiple of 32, 0 <= motion_frames < frames.                                */
 typedef struct fh_config {
   int32_t n_blocks;         /* 30 for Lite */
