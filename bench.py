@@ -39,6 +39,7 @@ WORKLOADS = {
     "slice768": ("slice768", 1, "full slice denoise at 768x768, latent 16x5x24x24 (2880 tokens), batch 1"),
 }
 ROOF_KERNEL = "gemm_ffn1"
+COPY_BYTES = 256 << 20        # calibration copy: reads and writes this many bytes
 
 
 def flops_per_slice(cfg, B, n_steps):
@@ -86,9 +87,10 @@ def cpu_baseline(cfg, sigmas, budget_s=15.0):
                       f"whole slice"}
 
 
-def traffic_from_profile(kernel_src_hash, launches_bytes=None):
+def traffic_from_profile(kernel_src_hash):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
+    size), if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "gemm_ffn1_slice_b1_counters.json")
     if not os.path.exists(path):
         return None
@@ -110,6 +112,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one elementwise copy of 256 MiB (read + write) first; rocprofv3 "
+                         "counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -135,6 +140,12 @@ def main():
     out = torch.empty_like(L)
     fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0 if args.no_graph else 1)
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         fh.fh_dit_denoise_slice(ctx, w, L, Mo, A, sig, out, ws, stream)
