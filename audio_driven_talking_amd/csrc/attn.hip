@@ -33,10 +33,9 @@ __device__ __forceinline__ bf16x8 load_v_frag(const bf16_t* p) {
 }
 
 __device__ __forceinline__ bf16x8 p_frag(const f32x16& st, int u) {
-  bf16x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = (__bf16)st[8 * u + e];
-  return f;
+  const u32x4 w = {pack2bf(st[8 * u], st[8 * u + 1]), pack2bf(st[8 * u + 2], st[8 * u + 3]),
+                   pack2bf(st[8 * u + 4], st[8 * u + 5]), pack2bf(st[8 * u + 6], st[8 * u + 7])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ void store_o(bf16_t* orow, const f32x16 (&acc)[4], float inv, int lh) {
@@ -54,23 +53,44 @@ __device__ __forceinline__ void store_o(bf16_t* orow, const f32x16 (&acc)[4], fl
 // Self-attention workgroup: 64 queries of one (lane, head); wave w takes
 // query group w & 1 (32 queries) and key half w >> 1. Each step stages one
 // 64-key block of each half (K [64 x 128] and V^T [128 x 64], bf16) into LDS
-// by DMA, XOR-swizzled by (row & 7) on 16-byte chunks, double-buffered; the
-// two halves' online-softmax states are merged through LDS at the end.
+// by DMA, XOR-swizzled on 16-byte chunks, double-buffered; the two halves'
+// online-softmax states are merged through LDS at the end.
+//
+// Key order: the MFMA row i of a 32-key tile reads key kperm(i) (bits 2 and 3
+// swapped), so the 8 scores a lane holds for one 16-key k-step are 8
+// contiguous keys; the matching V^T fragment is then one 16-byte LDS read.
+// Rescaling is lazy: the reference maximum moves only when a block's maximum
+// exceeds it by more than 2^TAU, so P stays <= 2^TAU (exact in the final
+// normalisation) and the accumulators are rarely touched by VALU.
 constexpr int AQ = 64;                 // queries per workgroup
 constexpr int KBLK = KB * HD * 2;      // bytes of one K (or V^T) block
 constexpr int ASTAGE = 4 * KBLK;       // K and V^T of both halves
+constexpr float TAU = 8.f;
+
+__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// Chunk swizzles. gfx950 serves 16-byte LDS reads in 16-lane groups over a
+// 256-byte bank window: the 16 K rows (256 B each) a fragment read touches
+// take 16 distinct chunks via row & 15; the 16 V^T rows (128 B, two per
+// window) take 8 distinct chunks per row parity via (row >> 1) & 7.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
     const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ k, int ldk,
     const bf16_t* __restrict__ vt, bf16_t* __restrict__ o, int ldo, int N, int D,
-    float scale_log2) {
+    float scale_log2, int n_qt, int n_heads, int n_wg) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * ASTAGE];
-  const int b = blockIdx.z, h = blockIdx.y;
+  // workgroups are dealt round-robin to the 8 XCDs; give each XCD a run of
+  // consecutive (query tile fastest) workgroups so the query tiles of a head
+  // share one L2 copy of its keys and values
+  const int wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (wg >= n_wg) return;
+  const int qt = wg % n_qt, h = (wg / n_qt) % n_heads, b = wg / (n_qt * n_heads);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave & 1, kh = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
-  const int q0 = blockIdx.x * AQ + qg * 32;
+  const int q0 = qt * AQ + qg * 32;
 
   bf16x8 qf[8];
   {
@@ -96,11 +116,11 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
       for (int i = 0; i < 4; ++i) {
         const int g = 4 * wave + i;
         const int krow = 4 * g + (lane >> 4);
-        const int kch = (lane & 15) ^ (krow & 7);
+        const int kch = (lane & 15) ^ kswz(krow);
         const int key = min(kb * KB + krow, N - 1);
         dma16(kbase + (int64_t)key * ldk + kch * 8, st + c * 2 * KBLK + g * 1024);
         const int vrow = 8 * g + (lane >> 3);
-        const int vch = (lane & 7) ^ (vrow & 7);
+        const int vch = (lane & 7) ^ vswz(vrow);
         const int vkey = min(kb * KB + vch * 8, N - 8);
         dma16(vbase + (int64_t)vrow * N + vkey, st + c * 2 * KBLK + KBLK + g * 1024);
       }
@@ -113,7 +133,8 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const int xr = lr & 7;
+  const int krow_l = kperm(lr);
+  const int kx = kswz(krow_l), vx = vswz(lr);
 
   issue(0, 0);
   for (int j = 0; j < nh0; ++j) {
@@ -130,57 +151,57 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
-      const char* krow = kp + (32 * t + lr) * (HD * 2);
+      const char* krow = kp + (32 * t + krow_l) * (HD * 2);
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(krow + (((2 * s + lh) ^ xr) << 4)), qf[s], st[t], 0, 0, 0);
+            *reinterpret_cast<const bf16x8*>(krow + (((2 * s + lh) ^ kx) << 4)), qf[s], st[t], 0, 0, 0);
+    }
+    // st[t][r] is the score of key kb*64 + 32t + 16(r>>3) + 8lh + (r&7)
+    if ((kb + 1) * KB > N) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * KB + 32 * t + 16 * (r >> 3) + 8 * lh + (r & 7) >= N) st[t][r] = -INFINITY;
     }
     float mx = -INFINITY;
-    const bool tail = (kb + 1) * KB > N;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[t][r] * scale_log2;
-        if (tail) {
-          const int key = kb * KB + 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (key >= N) v = -INFINITY;
-        }
-        st[t][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__any(mx > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(st[t][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[t][r], scale_log2, -m_run));
         st[t][r] = p;
         ps += p;
       }
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    l_run += ps;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8 pf = p_frag(st[t], u);
-        const int c0 = 4 * t + 2 * u;
+        const int c = 4 * t + 2 * u + lh;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const char* vrow = vp + (32 * dt + lr) * (KB * 2) + lh * 8;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((c0 ^ xr) << 4));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (((c0 + 1) ^ xr) << 4));
-          const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[dt], 0, 0, 0);
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(vp + (32 * dt + lr) * (KB * 2) + ((c ^ vx) << 4));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
         }
       }
   }
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   if (kh == 0) {
     const float m1 = mg[lane], l1 = mg[64 + lane];
     const float m = fmaxf(m_run, m1);
-    const float a0 = exp2f(m_run - m), a1 = exp2f(m1 - m);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
     const float inv = 1.f / (l_run * a0 + l1 * a1);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -290,8 +311,9 @@ hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const 
   if (B <= 0 || N <= 0) return hipSuccess;
   if (N % 32 || ldq % 8 || ldk % 8 || ldo % 4) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid((N + AQ - 1) / AQ, n_heads, B);
-  flash_attn_kernel<<<grid, 256, 0, s>>>(q, ldq, k, ldk, vt, o, ldo, N, n_heads * HD, scale_log2);
+  const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
+  flash_attn_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, ldq, k, ldk, vt, o, ldo, N, n_heads * HD,
+                                                       scale_log2, n_qt, n_heads, n_wg);
   return hipGetLastError();
 }
 

@@ -64,12 +64,15 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& ep, int m, int n, f32x4
 template <int BM, int BN, int BK, int NS>
 constexpr int smem_bytes() { return NS * (BM + BN) * BK * 2; }
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that 8
-// consecutive rows read at one logical chunk land on 8 different 16-byte bank
-// groups: rows of 128 B (BK 64) use row & 7; rows of 64 B (BK 32) pair up
-// into 128 B and use (row >> 1) & 3.
+// XOR swizzle of the 16-byte chunk index inside an LDS row. gfx950 serves a
+// 16-byte LDS read in groups of 16 lanes across 64 banks (a 256-byte window),
+// so the 16 consecutive rows a fragment read touches at one logical chunk
+// must land on 16 different 16-byte slots of that window: rows of 128 B
+// (K-slab 64) already alternate between the two halves by parity and XOR
+// with (row >> 1) & 7; rows of 64 B (K-slab 32) take the quarter from
+// row & 3 and XOR with (row >> 2) & 3.
 template <int BK>
-__device__ __forceinline__ int swz(int row) { return BK == 64 ? (row & 7) : ((row >> 1) & 3); }
+__device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
 template <int EPI, int BM, int BN, int BK, int NS>
 __global__ __launch_bounds__(256, (smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
@@ -100,16 +103,21 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // DMA: lane fills LDS row (RG g + lane/CH), physical chunk lane%CH, which
-  // holds logical chunk (lane%CH) ^ swz(row)
-  const int drow = lane / CH, dchunk = (lane % CH) ^ swz<BK>(drow);
+  // DMA: lane fills LDS row r = RG g + lane/CH, physical chunk lane%CH, which
+  // holds logical chunk (lane%CH) ^ swz(r)
+  const int drow = lane / CH;
   const bf16_t* ga[GA];
   const bf16_t* gw[GW];
 #pragma unroll
-  for (int i = 0; i < GA; ++i)
-    ga[i] = A + (int64_t)min(m0 + RG * (wave + 4 * i) + drow, M - 1) * lda + dchunk * 8;
+  for (int i = 0; i < GA; ++i) {
+    const int r = RG * (wave + 4 * i) + drow;
+    ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + ((lane % CH) ^ swz<BK>(r)) * 8;
+  }
 #pragma unroll
-  for (int i = 0; i < GW; ++i) gw[i] = W + (int64_t)(n0 + RG * (wave + 4 * i) + drow) * ldw + dchunk * 8;
+  for (int i = 0; i < GW; ++i) {
+    const int r = RG * (wave + 4 * i) + drow;
+    gw[i] = W + (int64_t)(n0 + r) * ldw + ((lane % CH) ^ swz<BK>(r)) * 8;
+  }
 
   auto issue = [&](int buf, int k0) {
     char* sa = smem + buf * SLAB;
@@ -211,12 +219,9 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
 // FLOP) where they still give enough workgroups, smaller ones otherwise.
 int gemm_tile_choice(int M, int N, int K) {
   const int64_t t256 = (int64_t)((M + 255) / 256) * (N / 256);
-  if (N % 256 == 0 && N >= 8192 && t256 >= 170) return 0;  // 256x256, K-slab 64, 2 stages
-  if (N <= 2048) {
-    if (K >= 4096) return M <= 1536 ? 4 : 5;  // 128x64 k64 s4 | 256x128 k32 s4
-    return M <= 1536 ? 3 : 2;                 // 64x64 k64 s4 | 64x128 k64 s3
-  }
-  return M <= 1536 ? 1 : 2;                   // 128x128 k32 s4 | 64x128 k64 s3
+  if (N % 256 == 0 && N >= 4096 && t256 >= 170) return 0;  // 256x256, K-slab 64, 2 stages
+  if (N <= 2048 && M <= 1536) return K >= 4096 ? 2 : 3;     // 128x64 k64 s4 | 64x64 k64 s4
+  return 1;                                                 // 128x128 k32 s4
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -226,10 +231,8 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
   switch (gemm_tile_choice(M, N, K)) {
     case 0: return launch<256, 256, 64, 2>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 1: return launch<128, 128, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 2: return launch<64, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 3: return launch<64, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 4: return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    default: return launch<256, 128, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 2: return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    default: return launch<64, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
 }
 
