@@ -70,6 +70,13 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
+// wait until every LDS read / write of this wave has completed
+__device__ __forceinline__ void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
+
 // workgroup barrier without the memory fence of __syncthreads (which would
 // also wait for every outstanding LDS DMA); callers order DMAs with wait_vm.
 __device__ __forceinline__ void barrier() {

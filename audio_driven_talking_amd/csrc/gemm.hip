@@ -3,20 +3,25 @@
 // row-major / transposed store).
 //
 // Both operands are K-contiguous (activations [tokens, K], weights [out, in]).
-// The MFMA is issued as W-fragment x A-fragment so that each lane of a 32x32
-// result holds 4 consecutive output columns of one row: the epilogue then
-// reads/writes 16-byte fp32 vectors (or 8-byte bf16 vectors).
+// The MFMA is issued as W-fragment x A-fragment, so each lane of a 32x32
+// result holds 4 consecutive output columns of one row.
 //
-// Workgroup tile BM x BN, K-slabs of 64, 256 threads = 4 waves in 2x2, each
-// wave (BM/2) x (BN/2) of MFMA 32x32x16 blocks.
-// Operand slabs go global -> LDS directly (global_load_lds_dwordx4: each wave
-// instruction fills 1 KB = 8 rows x 128 B), NS slabs deep, so NS-1 slabs are
-// in flight while one is multiplied; one barrier per slab. Inside a 128-byte
-// row the 16-byte chunks are XOR-swizzled by (row & 7), which makes the
-// fragment reads of 8 consecutive rows hit 8 different bank groups.
+// Workgroup tile BM x BN (BM, BN multiples of 64), K-slabs of BK = 32 or 64,
+// 256 threads = 4 waves in 2x2, each wave (BM/2) x (BN/2) of MFMA 32x32x16
+// blocks. Operand slabs go global -> LDS directly (global_load_lds_dwordx4:
+// each wave instruction fills 1 KB of whole rows), NS slabs deep, one barrier
+// per slab. A slab's fragments are read into registers during the previous
+// slab's MFMAs, and the DMA and LDS-read instructions are spread between the
+// MFMAs, so neither the address unit nor the LDS stalls the matrix core in
+// bursts. The 16-byte chunks of an LDS row are XOR-swizzled so that the
+// fragment reads of 16 consecutive rows fall in 16 distinct bank slots.
+// The epilogue stages each 32-row block of results in LDS and writes global
+// memory in whole row segments.
 // Tile order is XCD-aware: the grid is padded to a multiple of the 8 XCDs and
 // each XCD gets a contiguous run of tiles, M fastest, so the tiles sharing a
 // weight slab share an L2.
+#include <type_traits>
+
 #include "fh_common.h"
 #include "fh_kernels.h"
 
@@ -25,41 +30,21 @@ namespace {
 
 constexpr int KALIGN = 64;  // K must be a multiple of this (either slab depth divides it)
 
-template <int EPI>
-__device__ __forceinline__ void epilogue4(const EpiArgs& ep, int m, int n, f32x4 v) {
-  const float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
-  float c0 = v[0] + b.x, c1 = v[1] + b.y, c2 = v[2] + b.z, c3 = v[3] + b.w;
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16) {
-    if constexpr (EPI == EPI_GELU_BF16) {
-      c0 = gelu_tanh(c0); c1 = gelu_tanh(c1); c2 = gelu_tanh(c2); c3 = gelu_tanh(c3);
-    }
-    const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
-    *reinterpret_cast<u32x2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
-  } else if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES) {
-    f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
-    f32x4 x = *xp;
-    if constexpr (EPI == EPI_GATED_RES) {
-      const int lane = m / ep.rows_per_lane;
-      const float4 gt = *reinterpret_cast<const float4*>(ep.gate_tab + n);
-      const float4 ge = *reinterpret_cast<const float4*>(ep.gate_e0 + (int64_t)lane * ep.gate_stride + n);
-      c0 *= gt.x + ge.x; c1 *= gt.y + ge.y; c2 *= gt.z + ge.z; c3 *= gt.w + ge.w;
-    }
-    x[0] += c0; x[1] += c1; x[2] += c2; x[3] += c3;
-    *xp = x;
-  } else {  // EPI_SPLIT_T
-    if (n < ep.split) {
-      const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
-      *reinterpret_cast<u32x2*>(ep.out_bf + (int64_t)m * ep.ldo + n) = w;
-    } else {
-      const int lane = m / ep.rows_per_lane, t = m - lane * ep.rows_per_lane;
-      bf16_t* o = ep.out_t + ((int64_t)lane * ep.t_cols + (n - ep.split)) * ep.rows_per_lane + t;
-      o[0] = f2bf(c0);
-      o[ep.rows_per_lane] = f2bf(c1);
-      o[2 * ep.rows_per_lane] = f2bf(c2);
-      o[3 * ep.rows_per_lane] = f2bf(c3);
-    }
-  }
-}
+// Epilogue staging. After the main loop each wave owns the 32-row blocks of
+// its (BM/2) x C sub-tile, C = BN/2 columns. A block goes through the wave's
+// own LDS region so that global memory is written (and, for the residual
+// forms, read) in whole contiguous row segments instead of one 16-byte piece
+// of each of 32 rows per instruction. Row pitches carry 16 bytes of padding
+// against LDS bank conflicts.
+template <int C>
+struct Stage {
+  static constexpr int PB = 2 * C + 16;  // bf16 block [32][C]
+  static constexpr int PF = 4 * C + 16;  // f32 block [32][C]
+  static constexpr int PT = 64 + 16;     // bf16 transposed block [C][32]
+  static constexpr int BYTES = (32 * PF > C * PT ? 32 * PF : C * PT);
+};
+
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int BK, int NS>
 constexpr int smem_bytes() { return NS * (BM + BN) * BK * 2; }
@@ -86,8 +71,8 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   constexpr int GA = BM / RG / 4;      // 1 KB DMA groups per wave per slab, activations
   constexpr int GW = BN / RG / 4;      // ... weights
   constexpr int SLAB = (BM + BN) * ROWB;
-  constexpr int INFLIGHT = (NS - 2) * (GA + GW);  // DMAs of younger slabs allowed in flight
-  static_assert(GA >= 1 && GW >= 1 && INFLIGHT < 64, "tile shape");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && GA * RG * 4 == BM && GW * RG * 4 == BN, "tile shape");
+  static_assert(NS >= 2 && (NS - 1) * (GA + GW) < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
 
   int bid = blockIdx.x;
@@ -119,13 +104,11 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
     gw[i] = W + (int64_t)(n0 + r) * ldw + ((lane % CH) ^ swz<BK>(r)) * 8;
   }
 
-  auto issue = [&](int buf, int k0) {
+  // one DMA instruction d of a slab: d < GA an activation group, else a weight group
+  auto dma_one = [&](int d, int buf, int k0) {
     char* sa = smem + buf * SLAB;
-    char* sw = sa + BM * ROWB;
-#pragma unroll
-    for (int i = 0; i < GA; ++i) dma16(ga[i] + k0, sa + (wave + 4 * i) * 1024);
-#pragma unroll
-    for (int i = 0; i < GW; ++i) dma16(gw[i] + k0, sw + (wave + 4 * i) * 1024);
+    if (d < GA) dma16(ga[d] + k0, sa + (wave + 4 * d) * 1024);
+    else dma16(gw[d - GA] + k0, sa + BM * ROWB + (wave + 4 * (d - GA)) * 1024);
   };
 
   f32x16 acc[NI][MI];
@@ -136,61 +119,175 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment rows: activations wm*BM/2 + 32 j + lr, weights wn*BN/2 + 32 i + lr
+  // Fragments of a whole slab are held in registers, in two sets: while the
+  // MFMAs of slab kt run on one set, the fragments of slab kt + 1 are read
+  // into the other. Rows: activations wm*BM/2 + 32 j + lr, weights
+  // wn*BN/2 + 32 i + lr; k-step kk covers the slab's k-columns 16 kk .. +15.
+  constexpr int KK = BK / 16, P = NI * MI, NR = NI + MI, DPS = GA + GW;
+  constexpr int SLOTS = KK * P, READS = KK * NR;
   const int xr = swz<BK>(lr);
-  auto compute = [&](int buf) {
-    const char* sa = smem + buf * SLAB + (wm * (BM / 2) + lr) * ROWB;
-    const char* sw = smem + buf * SLAB + BM * ROWB + (wn * (BN / 2) + lr) * ROWB;
-    // fragments of k-step kk+1 are read while the MFMAs of k-step kk run
-    bf16x8 wf[2][NI], af[2][MI];
-    auto read = [&](int set, int kk) {
-      const int off = ((2 * kk + lh) ^ xr) * 16;
+  const int a_row = (wm * (BM / 2) + lr) * ROWB, w_row = BM * ROWB + (wn * (BN / 2) + lr) * ROWB;
+  bf16x8 wf[2][KK][NI], af[2][KK][MI];
+  // fragment read r of a slab: k-step r / NR; r % NR < NI a weight block, else activations
+  auto read_one = [&](int r, int set, int buf) {
+    const int kk = r / NR, q = r % NR;
+    const char* sb = smem + buf * SLAB + (((2 * kk + lh) ^ xr) * 16);
+    if (q < NI) wf[set][kk][q] = *reinterpret_cast<const bf16x8*>(sb + w_row + q * 32 * ROWB);
+    else af[set][kk][q - NI] = *reinterpret_cast<const bf16x8*>(sb + a_row + (q - NI) * 32 * ROWB);
+  };
+  // The slab's MFMAs on register set `set`, with the next slab's fragment
+  // reads (read r after MFMA slot r*SLOTS/READS) and this iteration's DMA
+  // instructions (d after slot d*SLOTS/DPS) spread between them, so the LDS
+  // and the address unit work while the matrix core is busy instead of
+  // stalling every wave on a burst of requests.
+  auto mma_slab = [&](auto set_c, int rbuf, int dbuf, int dk0) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) wf[set][i] = *reinterpret_cast<const bf16x8*>(sw + i * 32 * ROWB + off);
-#pragma unroll
-      for (int j = 0; j < MI; ++j) af[set][j] = *reinterpret_cast<const bf16x8*>(sa + j * 32 * ROWB + off);
-    };
-    read(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) read((kk + 1) & 1, kk + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next reads ahead of these MFMAs
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < MI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][i], af[kk & 1][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int j = 0; j < MI; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[set][kk][i], af[set][kk][j], acc[i][j], 0, 0, 0);
+          const int slot = kk * P + i * MI + j;
+#pragma unroll
+          for (int r = 0; r < READS; ++r)
+            if (r * SLOTS / READS == slot) read_one(r, set ^ 1, rbuf);
+#pragma unroll
+          for (int d = 0; d < DPS; ++d)
+            if (d * SLOTS / DPS == slot) dma_one(d, dbuf, dk0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
   };
 
+  // Slab kt lives in buffer kt % NS. Slabs 0 .. NS-1 are fetched up front.
+  // Iteration kt waits until slab kt + 1 has landed and every wave holds the
+  // fragments of slab kt in registers, then (one barrier) multiplies slab kt
+  // while it reads slab kt + 1's fragments and refills buffer kt % NS with
+  // slab kt + NS, which then has NS - 1 iterations to land. Slabs past the
+  // end re-fetch the last one into buffers nobody reads, which keeps the
+  // wait counts uniform.
   const int KT = K / BK;
-  // prologue: slabs 0 .. NS-2 in flight (slabs past the end re-fetch the last
-  // one into buffers nobody reads, keeping the wait count uniform)
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, KT - 1) * BK);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_vm<INFLIGHT>();   // this wave's DMAs of slab kt have landed
-    barrier();             // everyone's have; everyone is done with slab kt-1
-    issue((kt + NS - 1) % NS, min(kt + NS - 1, KT - 1) * BK);
-    compute(kt % NS);
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int d = 0; d < DPS; ++d) dma_one(d, s, min(s, KT - 1) * BK);
+  wait_vm<(NS - 1) * DPS>();
+  barrier();
+#pragma unroll
+  for (int r = 0; r < READS; ++r) read_one(r, 0, 0);
+  auto iteration = [&](int kt, auto set_c) {
+    wait_vm<(NS - 2) * DPS>();  // this wave's DMAs of slab kt + 1 have landed
+    wait_lgkm0();               // and its fragments of slab kt are in registers
+    barrier();                  // so for every wave: slab kt + 1 is in, buffer kt % NS is free
+    mma_slab(set_c, (kt + 1) % NS, kt % NS, min(kt + NS, KT - 1) * BK);
+  };
+  // two slabs per trip so that the register set of each is a constant
+  for (int kt = 0; kt < KT; kt += 2) {
+    iteration(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < KT) iteration(kt + 1, std::integral_constant<int, 1>{});
   }
   wait_vm<0>();
 
   // result (i, j): lane holds row m = m0 + wm*BM/2 + j*32 + lr and columns
   // n = n0 + wn*BN/2 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]
+  constexpr int C = BN / 2;
+  using ST = Stage<C>;
+  static_assert(4 * ST::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
+  wait_lgkm0();
+  barrier();  // every wave is done with the slab buffers (its DMAs landed above)
+  char* st = smem + wave * ST::BYTES;
+  const int nw = n0 + wn * C;  // first column of this wave's sub-tile
+  // the transposed form applies to a whole sub-tile (split is a multiple of BN)
+  const bool transposed = EPI == EPI_SPLIT_T && nw >= ep.split;
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
-    const int m = m0 + wm * (BM / 2) + j * 32 + lr;
-    if (m >= M) continue;
+    const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
+    if (mb >= M) break;
+    if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES) {
+      // raw f32 sums -> LDS; then x[m, n..n+3] += (sum + bias) * gate, by rows
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (BN / 2) + i * 32 + 8 * g + 4 * lh;
-        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        epilogue4<EPI>(ep, m, n, v);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(st + lr * ST::PF + (i * 32 + 8 * g + 4 * lh) * 4) = v;
+        }
+      lds_fence();
+#pragma unroll
+      for (int it = 0; it < 32 * C / 4 / 64; ++it) {
+        const int c = it * 64 + lane, row = c / (C / 4), c4 = (c % (C / 4)) * 4;
+        const int m = mb + row, n = nw + c4;
+        if (m < M) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(ep.bias + n);
+          f32x4 u = v + b;
+          if constexpr (EPI == EPI_GATED_RES) {
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(ep.gate_tab + n);
+            const f32x4 ge = *reinterpret_cast<const f32x4*>(ep.gate_e0 + (int64_t)(m / ep.rows_per_lane) * ep.gate_stride + n);
+            u = u * (gt + ge);
+          }
+          f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
+          *xp = *xp + u;
+        }
       }
+      lds_fence();
+    } else {
+      if (!transposed) {
+        // (sum + bias [, GELU]) as bf16 -> LDS; then 16-byte pieces of rows
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = nw + i * 32 + 8 * g + 4 * lh;
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
+            float c0 = acc[i][j][4 * g] + b.x, c1 = acc[i][j][4 * g + 1] + b.y;
+            float c2 = acc[i][j][4 * g + 2] + b.z, c3 = acc[i][j][4 * g + 3] + b.w;
+            if constexpr (EPI == EPI_GELU_BF16) {
+              c0 = gelu_tanh(c0); c1 = gelu_tanh(c1); c2 = gelu_tanh(c2); c3 = gelu_tanh(c3);
+            }
+            const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
+            *reinterpret_cast<u32x2*>(st + lr * ST::PB + (i * 32 + 8 * g + 4 * lh) * 2) = w;
+          }
+        lds_fence();
+#pragma unroll
+        for (int it = 0; it < 32 * C / 8 / 64; ++it) {
+          const int c = it * 64 + lane, row = c / (C / 8), c8 = (c % (C / 8)) * 8;
+          const int m = mb + row;
+          if (m < M)
+            *reinterpret_cast<u32x4*>(ep.out_bf + (int64_t)m * ep.ldo + nw + c8) =
+                *reinterpret_cast<const u32x4*>(st + row * ST::PB + c8 * 2);
+        }
+        lds_fence();
+      } else {
+        // (sum + bias) as bf16, transposed -> LDS [C][32]; then 8 consecutive
+        // tokens of one output column per 16-byte piece
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int nl = i * 32 + 8 * g + 4 * lh;
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + nw + nl);
+            bf16_t* sp = reinterpret_cast<bf16_t*>(st + nl * ST::PT) + lr;
+            sp[0] = f2bf(acc[i][j][4 * g] + b.x);
+            sp[ST::PT / 2] = f2bf(acc[i][j][4 * g + 1] + b.y);
+            sp[ST::PT] = f2bf(acc[i][j][4 * g + 2] + b.z);
+            sp[3 * ST::PT / 2] = f2bf(acc[i][j][4 * g + 3] + b.w);
+          }
+        lds_fence();
+#pragma unroll
+        for (int it = 0; it < C * 4 / 64; ++it) {
+          const int c = it * 64 + lane, nl = c / 4, t8 = (c % 4) * 8;
+          const int m = mb + t8;  // 8 rows, never across a lane: rows_per_lane % 8 == 0
+          if (m < M) {
+            const int bl = m / ep.rows_per_lane, t = m - bl * ep.rows_per_lane;
+            bf16_t* o = ep.out_t + ((int64_t)bl * ep.t_cols + (nw + nl - ep.split)) * ep.rows_per_lane + t;
+            *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(st + nl * ST::PT + t8 * 2);
+          }
+        }
+        lds_fence();
+      }
+    }
   }
 }
 
@@ -198,6 +295,9 @@ template <int BM, int BN, int BK, int NS>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                   const EpiArgs& ep, hipStream_t s) {
   if (N % BN) return hipErrorInvalidValue;
+  if (epi == EPI_SPLIT_T && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8))
+    return hipErrorInvalidValue;
+  if (epi == EPI_GATED_RES && ep.rows_per_lane <= 0) return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles + 7) / 8 * 8), block(256);
@@ -215,13 +315,15 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
 }  // namespace
 
 // Tile choice from measurements of the slice shapes on MI355X with weights
-// cold in HBM (as in a 30-block slice): big tiles (less L2->LDS traffic per
-// FLOP) where they still give enough workgroups, smaller ones otherwise.
+// cold in HBM (as in a 30-block slice). Big tiles need less L2->LDS traffic
+// per FLOP; the counts are chosen so one round of tiles about fills the 256
+// CUs (e.g. FFN-up at 1280 tokens: 7 x 35 = 245 tiles of 192 x 256).
 int gemm_tile_choice(int M, int N, int K) {
-  const int64_t t256 = (int64_t)((M + 255) / 256) * (N / 256);
-  if (N % 256 == 0 && N >= 4096 && t256 >= 170) return 0;  // 256x256, K-slab 64, 2 stages
-  if (N <= 2048 && M <= 1536) return K >= 4096 ? 2 : 3;     // 128x64 k64 s4 | 64x64 k64 s4
-  return 1;                                                 // 128x128 k32 s4
+  (void)K;
+  if (M <= 256) return 3;                                   // 64x128 k64 s4 (audio K/V)
+  if (N % 256 == 0 && N >= 8192) return M <= 1536 ? 0 : 1;  // 192x256 k32 s3 | s4
+  if (M <= 1536 && N <= 2048) return 2;                     // 128x64 k64 s4
+  return 4;                                                 // 192x128 k64 s3
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -229,10 +331,11 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
   if (M <= 0) return hipSuccess;
   if (N % 128 || K % KALIGN || lda % 8 || ldw % 8) return hipErrorInvalidValue;
   switch (gemm_tile_choice(M, N, K)) {
-    case 0: return launch<256, 256, 64, 2>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 1: return launch<128, 128, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 0: return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 1: return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 2: return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    default: return launch<64, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 3: return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    default: return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
 }
 
