@@ -38,6 +38,7 @@ struct WS {
   float* x;
   bf16_t *h, *qk, *vt, *ao, *qc, *u, *aud, *kc, *vct;
   float *emb, *t1, *e, *e0, *rcos, *rsin;
+  float* part;  // split-K partial sums of the width-D residual GEMMs, [2][B*N, D]
   size_t total;
 };
 
@@ -143,6 +144,7 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.e0 = (float*)take(R * 6 * D * 4);
   w.rcos = (float*)take(N * (g.head_dim / 2) * 4);
   w.rsin = (float*)take(N * (g.head_dim / 2) * 4);
+  w.part = (float*)take(2 * B * N * D * 4);
   w.total = off;
   return w;
 }
@@ -192,15 +194,19 @@ int audio_kv(fh_ctx* c, const WBlock& wb, int B, bf16_t* kc, bf16_t* vct, const 
   return FH_OK;
 }
 
+// pend_in: a residual update left pending by the previous block (applied by
+// the first LayerNorm); pend_out: if non-null, the FFN output projection may
+// leave its residual update pending there (split K) instead of applying it.
 int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int e0_stride,
-              const bf16_t* kc, const bf16_t* vct, const WS& ws, hipStream_t s) {
+              const bf16_t* kc, const bf16_t* vct, const WS& ws, hipStream_t s,
+              const fh::PendingRes* pend_in, fh::PendingRes* pend_out) {
   const fh_config& g = c->cfg;
   const int N = c->N, D = g.dim, M = B * N, Fd = g.ffn_dim;
   const float scale = 1.0f / std::sqrt((float)g.head_dim);
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
-                              nullptr, nullptr, s));
+                              nullptr, nullptr, pend_in, s));
   }
   {
     Timed t(c, FH_K_GEMM_QKV, s);
@@ -238,7 +244,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, nullptr, nullptr, nullptr, nullptr, 0, wb.norm3_g,
-                              wb.norm3_b, s));
+                              wb.norm3_b, nullptr, s));
   }
   {
     Timed t(c, FH_K_GEMM_CQ, s);
@@ -269,7 +275,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D,
-                              e0 + 4 * D, e0_stride, nullptr, nullptr, s));
+                              e0 + 4 * D, e0_stride, nullptr, nullptr, nullptr, s));
   }
   {
     Timed t(c, FH_K_GEMM_FFN1, s);
@@ -289,7 +295,19 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.gate_e0 = e0 + 5 * D;
     ep.gate_stride = e0_stride;
     ep.rows_per_lane = N;
-    FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ep, s));
+    if (pend_out && fh::gemm_splitk_ok(M, D, Fd)) {
+      FH_HIP(fh::gemm_bf16_splitk(ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ws.part, (size_t)2 * M * D, s));
+      pend_out->part = ws.part;
+      pend_out->nparts = 2;
+      pend_out->bias = ep.bias;
+      pend_out->gate_tab = ep.gate_tab;
+      pend_out->gate_e0 = ep.gate_e0;
+      pend_out->gate_stride = ep.gate_stride;
+      pend_out->rows_per_lane = N;
+    } else {
+      if (pend_out) *pend_out = fh::PendingRes();
+      FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ep, s));
+    }
   }
   return FH_OK;
 }
@@ -323,14 +341,18 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       const float* e = ws.e + (size_t)(st - c0) * D;
       const float* e0 = ws.e0 + (size_t)(st - c0) * 6 * D;
       FH_HIP(fh::patch_embed(out, B, C, N, w->patch_w, w->patch_b, ws.x, D, s));
+      // each block's FFN residual update may stay pending until the next LayerNorm
+      fh::PendingRes pend;
       for (int i = 0; i < g.n_blocks; ++i) {
+        fh::PendingRes next;
         int rc = run_block(c, w->blk[i], B, ws.x, e0, 0, ws.kc + i * slot_elems(c, B),
-                           ws.vct + i * slot_elems(c, B), ws, s);
+                           ws.vct + i * slot_elems(c, B), ws, s, &pend, &next);
         if (rc) return rc;
+        pend = next;
       }
       // head: LN modulated by (head.mod + e), then W_h, Euler step and motion pin
       FH_HIP(fh::layernorm_bf16(ws.x, ws.h, B * N, D, N, g.eps, w->head_mod, w->head_mod + D, e, e, 0,
-                                nullptr, nullptr, s));
+                                nullptr, nullptr, &pend, s));
       FH_HIP(fh::head_euler(ws.h, B, N, D, w->head_w, w->head_b, g.out_ch, out, out, motion, nmt,
                             sigmas[st + 1] - sigmas[st], s));
     }
@@ -496,7 +518,12 @@ int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, f
     FH_HIP(fh::gemv_bf16(temb + (size_t)r0 * D, R, D, w->time_proj_w, w->time_proj_b,
                          wsp.e0 + (size_t)r0 * 6 * D, 6 * D, 1, 0, s));
   }
-  return run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s);
+  // the same arithmetic as inside a slice: a pending FFN residual is applied at the end
+  fh::PendingRes pend;
+  rc = run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s, nullptr, &pend);
+  if (rc) return rc;
+  FH_HIP(fh::residual_from_parts(x, D, pend, batch * c->N, D, s));
+  return FH_OK;
 }
 
 int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float* latent,

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-typedef uint16_t bf16_t;
+#include "fh_common.h"
 
 namespace fh {
 
@@ -15,6 +15,7 @@ enum Epi {
   EPI_RES = 3,        // x[m, n] += C + bias
   EPI_SPLIT_T = 4,    // n < split: out_bf[m, n] = bf16(C + bias);
                       // n >= split: out_t[lane][n - split][m mod rows] = bf16(C + bias)
+  EPI_PARTIAL = 5,    // internal to gemm_bf16 (split K): part[k-part][m, n] = C over that K range
 };
 
 struct EpiArgs {
@@ -30,18 +31,55 @@ struct EpiArgs {
   bf16_t* out_t = nullptr;         // [lanes, t_cols, rows_per_lane]
   int split = 0;
   int t_cols = 0;                   // N - split
+  float* part = nullptr;             // EPI_PARTIAL: [splits][M][N]
+  size_t part_elems = 0;
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s);
 
+// A residual update x[m, n] += gate[lane(m), n] * (part[0][m, n] + ... + bias[n])
+// that a later kernel applies: a residual GEMM with its K split writes the
+// parts, and the next LayerNorm of x (or residual_from_parts) adds them, in
+// index order, so the result does not depend on scheduling.
+struct PendingRes {
+  const float* part = nullptr;       // [nparts][M][N]; nullptr = nothing pending
+  int nparts = 0;
+  const float* bias = nullptr;       // [N]
+  const float* gate_tab = nullptr;   // [N], nullptr = no gate
+  const float* gate_e0 = nullptr;    // [lanes, gate_stride]
+  int gate_stride = 0;
+  int rows_per_lane = 1;
+};
+
+// x[m, n..n+3] with the pending update applied (parts are [nparts][M][N]).
+__device__ __forceinline__ f32x4 apply_pending(const PendingRes& r, f32x4 x, int m, int n, int M, int N) {
+  const int64_t i = (int64_t)m * N + n, MN = (int64_t)M * N;
+  f32x4 v = *reinterpret_cast<const f32x4*>(r.part + i);
+  for (int k = 1; k < r.nparts; ++k) v = v + *reinterpret_cast<const f32x4*>(r.part + k * MN + i);
+  f32x4 u = v + *reinterpret_cast<const f32x4*>(r.bias + n);
+  if (r.gate_tab) {
+    const f32x4 gt = *reinterpret_cast<const f32x4*>(r.gate_tab + n);
+    const f32x4 ge = *reinterpret_cast<const f32x4*>(r.gate_e0 + (int64_t)(m / r.rows_per_lane) * r.gate_stride + n);
+    u = u * (gt + ge);
+  }
+  return x + u;
+}
+
+// Split-K form of the residual GEMMs: the two halves of K into part[0..1].
+bool gemm_splitk_ok(int M, int N, int K);
+hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                            float* part, size_t part_elems, hipStream_t s);
+hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s);
+
 // LayerNorm of fp32 rows (width D) to bf16. Modulated form (g == nullptr):
 //   out = LN(x) * (1 + tab_scale + e_scale[lane]) + tab_shift + e_shift[lane]
-// Affine form: out = LN(x) * g + b.
-hipError_t layernorm_bf16(const float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
+// Affine form: out = LN(x) * g + b. With a pending residual update (pend and
+// pend->part non-null, parts [nparts][rows][D]) x is first updated in place.
+hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
                           const float* tab_shift, const float* tab_scale, const float* e_shift,
                           const float* e_scale, int e_stride, const float* g, const float* b,
-                          hipStream_t s);
+                          const PendingRes* pend, hipStream_t s);
 
 // In-place RMSNorm over the first D columns of bf16 rows (stride ld), gain g0;
 // with nparts == 2 also columns [D, 2D) with gain g1. If cos_t != nullptr the

@@ -62,7 +62,7 @@ __device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7)
 template <int EPI, int BM, int BN, int BK, int NS>
 __global__ __launch_bounds__(256, (smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
-                  int M, int N, int K, int tiles_m, int tiles, EpiArgs ep) {
+                  int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
   constexpr int ROWB = BK * 2;         // bytes per LDS row of a slab
   constexpr int CH = BK / 8;           // 16-byte chunks per row
   constexpr int RG = 64 / CH;          // rows per 1 KB DMA group
@@ -78,9 +78,14 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
   bid = (bid & 7) * per_xcd + (bid >> 3);
-  if (bid >= tiles) return;
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  if (bid >= tiles * splits) return;
+  // split ks of K (splits > 1 only with EPI_PARTIAL) covers columns [ks K/splits, (ks+1) K/splits)
+  const int ks = bid / tiles, tile = bid - ks * tiles;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
+  K /= splits;
+  A += (int64_t)ks * K;
+  W += (int64_t)ks * K;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -204,8 +209,9 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   for (int j = 0; j < MI; ++j) {
     const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
     if (mb >= M) break;
-    if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES) {
-      // raw f32 sums -> LDS; then x[m, n..n+3] += (sum + bias) * gate, by rows
+    if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES || EPI == EPI_PARTIAL) {
+      // raw f32 sums -> LDS; then by rows: x[m, n..n+3] += (sum + bias) * gate,
+      // or (split K) the sums alone into this split's part
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -218,7 +224,10 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
       for (int it = 0; it < 32 * C / 4 / 64; ++it) {
         const int c = it * 64 + lane, row = c / (C / 4), c4 = (c % (C / 4)) * 4;
         const int m = mb + row, n = nw + c4;
-        if (m < M) {
+        if (m < M && EPI == EPI_PARTIAL) {
+          *reinterpret_cast<f32x4*>(ep.part + ((int64_t)ks * M + m) * N + n) =
+              *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
+        } else if (m < M) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
           const f32x4 b = *reinterpret_cast<const f32x4*>(ep.bias + n);
           f32x4 u = v + b;
@@ -291,24 +300,40 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   }
 }
 
+// x[m, n] += gate * (sum_s part[s][m, n] + bias[n]) (gate = 1 without a table),
+// the parts added in index order; 4 columns per thread
+__global__ __launch_bounds__(256) void residual_from_parts_kernel(float* __restrict__ x, int ldx, PendingRes r,
+                                                                  int M, int N) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+  f32x4* xp = reinterpret_cast<f32x4*>(x + (int64_t)m * ldx + n);
+  *xp = apply_pending(r, *xp, m, n, M, N);
+}
+
 template <int BM, int BN, int BK, int NS>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
-                  const EpiArgs& ep, hipStream_t s) {
-  if (N % BN) return hipErrorInvalidValue;
+                  const EpiArgs& ep, hipStream_t s, int splits = 1) {
+  if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
   if (epi == EPI_SPLIT_T && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8))
     return hipErrorInvalidValue;
   if (epi == EPI_GATED_RES && ep.rows_per_lane <= 0) return hipErrorInvalidValue;
+  if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
+    return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
-  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
+#define FH_GEMM(E) gemm_bf16_nt<E, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
   switch (epi) {
-    case EPI_BF16: gemm_bf16_nt<EPI_BF16, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
-    case EPI_GELU_BF16: gemm_bf16_nt<EPI_GELU_BF16, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
-    case EPI_GATED_RES: gemm_bf16_nt<EPI_GATED_RES, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
-    case EPI_RES: gemm_bf16_nt<EPI_RES, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
-    case EPI_SPLIT_T: gemm_bf16_nt<EPI_SPLIT_T, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, ep); break;
+    case EPI_BF16: FH_GEMM(EPI_BF16); break;
+    case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;
+    case EPI_GATED_RES: FH_GEMM(EPI_GATED_RES); break;
+    case EPI_RES: FH_GEMM(EPI_RES); break;
+    case EPI_SPLIT_T: FH_GEMM(EPI_SPLIT_T); break;
+    case EPI_PARTIAL: FH_GEMM(EPI_PARTIAL); break;
     default: return hipErrorInvalidValue;
   }
+#undef FH_GEMM
   return hipGetLastError();
 }
 
@@ -326,10 +351,33 @@ int gemm_tile_choice(int M, int N, int K) {
   return 4;                                                 // 192x128 k64 s3
 }
 
+bool gemm_splitk_ok(int M, int N, int K) {
+  // residual GEMMs of width <= 2048 with a long K at up to 1536 tokens: 128 x 128
+  // tiles over two halves of K fill the chip with less operand traffic per FLOP
+  // than 128 x 64 tiles; short K does not pay for the extra pass over the parts
+  return M > 0 && M <= 1536 && N % 128 == 0 && N <= 2048 && K >= 4096 && K % 128 == 0;
+}
+
+hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                            float* part, size_t part_elems, hipStream_t s) {
+  if (!gemm_splitk_ok(M, N, K) || lda % 8 || ldw % 8) return hipErrorInvalidValue;
+  EpiArgs ep;
+  ep.part = part;
+  ep.part_elems = part_elems;
+  return launch<128, 128, 64, 4>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
+}
+
+hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s) {
+  if (M <= 0 || !r.part) return hipSuccess;
+  if (N % 4 || ldx % 4 || r.nparts < 1 || (r.gate_tab && r.rows_per_lane <= 0)) return hipErrorInvalidValue;
+  residual_from_parts_kernel<<<(unsigned)(((int64_t)M * N / 4 + 255) / 256), 256, 0, s>>>(x, ldx, r, M, N);
+  return hipGetLastError();
+}
+
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (N % 128 || K % KALIGN || lda % 8 || ldw % 8) return hipErrorInvalidValue;
+  if (N % 128 || K % KALIGN || lda % 8 || ldw % 8 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
   switch (gemm_tile_choice(M, N, K)) {
     case 0: return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 1: return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);

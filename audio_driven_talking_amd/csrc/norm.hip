@@ -23,21 +23,27 @@ __device__ __forceinline__ float group_sum(float v, float* red, int w0, int nw) 
 }
 
 __global__ __launch_bounds__(256) void layernorm_kernel(
-    const float* __restrict__ x, bf16_t* __restrict__ out, int D, int rows_per_lane, float eps,
+    float* __restrict__ x, bf16_t* __restrict__ out, int rows, int D, int rows_per_lane, float eps,
     const float* __restrict__ tab_shift, const float* __restrict__ tab_scale,
     const float* __restrict__ e_shift, const float* __restrict__ e_scale, int e_stride,
-    const float* __restrict__ g, const float* __restrict__ b) {
+    const float* __restrict__ g, const float* __restrict__ b, PendingRes pend) {
   __shared__ float red[8];
   const int row = blockIdx.x;
   const int c = threadIdx.x * 8;
   const bool on = c < D;
-  const float* xr = x + (int64_t)row * D + c;
+  float* xr = x + (int64_t)row * D + c;
   float v[8];
   if (on) {
-    const float4 a0 = reinterpret_cast<const float4*>(xr)[0];
-    const float4 a1 = reinterpret_cast<const float4*>(xr)[1];
-    v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-    v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    f32x4 a0 = reinterpret_cast<const f32x4*>(xr)[0];
+    f32x4 a1 = reinterpret_cast<const f32x4*>(xr)[1];
+    if (pend.part) {  // finish the residual update of x first, and store it
+      a0 = apply_pending(pend, a0, row, c, rows, D);
+      a1 = apply_pending(pend, a1, row, c + 4, rows, D);
+      reinterpret_cast<f32x4*>(xr)[0] = a0;
+      reinterpret_cast<f32x4*>(xr)[1] = a1;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a0[e]; v[e + 4] = a1[e]; }
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
@@ -128,14 +134,20 @@ int threads_for(int D) { return ((D / 8 + 63) / 64) * 64; }
 
 }  // namespace
 
-hipError_t layernorm_bf16(const float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
+hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
                           const float* tab_shift, const float* tab_scale, const float* e_shift,
                           const float* e_scale, int e_stride, const float* g, const float* b,
-                          hipStream_t s) {
+                          const PendingRes* pend, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (D % 8 || threads_for(D) > 256) return hipErrorInvalidValue;
-  layernorm_kernel<<<rows, threads_for(D), 0, s>>>(x, out, D, rows_per_lane, eps, tab_shift, tab_scale,
-                                                   e_shift, e_scale, e_stride, g, b);
+  PendingRes p;
+  if (pend && pend->part) {
+    if (pend->nparts < 1 || !pend->bias || (pend->gate_tab && pend->rows_per_lane <= 0))
+      return hipErrorInvalidValue;
+    p = *pend;
+  }
+  layernorm_kernel<<<rows, threads_for(D), 0, s>>>(x, out, rows, D, rows_per_lane, eps, tab_shift, tab_scale,
+                                                   e_shift, e_scale, e_stride, g, b, p);
   return hipGetLastError();
 }
 
