@@ -21,7 +21,6 @@ namespace fh {
 namespace {
 
 constexpr int HD = 128;
-constexpr int QT = 128;
 constexpr int KB = 64;
 
 __device__ __forceinline__ bf16x8 load_v_frag(const bf16_t* p) {
@@ -232,15 +231,19 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void cross_attn_kernel(
+// Cross-attention: one wave (workgroup) per 32 queries of one (lane, head),
+// so a slice launches one wave per 32 tokens and head across the whole chip.
+// Keys are the audio tokens of the query's latent frame (or all of them);
+// each key block's K and V fragments are requested together, straight from
+// global memory (they are small and shared through L2), before the scores.
+__global__ __launch_bounds__(64) void cross_attn_kernel(
     const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc, int ldk,
     const bf16_t* __restrict__ vct, bf16_t* __restrict__ o, int ldo, int N, int La, int D, int hw,
     int apf, int full, float scale_log2) {
   const int b = blockIdx.z, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
-  const int q0 = blockIdx.x * QT + wave * 32;
-  if (q0 >= N) return;
+  const int q0 = blockIdx.x * 32;
 
   bf16x8 qf[8];
   {
@@ -260,14 +263,20 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
+    bf16x8 kf[8], vf[2][4];
+    const bf16_t* kp = kc + ((int64_t)b * La + k0 + lr) * ldk + h * HD + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vf[u][dt] = load_v_frag(vct + ((int64_t)b * D + h * HD + 32 * dt + lr) * La + k0 + 16 * u + 4 * lh);
     f32x16 st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.f;
-    const bf16_t* kp = kc + ((int64_t)b * La + k0 + lr) * ldk + h * HD + 8 * lh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * s),
-                                                   qf[s], st, 0, 0, 0);
+    for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], st, 0, 0, 0);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -294,10 +303,7 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(
     for (int u = 0; u < 2; ++u) {
       const bf16x8 pf = p_frag(st, u);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16_t* vp = vct + ((int64_t)b * D + h * HD + 32 * dt + lr) * La + k0 + 16 * u + 4 * lh;
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_v_frag(vp), pf, acc[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < 4; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u][dt], pf, acc[dt], 0, 0, 0);
     }
   }
   l_run += __shfl_xor(l_run, 32, 64);
@@ -325,8 +331,8 @@ hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const
     return hipErrorInvalidValue;
   if (!full && (N / hw) * apf > La) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid((N + QT - 1) / QT, n_heads, B);
-  cross_attn_kernel<<<grid, 256, 0, s>>>(q, ldq, kc, ldk, vct, o, ldo, N, La, n_heads * HD, hw, apf,
+  dim3 grid(N / 32, n_heads, B);
+  cross_attn_kernel<<<grid, 64, 0, s>>>(q, ldq, kc, ldk, vct, o, ldo, N, La, n_heads * HD, hw, apf,
                                          full, scale_log2);
   return hipGetLastError();
 }
