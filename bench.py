@@ -7,9 +7,10 @@ embedding, head and motion pin) of a batch of synthetic inputs already in
 HBM. Prints ONE JSON line. Only one GPU is used; --gpus > 1 exits.
 
 Extra objects on the line:
-  roofline      the FFN up-projection GEMM (the largest kernel): algorithmic
-                FLOPs per launch / its mean duration, timed with HIP events on
-                the launch stream over a second pass of the same K steps.
+  roofline      the FFN down-projection GEMM (the longest kernel; K split in
+                two halves): algorithmic FLOPs per launch / its mean duration,
+                timed with HIP events on the launch stream over a second pass
+                of the same K steps.
   cpu_baseline  the float64 numpy oracle timed on this host on a bounded
                 sample of the same workload (some of the slice's block-steps),
                 scaled to frames/s.
@@ -38,7 +39,7 @@ WORKLOADS = {
     "slice_b3": ("slice", 3, "full Lite slice denoise, batch 3 (three independent streams)"),
     "slice768": ("slice768", 1, "full slice denoise at 768x768, latent 16x5x24x24 (2880 tokens), batch 1"),
 }
-ROOF_KERNEL = "gemm_ffn1"
+ROOF_KERNEL = "gemm_ffn2"
 COPY_BYTES = 256 << 20        # calibration copy: reads and writes this many bytes
 
 
@@ -91,7 +92,7 @@ def traffic_from_profile(kernel_src_hash):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
     size), if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_ffn1_slice_b1_counters.json")
+    path = os.path.join(ROOT, "profiles", "gemm_ffn2_slice_b1_counters.json")
     if not os.path.exists(path):
         return None
     try:
@@ -163,7 +164,7 @@ def main():
     total_flops, hot_flops = flops_per_slice(cfg, B, n_steps)
     value = FRAMES_PER_SLICE * B * args.steps / T
 
-    # roofline kernel: HIP events around each FFN-up launch, same K steps, direct launches
+    # roofline kernel: HIP events around each FFN-down launch, same K steps, direct launches
     fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, fh.FH_K[ROOF_KERNEL])
     step()
     torch.cuda.synchronize()
@@ -181,7 +182,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_from_profile(hashlib.sha256(src).hexdigest()),
-                "kernel": f"{ROOF_KERNEL} (M={M}, N={cfg.ffn_dim}, K={cfg.dim}, "
+                "kernel": f"{ROOF_KERNEL} (M={M}, N={cfg.dim}, K={cfg.ffn_dim}, "
                           f"{k_flops / 1e9:.2f} GFLOP per launch)",
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
 
