@@ -236,10 +236,13 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
 // Keys are the audio tokens of the query's latent frame (or all of them);
 // each key block's K and V fragments are requested together, straight from
 // global memory (they are small and shared through L2), before the scores.
+constexpr int MAXG = 64;  // most column groups of the query sums of squares
+
 __global__ __launch_bounds__(64) void cross_attn_kernel(
     const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc, int ldk,
     const bf16_t* __restrict__ vct, bf16_t* __restrict__ o, int ldo, int N, int La, int D, int hw,
-    int apf, int full, float scale_log2) {
+    int apf, int full, float scale_log2, const float* __restrict__ ssq, int groups,
+    const float* __restrict__ g, float eps) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
@@ -251,6 +254,36 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(
     const bf16_t* qp = q + ((int64_t)b * N + qrow) * ldq + h * HD + 8 * lh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    if (ssq) {
+      // RMSNorm of the query row over the full width, from the column-group sums
+      // all of the row's group sums requested at once (16-byte loads), added in order
+      const f32x4* sp = reinterpret_cast<const f32x4*>(ssq + ((int64_t)b * N + qrow) * groups);
+      f32x4 part[MAXG / 4];
+#pragma unroll
+      for (int p = 0; p < MAXG / 4; ++p)
+        if (4 * p < groups) part[p] = sp[p];
+      float ss = 0.f;
+#pragma unroll
+      for (int p = 0; p < MAXG / 4; ++p)
+        if (4 * p < groups) ss = (((ss + part[p][0]) + part[p][1]) + part[p][2]) + part[p][3];
+      const float rs = rsqrtf(ss / (float)D + eps);
+      const float* gp = g + h * HD + 8 * lh;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp + 16 * s);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 16 * s + 4);
+        const u32x4 raw = __builtin_bit_cast(u32x4, qf[s]);
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          w[e] = pack2bf(__uint_as_float(raw[e] << 16) * rs * g0[2 * e],
+                         __uint_as_float(raw[e] & 0xffff0000u) * rs * g0[2 * e + 1]);
+          w[e + 2] = pack2bf(__uint_as_float(raw[e + 2] << 16) * rs * g1[2 * e],
+                             __uint_as_float(raw[e + 2] & 0xffff0000u) * rs * g1[2 * e + 1]);
+        }
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
   }
   const int k_lo = full ? 0 : (q0 / hw) * apf;
   const int k_hi = full ? La : k_lo + apf;
@@ -325,15 +358,17 @@ hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const 
 
 hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const bf16_t* vct,
                       bf16_t* o, int ldo, int B, int N, int La, int hw, int apf, int full,
-                      int n_heads, float scale, hipStream_t s) {
+                      int n_heads, float scale, const float* ssq, int groups, const float* g, float eps,
+                      hipStream_t s) {
   if (B <= 0 || N <= 0) return hipSuccess;
   if (N % 32 || hw % 32 || apf % 32 || La % 32 || ldq % 8 || ldk % 8 || ldo % 4)
     return hipErrorInvalidValue;
   if (!full && (N / hw) * apf > La) return hipErrorInvalidValue;
+  if (ssq && (groups < 4 || groups > MAXG || groups % 4 || !g)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(N / 32, n_heads, B);
   cross_attn_kernel<<<grid, 64, 0, s>>>(q, ldq, kc, ldk, vct, o, ldo, N, La, n_heads * HD, hw, apf,
-                                         full, scale_log2);
+                                        full, scale_log2, ssq, groups, g, eps);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ struct WS {
   bf16_t *h, *qk, *vt, *ao, *qc, *u, *aud, *kc, *vct;
   float *emb, *t1, *e, *e0, *rcos, *rsin;
   float* part;  // split-K partial sums of the width-D residual GEMMs, [2][B*N, D]
+  float* ssq;   // per-row column-group sums of squares of the cross-attention queries
   size_t total;
 };
 
@@ -145,6 +146,7 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.rcos = (float*)take(N * (g.head_dim / 2) * 4);
   w.rsin = (float*)take(N * (g.head_dim / 2) * 4);
   w.part = (float*)take(2 * B * N * D * 4);
+  w.ssq = (float*)take((D / 32) * B * N * 4);
   w.total = off;
   return w;
 }
@@ -247,22 +249,21 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
                               wb.norm3_b, nullptr, s));
   }
   {
+    // the query RMSNorm is split between this GEMM (per-row sums of squares of
+    // column groups) and the cross-attention kernel (the scaling)
     Timed t(c, FH_K_GEMM_CQ, s);
     fh::EpiArgs ep;
     ep.bias = wb.cq_b;
     ep.out_bf = ws.qc;
     ep.ldo = D;
-    FH_HIP(fh::gemm_bf16(fh::EPI_BF16, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
-  }
-  {
-    Timed t(c, FH_K_RMSNORM_ROPE, s);
-    FH_HIP(fh::rmsnorm_rope_bf16(ws.qc, D, M, D, 1, wb.norm_cq, nullptr, nullptr, nullptr, N, g.head_dim,
-                                 g.eps, s));
+    ep.ssq = ws.ssq;
+    FH_HIP(fh::gemm_bf16(fh::EPI_BF16_SSQ, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
   }
   {
     Timed t(c, FH_K_CROSS_ATTN, s);
     FH_HIP(fh::cross_attn(ws.qc, D, kc, D, vct, ws.ao, D, B, N, c->La, c->HW, g.audio_per_frame,
-                          g.cross_full, g.n_heads, scale, s));
+                          g.cross_full, g.n_heads, scale, ws.ssq, fh::gemm_ssq_groups(M, D, D),
+                          wb.norm_cq, g.eps, s));
   }
   {
     Timed t(c, FH_K_GEMM_CO, s);

@@ -16,6 +16,8 @@ enum Epi {
   EPI_SPLIT_T = 4,    // n < split: out_bf[m, n] = bf16(C + bias);
                       // n >= split: out_t[lane][n - split][m mod rows] = bf16(C + bias)
   EPI_PARTIAL = 5,    // internal to gemm_bf16 (split K): part[k-part][m, n] = C over that K range
+  EPI_BF16_SSQ = 6,   // as EPI_BF16, and ssq[m][p] = sum of the squares of the stored (bf16)
+                      // values of row m in column group p (gemm_ssq_groups(M, N, K) groups)
 };
 
 struct EpiArgs {
@@ -33,10 +35,13 @@ struct EpiArgs {
   int t_cols = 0;                   // N - split
   float* part = nullptr;             // EPI_PARTIAL: [splits][M][N]
   size_t part_elems = 0;
+  float* ssq = nullptr;              // EPI_BF16_SSQ: [M][groups]
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s);
+// number of column groups of EPI_BF16_SSQ's per-row partial sums for this shape
+int gemm_ssq_groups(int M, int N, int K);
 
 // A residual update x[m, n] += gate[lane(m), n] * (part[0][m, n] + ... + bias[n])
 // that a later kernel applies: a residual GEMM with its K split writes the
@@ -95,10 +100,15 @@ hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const 
                       bf16_t* o, int ldo, int B, int N, int n_heads, float scale, hipStream_t s);
 
 // Audio cross-attention with short key ranges: queries of latent frame f =
-// row / hw see keys [f*apf, f*apf + apf) (full != 0: all La keys).
+// row / hw see keys [f*apf, f*apf + apf) (full != 0: all La keys). With ssq
+// non-null the queries are first RMS-normalised over their whole row (width
+// n_heads*128): row m's sum of squares is ssq[m][0] + ... + ssq[m][groups-1]
+// (groups a multiple of 4; added in that order), then q * rsqrt(sum / width +
+// eps) * g, rounded to bf16.
 hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const bf16_t* vct,
                       bf16_t* o, int ldo, int B, int N, int La, int hw, int apf, int full,
-                      int n_heads, float scale, hipStream_t s);
+                      int n_heads, float scale, const float* ssq, int groups, const float* g, float eps,
+                      hipStream_t s);
 
 // Rotary angle tables [N, head_dim/2] (cos, sin), computed in float64.
 hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,

@@ -263,9 +263,20 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
         for (int it = 0; it < 32 * C / 8 / 64; ++it) {
           const int c = it * 64 + lane, row = c / (C / 8), c8 = (c % (C / 8)) * 8;
           const int m = mb + row;
-          if (m < M)
-            *reinterpret_cast<u32x4*>(ep.out_bf + (int64_t)m * ep.ldo + nw + c8) =
-                *reinterpret_cast<const u32x4*>(st + row * ST::PB + c8 * 2);
+          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * ST::PB + c8 * 2);
+          if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf + (int64_t)m * ep.ldo + nw + c8) = w;
+          if constexpr (EPI == EPI_BF16_SSQ) {
+            // squares of the stored values, summed over the C / 8 lanes of the row
+            float q = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+              q += lo * lo + hi * hi;
+            }
+#pragma unroll
+            for (int o = 1; o < C / 8; o <<= 1) q += __shfl_xor(q, o, 64);
+            if (m < M && c8 == 0) ep.ssq[(int64_t)m * (N / C) + nw / C] = q;
+          }
         }
         lds_fence();
       } else {
@@ -331,6 +342,7 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
     case EPI_RES: FH_GEMM(EPI_RES); break;
     case EPI_SPLIT_T: FH_GEMM(EPI_SPLIT_T); break;
     case EPI_PARTIAL: FH_GEMM(EPI_PARTIAL); break;
+    case EPI_BF16_SSQ: FH_GEMM(EPI_BF16_SSQ); break;
     default: return hipErrorInvalidValue;
   }
 #undef FH_GEMM
@@ -374,9 +386,15 @@ hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, in
   return hipGetLastError();
 }
 
+int gemm_ssq_groups(int M, int N, int K) {
+  static const int bn[] = {256, 256, 64, 128, 128};  // BN of each gemm_tile_choice
+  return N / (bn[gemm_tile_choice(M, N, K)] / 2);
+}
+
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
+  if (epi == EPI_BF16_SSQ && !ep.ssq) return hipErrorInvalidValue;
   if (N % 128 || K % KALIGN || lda % 8 || ldw % 8 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
   switch (gemm_tile_choice(M, N, K)) {
     case 0: return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
