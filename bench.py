@@ -119,8 +119,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the slice denoiser has no "
-              "multi-GPU path in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the slice denoiser is a "
+              "single-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
