@@ -17,3 +17,4 @@ Agreement with a trained FlashHead checkpoint is "parity unpinned": no page
 prints a tensor of the real model.
 """
 from .dit import *  # noqa: F401,F403
+from . import renoise  # noqa: F401
