@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libfh.so")
 
 FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHTS = range(7)
 FH_DTYPE_BF16, FH_DTYPE_F32 = 1, 2
-FH_OPT_GRAPH, FH_OPT_TIME_KERNEL = 1, 2
+FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER = 1, 2, 3
+FH_SAMPLER_EULER, FH_SAMPLER_RENOISE = 0, 1
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn",
                   "cross_attn", "layernorm", "rmsnorm_rope"]
 FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
@@ -29,8 +30,8 @@ FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
 # every symbol include/fh.h declares
 EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_weights_bind",
            "fh_weights_release", "fh_workspace_bytes", "fh_dit_block_forward",
-           "fh_dit_denoise_slice", "fh_set_option", "fh_kernel_time", "fh_last_error",
-           "fh_status_str"]
+           "fh_dit_denoise_slice", "fh_set_option", "fh_set_noise_seed", "fh_philox4x32_fill",
+           "fh_kernel_time", "fh_last_error", "fh_status_str"]
 
 
 class fh_config(ctypes.Structure):
@@ -71,6 +72,9 @@ def _load():
         "fh_dit_denoise_slice": (i32, [vp, vp, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_float), i32,
                                        vp, vp, sz, vp]),
         "fh_set_option": (i32, [vp, i32, i32]),
+        "fh_set_noise_seed": (i32, [vp, ctypes.c_uint64]),
+        "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                     ctypes.c_int64, vp, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
         "fh_status_str": (ctypes.c_char_p, [i32]),
@@ -250,7 +254,8 @@ def fh_dit_block_forward(ctx, w, block, x, temb, audio, ws, stream=None):
 
 def fh_dit_denoise_slice(ctx, w, latent, motion_latent, audio_tokens, sigmas, latent_out, ws,
                          stream=None):
-    """Denoise [B, C, F, H, W] latents with len(sigmas)-1 Euler steps (host sigmas)."""
+    """Denoise [B, C, F, H, W] latents with len(sigmas)-1 steps of the context's
+    sampler (Euler unless FH_OPT_SAMPLER says otherwise; host sigmas)."""
     d = _dims(ctx)
     B = latent.shape[0]
     C, F, H, W = d["in_ch"], d["frames"], d["height"], d["width"]
@@ -265,6 +270,23 @@ def fh_dit_denoise_slice(ctx, w, latent, motion_latent, audio_tokens, sigmas, la
 
 def fh_set_option(ctx, option, value):
     _check(ctx, lib.fh_set_option(ctx, int(option), int(value)))
+
+
+def fh_set_noise_seed(ctx, seed):
+    _check(ctx, lib.fh_set_noise_seed(ctx, int(seed) & (2**64 - 1)))
+
+
+def fh_philox4x32_fill(seed, lane, step, first_group, out, stream=None):
+    """Fill the device uint32 view `out` (4 words per group, a multiple of 4
+    long) with the sampler's Philox-4x32-10 words (see include/fh.h)."""
+    import torch
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.element_size() != 4 \
+            or not out.is_contiguous() or out.numel() % 4:
+        raise ValueError("out must be a contiguous 4-byte device tensor with a multiple of 4 elements")
+    st = lib.fh_philox4x32_fill(int(seed) & (2**64 - 1), int(lane), int(step), int(first_group),
+                                out.numel() // 4, ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_philox4x32_fill: {fh_status_str(st)}")
 
 
 def fh_kernel_time(ctx):

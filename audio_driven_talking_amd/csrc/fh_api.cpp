@@ -62,6 +62,8 @@ struct fh_ctx {
   std::string err;
   bool use_graph = true;
   int time_class = -1;
+  int sampler = FH_SAMPLER_EULER;
+  uint64_t noise_seed = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_free, ev_pending;
   double time_ms = 0.0;
   int64_t time_count = 0;
@@ -354,8 +356,13 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       // head: LN modulated by (head.mod + e), then W_h, Euler step and motion pin
       FH_HIP(fh::layernorm_bf16(ws.x, ws.h, B * N, D, N, g.eps, w->head_mod, w->head_mod + D, e, e, 0,
                                 nullptr, nullptr, &pend, s));
+      fh::SamplerArgs sa;
+      sa.renoise = c->sampler == FH_SAMPLER_RENOISE;
+      sa.step = (uint32_t)st;
+      sa.k0 = (uint32_t)c->noise_seed;
+      sa.k1 = (uint32_t)(c->noise_seed >> 32);
       FH_HIP(fh::head_euler(ws.h, B, N, D, w->head_w, w->head_b, g.out_ch, out, out, motion, nmt,
-                            sigmas[st + 1] - sigmas[st], s));
+                            sigmas[st], sigmas[st + 1], sa, s));
     }
   }
   return FH_OK;
@@ -550,7 +557,7 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   std::vector<uint64_t> key = {(uint64_t)(uintptr_t)w, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
                                (uint64_t)(uintptr_t)motion_latent, (uint64_t)(uintptr_t)audio_tokens,
                                (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
-                               (uint64_t)n_steps};
+                               (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed};
   for (int i = 0; i <= n_steps && n_steps > 0; ++i) {
     uint32_t b;
     std::memcpy(&b, &sigmas[i], 4);
@@ -599,7 +606,27 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     c->time_class = value;
     return FH_OK;
   }
+  if (option == FH_OPT_SAMPLER) {
+    if (value != FH_SAMPLER_EULER && value != FH_SAMPLER_RENOISE)
+      return fail(c, FH_EINVAL, "unknown sampler %d", value);
+    c->sampler = value;
+    return FH_OK;
+  }
   return fail(c, FH_EINVAL, "unknown option %d", option);
+}
+
+int fh_set_noise_seed(fh_ctx* c, uint64_t seed) {
+  if (!c) return FH_EINVAL;
+  c->noise_seed = seed;
+  return FH_OK;
+}
+
+int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t first_group, int64_t n_groups,
+                       uint32_t* out, void* stream) {
+  if (n_groups < 0 || (n_groups > 0 && !out) || ((uintptr_t)out & 15)) return FH_EINVAL;
+  if (n_groups > 0 && (uint64_t)first_group + (uint64_t)(n_groups - 1) > 0xFFFFFFFFull) return FH_EINVAL;
+  const hipError_t e = fh::philox_fill(out, n_groups, first_group, lane, step, seed, (hipStream_t)stream);
+  return e == hipSuccess ? FH_OK : FH_EHIP;
 }
 
 int fh_kernel_time(fh_ctx* c, double* total_ms, int64_t* launches) {

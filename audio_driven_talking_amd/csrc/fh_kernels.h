@@ -129,9 +129,19 @@ hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, 
 // (bf16, from layernorm_bf16 with the head's shift/scale):
 //   v = h W_h^T + b_h;  lat_next = token in a motion frame ? motion : lat_cur + dsig * v
 // (latents [B, Co, N]; lat_next may alias lat_cur). Co must be a multiple of 16.
+// Sampler of the fused head update: Euler, or re-noising with counter-based
+// noise of step `step` under the 64-bit seed (k0 low, k1 high word).
+struct SamplerArgs {
+  int renoise = 0;
+  uint32_t step = 0, k0 = 0, k1 = 0;
+};
 hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
-                      float dsig, hipStream_t s);
+                      float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s);
+// Raw generator words: out[4 g + j] = word j of Philox-4x32-10 at counter
+// (first_group + g, lane, step, 0) under key (seed low, high), g < n_groups.
+hipError_t philox_fill(uint32_t* out, int64_t n_groups, uint32_t first_group, uint32_t lane, uint32_t step,
+                       uint64_t seed, hipStream_t s);
 
 // out = latent with the first n_motion_tok tokens of every (lane, channel) from motion.
 hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC, int N,

@@ -124,19 +124,62 @@ __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restric
   }
 }
 
+// Counter-based generator: Philox-4x32 with 10 rounds (Salmon, Moraes, Dror,
+// Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011). A round
+// multiplies words 0 and 2 by the two round constants (64-bit products), and
+// the new words are (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)); the key advances by the two Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const u32x4 n = {(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
+                     (uint32_t)p0};
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Standard-normal noise of latent element i of batch lane b at step k:
+// counter (i / 4, b, k, 0), key (seed low, high); element i takes the word
+// pair (i mod 4) / 2 as two 24-bit uniforms in (0, 1] and the Box-Muller
+// transform, cosine for even i, sine for odd i.
+__device__ __forceinline__ float latent_noise(uint32_t i, uint32_t b, uint32_t k, uint32_t k0, uint32_t k1) {
+  const u32x4 w = philox4x32_10(u32x4{i >> 2, b, k, 0u}, k0, k1);
+  const int p = (i >> 1) & 1;
+  const float ua = (float)((w[2 * p] >> 8) + 1u) * 0x1p-24f;
+  const float ub = (float)((w[2 * p + 1] >> 8) + 1u) * 0x1p-24f;
+  const float r = sqrtf(-2.f * logf(ua));
+  const float th = 6.28318530717958647692f * ub;
+  return r * ((i & 1) ? sinf(th) : cosf(th));
+}
+
+__global__ void philox_fill_kernel(uint32_t* __restrict__ out, int64_t n, uint32_t g0, uint32_t lane,
+                                   uint32_t step, uint32_t k0, uint32_t k1) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n) return;
+  const u32x4 w = philox4x32_10(u32x4{g0 + (uint32_t)g, lane, step, 0u}, k0, k1);
+  *reinterpret_cast<u32x4*>(out + 4 * g) = w;
+}
+
 // Output head on the modulated, normalised rows h (bf16 [B*N, D]) fused with
-// the Euler update: MFMA 16x16x32, one wave per 16 tokens and 16 channels;
+// the sampler update: MFMA 16x16x32, one wave per 16 tokens and 16 channels;
 // lane l holds token (l % 16) and channels 4 (l / 16) + {0..3} of its group.
+// Euler: x' = x + (s' - s) v. Re-noising: x' = (1 - s') (x - s v) + s' eps,
+// eps from latent_noise (element index c * N + token within the lane).
 __global__ __launch_bounds__(256) void head_euler_kernel(
     const bf16_t* __restrict__ h, int B, int N, int D, const bf16_t* __restrict__ Wh,
     const float* __restrict__ bh, int Co, const float* lat_cur, float* lat_next,
-    const float* __restrict__ motion, int nmt, float dsig) {
+    const float* __restrict__ motion, int nmt, float sigma, float sigma_next, SamplerArgs sa) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = (blockIdx.x * 4 + wave) * 16;
   if (t0 >= B * N) return;
   const int lr = lane & 15, lq = lane >> 4;
   const int row = min(t0 + lr, B * N - 1);
   const bf16_t* hp = h + (int64_t)row * D + 8 * lq;
+  const float dsig = sigma_next - sigma;
   for (int cg = 0; cg < Co; cg += 16) {
     const bf16_t* wp = Wh + (int64_t)(cg + lr) * D + 8 * lq;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -151,10 +194,17 @@ __global__ __launch_bounds__(256) void head_euler_kernel(
       for (int i = 0; i < 4; ++i) {
         const int co = cg + 4 * lq + i;
         const int64_t idx = ((int64_t)b * Co + co) * N + tok;
-        if (tok < nmt)
+        if (tok < nmt) {
           lat_next[idx] = motion[((int64_t)b * Co + co) * nmt + tok];
-        else
-          lat_next[idx] = lat_cur[idx] + dsig * (acc[i] + bh[co]);
+        } else {
+          const float v = acc[i] + bh[co];
+          if (sa.renoise) {
+            const float eps = latent_noise((uint32_t)(co * N + tok), (uint32_t)b, sa.step, sa.k0, sa.k1);
+            lat_next[idx] = (1.f - sigma_next) * (lat_cur[idx] - sigma * v) + sigma_next * eps;
+          } else {
+            lat_next[idx] = lat_cur[idx] + dsig * v;
+          }
+        }
       }
     }
   }
@@ -210,10 +260,18 @@ hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, 
 
 hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
-                      float dsig, hipStream_t s) {
+                      float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s) {
   if (D % 32 || Co % 16) return hipErrorInvalidValue;
   head_euler_kernel<<<(B * N + 63) / 64, 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
-                                                      n_motion_tok, dsig);
+                                                      n_motion_tok, sigma, sigma_next, sa);
+  return hipGetLastError();
+}
+
+hipError_t philox_fill(uint32_t* out, int64_t n_groups, uint32_t first_group, uint32_t lane, uint32_t step,
+                       uint64_t seed, hipStream_t s) {
+  if (n_groups <= 0) return hipSuccess;
+  philox_fill_kernel<<<(unsigned)((n_groups + 255) / 256), 256, 0, s>>>(out, n_groups, first_group, lane, step,
+                                                                        (uint32_t)seed, (uint32_t)(seed >> 32));
   return hipGetLastError();
 }
 

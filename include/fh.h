@@ -152,17 +152,47 @@ int fh_dit_denoise_slice(fh_ctx* ctx, const fh_weights* w, int batch, const floa
 
 /* Execution options of a context.
  *   FH_OPT_GRAPH: 1 (default) capture fh_dit_denoise_slice into a HIP graph
- *     per (batch, pointers, sigmas) and replay it; 0 launch kernels directly.
+ *     per (batch, pointers, sigmas, sampler, seed) and replay it; 0 launch
+ *     kernels directly.
  *   FH_OPT_TIME_KERNEL: a kernel class (FH_K_*) to time with HIP events on the
  *     call's stream around each of its launches (forces direct launches);
- *     -1 (default) times nothing. fh_kernel_time reads and resets the sums. */
-enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2 };
+ *     -1 (default) times nothing. fh_kernel_time reads and resets the sums.
+ *   FH_OPT_SAMPLER: the update of fh_dit_denoise_slice's steps.
+ *     FH_SAMPLER_EULER (default): x' = x + (s' - s) v.
+ *     FH_SAMPLER_RENOISE: x' = (1 - s') (x - s v) + s' eps, the re-noising
+ *       update the audio-cpp page "SoulX-FlashHead" (section "Variant
+ *       boundaries") names for distilled checkpoints, read in the flow-matching
+ *       convention x_s = (1 - s) x0 + s eps, v = eps - x0. eps is standard
+ *       normal noise drawn per step from the context's seed
+ *       (fh_set_noise_seed) by a counter-based generator, so it is
+ *       reproducible and independent of launch order: element i (flat index
+ *       over [C, F, H, W]) of batch lane b at step k takes Philox-4x32-10
+ *       (Salmon et al., SC 2011) at counter (i / 4, b, k, 0) under key (seed
+ *       low, high 32 bits); of the four words it uses pair (i mod 4) / 2 as
+ *       u = ((w >> 8) + 1) / 2^24 each, and eps = sqrt(-2 ln u_a) times
+ *       cos(2 pi u_b) for even i, sin(2 pi u_b) for odd i (Box-Muller).
+ *       Motion frames are pinned after every step as with Euler; at s' = 0
+ *       the two updates coincide.                                            */
+enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2, FH_OPT_SAMPLER = 3 };
+enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
 enum {
   FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
   FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,
   FH_K_COUNT = 10
 };
 int fh_set_option(fh_ctx* ctx, int option, int value);
+/* Seed of FH_SAMPLER_RENOISE's noise (default 0). Returns FH_EINVAL for a null ctx. */
+int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
+
+/* The generator of FH_SAMPLER_RENOISE, exposed for callers that draw matching
+ * noise and for testing: out[4 g + j] = word j of Philox-4x32-10 at counter
+ * (first_group + g, lane, step, 0) under key (seed low, high 32 bits), for
+ * g in [0, n_groups). out is a device buffer of 4 n_groups uint32, 16-byte
+ * aligned; the call enqueues one kernel on `stream`. FH_EINVAL for a null or
+ * misaligned out, n_groups < 0, or a counter range past 2^32; FH_EHIP if the
+ * launch fails.                                                             */
+int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t first_group, int64_t n_groups,
+                       uint32_t* out, void* stream);
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_symbols():
     txt = open(os.path.join(ROOT, "include", "fh.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(fh_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(fh_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -155,3 +155,19 @@ def test_call_argument_errors_before_any_launch():
     assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, 10) == fh.FH_EINVAL
     fh.lib.fh_weights_release(w)
     assert fh.fh_status_str(fh.FH_EWORKSPACE).startswith("workspace")
+
+
+def test_sampler_option_and_generator_argument_errors():
+    ctx = fh.fh_create(cfg_dict("toy"))
+    assert fh.lib.fh_set_option(ctx, fh.FH_OPT_SAMPLER, 2) == fh.FH_EINVAL
+    assert "sampler" in fh.fh_last_error(ctx)
+    assert fh.lib.fh_set_option(ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE) == fh.FH_OK
+    assert fh.lib.fh_set_noise_seed(ctx, 2**64 - 1) == fh.FH_OK
+    assert fh.lib.fh_set_noise_seed(None, 1) == fh.FH_EINVAL
+    vp = ctypes.c_void_p
+    # argument checks happen before any launch: no GPU needed
+    assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, 4, None, None) == fh.FH_EINVAL           # null out
+    assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, 4, vp(1 << 40 | 4), None) == fh.FH_EINVAL  # misaligned
+    assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, -1, vp(1 << 40), None) == fh.FH_EINVAL     # negative
+    assert fh.lib.fh_philox4x32_fill(1, 0, 0, 2**32 - 2, 3, vp(1 << 40), None) == fh.FH_EINVAL  # past 2^32
+    assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, 0, None, None) == fh.FH_OK                # nothing to do

@@ -204,7 +204,7 @@ def test_slice_ragged_tiles(fh):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("case", ["slice_b1", "slice_b3", "slice768"])
+@pytest.mark.parametrize("case", ["slice_b1", "slice_b3", "slice768", "slice_b1_renoise"])
 def test_full_slice_against_stored_oracle(fh, case):
     """The full 30-block, 4-step workloads against oracle outputs written by
     tests/golden/make_golden.py (float64 oracle, same seeded weights)."""
@@ -217,6 +217,9 @@ def test_full_slice_against_stored_oracle(fh, case):
     W = synth.make_weights(cfg)
     assert synth.weights_digest(W) == str(g["digest"]), "weights differ from the stored oracle's"
     m = Model(fh, cfg, W, B)
+    if "sampler" in g.files and str(g["sampler"]) == "renoise":
+        fh.fh_set_option(m.ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE)
+        fh.fh_set_noise_seed(m.ctx, int(g["noise_seed"]))
     lat, mot, aud = synth.slice_inputs(cfg, B)
     say(f"{case}: full slice B={B}")
     got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
@@ -226,3 +229,68 @@ def test_full_slice_against_stored_oracle(fh, case):
         say(f"  lane {b} rel err {err:.3e}")
         assert err <= TOL
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+
+
+# ------------------------------------------------------------------ re-noising sampler
+from oracle import renoise as R  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,lane,step,g0,n", [(0, 0, 0, 0, 4096), (42, 3, 2, 1000, 777),
+                                                 ((1 << 40) + 7, 1, 9, 0, 64),
+                                                 ((1 << 64) - 1, 65535, 3, (1 << 32) - 100, 100)])
+def test_philox_words_bit_exact(fh, seed, lane, step, g0, n):
+    """The library's generator words equal the oracle's, bit for bit."""
+    say(f"philox fill seed={seed} lane={lane} step={step} g0={g0} n={n}")
+    out = torch.empty(4 * n, dtype=torch.int32, device="cuda")
+    fh.fh_philox4x32_fill(seed, lane, step, g0, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(n, 4)
+    g = np.arange(g0, g0 + n, dtype=np.uint64)
+    ctr = np.stack([g, np.full(n, lane, np.uint64), np.full(n, step, np.uint64), np.zeros(n, np.uint64)], -1)
+    ref = R.philox4x32(ctr, np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_toy_renoise_slice(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    Wf = synth.weights_f32(W)
+    fh.fh_set_option(m.ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE)
+    fh.fh_set_noise_seed(m.ctx, 77)
+    say("toy re-noise slice B=2, seed 77")
+    got = m.slice(lat, mot, aud, sig)
+    ref = R.denoise_slice_renoise(lat, mot, aud, sig, Wf, cfg, 77)
+    for b in range(2):
+        err = O.rel_err(got[b:b + 1], ref[b:b + 1], cfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e}")
+        assert err <= TOL
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig, graph=False), got)  # graph == direct
+    say("  another seed draws other noise; the first seed again reproduces")
+    fh.fh_set_noise_seed(m.ctx, 78)
+    other = m.slice(lat, mot, aud, sig)
+    assert not np.allclose(other, got)
+    fh.fh_set_noise_seed(m.ctx, 77)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig), got)
+    say("  Euler on the same context (graphs cached per sampler)")
+    fh.fh_set_option(m.ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_EULER)
+    eul = m.slice(lat, mot, aud, sig)
+    assert O.rel_err(eul, O.denoise_slice(lat, mot, aud, sig, Wf, cfg), cfg.motion_frames) <= TOL
+
+
+def test_toy_renoise_last_step_is_euler(fh):
+    """sigma' = 0: the re-noising update is the Euler update whatever the noise."""
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = [0.25, 0.0]
+    say("toy one step to sigma 0: Euler vs re-noise")
+    eul = m.slice(lat, mot, aud, sig)
+    fh.fh_set_option(m.ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE)
+    fh.fh_set_noise_seed(m.ctx, 5)
+    ren = m.slice(lat, mot, aud, sig)
+    np.testing.assert_allclose(ren, eul, rtol=0, atol=1e-6 * np.abs(eul).max())
