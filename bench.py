@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="slice", choices=sorted(WORKLOADS))
+    ap.add_argument("--sampler", default="euler", choices=["euler", "renoise"],
+                    help="step update: Euler (the metric's configuration) or the re-noising variant")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
@@ -140,6 +142,9 @@ def main():
     L, Mo, A = (torch.from_numpy(a).cuda() for a in (lat, mot, aud))
     out = torch.empty_like(L)
     fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0 if args.no_graph else 1)
+    if args.sampler == "renoise":
+        fh.fh_set_option(ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE)
+        fh.fh_set_noise_seed(ctx, 20240601)
     stream = torch.cuda.current_stream()
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, device="cuda")
@@ -208,7 +213,7 @@ def main():
                    "euler_steps": n_steps, "dim": cfg.dim, "heads": cfg.n_heads,
                    "ffn": cfg.ffn_dim, "audio_tokens": cfg.audio_tokens,
                    "cross_attention": "full" if cfg.cross_full else "frame-local",
-                   "graph": not args.no_graph},
+                   "sampler": args.sampler, "graph": not args.no_graph},
         "latent_token_steps_per_s": round(B * cfg.tokens * n_steps * args.steps / T, 1),
         "mfma_frac_end_to_end": round(total_flops / (T / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),
