@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libfh.so")
 
 FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHTS = range(7)
 FH_DTYPE_BF16, FH_DTYPE_F32 = 1, 2
-FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER = 1, 2, 3
+FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER, FH_OPT_PRECISION = 1, 2, 3, 4
 FH_SAMPLER_EULER, FH_SAMPLER_RENOISE = 0, 1
+FH_PREC_BF16, FH_PREC_FP8_FFN = 0, 1
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn",
                   "cross_attn", "layernorm", "rmsnorm_rope"]
 FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
@@ -31,6 +32,7 @@ FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
 EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_weights_bind",
            "fh_weights_release", "fh_workspace_bytes", "fh_dit_block_forward",
            "fh_dit_denoise_slice", "fh_set_option", "fh_set_noise_seed", "fh_philox4x32_fill",
+           "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
            "fh_kernel_time", "fh_last_error", "fh_status_str"]
 
 
@@ -73,6 +75,9 @@ def _load():
                                        vp, vp, sz, vp]),
         "fh_set_option": (i32, [vp, i32, i32]),
         "fh_set_noise_seed": (i32, [vp, ctypes.c_uint64]),
+        "fh_fp8_weight_bytes": (sz, [vp]),
+        "fh_weights_quantize_fp8": (i32, [vp, vp, vp, sz, vp]),
+        "fh_mxfp8_quantize": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
         "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                      ctypes.c_int64, vp, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -287,6 +292,37 @@ def fh_philox4x32_fill(seed, lane, step, first_group, out, stream=None):
                                 out.numel() // 4, ctypes.c_void_p(out.data_ptr()), _stream(stream))
     if st != FH_OK:
         raise FHError(st, f"fh_philox4x32_fill: {fh_status_str(st)}")
+
+
+def fh_fp8_weight_bytes(ctx):
+    return int(lib.fh_fp8_weight_bytes(ctx))
+
+
+def fh_weights_quantize_fp8(ctx, w, stream=None, device="cuda"):
+    """Quantise w's FFN matrices to MX-FP8 into a new device buffer kept on w."""
+    import torch
+    buf = torch.empty(fh_fp8_weight_bytes(ctx) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    _check(ctx, lib.fh_weights_quantize_fp8(ctx, w, ctypes.c_void_p(buf.data_ptr() + off),
+                                            buf.numel() - off, _stream(stream)))
+    w.fp8_buffer = buf
+
+
+def fh_mxfp8_quantize(x, stream=None):
+    """MX-FP8 codes [rows, K] (uint8) and scales [K/64, rows] (int16 bit patterns)
+    of a contiguous float32 device tensor [rows, K]."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.float32 or x.dim() != 2 \
+            or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D float32 device tensor")
+    rows, K = x.shape
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(K // 64 if K % 64 == 0 else 0, rows, dtype=torch.int16, device=x.device)
+    st = lib.fh_mxfp8_quantize(ctypes.c_void_p(x.data_ptr()), rows, K, ctypes.c_void_p(codes.data_ptr()),
+                               ctypes.c_void_p(scales.data_ptr()), _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_mxfp8_quantize: {fh_status_str(st)}")
+    return codes, scales
 
 
 def fh_kernel_time(ctx):

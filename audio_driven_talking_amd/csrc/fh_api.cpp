@@ -26,6 +26,9 @@ struct WBlock {
   const bf16_t *qkv_w, *o_w, *cq_w, *ckv_w, *co_w, *ffn1_w, *ffn2_w;
   const float *mod, *qkv_b, *norm_q, *norm_k, *o_b, *norm3_g, *norm3_b, *cq_b, *ckv_b, *norm_cq,
       *norm_ck, *co_b, *ffn1_b, *ffn2_b;
+  // MX-FP8 copies of the FFN matrices (fh_weights_quantize_fp8), else null
+  const uint8_t *ffn1_q = nullptr, *ffn2_q = nullptr;
+  const uint16_t *ffn1_s = nullptr, *ffn2_s = nullptr;
 };
 
 struct GraphEntry {
@@ -40,6 +43,8 @@ struct WS {
   float *emb, *t1, *e, *e0, *rcos, *rsin;
   float* part;  // split-K partial sums of the width-D residual GEMMs, [2][B*N, D]
   float* ssq;   // per-row column-group sums of squares of the cross-attention queries
+  uint8_t *hq, *uq;   // MX-FP8 FFN operands: normalised rows [B*N, D], hidden [B*N, Fd]
+  uint16_t *hs, *us;  // and their scales [D/64][B*N], [Fd/64][B*N]
   size_t total;
 };
 
@@ -53,6 +58,7 @@ struct fh_weights {
   const bf16_t *time_in_w, *time_out_w, *time_proj_w, *patch_w, *head_w;
   const float *time_in_b, *time_out_b, *time_proj_b, *patch_b, *head_b, *head_mod;
   std::vector<WBlock> blk;
+  bool fp8 = false;  // MX-FP8 FFN copies attached
 };
 
 struct fh_ctx {
@@ -64,6 +70,7 @@ struct fh_ctx {
   int time_class = -1;
   int sampler = FH_SAMPLER_EULER;
   uint64_t noise_seed = 0;
+  int precision = FH_PREC_BF16;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_free, ev_pending;
   double time_ms = 0.0;
   int64_t time_count = 0;
@@ -149,6 +156,10 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.rsin = (float*)take(N * (g.head_dim / 2) * 4);
   w.part = (float*)take(2 * B * N * D * 4);
   w.ssq = (float*)take((D / 32) * B * N * 4);
+  w.hq = (uint8_t*)take(B * N * D);
+  w.hs = (uint16_t*)take((D / 64) * B * N * 2);
+  w.uq = (uint8_t*)take(B * N * Fd);
+  w.us = (uint16_t*)take((Fd / 64) * B * N * 2);
   w.total = off;
   return w;
 }
@@ -275,18 +286,27 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.ldx = D;
     FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
   }
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D,
-                              e0 + 4 * D, e0_stride, nullptr, nullptr, nullptr, s));
+                              e0 + 4 * D, e0_stride, nullptr, nullptr, nullptr, s, fp8 ? ws.hq : nullptr,
+                              fp8 ? ws.hs : nullptr));
   }
   {
     Timed t(c, FH_K_GEMM_FFN1, s);
     fh::EpiArgs ep;
     ep.bias = wb.ffn1_b;
-    ep.out_bf = ws.u;
-    ep.ldo = Fd;
-    FH_HIP(fh::gemm_bf16(fh::EPI_GELU_BF16, ws.h, D, wb.ffn1_w, D, M, Fd, D, ep, s));
+    if (fp8) {  // MX-FP8 operands, GELU output quantised to MX-FP8 for the next GEMM
+      ep.out_q = ws.uq;
+      ep.ldq = Fd;
+      ep.q_scale = ws.us;
+      FH_HIP(fh::gemm_mx(fh::EPI_GELU_MX, ws.hq, D, ws.hs, wb.ffn1_q, D, wb.ffn1_s, M, Fd, D, ep, s));
+    } else {
+      ep.out_bf = ws.u;
+      ep.ldo = Fd;
+      FH_HIP(fh::gemm_bf16(fh::EPI_GELU_BF16, ws.h, D, wb.ffn1_w, D, M, Fd, D, ep, s));
+    }
   }
   {
     Timed t(c, FH_K_GEMM_FFN2, s);
@@ -299,7 +319,11 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.gate_stride = e0_stride;
     ep.rows_per_lane = N;
     if (pend_out && fh::gemm_splitk_ok(M, D, Fd)) {
-      FH_HIP(fh::gemm_bf16_splitk(ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ws.part, (size_t)2 * M * D, s));
+      if (fp8)
+        FH_HIP(fh::gemm_mx_splitk(ws.uq, Fd, ws.us, wb.ffn2_q, Fd, wb.ffn2_s, M, D, Fd, ws.part,
+                                  (size_t)2 * M * D, s));
+      else
+        FH_HIP(fh::gemm_bf16_splitk(ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ws.part, (size_t)2 * M * D, s));
       pend_out->part = ws.part;
       pend_out->nparts = 2;
       pend_out->bias = ep.bias;
@@ -309,7 +333,10 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
       pend_out->rows_per_lane = N;
     } else {
       if (pend_out) *pend_out = fh::PendingRes();
-      FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ep, s));
+      if (fp8)
+        FH_HIP(fh::gemm_mx(fh::EPI_GATED_RES, ws.uq, Fd, ws.us, wb.ffn2_q, Fd, wb.ffn2_s, M, D, Fd, ep, s));
+      else
+        FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ep, s));
     }
   }
   return FH_OK;
@@ -513,6 +540,8 @@ int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, f
   if (!x || !temb || !audio) return fail(c, FH_EINVAL, "null x, temb or audio");
   int rc = FH_OK;
   if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
+  if (c->precision == FH_PREC_FP8_FFN && !w->fp8)
+    return fail(c, FH_EINVAL, "FH_PREC_FP8_FFN needs fh_weights_quantize_fp8 on these weights");
   hipStream_t s = (hipStream_t)stream;
   const fh_config& g = c->cfg;
   const int D = g.dim;
@@ -548,6 +577,8 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
     if (!std::isfinite(sigmas[i])) return fail(c, FH_EINVAL, "sigma[%d] is not finite", i);
   int rc = FH_OK;
   if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
+  if (c->precision == FH_PREC_FP8_FFN && !w->fp8)
+    return fail(c, FH_EINVAL, "FH_PREC_FP8_FFN needs fh_weights_quantize_fp8 on these weights");
   hipStream_t s = (hipStream_t)stream;
   WS wsp = carve(c, batch, (char*)ws);
 
@@ -557,7 +588,8 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   std::vector<uint64_t> key = {(uint64_t)(uintptr_t)w, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
                                (uint64_t)(uintptr_t)motion_latent, (uint64_t)(uintptr_t)audio_tokens,
                                (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
-                               (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed};
+                               (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed,
+                               (uint64_t)c->precision};
   for (int i = 0; i <= n_steps && n_steps > 0; ++i) {
     uint32_t b;
     std::memcpy(&b, &sigmas[i], 4);
@@ -606,6 +638,12 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     c->time_class = value;
     return FH_OK;
   }
+  if (option == FH_OPT_PRECISION) {
+    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN)
+      return fail(c, FH_EINVAL, "unknown precision %d", value);
+    c->precision = value;
+    return FH_OK;
+  }
   if (option == FH_OPT_SAMPLER) {
     if (value != FH_SAMPLER_EULER && value != FH_SAMPLER_RENOISE)
       return fail(c, FH_EINVAL, "unknown sampler %d", value);
@@ -619,6 +657,56 @@ int fh_set_noise_seed(fh_ctx* c, uint64_t seed) {
   if (!c) return FH_EINVAL;
   c->noise_seed = seed;
   return FH_OK;
+}
+
+namespace {
+// per block: ffn1 codes [Fd][D], ffn2 codes [D][Fd], then their scales
+// [D/64][Fd] and [Fd/64][D] (uint16), each at a 256-byte boundary
+size_t fp8_block_bytes(const fh_config& g) {
+  auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t D = g.dim, Fd = g.ffn_dim;
+  return r(Fd * D) + r(D * Fd) + r(D / 64 * Fd * 2) + r(Fd / 64 * D * 2);
+}
+}  // namespace
+
+size_t fh_fp8_weight_bytes(const fh_ctx* c) {
+  if (!c) return 0;
+  return fp8_block_bytes(c->cfg) * (size_t)c->cfg.n_blocks;
+}
+
+int fh_weights_quantize_fp8(fh_ctx* c, fh_weights* w, void* buf, size_t bytes, void* stream) {
+  if (!c) return FH_EINVAL;
+  if (!w || w->ctx != c) return fail(c, FH_EINVAL, "weights are null or bound to another context");
+  if (!buf || ((uintptr_t)buf & 255)) return fail(c, FH_EINVAL, "buffer must be a non-null 256-byte aligned device pointer");
+  if (bytes < fh_fp8_weight_bytes(c))
+    return fail(c, FH_EINVAL, "buffer of %zu bytes is smaller than the %zu bytes needed", bytes, fh_fp8_weight_bytes(c));
+  const fh_config& g = c->cfg;
+  const int D = g.dim, Fd = g.ffn_dim;
+  hipStream_t s = (hipStream_t)stream;
+  auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  char* p = (char*)buf;
+  for (int i = 0; i < g.n_blocks; ++i) {
+    WBlock& b = w->blk[i];
+    uint8_t* q1 = (uint8_t*)p;
+    uint8_t* q2 = q1 + r((size_t)Fd * D);
+    uint16_t* s1 = (uint16_t*)(q2 + r((size_t)D * Fd));
+    uint16_t* s2 = (uint16_t*)((char*)s1 + r((size_t)D / 64 * Fd * 2));
+    FH_HIP(fh::mx_quantize(nullptr, b.ffn1_w, Fd, D, q1, s1, s));
+    FH_HIP(fh::mx_quantize(nullptr, b.ffn2_w, D, Fd, q2, s2, s));
+    b.ffn1_q = q1; b.ffn1_s = s1; b.ffn2_q = q2; b.ffn2_s = s2;
+    p += fp8_block_bytes(g);
+  }
+  w->fp8 = true;
+  return FH_OK;
+}
+
+int fh_mxfp8_quantize(const float* in, int64_t rows, int32_t K, uint8_t* codes, uint16_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 64) return FH_EINVAL;
+  if (rows == 0) return FH_OK;
+  if (!in || !codes || !scales || ((uintptr_t)in & 15) || ((uintptr_t)codes & 15) || ((uintptr_t)scales & 1))
+    return FH_EINVAL;
+  const hipError_t e = fh::mx_quantize(in, nullptr, rows, K, codes, scales, (hipStream_t)stream);
+  return e == hipSuccess ? FH_OK : FH_EHIP;
 }
 
 int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t first_group, int64_t n_groups,

@@ -70,6 +70,31 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
+// MX-FP8 (OCP microscaling: e4m3 elements, one E8M0 power-of-two scale per 32
+// consecutive elements along K). A block with max |x| = a > 0 takes the
+// shared exponent floor(log2 a) - 8 (e4m3's largest power of two is 2^8),
+// clamped below at -127 (E8M0 byte = exponent + 127); an all-zero block 0.
+// Elements are x * 2^-exponent clamped to +-448 and rounded to nearest even.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (amax == 0.f) return 0;
+  const int eb = (int)((__float_as_uint(amax) >> 23) & 255);
+  return eb == 0 ? -127 : max(eb - 127 - 8, -127);
+}
+// 2^-e for a shared exponent e in [-127, 119] (exact)
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+// two scaled values -> two e4m3 bytes (low 16 bits)
+__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+// eight scaled values -> eight e4m3 bytes
+__device__ __forceinline__ u32x2 pack8_e4m3(const float* v, float inv) {
+  const u32x2 w = {pack2_e4m3(v[0] * inv, v[1] * inv) | (pack2_e4m3(v[2] * inv, v[3] * inv) << 16),
+                   pack2_e4m3(v[4] * inv, v[5] * inv) | (pack2_e4m3(v[6] * inv, v[7] * inv) << 16)};
+  return w;
+}
+
 // wait until every LDS read / write of this wave has completed
 __device__ __forceinline__ void wait_lgkm0() {
   asm volatile("" ::: "memory");

@@ -18,7 +18,14 @@ enum Epi {
   EPI_PARTIAL = 5,    // internal to gemm_bf16 (split K): part[k-part][m, n] = C over that K range
   EPI_BF16_SSQ = 6,   // as EPI_BF16, and ssq[m][p] = sum of the squares of the stored (bf16)
                       // values of row m in column group p (gemm_ssq_groups(M, N, K) groups)
+  EPI_GELU_MX = 7,    // gelu_tanh(C + bias) quantised to MX-FP8: out_q[m, n] codes, q_scale
+                      // (MX scale layout below, rows = M)
 };
+
+// MX-FP8 operand layout used by the FP8 GEMM: codes [rows][K] (e4m3 bytes,
+// K-contiguous) and the E8M0 scales of the 32-element blocks stored by
+// 64-element slab: scale[s][row] = uint16 with block 2s in the low byte and
+// block 2s+1 in the high byte (s < K / 64).
 
 struct EpiArgs {
   const float* bias = nullptr;
@@ -36,12 +43,29 @@ struct EpiArgs {
   float* part = nullptr;             // EPI_PARTIAL: [splits][M][N]
   size_t part_elems = 0;
   float* ssq = nullptr;              // EPI_BF16_SSQ: [M][groups]
+  uint8_t* out_q = nullptr;          // EPI_GELU_MX: codes [M][ldq bytes]
+  int ldq = 0;
+  uint16_t* q_scale = nullptr;       // EPI_GELU_MX: scales [N / 64][M]
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s);
 // number of column groups of EPI_BF16_SSQ's per-row partial sums for this shape
 int gemm_ssq_groups(int M, int N, int K);
+
+// MX-FP8 GEMM: C = dequant(A) dequant(W)^T on the scaled MFMA, A codes [M][lda
+// bytes] with scales As ([K/64][M]), W codes [N][ldw] with scales Ws ([K/64][N]).
+// Epilogues as gemm_bf16 (incl. EPI_GELU_MX); K a multiple of 64, N of 128.
+hipError_t gemm_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
+                   const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s);
+// split-K form into part[0..1] (as gemm_bf16_splitk)
+hipError_t gemm_mx_splitk(const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
+                          const uint16_t* Ws, int M, int N, int K, float* part, size_t part_elems,
+                          hipStream_t s);
+// quantise rows [rows][K] of f32 (in_f) or bf16 (in_b) values to MX-FP8 codes [rows][K]
+// and scales [K/64][rows]; K a multiple of 64
+hipError_t mx_quantize(const float* in_f, const bf16_t* in_b, int64_t rows, int K, uint8_t* codes,
+                       uint16_t* scales, hipStream_t s);
 
 // A residual update x[m, n] += gate[lane(m), n] * (part[0][m, n] + ... + bias[n])
 // that a later kernel applies: a residual GEMM with its K split writes the
@@ -81,10 +105,13 @@ hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, in
 //   out = LN(x) * (1 + tab_scale + e_scale[lane]) + tab_shift + e_shift[lane]
 // Affine form: out = LN(x) * g + b. With a pending residual update (pend and
 // pend->part non-null, parts [nparts][rows][D]) x is first updated in place.
+// With out_q non-null the output is MX-FP8 instead (codes [rows][D], scales
+// [D/64][rows] in q_scale; D a multiple of 64) and out is not written.
 hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
                           const float* tab_shift, const float* tab_scale, const float* e_shift,
                           const float* e_scale, int e_stride, const float* g, const float* b,
-                          const PendingRes* pend, hipStream_t s);
+                          const PendingRes* pend, hipStream_t s, uint8_t* out_q = nullptr,
+                          uint16_t* q_scale = nullptr);
 
 // In-place RMSNorm over the first D columns of bf16 rows (stride ld), gain g0;
 // with nparts == 2 also columns [D, 2D) with gain g1. If cos_t != nullptr the

@@ -59,6 +59,172 @@ constexpr int smem_bytes() { return NS * (BM + BN) * BK * 2; }
 template <int BK>
 __device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
+// The epilogue of a BM x BN tile whose MFMA 32x32 results sit in acc: result
+// (i, j) of a wave holds row m = m0 + wm*BM/2 + j*32 + lr and columns
+// n = n0 + wn*BN/2 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]. The
+// slab buffers must be free (smem reused for staging).
+template <int EPI, int BM, int BN>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char* smem, const EpiArgs& ep,
+                                           int M, int N, int m0, int n0, int wm, int wn, int wave, int lane,
+                                           int ks) {
+  constexpr int MI = BM / 64, NI = BN / 64, C = BN / 2;
+  using ST = Stage<C>;
+  const int lr = lane & 31, lh = lane >> 5;
+  char* st = smem + wave * ST::BYTES;
+  const int nw = n0 + wn * C;  // first column of this wave's sub-tile
+  // the transposed form applies to a whole sub-tile (split is a multiple of BN)
+  const bool transposed = EPI == EPI_SPLIT_T && nw >= ep.split;
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
+    if (mb >= M) break;
+    if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES || EPI == EPI_PARTIAL) {
+      // raw f32 sums -> LDS; then by rows: x[m, n..n+3] += (sum + bias) * gate,
+      // or (split K) the sums alone into this split's part
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(st + lr * ST::PF + (i * 32 + 8 * g + 4 * lh) * 4) = v;
+        }
+      lds_fence();
+#pragma unroll
+      for (int it = 0; it < 32 * C / 4 / 64; ++it) {
+        const int c = it * 64 + lane, row = c / (C / 4), c4 = (c % (C / 4)) * 4;
+        const int m = mb + row, n = nw + c4;
+        if (m < M && EPI == EPI_PARTIAL) {
+          *reinterpret_cast<f32x4*>(ep.part + ((int64_t)ks * M + m) * N + n) =
+              *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
+        } else if (m < M) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(ep.bias + n);
+          f32x4 u = v + b;
+          if constexpr (EPI == EPI_GATED_RES) {
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(ep.gate_tab + n);
+            const f32x4 ge = *reinterpret_cast<const f32x4*>(ep.gate_e0 + (int64_t)(m / ep.rows_per_lane) * ep.gate_stride + n);
+            u = u * (gt + ge);
+          }
+          f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
+          *xp = *xp + u;
+        }
+      }
+      lds_fence();
+    } else if constexpr (EPI == EPI_GELU_MX) {
+      // raw f32 sums -> LDS; then per lane one 32-column block of a row: bias,
+      // GELU, MX-FP8 quantisation, 32 code bytes and the block's scale byte
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(st + lr * ST::PF + (i * 32 + 8 * g + 4 * lh) * 4) = v;
+        }
+      lds_fence();
+      constexpr int CB = C / 32, NB = 32 * CB;  // 32-column blocks per row, per 32-row block
+#pragma unroll
+      for (int it = 0; it < (NB + 63) / 64; ++it) {
+        const int blk = it * 64 + lane, row = blk / CB, cb = blk % CB;
+        const int m = mb + row, n = nw + 32 * cb;
+        if (blk < NB && m < M) {
+          float y[32];
+          float amax = 0.f;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * ST::PF + (32 * cb + 4 * t) * 4);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(ep.bias + n + 4 * t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y[4 * t + e] = gelu_tanh(v[e] + b[e]);
+              amax = fmaxf(amax, fabsf(y[4 * t + e]));
+            }
+          }
+          const int ex = mx_shared_exp(amax);
+          const float inv = mx_inv_scale(ex);
+          u32x4 w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x2 a = pack8_e4m3(y + 16 * h, inv), c = pack8_e4m3(y + 16 * h + 8, inv);
+            w[h] = u32x4{a.x, a.y, c.x, c.y};
+          }
+          u32x4* op = reinterpret_cast<u32x4*>(ep.out_q + (int64_t)m * ep.ldq + n);
+          op[0] = w[0];
+          op[1] = w[1];
+          reinterpret_cast<uint8_t*>(ep.q_scale)[((int64_t)(n / 64) * M + m) * 2 + ((n / 32) & 1)] =
+              (uint8_t)(ex + 127);
+        }
+      }
+      lds_fence();
+    } else {
+      if (!transposed) {
+        // (sum + bias [, GELU]) as bf16 -> LDS; then 16-byte pieces of rows
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = nw + i * 32 + 8 * g + 4 * lh;
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
+            float c0 = acc[i][j][4 * g] + b.x, c1 = acc[i][j][4 * g + 1] + b.y;
+            float c2 = acc[i][j][4 * g + 2] + b.z, c3 = acc[i][j][4 * g + 3] + b.w;
+            if constexpr (EPI == EPI_GELU_BF16) {
+              c0 = gelu_tanh(c0); c1 = gelu_tanh(c1); c2 = gelu_tanh(c2); c3 = gelu_tanh(c3);
+            }
+            const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
+            *reinterpret_cast<u32x2*>(st + lr * ST::PB + (i * 32 + 8 * g + 4 * lh) * 2) = w;
+          }
+        lds_fence();
+#pragma unroll
+        for (int it = 0; it < 32 * C / 8 / 64; ++it) {
+          const int c = it * 64 + lane, row = c / (C / 8), c8 = (c % (C / 8)) * 8;
+          const int m = mb + row;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * ST::PB + c8 * 2);
+          if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf + (int64_t)m * ep.ldo + nw + c8) = w;
+          if constexpr (EPI == EPI_BF16_SSQ) {
+            // squares of the stored values, summed over the C / 8 lanes of the row
+            float q = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+              q += lo * lo + hi * hi;
+            }
+#pragma unroll
+            for (int o = 1; o < C / 8; o <<= 1) q += __shfl_xor(q, o, 64);
+            if (m < M && c8 == 0) ep.ssq[(int64_t)m * (N / C) + nw / C] = q;
+          }
+        }
+        lds_fence();
+      } else {
+        // (sum + bias) as bf16, transposed -> LDS [C][32]; then 8 consecutive
+        // tokens of one output column per 16-byte piece
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int nl = i * 32 + 8 * g + 4 * lh;
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + nw + nl);
+            bf16_t* sp = reinterpret_cast<bf16_t*>(st + nl * ST::PT) + lr;
+            sp[0] = f2bf(acc[i][j][4 * g] + b.x);
+            sp[ST::PT / 2] = f2bf(acc[i][j][4 * g + 1] + b.y);
+            sp[ST::PT] = f2bf(acc[i][j][4 * g + 2] + b.z);
+            sp[3 * ST::PT / 2] = f2bf(acc[i][j][4 * g + 3] + b.w);
+          }
+        lds_fence();
+#pragma unroll
+        for (int it = 0; it < C * 4 / 64; ++it) {
+          const int c = it * 64 + lane, nl = c / 4, t8 = (c % 4) * 8;
+          const int m = mb + t8;  // 8 rows, never across a lane: rows_per_lane % 8 == 0
+          if (m < M) {
+            const int bl = m / ep.rows_per_lane, t = m - bl * ep.rows_per_lane;
+            bf16_t* o = ep.out_t + ((int64_t)bl * ep.t_cols + (nw + nl - ep.split)) * ep.rows_per_lane + t;
+            *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(st + nl * ST::PT + t8 * 2);
+          }
+        }
+        lds_fence();
+      }
+    }
+  }
+}
+
 template <int EPI, int BM, int BN, int BK, int NS>
 __global__ __launch_bounds__(256, (smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
@@ -194,121 +360,227 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   }
   wait_vm<0>();
 
-  // result (i, j): lane holds row m = m0 + wm*BM/2 + j*32 + lr and columns
-  // n = n0 + wn*BN/2 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]
-  constexpr int C = BN / 2;
-  using ST = Stage<C>;
-  static_assert(4 * ST::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
+  static_assert(4 * Stage<BN / 2>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
   wait_lgkm0();
   barrier();  // every wave is done with the slab buffers (its DMAs landed above)
-  char* st = smem + wave * ST::BYTES;
-  const int nw = n0 + wn * C;  // first column of this wave's sub-tile
-  // the transposed form applies to a whole sub-tile (split is a multiple of BN)
-  const bool transposed = EPI == EPI_SPLIT_T && nw >= ep.split;
+  store_tile<EPI, BM, BN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
+}
+
+// ---------------------------------------------------------------- MX-FP8
+// The same pipeline on MX-FP8 operands and the block-scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3): K-slabs of 64 bytes, each
+// one MFMA k-step. A lane of half h holds bytes [16h, 16h + 16) and
+// [32 + 16h, 48 + 16h) of its row's 64 (two 16-byte LDS reads), which puts
+// bytes 0..15 of both halves in 32-element block 0 and bytes 16..31 in
+// block 1; the E8M0 scale of (row, block b) comes from the lane of half b,
+// so each lane passes the byte of block h of its row. The slab's scales
+// (two bytes per row) travel with it by 4-byte-per-lane DMAs (a lane moves
+// the pair of two rows; one instruction covers 128 rows): the activation
+// rows' scales first (rounded up to 128 rows), then the weight rows'.
+template <int BM>
+constexpr int mx_arows() { return (BM + 127) / 128 * 128; }
+template <int BM, int BN>
+constexpr int mx_slab_bytes() { return (BM + BN) * 64 + ((mx_arows<BM>() + BN) * 2 + 1023) / 1024 * 1024; }
+
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }  // 64-byte rows
+
+template <int EPI, int BM, int BN, int NS>
+__global__ __launch_bounds__(256, 1)
+void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restrict__ As,
+                const uint8_t* __restrict__ W, int ldw, const uint16_t* __restrict__ Ws,
+                int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
+  constexpr int ROWB = 64, CH = 4, RG = 16;   // bytes per LDS row, 16-byte chunks, rows per 1 KB DMA
+  constexpr int MI = BM / 64, NI = BN / 64;
+  constexpr int GA = BM / RG / 4, GW = BN / RG / 4;  // 1 KB code DMAs per wave per slab
+  constexpr int SQA = mx_arows<BM>() / 128, SQ = SQA + BN / 128;  // 256-byte scale DMAs per slab
+  constexpr int SPW = (SQ + 3) / 4;                  // scale DMAs per wave (the last one repeated)
+  constexpr int DPS = GA + GW + SPW;
+  constexpr int SCB = (BM + BN) * ROWB;              // scale area of a slab
+  constexpr int SLAB = mx_slab_bytes<BM, BN>();
+  static_assert(GA * RG * 4 == BM && GW * RG * 4 == BN && BN % 128 == 0, "tile shape");
+  static_assert(NS >= 2 && (NS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
+
+  int bid = blockIdx.x;
+  const int per_xcd = gridDim.x >> 3;
+  bid = (bid & 7) * per_xcd + (bid >> 3);
+  if (bid >= tiles * splits) return;
+  const int ks = bid / tiles, tile = bid - ks * tiles;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int slabs_all = K / 64;
+  K /= splits;
+  const int s_base = ks * (K / 64);  // first slab of this split
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  (void)slabs_all;
+
+  const int drow = lane / CH;
+  const uint8_t* ga[GA];
+  const uint8_t* gw[GW];
 #pragma unroll
-  for (int j = 0; j < MI; ++j) {
-    const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
-    if (mb >= M) break;
-    if constexpr (EPI == EPI_GATED_RES || EPI == EPI_RES || EPI == EPI_PARTIAL) {
-      // raw f32 sums -> LDS; then by rows: x[m, n..n+3] += (sum + bias) * gate,
-      // or (split K) the sums alone into this split's part
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(st + lr * ST::PF + (i * 32 + 8 * g + 4 * lh) * 4) = v;
-        }
-      lds_fence();
-#pragma unroll
-      for (int it = 0; it < 32 * C / 4 / 64; ++it) {
-        const int c = it * 64 + lane, row = c / (C / 4), c4 = (c % (C / 4)) * 4;
-        const int m = mb + row, n = nw + c4;
-        if (m < M && EPI == EPI_PARTIAL) {
-          *reinterpret_cast<f32x4*>(ep.part + ((int64_t)ks * M + m) * N + n) =
-              *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
-        } else if (m < M) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * ST::PF + c4 * 4);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(ep.bias + n);
-          f32x4 u = v + b;
-          if constexpr (EPI == EPI_GATED_RES) {
-            const f32x4 gt = *reinterpret_cast<const f32x4*>(ep.gate_tab + n);
-            const f32x4 ge = *reinterpret_cast<const f32x4*>(ep.gate_e0 + (int64_t)(m / ep.rows_per_lane) * ep.gate_stride + n);
-            u = u * (gt + ge);
-          }
-          f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
-          *xp = *xp + u;
-        }
-      }
-      lds_fence();
-    } else {
-      if (!transposed) {
-        // (sum + bias [, GELU]) as bf16 -> LDS; then 16-byte pieces of rows
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = nw + i * 32 + 8 * g + 4 * lh;
-            const float4 b = *reinterpret_cast<const float4*>(ep.bias + n);
-            float c0 = acc[i][j][4 * g] + b.x, c1 = acc[i][j][4 * g + 1] + b.y;
-            float c2 = acc[i][j][4 * g + 2] + b.z, c3 = acc[i][j][4 * g + 3] + b.w;
-            if constexpr (EPI == EPI_GELU_BF16) {
-              c0 = gelu_tanh(c0); c1 = gelu_tanh(c1); c2 = gelu_tanh(c2); c3 = gelu_tanh(c3);
-            }
-            const u32x2 w = {pack2bf(c0, c1), pack2bf(c2, c3)};
-            *reinterpret_cast<u32x2*>(st + lr * ST::PB + (i * 32 + 8 * g + 4 * lh) * 2) = w;
-          }
-        lds_fence();
-#pragma unroll
-        for (int it = 0; it < 32 * C / 8 / 64; ++it) {
-          const int c = it * 64 + lane, row = c / (C / 8), c8 = (c % (C / 8)) * 8;
-          const int m = mb + row;
-          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * ST::PB + c8 * 2);
-          if (m < M) *reinterpret_cast<u32x4*>(ep.out_bf + (int64_t)m * ep.ldo + nw + c8) = w;
-          if constexpr (EPI == EPI_BF16_SSQ) {
-            // squares of the stored values, summed over the C / 8 lanes of the row
-            float q = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
-              q += lo * lo + hi * hi;
-            }
-#pragma unroll
-            for (int o = 1; o < C / 8; o <<= 1) q += __shfl_xor(q, o, 64);
-            if (m < M && c8 == 0) ep.ssq[(int64_t)m * (N / C) + nw / C] = q;
-          }
-        }
-        lds_fence();
-      } else {
-        // (sum + bias) as bf16, transposed -> LDS [C][32]; then 8 consecutive
-        // tokens of one output column per 16-byte piece
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int nl = i * 32 + 8 * g + 4 * lh;
-            const float4 b = *reinterpret_cast<const float4*>(ep.bias + nw + nl);
-            bf16_t* sp = reinterpret_cast<bf16_t*>(st + nl * ST::PT) + lr;
-            sp[0] = f2bf(acc[i][j][4 * g] + b.x);
-            sp[ST::PT / 2] = f2bf(acc[i][j][4 * g + 1] + b.y);
-            sp[ST::PT] = f2bf(acc[i][j][4 * g + 2] + b.z);
-            sp[3 * ST::PT / 2] = f2bf(acc[i][j][4 * g + 3] + b.w);
-          }
-        lds_fence();
-#pragma unroll
-        for (int it = 0; it < C * 4 / 64; ++it) {
-          const int c = it * 64 + lane, nl = c / 4, t8 = (c % 4) * 8;
-          const int m = mb + t8;  // 8 rows, never across a lane: rows_per_lane % 8 == 0
-          if (m < M) {
-            const int bl = m / ep.rows_per_lane, t = m - bl * ep.rows_per_lane;
-            bf16_t* o = ep.out_t + ((int64_t)bl * ep.t_cols + (nw + nl - ep.split)) * ep.rows_per_lane + t;
-            *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(st + nl * ST::PT + t8 * 2);
-          }
-        }
-        lds_fence();
-      }
-    }
+  for (int i = 0; i < GA; ++i) {
+    const int r = RG * (wave + 4 * i) + drow;
+    ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
   }
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int r = RG * (wave + 4 * i) + drow;
+    gw[i] = W + (int64_t)(n0 + r) * ldw + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
+  }
+  // scale DMA t of this wave (instruction q): rows 128 q + 2 lane and the next,
+  // of the activations for q < SQA (past M: the last row pair again), else of
+  // the weights
+  const uint16_t* gs[SPW];
+#pragma unroll
+  for (int t = 0; t < SPW; ++t) {
+    const int q = min(wave + 4 * t, SQ - 1);
+    gs[t] = q < SQA ? As + (int64_t)s_base * M + min(m0 + 128 * q + 2 * lane, M - 2)
+                    : Ws + (int64_t)s_base * N + (n0 + 128 * (q - SQA) + 2 * lane);
+  }
+  auto dma_one = [&](int d, int buf, int slab) {
+    char* sb = smem + buf * SLAB;
+    if (d < GA) {
+      dma16(ga[d] + slab * 64, sb + (wave + 4 * d) * 1024);
+    } else if (d < GA + GW) {
+      dma16(gw[d - GA] + slab * 64, sb + BM * ROWB + (wave + 4 * (d - GA)) * 1024);
+    } else {
+      const int t = d - GA - GW, q = min(wave + 4 * t, SQ - 1);
+      const int64_t step = q < SQA ? M : N;  // u16 elements per slab in this scale array
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gs[t] + slab * step), (lds_void*)(sb + SCB + q * 256), 4, 0, 0);
+    }
+  };
+
+  f32x16 acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  constexpr int P = NI * MI, NR = NI + MI;
+  const int a_row = wm * (BM / 2) + lr, w_row = BM + wn * (BN / 2) + lr;  // slab rows (W after A)
+  v8i wf[2][NI], af[2][MI];
+  int wsc[2][NI], asc[2][MI];
+  // fragment read r of a slab (and its scale byte): r < NI weights, else activations
+  auto read_one = [&](int r, int set, int buf) {
+    const char* sb = smem + buf * SLAB;
+    const int row = r < NI ? w_row + 32 * r : a_row + 32 * (r - NI);
+    const char* rp = sb + row * ROWB;
+    const int x = swz64(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + ((lh ^ x) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (((2 + lh) ^ x) << 4));
+    const v8i f = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const int srow = r < NI ? mx_arows<BM>() + (row - BM) : row;  // row in the scale area
+    const int sc = (int)(*reinterpret_cast<const uint16_t*>(sb + SCB + srow * 2) >> (8 * lh));
+    if (r < NI) { wf[set][r] = f; wsc[set][r] = sc; }
+    else { af[set][r - NI] = f; asc[set][r - NI] = sc; }
+  };
+  auto mma_slab = [&](auto set_c, int rbuf, int dbuf, int dslab) {
+    constexpr int set = decltype(set_c)::value;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[set][i], af[set][j], acc[i][j], 0, 0,
+                                                                    0, wsc[set][i], 0, asc[set][j]);
+        const int slot = i * MI + j;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (r * P / NR == slot) read_one(r, set ^ 1, rbuf);
+#pragma unroll
+        for (int d = 0; d < DPS; ++d)
+          if (d * P / DPS == slot) dma_one(d, dbuf, dslab);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  const int KT = K / 64;
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0)
+#pragma unroll
+    for (int d = 0; d < DPS; ++d) dma_one(d, s0, min(s0, KT - 1));
+  wait_vm<(NS - 1) * DPS>();
+  barrier();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_one(r, 0, 0);
+  auto iteration = [&](int kt, auto set_c) {
+    wait_vm<(NS - 2) * DPS>();  // this wave's DMAs of slab kt + 1 have landed
+    wait_lgkm0();               // and its fragments of slab kt are in registers
+    barrier();                  // so for every wave: slab kt + 1 is in, buffer kt % NS is free
+    mma_slab(set_c, (kt + 1) % NS, kt % NS, min(kt + NS, KT - 1));
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    iteration(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < KT) iteration(kt + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vm<0>();
+  static_assert(4 * Stage<BN / 2>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
+  wait_lgkm0();
+  barrier();
+  store_tile<EPI, BM, BN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
+}
+
+// one thread per 32-element block: codes and the block's scale byte
+template <typename T>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ in, int64_t rows, int K,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ scales) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nb = K / 32;
+  if (b >= rows * nb) return;
+  const int64_t row = b / nb;
+  const int kb = (int)(b - row * nb);
+  const T* p = in + row * K + 32 * kb;
+  float y[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    if constexpr (sizeof(T) == 4) y[e] = p[e];
+    else y[e] = bf2f(p[e]);
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+  const int ex = mx_shared_exp(amax);
+  const float inv = mx_inv_scale(ex);
+  u32x4 w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x2 a = pack8_e4m3(y + 16 * h, inv), c = pack8_e4m3(y + 16 * h + 8, inv);
+    w[h] = u32x4{a.x, a.y, c.x, c.y};
+  }
+  u32x4* op = reinterpret_cast<u32x4*>(codes + row * K + 32 * kb);
+  op[0] = w[0];
+  op[1] = w[1];
+  reinterpret_cast<uint8_t*>(scales)[((int64_t)(kb / 2) * rows + row) * 2 + (kb & 1)] = (uint8_t)(ex + 127);
+}
+
+template <int BM, int BN, int NS>
+hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
+                     const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s,
+                     int splits = 1) {
+  if (N % BN || splits < 1 || K % (splits * 64) || lda % 16 || ldw % 16 || M % 2) return hipErrorInvalidValue;
+  if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
+    return hipErrorInvalidValue;
+  if (epi == EPI_GELU_MX && (!ep.out_q || !ep.q_scale || ep.ldq % 16)) return hipErrorInvalidValue;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = tiles_m * (N / BN);
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
+#define FH_MX(E) gemm_mx_nt<E, BM, BN, NS><<<grid, block, 0, s>>>(A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
+  switch (epi) {
+    case EPI_BF16: FH_MX(EPI_BF16); break;
+    case EPI_GELU_MX: FH_MX(EPI_GELU_MX); break;
+    case EPI_GATED_RES: FH_MX(EPI_GATED_RES); break;
+    case EPI_RES: FH_MX(EPI_RES); break;
+    case EPI_PARTIAL: FH_MX(EPI_PARTIAL); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FH_MX
+  return hipGetLastError();
 }
 
 // x[m, n] += gate * (sum_s part[s][m, n] + bias[n]) (gate = 1 without a table),
@@ -403,6 +675,34 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
     case 3: return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     default: return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
+}
+
+hipError_t gemm_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
+                   const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (N % 128 || K % 64 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
+  if (N % 256 == 0 && N >= 4096) return launch_mx<192, 256, 4>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
+  return launch_mx<192, 128, 5>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
+}
+
+hipError_t gemm_mx_splitk(const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
+                          const uint16_t* Ws, int M, int N, int K, float* part, size_t part_elems,
+                          hipStream_t s) {
+  if (!gemm_splitk_ok(M, N, K)) return hipErrorInvalidValue;
+  EpiArgs ep;
+  ep.part = part;
+  ep.part_elems = part_elems;
+  return launch_mx<128, 128, 6>(EPI_PARTIAL, A, lda, As, W, ldw, Ws, M, N, K, ep, s, 2);
+}
+
+hipError_t mx_quantize(const float* in_f, const bf16_t* in_b, int64_t rows, int K, uint8_t* codes,
+                       uint16_t* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K % 64 || (!in_f == !in_b) || !codes || !scales) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((rows * (K / 32) + 255) / 256);
+  if (in_f) mx_quantize_kernel<float><<<grid, 256, 0, s>>>(in_f, rows, K, codes, scales);
+  else mx_quantize_kernel<bf16_t><<<grid, 256, 0, s>>>(in_b, rows, K, codes, scales);
+  return hipGetLastError();
 }
 
 }  // namespace fh

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
     float* __restrict__ x, bf16_t* __restrict__ out, int rows, int D, int rows_per_lane, float eps,
     const float* __restrict__ tab_shift, const float* __restrict__ tab_scale,
     const float* __restrict__ e_shift, const float* __restrict__ e_scale, int e_stride,
-    const float* __restrict__ g, const float* __restrict__ b, PendingRes pend) {
+    const float* __restrict__ g, const float* __restrict__ b, PendingRes pend, uint8_t* __restrict__ out_q,
+    uint16_t* __restrict__ q_scale) {
   __shared__ float red[8];
   const int row = blockIdx.x;
   const int c = threadIdx.x * 8;
@@ -74,11 +75,26 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
       add[e] = tab_shift[c + e] + eh[c + e];
     }
   }
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (v[e] - mean) * rstd * mul[e] + add[e];
+  if (out_q) {
+    // MX-FP8: a 32-column block is 4 consecutive threads (D is a multiple of 64)
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ex = mx_shared_exp(amax);
+    *reinterpret_cast<u32x2*>(out_q + (int64_t)row * D + c) = pack8_e4m3(y, mx_inv_scale(ex));
+    if ((threadIdx.x & 3) == 0)
+      reinterpret_cast<uint8_t*>(q_scale)[((int64_t)(c / 64) * rows + row) * 2 + ((c / 32) & 1)] =
+          (uint8_t)(ex + 127);
+    return;
+  }
   u32x4 w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = pack2bf((v[2 * e] - mean) * rstd * mul[2 * e] + add[2 * e],
-                   (v[2 * e + 1] - mean) * rstd * mul[2 * e + 1] + add[2 * e + 1]);
+  for (int e = 0; e < 4; ++e) w[e] = pack2bf(y[2 * e], y[2 * e + 1]);
   *reinterpret_cast<u32x4*>(out + (int64_t)row * D + c) = w;
 }
 
@@ -137,9 +153,10 @@ int threads_for(int D) { return ((D / 8 + 63) / 64) * 64; }
 hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_lane, float eps,
                           const float* tab_shift, const float* tab_scale, const float* e_shift,
                           const float* e_scale, int e_stride, const float* g, const float* b,
-                          const PendingRes* pend, hipStream_t s) {
+                          const PendingRes* pend, hipStream_t s, uint8_t* out_q, uint16_t* q_scale) {
   if (rows <= 0) return hipSuccess;
   if (D % 8 || threads_for(D) > 256) return hipErrorInvalidValue;
+  if (out_q && (D % 64 || !q_scale)) return hipErrorInvalidValue;
   PendingRes p;
   if (pend && pend->part) {
     if (pend->nparts < 1 || !pend->bias || (pend->gate_tab && pend->rows_per_lane <= 0))
@@ -147,7 +164,7 @@ hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_l
     p = *pend;
   }
   layernorm_kernel<<<rows, threads_for(D), 0, s>>>(x, out, rows, D, rows_per_lane, eps, tab_shift, tab_scale,
-                                                   e_shift, e_scale, e_stride, g, b, p);
+                                                   e_shift, e_scale, e_stride, g, b, p, out_q, q_scale);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 """Throughput of the FlashHead Lite slice denoiser on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload slice|slice_b3|slice768]
+                    [--sampler euler|renoise] [--precision bf16|fp8ffn]
 
 A step is one full slice denoise (30 blocks x 4 Euler steps, audio K/V, time
 embedding, head and motion pin) of a batch of synthetic inputs already in
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 FRAMES_PER_SLICE = 24         # each slice emits its last 24 frames
 METRIC = "DiT slice denoise video frames/s (30 blk×4 steps) + % bf16 MFMA peak"
@@ -88,11 +90,11 @@ def cpu_baseline(cfg, sigmas, budget_s=15.0):
                       f"whole slice"}
 
 
-def traffic_from_profile(kernel_src_hash):
+def traffic_from_profile(kernel_src_hash, name):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
-    size), if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_ffn2_slice_b1_counters.json")
+    counter summary profiles/<name> (FETCH_SIZE and WRITE_SIZE scaled by a copy
+    kernel of known size), if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
@@ -112,6 +114,9 @@ def main():
     ap.add_argument("--workload", default="slice", choices=sorted(WORKLOADS))
     ap.add_argument("--sampler", default="euler", choices=["euler", "renoise"],
                     help="step update: Euler (the metric's configuration) or the re-noising variant")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8ffn"],
+                    help="bf16 everywhere (the metric's configuration), or the FFN's two GEMMs in "
+                         "block-scaled FP8 (MX e4m3, one power-of-two scale per 32 along K)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
@@ -137,6 +142,10 @@ def main():
     ctx = fh.fh_create(cfg)
     w = fh.fh_weights_bind(ctx, W)
     del W
+    fp8 = args.precision == "fp8ffn"
+    if fp8:
+        fh.fh_weights_quantize_fp8(ctx, w)
+        fh.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN)
     ws = fh.workspace(ctx, B)
     lat, mot, aud = synth.slice_inputs(cfg, B)
     L, Mo, A = (torch.from_numpy(a).cuda() for a in (lat, mot, aud))
@@ -183,12 +192,14 @@ def main():
     k_flops = 2.0 * M * cfg.ffn_dim * cfg.dim
     k_avg_s = kms / 1e3 / max(kn, 1)
     achieved = k_flops / k_avg_s / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     src = open(os.path.join(ROOT, "audio_driven_talking_amd", "csrc", "gemm.hip"), "rb").read()
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_profile(hashlib.sha256(src).hexdigest()),
+    counters = "gemm_mx_ffn2_slice_b1_counters.json" if fp8 else "gemm_ffn2_slice_b1_counters.json"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_from_profile(hashlib.sha256(src).hexdigest(), counters),
                 "kernel": f"{ROOF_KERNEL} (M={M}, N={cfg.dim}, K={cfg.ffn_dim}, "
-                          f"{k_flops / 1e9:.2f} GFLOP per launch)",
+                          f"{'MX-FP8 e4m3' if fp8 else 'bf16'}, {k_flops / 1e9:.2f} GFLOP per launch)",
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
 
     breakdown = None
@@ -207,13 +218,15 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "frames/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16, FFN GEMMs mxfp8 (e4m3)" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) latent/motion/audio)",
         "config": {"workload": desc, "batch": B, "tokens": cfg.tokens, "blocks": cfg.n_blocks,
                    "euler_steps": n_steps, "dim": cfg.dim, "heads": cfg.n_heads,
                    "ffn": cfg.ffn_dim, "audio_tokens": cfg.audio_tokens,
                    "cross_attention": "full" if cfg.cross_full else "frame-local",
-                   "sampler": args.sampler, "graph": not args.no_graph},
+                   "sampler": args.sampler, "precision": args.precision,
+                   "graph": not args.no_graph},
         "latent_token_steps_per_s": round(B * cfg.tokens * n_steps * args.steps / T, 1),
         "mfma_frac_end_to_end": round(total_flops / (T / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),

@@ -173,14 +173,41 @@ int fh_dit_denoise_slice(fh_ctx* ctx, const fh_weights* w, int batch, const floa
  *       cos(2 pi u_b) for even i, sin(2 pi u_b) for odd i (Box-Muller).
  *       Motion frames are pinned after every step as with Euler; at s' = 0
  *       the two updates coincide.                                            */
-enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2, FH_OPT_SAMPLER = 3 };
+enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2, FH_OPT_SAMPLER = 3, FH_OPT_PRECISION = 4 };
 enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
+/*   FH_OPT_PRECISION: FH_PREC_BF16 (default): bf16 operands everywhere.
+ *     FH_PREC_FP8_FFN: the FFN's two GEMMs take MX-FP8 operands on gfx950's
+ *       block-scaled MFMA -- the FP8 precision path the page "SoulX-LiveAct,
+ *       real-time human animation video from audio and a still image"
+ *       credits for the sibling system's speed. Operands are OCP
+ *       microscaling FP8: e4m3 elements with one E8M0 power-of-two scale per
+ *       32 consecutive elements along K (fh_mxfp8_quantize gives the rule).
+ *       The FFN's LayerNorm and GELU emit MX-FP8 directly; the weights need
+ *       fh_weights_quantize_fp8 first (FH_EINVAL otherwise). Results differ
+ *       from the bf16 path by the FP8 rounding (a few percent).            */
+enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1 };
 enum {
   FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
   FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,
   FH_K_COUNT = 10
 };
 int fh_set_option(fh_ctx* ctx, int option, int value);
+/* Bytes of the device buffer fh_weights_quantize_fp8 fills (0 for a null ctx). */
+size_t fh_fp8_weight_bytes(const fh_ctx* ctx);
+/* Quantise the FFN matrices of bound weights to MX-FP8 into a caller-owned
+ * device buffer (256-byte aligned, fh_fp8_weight_bytes bytes; it must outlive
+ * w) and attach them to w. Enqueued on `stream`. FH_EINVAL for a null,
+ * foreign or misaligned argument or a short buffer; FH_EHIP on launch errors. */
+int fh_weights_quantize_fp8(fh_ctx* ctx, fh_weights* w, void* dev_buf, size_t bytes, void* stream);
+/* The MX-FP8 quantiser used by FH_PREC_FP8_FFN, on caller data: device f32
+ * in [rows][K] (K a multiple of 64, 16-byte aligned) -> codes [rows][K] (e4m3
+ * bytes) and scales [K/64][rows] uint16 (low byte: E8M0 of the 32-element
+ * block 2s, high byte: block 2s + 1). A block with max |x| = a > 0 has
+ * shared exponent floor(log2 a) - 8 (>= -127; E8M0 = exponent + 127), an
+ * all-zero block 0; codes are x * 2^-exponent clamped to +-448 and rounded
+ * to nearest even. FH_EINVAL for bad sizes or pointers, FH_EHIP on errors. */
+int fh_mxfp8_quantize(const float* in, int64_t rows, int32_t K, uint8_t* codes, uint16_t* scales, void* stream);
+
 /* Seed of FH_SAMPLER_RENOISE's noise (default 0). Returns FH_EINVAL for a null ctx. */
 int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
 

@@ -257,7 +257,7 @@ def block_weights(W, i):
     return {k[len(p):]: v for k, v in W.items() if k.startswith(p)}
 
 
-def dit_block(x, e0, audio, Wb, cfg, ang):
+def dit_block(x, e0, audio, Wb, cfg, ang, ffn_linear=linear):
     """One Wan-style block on the residual stream x [B, N, D].
 
     mods = table + e0 ([B, 6, D]): shift/scale/gate for self-attention, then
@@ -265,6 +265,9 @@ def dit_block(x, e0, audio, Wb, cfg, ang):
       x += gate_sa * O(SA(LN(x)(1+scale_sa)+shift_sa))
       x += CO(CA(LN_affine(x), audio))           (ungated)
       x += gate_ff * FFN(LN(x)(1+scale_ff)+shift_ff)
+
+    ffn_linear is the product used for the FFN's two layers: ``linear`` here,
+    or the block-scaled FP8 product of oracle/mxfp8.py for the FP8 variant.
     """
     x = to64(x)
     m = to64(Wb["mod"])[None] + to64(e0)
@@ -274,15 +277,15 @@ def dit_block(x, e0, audio, Wb, cfg, ang):
     kc, vc = audio_kv(audio, Wb, cfg)
     x = x + linear(cross_attention(h3, kc, vc, Wb, cfg), Wb["co.w"], Wb["co.b"])
     h = modulate(layer_norm(x, cfg.eps), m[:, 3], m[:, 4])
-    u = gelu_tanh(linear(h, Wb["ffn1.w"], Wb["ffn1.b"]))
-    return x + m[:, 5][:, None, :] * linear(u, Wb["ffn2.w"], Wb["ffn2.b"])
+    u = gelu_tanh(ffn_linear(h, Wb["ffn1.w"], Wb["ffn1.b"]))
+    return x + m[:, 5][:, None, :] * ffn_linear(u, Wb["ffn2.w"], Wb["ffn2.b"])
 
 
-def dit_block_from_temb(x, e, audio, W, i, cfg):
+def dit_block_from_temb(x, e, audio, W, i, cfg, ffn_linear=linear):
     """Block i with its modulation derived from a time embedding e [B, D]:
     e0 = Linear(SiLU(e)) (the shared time projection)."""
     e0 = linear(silu(e), W["time_proj.w"], W["time_proj.b"]).reshape(-1, 6, cfg.dim)
-    return dit_block(x, e0, audio, block_weights(W, i), cfg, rope_angles(cfg))
+    return dit_block(x, e0, audio, block_weights(W, i), cfg, rope_angles(cfg), ffn_linear)
 
 
 def patchify(latent):
@@ -298,14 +301,14 @@ def unpatchify(tokens, cfg):
     return np.moveaxis(t, -1, 1)
 
 
-def dit_flow(latent, sigma, audio, W, cfg, blocks=None):
+def dit_flow(latent, sigma, audio, W, cfg, blocks=None, ffn_linear=linear):
     """Flow prediction v [B, C, F, H, W] of the DiT at noise level sigma (scalar)."""
     B = latent.shape[0]
     e, e0 = time_embedding(np.full(B, sigma, dtype=np.float64), W, cfg)
     ang = rope_angles(cfg)
     x = linear(patchify(latent), W["patch.w"], W["patch.b"])
     for i in (range(cfg.n_blocks) if blocks is None else blocks):
-        x = dit_block(x, e0, audio, block_weights(W, i), cfg, ang)
+        x = dit_block(x, e0, audio, block_weights(W, i), cfg, ang, ffn_linear)
     hm = to64(W["head.mod"])[None] + e[:, None, :]          # [B, 2, D]: shift, scale
     h = modulate(layer_norm(x, cfg.eps), hm[:, 0], hm[:, 1])
     return unpatchify(linear(h, W["head.w"], W["head.b"]), cfg)
@@ -330,12 +333,12 @@ def euler_step(latent, v, sigma, sigma_next):
     return to64(latent) + (float(sigma_next) - float(sigma)) * to64(v)
 
 
-def denoise_slice(noise, motion, audio, sigmas, W, cfg):
+def denoise_slice(noise, motion, audio, sigmas, W, cfg, ffn_linear=linear):
     """Noise latent [B,C,F,H,W] -> denoised latent after len(sigmas)-1 steps,
     the motion frames pinned before the first step and after every step."""
     x = pin_motion(noise, motion)
     for i in range(len(sigmas) - 1):
-        v = dit_flow(x, sigmas[i], audio, W, cfg)
+        v = dit_flow(x, sigmas[i], audio, W, cfg, ffn_linear=ffn_linear)
         x = pin_motion(euler_step(x, v, sigmas[i], sigmas[i + 1]), motion)
     return x
 

@@ -21,6 +21,9 @@ to +-448 first (x / X < 512 can exceed 448). An all-zero block gets X = 1.
 e4m3 ("FN"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals
 m/8 * 2^-6; no infinities; S.1111.111 is NaN (never produced here).
 
+mx_linear is the FFN product of the FP8 variant of the block
+(``dit_block(..., ffn_linear=mx_linear)``).
+
 Decisions are taken on float32 inputs in float32-exact arithmetic (a power-
 of-two division and a rounding on a power-of-two grid are exact in float64),
 as the GPU takes them, so both sides produce the same codes.
@@ -29,7 +32,9 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["BLOCK", "e4m3_decode", "e4m3_encode", "mx_quantize", "mx_dequantize"]
+from .dit import linear
+
+__all__ = ["BLOCK", "e4m3_decode", "e4m3_encode", "mx_quantize", "mx_dequantize", "mx_linear"]
 
 BLOCK = 32
 E4M3_MAX = 448.0
@@ -66,7 +71,7 @@ def e4m3_encode(q):
     mf = np.rint(mf).astype(np.int64)
     code = (ef << 3) | mf
     code = np.where(mag == 0, 0, code)
-    return (code | np.where(q < 0, 0x80, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(q), 0x80, 0)).astype(np.uint8)  # the sign survives rounding to 0
 
 
 def mx_quantize(x):
@@ -92,3 +97,17 @@ def mx_dequantize(codes, scales):
     K = v.shape[-1]
     s = 2.0 ** (np.asarray(scales, dtype=np.float64) - 127.0)
     return (v.reshape(*v.shape[:-1], K // BLOCK, BLOCK) * s[..., None]).reshape(v.shape)
+
+
+def mx_linear(x, w, b=None):
+    """y = Q(x) Q(W)^T + b: both operands MX-quantised along their shared
+    K axis (x's rows and W's rows, W stored [out, in]) from float32 values,
+    then the product of the decoded values and the bias add in float64.
+
+    This is the FP8 GEMM's arithmetic with exact accumulation: the hardware's
+    scaled product sums the same decoded values (each code times its block's
+    power of two) in float32.
+    """
+    xq = mx_dequantize(*mx_quantize(np.asarray(x, dtype=np.float64).astype(np.float32)))
+    wq = mx_dequantize(*mx_quantize(np.asarray(w, dtype=np.float64).astype(np.float32)))
+    return linear(xq, wq, b)

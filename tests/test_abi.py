@@ -171,3 +171,35 @@ def test_sampler_option_and_generator_argument_errors():
     assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, -1, vp(1 << 40), None) == fh.FH_EINVAL     # negative
     assert fh.lib.fh_philox4x32_fill(1, 0, 0, 2**32 - 2, 3, vp(1 << 40), None) == fh.FH_EINVAL  # past 2^32
     assert fh.lib.fh_philox4x32_fill(1, 0, 0, 0, 0, None, None) == fh.FH_OK                # nothing to do
+
+
+def test_fp8_precision_argument_errors():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    st, w = _bind(ctx)
+    assert st == fh.FH_OK
+    L, vp = fh.lib, ctypes.c_void_p
+    c = synth.CONFIGS["toy"]
+    r = lambda b: (b + 255) // 256 * 256
+    per = r(c.ffn_dim * c.dim) * 2 + r(c.dim // 64 * c.ffn_dim * 2) + r(c.ffn_dim // 64 * c.dim * 2)
+    assert fh.fh_fp8_weight_bytes(ctx) == per * c.n_blocks
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 7) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN) == fh.FH_OK
+    # FP8 asked for before quantised weights exist: rejected before any launch
+    fake = vp(1 << 40)
+    need = fh.fh_workspace_bytes(ctx, 1)
+    sig = (ctypes.c_float * 2)(1.0, 0.0)
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EINVAL
+    assert "fh_weights_quantize_fp8" in fh.fh_last_error(ctx)
+    assert L.fh_dit_block_forward(ctx, w, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EINVAL
+    # quantisation buffer checks
+    nb = fh.fh_fp8_weight_bytes(ctx)
+    assert L.fh_weights_quantize_fp8(ctx, w, None, nb, None) == fh.FH_EINVAL
+    assert L.fh_weights_quantize_fp8(ctx, w, vp((1 << 40) + 16), nb, None) == fh.FH_EINVAL   # misaligned
+    assert L.fh_weights_quantize_fp8(ctx, w, fake, nb - 1, None) == fh.FH_EINVAL              # short
+    assert "smaller" in fh.fh_last_error(ctx)
+    # quantiser argument checks
+    assert L.fh_mxfp8_quantize(fake, 4, 96, fake, fake, None) == fh.FH_EINVAL    # K not a multiple of 64
+    assert L.fh_mxfp8_quantize(None, 4, 64, fake, fake, None) == fh.FH_EINVAL
+    assert L.fh_mxfp8_quantize(vp((1 << 40) + 4), 4, 64, fake, fake, None) == fh.FH_EINVAL
+    assert L.fh_mxfp8_quantize(fake, 0, 64, None, None, None) == fh.FH_OK
+    fh.lib.fh_weights_release(w)

@@ -294,3 +294,104 @@ def test_toy_renoise_last_step_is_euler(fh):
     fh.fh_set_noise_seed(m.ctx, 5)
     ren = m.slice(lat, mot, aud, sig)
     np.testing.assert_allclose(ren, eul, rtol=0, atol=1e-6 * np.abs(eul).max())
+
+
+# ------------------------------------------------------------------ MX-FP8 FFN
+from oracle import mxfp8 as Q  # noqa: E402
+
+# Two bars for the FP8 path. Against the oracle whose FFN takes the same
+# MX-FP8 product (oracle.mxfp8.mx_linear: same codes and scales, exact sums)
+# the library is held to TOL, the bf16 path's own bar: what remains is bf16
+# rounding and the few codes that flip where bf16 and float64 inputs straddle
+# a rounding point. Against the exact oracle, quantisation itself counts: an
+# e4m3 rounding (step 1/8 of the binade, log-uniform mantissa) leaves about
+# 2.65 % RMS relative error per element; the FFN rounds four operands in
+# series (LN output, W1, GELU output, W2), about sqrt(4) * 2.65 = 5.3 % RMS of
+# the FFN branch, which dominates a block's update (the CPU oracles alone
+# differ by 5.8 % RMS, 5.4 % in the max norm on the full-width block).
+# The max-norm ratio tracks the RMS ratio for these near-Gaussian errors, so
+# the bar is that size with a margin of about 1.7.
+TOL_FP8 = 1e-1
+
+
+def _scales_to_rows(sc, rows, K):
+    """[K/64, rows] uint16 (as int16) -> [rows, K/32] E8M0 bytes."""
+    u = sc.cpu().numpy().view(np.uint16).astype(np.uint32)
+    out = np.empty((rows, K // 32), np.uint8)
+    out[:, 0::2] = (u & 255).T
+    out[:, 1::2] = (u >> 8).T
+    return out
+
+
+def test_mxfp8_quantizer_bit_exact(fh):
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((96, 512)) * np.exp(rng.uniform(-30, 30, (96, 1)))).astype(np.float32)
+    x[0, :64] = 0.0
+    x[1, :32] = -0.0
+    x[2, 32:64] = np.float32(1e-42)                              # subnormal block
+    x[3, :] = np.where(np.arange(512) % 2 == 0, 448.0, -511.9)    # saturation
+    say("MX-FP8 quantiser: library vs oracle codes and scales")
+    codes, scales = fh.fh_mxfp8_quantize(dev(x))
+    torch.cuda.synchronize()
+    rc, rs = Q.mx_quantize(x)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(_scales_to_rows(scales, 96, 512), rs)
+
+
+def _fp8_model(fh, cfg, W, B):
+    m = Model(fh, cfg, W, B)
+    fh.fh_weights_quantize_fp8(m.ctx, m.w)
+    fh.fh_set_option(m.ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN)
+    return m
+
+
+def test_fp8_ffn_toy_slice(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = _fp8_model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say("toy slice, FP8 FFN, 4 steps")
+    got = m.slice(lat, mot, aud, sig)
+    Wf = synth.weights_f32(W)
+    ref_q = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear)
+    ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
+    err_q, err = O.rel_err(got, ref_q, cfg.motion_frames), O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err vs the MX-FP8 oracle {err_q:.3e} (bar {TOL}), vs the exact oracle {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL and err <= TOL_FP8
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig, graph=False), got)  # graph == direct
+
+
+def test_fp8_ffn_block(fh):
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    m = _fp8_model(fh, cfg, W, 1)
+    x, e, a = synth.block_inputs(cfg, 1)
+    say("full-width block, FP8 FFN")
+    got = m.block(0, x, e, a)
+    Wf = synth.weights_f32(W)
+    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, ffn_linear=Q.mx_linear), x)
+    err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
+    say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL}), "
+        f"vs the exact oracle {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL and err <= TOL_FP8
+
+
+@pytest.mark.parametrize("case,bar", [("slice_b1_fp8ffn", TOL), ("slice_b1", TOL_FP8)])
+def test_fp8_ffn_full_slice(fh, case, bar):
+    path = os.path.join(GOLDEN, case + ".npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path, allow_pickle=False)
+    cfg = synth.CONFIGS[str(g["config"])]
+    W = synth.make_weights(cfg)
+    assert synth.weights_digest(W) == str(g["digest"])
+    m = _fp8_model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    say(f"full slice B=1, FP8 FFN, against {case}")
+    got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
+    err = O.rel_err(got, g["out"], cfg.motion_frames)
+    say(f"  rel err {err:.3e} (bar {bar})")
+    assert err <= bar
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)

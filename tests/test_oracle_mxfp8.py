@@ -40,6 +40,7 @@ def test_encoder_is_nearest_even_by_brute_force():
     ref = np.where(tie, np.where(cand % 2 == 0, cand, 999).min(1), cand.min(1))
     np.testing.assert_array_equal(got, ref.astype(np.uint8))
     np.testing.assert_array_equal(Q.e4m3_encode(-q), ref.astype(np.uint8) | 0x80)  # sign bit only
+    np.testing.assert_array_equal(Q.e4m3_encode([0.0, -0.0, -2.0 ** -12]), [0x00, 0x80, 0x80])  # signed zeros
 
 
 def test_scales_put_block_max_in_range_and_round_trip_is_half_a_step():
@@ -74,3 +75,75 @@ def test_scaled_dot_products_track_exact_ones():
     got = Q.mx_dequantize(*Q.mx_quantize(a)) @ Q.mx_dequantize(*Q.mx_quantize(w)).T
     rel = np.abs(got - ref).max() / np.abs(ref).max()
     assert rel < 0.05
+
+
+def _representable(rng, rows, K):
+    """float32 [rows, K] whose every 32-block is e4m3 codes times one power of
+    two, the block maximum a full-range code (so MX quantisation is the
+    identity), with block scales spread over 2^-40 .. 2^40 along K and rows."""
+    codes = rng.integers(0, 0x7E, (rows, K)).astype(np.uint8)
+    codes = codes | (rng.integers(0, 2, (rows, K)).astype(np.uint8) << 7)
+    codes[:, ::32] = 0x7E | (codes[:, ::32] & 0x80)          # |max| = 448 in every block
+    v = Q.e4m3_decode(codes).reshape(rows, K // 32, 32)
+    e = rng.integers(-40, 40, (rows, K // 32))
+    return (v * 2.0 ** e[..., None]).reshape(rows, K).astype(np.float32)
+
+
+def test_mx_linear_is_exact_on_representable_operands():
+    """Quantisation must act along K on both operands: the blocks of x's rows
+    and W's rows are representable there (and only there: along any other
+    axis their scales, 2^80 apart, would flush the small values)."""
+    rng = np.random.default_rng(3)
+    x = _representable(rng, 24, 256)
+    w = _representable(rng, 64, 256)
+    b = rng.standard_normal(64)
+    np.testing.assert_array_equal(Q.mx_dequantize(*Q.mx_quantize(x)), x)  # identity on the grid
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b
+    np.testing.assert_array_equal(Q.mx_linear(x, w, b), ref)
+    # the same operands blocked along the other axis are not representable
+    wt = Q.mx_dequantize(*Q.mx_quantize(np.ascontiguousarray(w.T))).T
+    assert not np.array_equal(wt, w)
+
+
+def test_mx_linear_error_within_the_elementwise_bound():
+    """|Q(x)Q(W)^T - x W^T| <= |x| e_W^T + e_x |W|^T + e_x e_W^T, with the element
+    bound e = max(2^-4 |v|, 2^-10 X) (half a step, normal or subnormal grid),
+    X = 2^(floor(log2 amax) - 8) from the block maximum, and 2^-3 |v| for
+    elements above 448 X (saturation)."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((32, 512)) * np.exp(rng.uniform(-4, 4, (32, 512)))).astype(np.float32)
+    w = (rng.standard_normal((48, 512)) * 0.03).astype(np.float32)
+
+    def bound(v):
+        v = v.astype(np.float64)
+        vb = np.abs(v).reshape(v.shape[0], -1, 32)
+        X = 2.0 ** (np.floor(np.log2(vb.max(-1))) - 8)[..., None]
+        e = np.maximum(2.0 ** -4 * vb, 2.0 ** -10 * X)
+        e = np.where(vb > 448 * X, 2.0 ** -3 * vb, e)
+        return e.reshape(v.shape)
+
+    ex, ew = bound(x), bound(w)
+    ax, aw = np.abs(x.astype(np.float64)), np.abs(w.astype(np.float64))
+    lim = ax @ ew.T + ex @ aw.T + ex @ ew.T
+    err = np.abs(Q.mx_linear(x, w) - x.astype(np.float64) @ w.astype(np.float64).T)
+    assert np.all(err <= lim * (1 + 1e-9))
+    assert err.max() > 0                                     # it does quantise
+
+
+def test_block_routes_both_ffn_layers_through_the_product_hook():
+    import oracle as O
+    from synth import CONFIGS, make_weights, weights_f32, block_inputs
+    cfg = CONFIGS["toy"]
+    W = weights_f32(make_weights(cfg))
+    x, e, a = block_inputs(cfg, 1)
+    seen = []
+
+    def spy(h, w, b):
+        seen.append((h.shape[-1], w.shape))
+        return O.linear(h, w, b)
+
+    ref = O.dit_block_from_temb(x, e, a, W, 0, cfg)
+    got = O.dit_block_from_temb(x, e, a, W, 0, cfg, ffn_linear=spy)
+    np.testing.assert_array_equal(got, ref)
+    F = W["blocks.0.ffn1.w"].shape[0]
+    assert seen == [(cfg.dim, (F, cfg.dim)), (F, (cfg.dim, F))]
