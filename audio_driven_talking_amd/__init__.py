@@ -33,6 +33,7 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_weights_release", "fh_workspace_bytes", "fh_dit_block_forward",
            "fh_dit_denoise_slice", "fh_set_option", "fh_set_noise_seed", "fh_philox4x32_fill",
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
+           "fh_mxfp8_gemm",
            "fh_kernel_time", "fh_last_error", "fh_status_str"]
 
 
@@ -78,6 +79,7 @@ def _load():
         "fh_fp8_weight_bytes": (sz, [vp]),
         "fh_weights_quantize_fp8": (i32, [vp, vp, vp, sz, vp]),
         "fh_mxfp8_quantize": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
+        "fh_mxfp8_gemm": (i32, [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]),
         "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                      ctypes.c_int64, vp, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -323,6 +325,31 @@ def fh_mxfp8_quantize(x, stream=None):
     if st != FH_OK:
         raise FHError(st, f"fh_mxfp8_quantize: {fh_status_str(st)}")
     return codes, scales
+
+
+def fh_mxfp8_gemm(a_codes, a_scales, w_codes, w_scales, bias, y, part=None, stream=None):
+    """y += dec(A) dec(W)^T + bias (float32, in place) from MX-FP8 codes and
+    scales as fh_mxfp8_quantize returns them; with `part` (float32, 2*M*N
+    elements) K is split in two halves."""
+    import torch
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    for t, dt in ((a_codes, torch.uint8), (w_codes, torch.uint8), (a_scales, torch.int16),
+                  (w_scales, torch.int16), (bias, torch.float32), (y, torch.float32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("operands must be contiguous device tensors of the documented dtypes")
+    if w_codes.shape[1] != K or tuple(y.shape) != (M, N) or bias.numel() != N:
+        raise ValueError("shape mismatch")
+    if part is not None and (part.dtype != torch.float32 or part.numel() < 2 * M * N):
+        raise ValueError("part must hold 2*M*N float32")
+    p = ctypes.c_void_p(part.data_ptr()) if part is not None else None
+    st = lib.fh_mxfp8_gemm(ctypes.c_void_p(a_codes.data_ptr()), ctypes.c_void_p(a_scales.data_ptr()),
+                           ctypes.c_void_p(w_codes.data_ptr()), ctypes.c_void_p(w_scales.data_ptr()),
+                           M, N, K, ctypes.c_void_p(bias.data_ptr()), ctypes.c_void_p(y.data_ptr()), p,
+                           _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_mxfp8_gemm: {fh_status_str(st)}")
+    return y
 
 
 def fh_kernel_time(ctx):

@@ -1,6 +1,6 @@
 """Build libfh.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m audio_driven_talking_amd.build
+    python audio_driven_talking_amd/build.py   (or __graft_entry__.build())
 
 Every source is compiled on each call; the shared library lands next to this
 file, where the binding loads it from.

@@ -709,6 +709,36 @@ int fh_mxfp8_quantize(const float* in, int64_t rows, int32_t K, uint8_t* codes, 
   return e == hipSuccess ? FH_OK : FH_EHIP;
 }
 
+int fh_mxfp8_gemm(const uint8_t* a, const uint16_t* a_scales, const uint8_t* w, const uint16_t* w_scales,
+                  int64_t M, int32_t N, int32_t K, const float* bias, float* y, float* part, void* stream) {
+  if (M < 0 || M > (1 << 24) || N <= 0 || N % 128 || K <= 0 || K % 64 || M % 2) return FH_EINVAL;
+  if (M == 0) return FH_OK;
+  auto al = [](const void* p, uintptr_t n) { return p && ((uintptr_t)p % n) == 0; };
+  if (!al(a, 16) || !al(w, 16) || !al(a_scales, 4) || !al(w_scales, 4) || !al(bias, 16) || !al(y, 16) ||
+      (part && !al(part, 16)))
+    return FH_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (part) {
+    if (!fh::gemm_splitk_ok((int)M, N, K)) return FH_EINVAL;
+    e = fh::gemm_mx_splitk(a, K, a_scales, w, K, w_scales, (int)M, N, K, part, (size_t)2 * M * N, s);
+    if (e == hipSuccess) {
+      fh::PendingRes r;
+      r.part = part;
+      r.nparts = 2;
+      r.bias = bias;
+      e = fh::residual_from_parts(y, N, r, (int)M, N, s);
+    }
+  } else {
+    fh::EpiArgs ep;
+    ep.x = y;
+    ep.ldx = N;
+    ep.bias = bias;
+    e = fh::gemm_mx(fh::EPI_RES, a, K, a_scales, w, K, w_scales, (int)M, N, K, ep, s);
+  }
+  return e == hipSuccess ? FH_OK : FH_EHIP;
+}
+
 int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t first_group, int64_t n_groups,
                        uint32_t* out, void* stream) {
   if (n_groups < 0 || (n_groups > 0 && !out) || ((uintptr_t)out & 15)) return FH_EINVAL;

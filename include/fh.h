@@ -208,6 +208,22 @@ int fh_weights_quantize_fp8(fh_ctx* ctx, fh_weights* w, void* dev_buf, size_t by
  * to nearest even. FH_EINVAL for bad sizes or pointers, FH_EHIP on errors. */
 int fh_mxfp8_quantize(const float* in, int64_t rows, int32_t K, uint8_t* codes, uint16_t* scales, void* stream);
 
+/* The MX-FP8 GEMM of FH_PREC_FP8_FFN on caller data, in the residual form
+ * the FFN uses: y[m][n] += sum_k A(m,k) W(n,k) + bias[n] in float32, where
+ * A(m,k) and W(n,k) are the decoded values (e4m3 code times 2^(E8M0 - 127)
+ * of its 32-element block) of codes a [M][K], w [N][K] with scales
+ * a_scales [K/64][M], w_scales [K/64][N] laid out as fh_mxfp8_quantize
+ * writes them; y [M][N] and bias [N] are float32 (zero y for a plain
+ * product). With part == NULL one pass over K; with part (2*M*N floats of
+ * device scratch) K is split in two halves whose sums are added in order
+ * (needs M <= 1536, N <= 2048, K >= 4096, K % 128 == 0). Sizes: M even,
+ * N % 128 == 0, K % 64 == 0; codes, y, bias and part 16-byte aligned,
+ * scales 4-byte aligned. All device pointers, enqueued on `stream`.
+ * FH_EINVAL for bad sizes or pointers, FH_EHIP on launch errors.
+ * (OCP Microscaling: block-scaled operands of the scaled matrix product.) */
+int fh_mxfp8_gemm(const uint8_t* a, const uint16_t* a_scales, const uint8_t* w, const uint16_t* w_scales,
+                  int64_t M, int32_t N, int32_t K, const float* bias, float* y, float* part, void* stream);
+
 /* Seed of FH_SAMPLER_RENOISE's noise (default 0). Returns FH_EINVAL for a null ctx. */
 int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
 

@@ -203,3 +203,28 @@ def test_fp8_precision_argument_errors():
     assert L.fh_mxfp8_quantize(vp((1 << 40) + 4), 4, 64, fake, fake, None) == fh.FH_EINVAL
     assert L.fh_mxfp8_quantize(fake, 0, 64, None, None, None) == fh.FH_OK
     fh.lib.fh_weights_release(w)
+
+
+def test_mxfp8_gemm_argument_errors():
+    """Every rejected case returns FH_EINVAL before any launch."""
+    L, vp = fh.lib, ctypes.c_void_p
+    f = vp(1 << 40)                       # 256-aligned stand-in device address (never touched)
+    mis16, mis4 = vp((1 << 40) + 8), vp((1 << 40) + 2)
+
+    def call(a=f, sa=f, w=f, sw=f, M=64, N=128, K=64, bias=f, y=f, part=None):
+        return L.fh_mxfp8_gemm(a, sa, w, sw, M, N, K, bias, y, part, None)
+
+    assert call(M=63) == fh.FH_EINVAL                        # M odd
+    assert call(M=-2) == fh.FH_EINVAL
+    assert call(N=192) == fh.FH_EINVAL                       # N % 128
+    assert call(N=0) == fh.FH_EINVAL
+    assert call(K=96) == fh.FH_EINVAL                        # K % 64
+    for kw in ({"a": None}, {"sa": None}, {"w": None}, {"sw": None}, {"bias": None}, {"y": None}):
+        assert call(**kw) == fh.FH_EINVAL, kw
+    for kw in ({"a": mis16}, {"w": mis16}, {"bias": mis16}, {"y": mis16}, {"part": mis16},
+               {"sa": mis4}, {"sw": mis4}):
+        assert call(**kw) == fh.FH_EINVAL, kw
+    assert call(part=f, K=2048) == fh.FH_EINVAL              # split needs K >= 4096
+    assert call(part=f, M=1538, K=4096) == fh.FH_EINVAL      # and M <= 1536
+    assert call(part=f, N=2176, K=4096) == fh.FH_EINVAL      # and N <= 2048
+    assert call(M=0, a=None, y=None) == fh.FH_OK             # empty: nothing to do
