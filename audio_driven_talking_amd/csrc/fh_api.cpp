@@ -45,6 +45,9 @@ struct WS {
   float* ssq;   // per-row column-group sums of squares of the cross-attention queries
   uint8_t *hq, *uq;   // MX-FP8 FFN operands: normalised rows [B*N, D], hidden [B*N, Fd]
   uint16_t *hs, *us;  // and their scales [D/64][B*N], [Fd/64][B*N]
+  // float32 activations of FH_PREC_FP32 (carved only for that precision)
+  float *fh = nullptr, *fqkv = nullptr, *fao = nullptr, *fqc = nullptr, *fu = nullptr, *fkc = nullptr,
+        *fvc = nullptr;
   size_t total;
 };
 
@@ -160,6 +163,15 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.hs = (uint16_t*)take((D / 64) * B * N * 2);
   w.uq = (uint8_t*)take(B * N * Fd);
   w.us = (uint16_t*)take((Fd / 64) * B * N * 2);
+  if (c->precision == FH_PREC_FP32) {
+    w.fh = (float*)take(B * N * D * 4);
+    w.fqkv = (float*)take(B * N * 3 * D * 4);
+    w.fao = (float*)take(B * N * D * 4);
+    w.fqc = (float*)take(B * N * D * 4);
+    w.fu = (float*)take(B * N * Fd * 4);
+    w.fkc = (float*)take(nb * B * La * D * 4);
+    w.fvc = (float*)take(nb * B * La * D * 4);
+  }
   w.total = off;
   return w;
 }
@@ -342,6 +354,88 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
   return FH_OK;
 }
 
+// ---- float32 debug precision: the same block in float32 kernels, residual
+// updates applied at once (no pending parts)
+int audio_kv_f32(fh_ctx* c, const WBlock& wb, int B, const float* audio, float* kc, float* vc, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int D = g.dim, M = B * c->La;
+  fh::EpiF32Args ep;
+  ep.bias = wb.ckv_b;
+  ep.out = kc;
+  ep.ldo = D;
+  FH_HIP(fh::gemm_f32(fh::F32_OUT, audio, D, wb.ckv_w, D, M, D, D, ep, s));
+  ep.bias = wb.ckv_b + D;
+  ep.out = vc;
+  FH_HIP(fh::gemm_f32(fh::F32_OUT, audio, D, wb.ckv_w + (size_t)D * D, D, M, D, D, ep, s));
+  FH_HIP(fh::rmsnorm_rope_f32(kc, D, M, D, wb.norm_ck, nullptr, nullptr, c->La, g.head_dim, g.eps, s));
+  return FH_OK;
+}
+
+int run_block_f32(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int e0_stride,
+                  const float* kc, const float* vc, const WS& ws, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int N = c->N, D = g.dim, M = B * N, Fd = g.ffn_dim;
+  const float scale = 1.0f / std::sqrt((float)g.head_dim);
+  fh::EpiF32Args gated;
+  gated.x = x;
+  gated.ldx = D;
+  gated.gate_stride = e0_stride;
+  gated.rows_per_lane = N;
+  // self-attention branch
+  FH_HIP(fh::layernorm_f32(x, ws.fh, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride, nullptr,
+                           nullptr, s));
+  {
+    fh::EpiF32Args ep;
+    ep.bias = wb.qkv_b;
+    ep.out = ws.fqkv;
+    ep.ldo = 3 * D;
+    FH_HIP(fh::gemm_f32(fh::F32_OUT, ws.fh, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
+  }
+  FH_HIP(fh::rmsnorm_rope_f32(ws.fqkv, 3 * D, M, D, wb.norm_q, ws.rcos, ws.rsin, N, g.head_dim, g.eps, s));
+  FH_HIP(fh::rmsnorm_rope_f32(ws.fqkv + D, 3 * D, M, D, wb.norm_k, ws.rcos, ws.rsin, N, g.head_dim, g.eps, s));
+  FH_HIP(fh::attn_f32(ws.fqkv, 3 * D, ws.fqkv + D, 3 * D, ws.fqkv + 2 * D, 3 * D, ws.fao, D, B, N, N,
+                      g.n_heads, scale, c->HW, 0, 0, s));
+  gated.bias = wb.o_b;
+  gated.gate_tab = wb.mod + 2 * D;
+  gated.gate_e0 = e0 + 2 * D;
+  FH_HIP(fh::gemm_f32(fh::F32_GATED_RES, ws.fao, D, wb.o_w, D, M, D, D, gated, s));
+  // audio cross-attention branch
+  FH_HIP(fh::layernorm_f32(x, ws.fh, M, D, N, g.eps, nullptr, nullptr, nullptr, nullptr, 0, wb.norm3_g,
+                           wb.norm3_b, s));
+  {
+    fh::EpiF32Args ep;
+    ep.bias = wb.cq_b;
+    ep.out = ws.fqc;
+    ep.ldo = D;
+    FH_HIP(fh::gemm_f32(fh::F32_OUT, ws.fh, D, wb.cq_w, D, M, D, D, ep, s));
+  }
+  FH_HIP(fh::rmsnorm_rope_f32(ws.fqc, D, M, D, wb.norm_cq, nullptr, nullptr, N, g.head_dim, g.eps, s));
+  FH_HIP(fh::attn_f32(ws.fqc, D, kc, D, vc, D, ws.fao, D, B, N, c->La, g.n_heads, scale, c->HW,
+                      g.audio_per_frame, g.cross_full ? 0 : 1, s));
+  {
+    fh::EpiF32Args ep;
+    ep.bias = wb.co_b;
+    ep.x = x;
+    ep.ldx = D;
+    FH_HIP(fh::gemm_f32(fh::F32_RES, ws.fao, D, wb.co_w, D, M, D, D, ep, s));
+  }
+  // FFN branch
+  FH_HIP(fh::layernorm_f32(x, ws.fh, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D, e0 + 4 * D,
+                           e0_stride, nullptr, nullptr, s));
+  {
+    fh::EpiF32Args ep;
+    ep.bias = wb.ffn1_b;
+    ep.out = ws.fu;
+    ep.ldo = Fd;
+    FH_HIP(fh::gemm_f32(fh::F32_GELU, ws.fh, D, wb.ffn1_w, D, M, Fd, D, ep, s));
+  }
+  gated.bias = wb.ffn2_b;
+  gated.gate_tab = wb.mod + 5 * D;
+  gated.gate_e0 = e0 + 5 * D;
+  FH_HIP(fh::gemm_f32(fh::F32_GATED_RES, ws.fu, Fd, wb.ffn2_w, Fd, M, D, Fd, gated, s));
+  return FH_OK;
+}
+
 // The whole slice: audio K/V of every block, motion pin, then per step the
 // time embedding, patch embedding, all blocks and the head + Euler update.
 int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, const float* motion,
@@ -353,9 +447,12 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   FH_HIP(fh::pin_motion(latent, motion, out, B * C, N, nmt, s));
   if (n_steps == 0) return FH_OK;
   FH_HIP(fh::rope_table(ws.rcos, ws.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
-  FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
+  const bool f32 = c->precision == FH_PREC_FP32;
+  if (!f32) FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
   for (int i = 0; i < g.n_blocks; ++i) {
-    int rc = audio_kv(c, w->blk[i], B, ws.kc + i * slot_elems(c, B), ws.vct + i * slot_elems(c, B), ws, s);
+    int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
+                                ws.fvc + i * slot_elems(c, B), s)
+                 : audio_kv(c, w->blk[i], B, ws.kc + i * slot_elems(c, B), ws.vct + i * slot_elems(c, B), ws, s);
     if (rc) return rc;
   }
   for (int c0 = 0; c0 < n_steps; c0 += GEMV_ROWS) {
@@ -371,6 +468,23 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       const float* e = ws.e + (size_t)(st - c0) * D;
       const float* e0 = ws.e0 + (size_t)(st - c0) * 6 * D;
       FH_HIP(fh::patch_embed(out, B, C, N, w->patch_w, w->patch_b, ws.x, D, s));
+      fh::SamplerArgs sa;
+      sa.renoise = c->sampler == FH_SAMPLER_RENOISE;
+      sa.step = (uint32_t)st;
+      sa.k0 = (uint32_t)c->noise_seed;
+      sa.k1 = (uint32_t)(c->noise_seed >> 32);
+      if (f32) {
+        for (int i = 0; i < g.n_blocks; ++i) {
+          int rc = run_block_f32(c, w->blk[i], B, ws.x, e0, 0, ws.fkc + i * slot_elems(c, B),
+                                 ws.fvc + i * slot_elems(c, B), ws, s);
+          if (rc) return rc;
+        }
+        FH_HIP(fh::layernorm_f32(ws.x, ws.fh, B * N, D, N, g.eps, w->head_mod, w->head_mod + D, e, e, 0,
+                                 nullptr, nullptr, s));
+        FH_HIP(fh::head_euler_f32(ws.fh, B, N, D, w->head_w, w->head_b, g.out_ch, out, out, motion, nmt,
+                                  sigmas[st], sigmas[st + 1], sa, s));
+        continue;
+      }
       // each block's FFN residual update may stay pending until the next LayerNorm
       fh::PendingRes pend;
       for (int i = 0; i < g.n_blocks; ++i) {
@@ -383,11 +497,6 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       // head: LN modulated by (head.mod + e), then W_h, Euler step and motion pin
       FH_HIP(fh::layernorm_bf16(ws.x, ws.h, B * N, D, N, g.eps, w->head_mod, w->head_mod + D, e, e, 0,
                                 nullptr, nullptr, &pend, s));
-      fh::SamplerArgs sa;
-      sa.renoise = c->sampler == FH_SAMPLER_RENOISE;
-      sa.step = (uint32_t)st;
-      sa.k0 = (uint32_t)c->noise_seed;
-      sa.k1 = (uint32_t)(c->noise_seed >> 32);
       FH_HIP(fh::head_euler(ws.h, B, N, D, w->head_w, w->head_b, g.out_ch, out, out, motion, nmt,
                             sigmas[st], sigmas[st + 1], sa, s));
     }
@@ -547,14 +656,20 @@ int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, f
   const int D = g.dim;
   WS wsp = carve(c, batch, (char*)ws);
   FH_HIP(fh::rope_table(wsp.rcos, wsp.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
-  FH_HIP(fh::f32_to_bf16(audio, wsp.aud, (int64_t)batch * c->La * D, s));
-  rc = audio_kv(c, w->blk[block], batch, wsp.kc, wsp.vct, wsp, s);
+  const bool f32 = c->precision == FH_PREC_FP32;
+  if (f32) {
+    rc = audio_kv_f32(c, w->blk[block], batch, audio, wsp.fkc, wsp.fvc, s);
+  } else {
+    FH_HIP(fh::f32_to_bf16(audio, wsp.aud, (int64_t)batch * c->La * D, s));
+    rc = audio_kv(c, w->blk[block], batch, wsp.kc, wsp.vct, wsp, s);
+  }
   if (rc) return rc;
   for (int r0 = 0; r0 < batch; r0 += GEMV_ROWS) {
     const int R = batch - r0 < GEMV_ROWS ? batch - r0 : GEMV_ROWS;
     FH_HIP(fh::gemv_bf16(temb + (size_t)r0 * D, R, D, w->time_proj_w, w->time_proj_b,
                          wsp.e0 + (size_t)r0 * 6 * D, 6 * D, 1, 0, s));
   }
+  if (f32) return run_block_f32(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.fkc, wsp.fvc, wsp, s);
   // the same arithmetic as inside a slice: a pending FFN residual is applied at the end
   fh::PendingRes pend;
   rc = run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s, nullptr, &pend);
@@ -639,7 +754,7 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     return FH_OK;
   }
   if (option == FH_OPT_PRECISION) {
-    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN)
+    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32)
       return fail(c, FH_EINVAL, "unknown precision %d", value);
     c->precision = value;
     return FH_OK;

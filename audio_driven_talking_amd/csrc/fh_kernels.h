@@ -176,4 +176,45 @@ hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC,
 
 hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s);
 
+// ---- float32 debug path (FH_PREC_FP32): activations and products in float32 ----
+enum EpiF32 {
+  F32_OUT = 0,        // out[m, n] = C + bias
+  F32_GELU = 1,       // out[m, n] = gelu_tanh(C + bias)
+  F32_RES = 2,        // x[m, n] += C + bias
+  F32_GATED_RES = 3,  // x[m, n] += (gate_tab[n] + gate_e0[lane(m)][n]) (C + bias)
+};
+struct EpiF32Args {
+  const float* bias = nullptr;
+  float* out = nullptr;
+  int ldo = 0;
+  float* x = nullptr;
+  int ldx = 0;
+  const float* gate_tab = nullptr;
+  const float* gate_e0 = nullptr;
+  int gate_stride = 0;
+  int rows_per_lane = 1;
+};
+// C = A W^T with A float32 [M][lda], W bf16 [N][ldw] (N % 64 == 0, K % 16 == 0,
+// lda and ldw multiples of 4, A 16-byte and W 8-byte aligned rows).
+hipError_t gemm_f32(int epi, const float* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                    const EpiF32Args& ep, hipStream_t s);
+// LayerNorm of float32 rows to float32, modulated (g == nullptr) or affine, as layernorm_bf16.
+hipError_t layernorm_f32(const float* x, float* out, int rows, int D, int rows_per_lane, float eps,
+                         const float* tab_shift, const float* tab_scale, const float* e_shift,
+                         const float* e_scale, int e_stride, const float* g, const float* b, hipStream_t s);
+// In-place RMSNorm (gain g) of the first D columns of float32 rows, then the rotary
+// turn of rmsnorm_rope_bf16 when cos_t is non-null.
+hipError_t rmsnorm_rope_f32(float* p, int ld, int rows, int D, const float* g, const float* cos_t,
+                            const float* sin_t, int rows_per_lane, int head_dim, float eps, hipStream_t s);
+// Exact softmax attention in float32, one query row and head per workgroup (head_dim 128):
+// lane b's query n sees keys [0, Nk) of lane b, or with local != 0 the apf keys of
+// its latent frame n / hw; at most 4096 keys in a range.
+hipError_t attn_f32(const float* q, int ldq, const float* k, int ldk, const float* v, int ldv, float* o,
+                    int ldo, int B, int Nq, int Nk, int n_heads, float scale, int hw, int apf, int local,
+                    hipStream_t s);
+// head_euler on float32 rows h [B*N, D].
+hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
+                          const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
+                          float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s);
+
 }  // namespace fh

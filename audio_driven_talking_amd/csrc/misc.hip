@@ -210,6 +210,32 @@ __global__ __launch_bounds__(256) void head_euler_kernel(
   }
 }
 
+// Float32 form of the head update (debug precision): one thread per latent
+// element (lane, channel, token), v = h[row] . W_h[co] + b_h[co] in float32.
+__global__ __launch_bounds__(256) void head_euler_f32_kernel(
+    const float* __restrict__ h, int B, int N, int D, const bf16_t* __restrict__ Wh,
+    const float* __restrict__ bh, int Co, const float* lat_cur, float* lat_next,
+    const float* __restrict__ motion, int nmt, float sigma, float sigma_next, SamplerArgs sa) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * Co * N) return;
+  const int tok = (int)(i % N), co = (int)((i / N) % Co), b = (int)(i / ((int64_t)N * Co));
+  if (tok < nmt) {
+    lat_next[i] = motion[((int64_t)b * Co + co) * nmt + tok];
+    return;
+  }
+  const float* hr = h + ((int64_t)b * N + tok) * D;
+  const bf16_t* wr = Wh + (int64_t)co * D;
+  float v = 0.f;
+  for (int d = 0; d < D; ++d) v = fmaf(hr[d], bf2f(wr[d]), v);
+  v += bh[co];
+  if (sa.renoise) {
+    const float eps = latent_noise((uint32_t)(co * N + tok), (uint32_t)b, sa.step, sa.k0, sa.k1);
+    lat_next[i] = (1.f - sigma_next) * (lat_cur[i] - sigma * v) + sigma_next * eps;
+  } else {
+    lat_next[i] = lat_cur[i] + (sigma_next - sigma) * v;
+  }
+}
+
 __global__ void pin_motion_kernel(const float* __restrict__ lat, const float* __restrict__ motion,
                                   float* __restrict__ out, int64_t total, int N, int nmt) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -225,6 +251,16 @@ __global__ void f32_to_bf16_kernel(const float* __restrict__ in, bf16_t* __restr
 }
 
 }  // namespace
+
+hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
+                          const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
+                          float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s) {
+  const int64_t total = (int64_t)B * Co * N;
+  if (total <= 0) return hipSuccess;
+  head_euler_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next,
+                                                                       motion, n_motion_tok, sigma, sigma_next, sa);
+  return hipGetLastError();
+}
 
 hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,
                       hipStream_t s) {

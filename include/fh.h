@@ -115,7 +115,8 @@ void fh_weights_release(fh_weights* w);
 /* Device workspace (bytes, 256-byte aligned start required) for a batch of
  * `batch` independent lanes: activations, the audio keys/values of every
  * block, the rotary tables and the time embedding (the FlashHead type's
- * `work` scratch). 0 for batch <= 0 or a null ctx.                           */
+ * `work` scratch), for the context's current precision (FH_PREC_FP32 needs
+ * more). 0 for batch <= 0 or a null ctx.                                     */
 size_t fh_workspace_bytes(const fh_ctx* ctx, int batch);
 
 /* One DiT block (block index `block`) on the residual stream, in place.
@@ -184,8 +185,13 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       32 consecutive elements along K (fh_mxfp8_quantize gives the rule).
  *       The FFN's LayerNorm and GELU emit MX-FP8 directly; the weights need
  *       fh_weights_quantize_fp8 first (FH_EINVAL otherwise). Results differ
- *       from the bf16 path by the FP8 rounding (a few percent).            */
-enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1 };
+ *       from the bf16 path by the FP8 rounding (a few percent).
+ *     FH_PREC_FP32: debug precision -- every activation and product in
+ *       float32 (bf16 weights widened exactly), plain kernels, for checking
+ *       the block structure to ~1e-5. Slow. fh_workspace_bytes grows under
+ *       this precision (float32 activations and audio K/V), so query it after
+ *       setting the option; a smaller workspace is FH_EWORKSPACE.          */
+enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2 };
 enum {
   FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
   FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,

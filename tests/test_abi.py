@@ -228,3 +228,27 @@ def test_mxfp8_gemm_argument_errors():
     assert call(part=f, M=1538, K=4096) == fh.FH_EINVAL      # and M <= 1536
     assert call(part=f, N=2176, K=4096) == fh.FH_EINVAL      # and N <= 2048
     assert call(M=0, a=None, y=None) == fh.FH_OK             # empty: nothing to do
+
+
+def test_fp32_precision_option_and_workspace():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    L = fh.lib
+    base = fh.fh_workspace_bytes(ctx, 1)
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 3) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP32) == fh.FH_OK
+    c = synth.CONFIGS["toy"]
+    N, D, Fd, La = c.frames * c.height * c.width, c.dim, c.ffn_dim, c.frames * c.audio_per_frame
+    r = lambda b: (b + 255) // 256 * 256
+    # float32 h, qkv, attention output, cross query, FFN hidden, audio K and V of every block
+    extra = 3 * r(N * D * 4) + r(N * 3 * D * 4) + r(N * Fd * 4) + 2 * r(c.n_blocks * La * D * 4)
+    assert fh.fh_workspace_bytes(ctx, 1) == base + extra
+    # a workspace sized for bf16 is refused under FP32, before any launch
+    st, w = _bind(ctx)
+    assert st == fh.FH_OK
+    fake = ctypes.c_void_p(1 << 40)
+    sig = (ctypes.c_float * 2)(1.0, 0.0)
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake, fake, base, None) == fh.FH_EWORKSPACE
+    assert L.fh_dit_block_forward(ctx, w, 0, 1, fake, fake, fake, fake, base, None) == fh.FH_EWORKSPACE
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_BF16) == fh.FH_OK
+    assert fh.fh_workspace_bytes(ctx, 1) == base
+    fh.lib.fh_weights_release(w)

@@ -35,10 +35,12 @@ def say(msg):
 class Model:
     """Context + bound weights + workspace for one configuration."""
 
-    def __init__(self, fh, cfg, W, batch):
+    def __init__(self, fh, cfg, W, batch, precision=None):
         self.fh, self.cfg, self.W = fh, cfg, W
         self.ctx = fh.fh_create(cfg)
         self.w = fh.fh_weights_bind(self.ctx, W)
+        if precision is not None:  # before sizing the workspace: it depends on the precision
+            fh.fh_set_option(self.ctx, fh.FH_OPT_PRECISION, precision)
         self.ws = fh.workspace(self.ctx, batch)
 
     def slice(self, lat, mot, aud, sig, graph=True, out=None):
@@ -479,4 +481,87 @@ def test_fp8_ffn_full_slice(fh, case, bar):
     err = O.rel_err(got, g["out"], cfg.motion_frames)
     say(f"  rel err {err:.3e} (bar {bar})")
     assert err <= bar
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+
+
+# ------------------------------------------------------------------ float32 debug precision
+# Bar of the float32 debug precision against the float64 oracle. Every
+# product and sum is float32 (unit roundoff 6e-8): a dot product of K terms
+# errs by about sqrt(K) 6e-8 of its magnitude sum (2.4e-6 at K = 1536, 5.7e-6
+# at 8960), exponentials and square roots by a few ulp; through 30 blocks and
+# 4 steps the relative error stays near 1e-5; the stated bar for a float32
+# build, 1e-4, leaves a margin of about 10.
+TOL_F32 = 1e-4
+
+
+def test_fp32_toy_slice(fh):
+    """The toy configuration as stated for the float32 build: 2 blocks of width
+    256, 128 tokens, 64 audio tokens, one Euler step from sigma 1 to 0."""
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1, precision=fh.FH_PREC_FP32)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.TOY_SIGMAS)
+    say("toy slice, float32 debug precision")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err {err:.3e} (bar {TOL_F32})")
+    assert err <= TOL_F32
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig, graph=False), got)
+
+
+@pytest.mark.parametrize("variant", ["B2_4steps", "full_cross", "renoise"])
+def test_fp32_toy_variants(fh, variant):
+    cfg = synth.CONFIGS["toy"]
+    if variant == "full_cross":
+        cfg = cfg.replace(cross_full=True)
+    B = 2 if variant == "B2_4steps" else 1
+    W = synth.make_weights(cfg)
+    Wf = synth.weights_f32(W)
+    m = Model(fh, cfg, W, B, precision=fh.FH_PREC_FP32)
+    lat, mot, aud = synth.slice_inputs(cfg, B)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say(f"toy slice, float32 debug precision, {variant}")
+    if variant == "renoise":
+        fh.fh_set_option(m.ctx, fh.FH_OPT_SAMPLER, fh.FH_SAMPLER_RENOISE)
+        fh.fh_set_noise_seed(m.ctx, 99)
+        ref = R.denoise_slice_renoise(lat, mot, aud, sig, Wf, cfg, 99)
+    else:
+        ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
+    got = m.slice(lat, mot, aud, sig)
+    for b in range(B):
+        err = O.rel_err(got[b:b + 1], ref[b:b + 1], cfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e} (bar {TOL_F32})")
+        assert err <= TOL_F32
+
+
+def test_fp32_block(fh):
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1, precision=fh.FH_PREC_FP32)
+    x, e, a = synth.block_inputs(cfg, 1)
+    say("full-width block, float32 debug precision")
+    got = m.block(0, x, e, a)
+    err = delta_err(got, O.dit_block_from_temb(x, e, a, synth.weights_f32(W), 0, cfg), x)
+    say(f"  rel err of the update {err:.3e} (bar {TOL_F32})")
+    assert err <= TOL_F32
+
+
+def test_fp32_full_slice(fh):
+    path = os.path.join(GOLDEN, "slice_b1.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path, allow_pickle=False)
+    cfg = synth.CONFIGS[str(g["config"])]
+    W = synth.make_weights(cfg)
+    assert synth.weights_digest(W) == str(g["digest"])
+    m = Model(fh, cfg, W, 1, precision=fh.FH_PREC_FP32)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    say("full slice B=1, float32 debug precision, against slice_b1")
+    got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
+    err = O.rel_err(got, g["out"], cfg.motion_frames)
+    say(f"  rel err {err:.3e} (bar {TOL_F32})")
+    assert err <= TOL_F32
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
