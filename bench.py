@@ -81,13 +81,26 @@ def cpu_baseline(cfg, sigmas, budget_s=15.0):
             break
     t_block = (time.perf_counter() - t0) / k
     t_slice = t_block * cfg.n_blocks * (len(sigmas) - 1)
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    cpu = "unknown"
+    try:
+        cpu = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": FRAMES_PER_SLICE / t_slice, "unit": "frames/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu,
+            "blas": ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in blas})),
             "sample": f"{k} of the {cfg.n_blocks * (len(sigmas) - 1)} block-steps of one batch-1 "
                       f"slice (float64 numpy oracle, {t_block:.3f} s per block-step), scaled to the "
                       f"whole slice"}
+
+
+def device_info(torch):
+    """Name, compute units and L2 size of cuda:0 as the runtime reports them."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "compute_units": p.multi_processor_count,
+            "gcn_arch": getattr(p, "gcnArchName", ""), "l2_bytes": getattr(p, "L2_cache_size", None)}
 
 
 def traffic_from_profile(kernel_src_hash, name):
@@ -168,12 +181,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     T = time.perf_counter() - t0
     ms = 1e3 * T / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    p50 = per_step[len(per_step) // 2]
+    p90 = per_step[min(len(per_step) - 1, int(0.9 * len(per_step)))]
 
     total_flops, hot_flops = flops_per_slice(cfg, B, n_steps)
     value = FRAMES_PER_SLICE * B * args.steps / T
@@ -227,7 +246,9 @@ def main():
                    "cross_attention": "full" if cfg.cross_full else "frame-local",
                    "sampler": args.sampler, "precision": args.precision,
                    "graph": not args.no_graph},
+        "ms_per_step_p50": round(p50, 4), "ms_per_step_p90": round(p90, 4),
         "latent_token_steps_per_s": round(B * cfg.tokens * n_steps * args.steps / T, 1),
+        "device": device_info(torch),
         "mfma_frac_end_to_end": round(total_flops / (T / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),
         "roofline": roofline,
