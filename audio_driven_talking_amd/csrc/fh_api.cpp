@@ -2,6 +2,7 @@
 // the block / slice schedules, HIP graph capture and replay, kernel timing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -62,7 +63,13 @@ struct fh_weights {
   const float *time_in_b, *time_out_b, *time_proj_b, *patch_b, *head_b, *head_mod;
   std::vector<WBlock> blk;
   bool fp8 = false;  // MX-FP8 FFN copies attached
+  // identity of this binding's device pointers for the graph cache: new on
+  // every bind and every FP8 attach, so a graph captured on other pointers
+  // (e.g. of a released binding whose host address is reused) never matches
+  uint64_t serial = 0;
 };
+
+static std::atomic<uint64_t> g_weights_serial{1};
 
 struct fh_ctx {
   fh_config cfg;
@@ -177,10 +184,14 @@ WS carve(const fh_ctx* c, int B, char* base) {
 }
 
 // -------- kernel timing (events around the launches of one kernel class)
+// GEMM classes are one kernel launch each: their events are armed for the
+// launch itself (recorded by the dispatch at the kernel's start and end);
+// the other classes are bracketed by event records on the stream.
 struct Timed {
   fh_ctx* c;
   int cls;
   hipStream_t s;
+  bool at_launch = false;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   Timed(fh_ctx* c_, int cls_, hipStream_t s_) : c(c_), cls(cls_), s(s_) {
     if (c->time_class != cls) return;
@@ -193,11 +204,21 @@ struct Timed {
         return;
       }
     }
-    hipEventRecord(ev.first, s);
+    at_launch = cls == FH_K_GEMM_QKV || cls == FH_K_GEMM_O || cls == FH_K_GEMM_CQ || cls == FH_K_GEMM_CO ||
+                cls == FH_K_GEMM_FFN1 || cls == FH_K_GEMM_FFN2;
+    if (at_launch) fh::arm_launch_events(ev.first, ev.second);
+    else hipEventRecord(ev.first, s);
   }
   ~Timed() {
     if (!ev.first) return;
-    hipEventRecord(ev.second, s);
+    if (at_launch) {
+      if (!fh::launch_events_used()) {  // no launch took them (an error before it): not a sample
+        c->ev_free.push_back(ev);
+        return;
+      }
+    } else {
+      hipEventRecord(ev.second, s);
+    }
     c->ev_pending.push_back(ev);
   }
 };
@@ -604,6 +625,7 @@ int fh_weights_bind(fh_ctx* c, const void* blob, size_t blob_bytes, const fh_ten
     ptr[s.name] = (const char*)blob + t.offset;
   }
   fh_weights* w = new fh_weights();
+  w->serial = g_weights_serial++;
   w->ctx = c;
   auto M = [&](const std::string& n) { return (const bf16_t*)ptr[n]; };
   auto V = [&](const std::string& n) { return (const float*)ptr[n]; };
@@ -700,7 +722,7 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   if (!c->use_graph || c->time_class >= 0)
     return enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, sigmas, n_steps, latent_out, wsp, s);
 
-  std::vector<uint64_t> key = {(uint64_t)(uintptr_t)w, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
+  std::vector<uint64_t> key = {w->serial, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
                                (uint64_t)(uintptr_t)motion_latent, (uint64_t)(uintptr_t)audio_tokens,
                                (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
                                (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed,
@@ -812,6 +834,7 @@ int fh_weights_quantize_fp8(fh_ctx* c, fh_weights* w, void* buf, size_t bytes, v
     p += fp8_block_bytes(g);
   }
   w->fp8 = true;
+  w->serial = g_weights_serial++;  // new FFN pointers: graphs captured before must not match
   return FH_OK;
 }
 

@@ -7,6 +7,12 @@
 
 namespace fh {
 
+// Kernel timing: arm_launch_events(start, stop) makes the next GEMM launch on
+// this thread record start and stop from its own dispatch (hipExtLaunchKernel);
+// launch_events_used() then tells (and resets) whether a launch took them.
+void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+bool launch_events_used();
+
 // Epilogues of the bf16 GEMM C[M,N] = A[M,K] * W[N,K]^T (+ bias[N]).
 enum Epi {
   EPI_BF16 = 0,       // out_bf[m, n] = bf16(C + bias)

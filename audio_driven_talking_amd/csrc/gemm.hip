@@ -23,9 +23,44 @@
 #include <type_traits>
 
 #include "fh_common.h"
+#include <hip/hip_ext.h>
+
 #include "fh_kernels.h"
 
 namespace fh {
+
+namespace {
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+thread_local LaunchEvents t_launch_ev;
+
+// a GEMM launch: through hipExtLaunchKernelGGL with the armed events, if any
+template <typename Kern, typename... Args>
+void launch_gemm(Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchEvents& e = t_launch_ev;
+  if (e.start) {
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e.start, e.stop, 0, args...);
+    e.start = e.stop = nullptr;
+    e.used = true;
+  } else {
+    kern<<<grid, block, 0, s>>>(args...);
+  }
+}
+}  // namespace
+
+void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_launch_ev.start = start;
+  t_launch_ev.stop = stop;
+  t_launch_ev.used = false;
+}
+
+bool launch_events_used() {
+  const bool u = t_launch_ev.used;
+  t_launch_ev = LaunchEvents();
+  return u;
+}
 namespace {
 
 constexpr int KALIGN = 64;  // K must be a multiple of this (either slab depth divides it)
@@ -570,7 +605,7 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
-#define FH_MX(E) gemm_mx_nt<E, BM, BN, NS><<<grid, block, 0, s>>>(A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
+#define FH_MX(E) launch_gemm(gemm_mx_nt<E, BM, BN, NS>, grid, block, s, A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
   switch (epi) {
     case EPI_BF16: FH_MX(EPI_BF16); break;
     case EPI_GELU_MX: FH_MX(EPI_GELU_MX); break;
@@ -606,7 +641,7 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
-#define FH_GEMM(E) gemm_bf16_nt<E, BM, BN, BK, NS><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
+#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
   switch (epi) {
     case EPI_BF16: FH_GEMM(EPI_BF16); break;
     case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;

@@ -565,3 +565,53 @@ def test_fp32_full_slice(fh):
     say(f"  rel err {err:.3e} (bar {TOL_F32})")
     assert err <= TOL_F32
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+
+
+# ------------------------------------------------------------------ graph cache
+def test_rebinding_weights_never_replays_a_stale_graph(fh):
+    """A slice graph is cached per binding. Release a binding and bind other
+    weights through the same context, with the same device buffers: the new
+    call must use the new weights (the released binding's host address may be
+    reused by the new one), every replay must equal the direct launches, and
+    the FP8 attach (new FFN pointers) must not replay a bf16 graph."""
+    import gc
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    ctx = fh.fh_create(cfg)
+    ws = fh.workspace(ctx, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    L, Mo, A = dev(lat), dev(mot), dev(aud)
+    out = torch.empty_like(L)
+    sig = list(synth.TOY_SIGMAS)
+
+    def run(w):
+        fh.fh_dit_denoise_slice(ctx, w, L, Mo, A, sig, out, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    say("graph cache: bind, run twice, release, bind other weights, run")
+    w1 = fh.fh_weights_bind(ctx, W)
+    a1 = run(w1)
+    np.testing.assert_array_equal(run(w1), a1)          # replay == capture
+    del w1
+    gc.collect()
+    W2 = dict(W)
+    W2["head.b"] = (np.asarray(W["head.b"], dtype=np.float32) + 1.0).astype(np.float32)
+    w2 = fh.fh_weights_bind(ctx, W2)
+    a2 = run(w2)
+    ref2 = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W2), cfg)
+    assert O.rel_err(a2, ref2, cfg.motion_frames) <= TOL
+    assert not np.array_equal(a2, a1)
+    for _ in range(3):                                   # replays with eager work between
+        torch.zeros(1 << 20, device="cuda").add_(1.0)
+        np.testing.assert_array_equal(run(w2), a2)
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0)
+    np.testing.assert_array_equal(run(w2), a2)           # direct launches == graph
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 1)
+    say("graph cache: FP8 attach on the same binding")
+    fh.fh_weights_quantize_fp8(ctx, w2)
+    fh.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN)
+    a3 = run(w2)
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0)
+    np.testing.assert_array_equal(run(w2), a3)
+    assert O.rel_err(a3, ref2, cfg.motion_frames) <= TOL_FP8
