@@ -19,3 +19,4 @@ prints a tensor of the real model.
 from .dit import *  # noqa: F401,F403
 from . import renoise  # noqa: F401
 from . import mxfp8  # noqa: F401
+from . import audio  # noqa: F401

@@ -19,7 +19,7 @@ Distributions (none is on the pages; they are stated here once):
   * biases, modulation tables: N(0, 0.02), float32;
   * norm gains: 1 + N(0, 0.02), float32;
   * latent noise, motion latent, audio tokens, residual stream, time
-    embedding: N(0, 1), float32.
+    embedding, speech-encoder states: N(0, 1), float32.
 Every tensor has its own generator, keyed by (seed, crc32(name)), so a subset
 of blocks can be drawn without drawing the rest.
 """
@@ -39,6 +39,7 @@ MOTION_SEED = 43
 AUDIO_SEED = 44
 RESID_SEED = 41
 TEMB_SEED = 45
+STATES_SEED = 46
 LANE_SEED_STRIDE = 100
 
 
@@ -200,3 +201,67 @@ def block_inputs(cfg: DiTConfig, batch: int = 1):
     a = np.stack([normal((cfg.audio_tokens, cfg.dim), AUDIO_SEED + LANE_SEED_STRIDE * b)
                   for b in range(batch)])
     return x, e, a
+
+
+# ---------------------------------------------------------------- audio projection front end
+@dataclasses.dataclass(frozen=True)
+class AudioProjConfig:
+    """Sizes of the audio projection (speech-encoder states -> audio tokens).
+
+    The gizai:flashhead page fixes 12 layers' states at 200 frames, 5 states
+    around each of 33 frames, 5 latent frames of 32 tokens; channels 768 is the
+    width of wav2vec 2.0 base; the hidden width is not on the pages (a plain
+    choice)."""
+    layers: int = 12
+    state_frames: int = 200
+    channels: int = 768
+    window: int = 5
+    video_frames: int = 33
+    temporal_stride: int = 8
+    hidden: int = 512
+    tokens: int = 32
+    dim: int = 1536
+    eps: float = 1e-6
+
+    @property
+    def latent_frames(self) -> int:
+        return 1 + (self.video_frames - 1) // self.temporal_stride
+
+    @property
+    def feat(self) -> int:
+        return self.window * self.layers * self.channels
+
+    def replace(self, **kw) -> "AudioProjConfig":
+        return dataclasses.replace(self, **kw)
+
+
+AUDIO_CONFIGS = {
+    # matches the toy DiT: 2 latent frames x 32 tokens of width 256
+    "toy": AudioProjConfig(layers=2, state_frames=40, channels=64, video_frames=9, hidden=128, dim=256),
+    # the Lite slice: 5 latent frames x 32 tokens of width 1536
+    "lite": AudioProjConfig(),
+}
+
+
+def audio_param_specs(acfg: AudioProjConfig):
+    """(name, shape, kind) of the audio projection's tensors, in blob order."""
+    F, P, TD, D = acfg.feat, acfg.hidden, acfg.tokens * acfg.dim, acfg.dim
+    return [
+        ("proj1.w", (P, F), "matrix"), ("proj1.b", (P,), "vector"),
+        ("proj1vf.w", (P, F), "matrix"), ("proj1vf.b", (P,), "vector"),
+        ("proj2.w", (P, P), "matrix"), ("proj2.b", (P,), "vector"),
+        ("proj3.w", (TD, P), "matrix"), ("proj3.b", (TD,), "vector"),
+        ("projNorm.g", (D,), "gain"), ("projNorm.b", (D,), "vector"),
+    ]
+
+
+def make_audio_weights(acfg: AudioProjConfig, seed: int = WEIGHT_SEED):
+    """dict name -> array, drawn as make_weights draws the DiT's."""
+    return {n: _draw(seed, n, shape, kind) for n, shape, kind in audio_param_specs(acfg)}
+
+
+def audio_states(acfg: AudioProjConfig, batch: int = 1):
+    """Speech-encoder states [B, layers, state_frames, channels], N(0, 1); lane b
+    draws from seed 46 + 100 b."""
+    return np.stack([normal((acfg.layers, acfg.state_frames, acfg.channels), STATES_SEED + LANE_SEED_STRIDE * b)
+                     for b in range(batch)])
