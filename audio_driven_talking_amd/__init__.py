@@ -33,7 +33,8 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_weights_release", "fh_workspace_bytes", "fh_dit_block_forward",
            "fh_dit_denoise_slice", "fh_set_option", "fh_set_noise_seed", "fh_philox4x32_fill",
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
-           "fh_mxfp8_gemm",
+           "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
+           "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
            "fh_kernel_time", "fh_last_error", "fh_status_str"]
 
 
@@ -47,6 +48,11 @@ class fh_config(ctypes.Structure):
 class fh_tensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 4), ("offset", ctypes.c_uint64)]
+
+
+class fh_audio_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layers", "state_frames", "channels", "window", "temporal_stride", "hidden")]
 
 
 class FHError(RuntimeError):
@@ -80,6 +86,12 @@ def _load():
         "fh_weights_quantize_fp8": (i32, [vp, vp, vp, sz, vp]),
         "fh_mxfp8_quantize": (i32, [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]),
         "fh_mxfp8_gemm": (i32, [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]),
+        "fh_audio_weight_count": (i32, [vp, vp]),
+        "fh_audio_weight_spec": (i32, [vp, vp, i32, vp]),
+        "fh_audio_weights_bind": (i32, [vp, vp, vp, sz, vp, i32, vp]),
+        "fh_audio_weights_release": (None, [vp]),
+        "fh_audio_workspace_bytes": (sz, [vp, i32]),
+        "fh_audio_project": (i32, [vp, vp, i32, vp, vp, vp, sz, vp]),
         "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                      ctypes.c_int64, vp, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -183,11 +195,10 @@ def _host_bytes(a):
     raise TypeError(f"unsupported array dtype {a.dtype}")
 
 
-def fh_weights_bind(ctx: Context, tensors: dict, device="cuda") -> Weights:
-    """Pack `tensors` (name -> bf16-bits uint16 / float32 arrays or tensors) into
-    one device blob at 256-byte aligned offsets and bind it."""
+def _pack_blob(specs, tensors, device):
+    """One device blob holding `tensors` in `specs` order at 256-byte aligned
+    offsets, and its fh_tensor index (with the name buffers kept alive)."""
     import torch
-    specs = fh_weight_specs(ctx)
     entries, off = [], 0
     for name, _, shape in specs:
         if name not in tensors:
@@ -207,12 +218,19 @@ def fh_weights_bind(ctx: Context, tensors: dict, device="cuda") -> Weights:
         index[i].name = nb
         index[i].dtype = code
         index[i].ndim = len(shape)
-        for j, s in enumerate(shape):
-            index[i].shape[j] = s
+        for j, sz in enumerate(shape):
+            index[i].shape[j] = sz
         index[i].offset = o
+    return blob, index, names
+
+
+def fh_weights_bind(ctx: Context, tensors: dict, device="cuda") -> Weights:
+    """Pack `tensors` (name -> bf16-bits uint16 / float32 arrays or tensors) into
+    one device blob at 256-byte aligned offsets and bind it."""
+    blob, index, _names = _pack_blob(fh_weight_specs(ctx), tensors, device)
     h = ctypes.c_void_p()
     _check(ctx, lib.fh_weights_bind(ctx, ctypes.c_void_p(blob.data_ptr()), blob.numel(), index,
-                                    len(entries), ctypes.byref(h)))
+                                    len(index), ctypes.byref(h)))
     return Weights(h, blob, ctx)
 
 
@@ -365,3 +383,72 @@ def fh_last_error(ctx):
 
 def fh_status_str(status):
     return lib.fh_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------- audio projection front end
+def audio_config_struct(acfg) -> fh_audio_config:
+    """fh_audio_config from a mapping or an object with the same field names."""
+    get = (lambda k: acfg[k]) if isinstance(acfg, dict) else (lambda k: getattr(acfg, k))
+    c = fh_audio_config()
+    for n, _ in fh_audio_config._fields_:
+        setattr(c, n, int(get(n)))
+    return c
+
+
+class AudioWeights:
+    """An fh_audio_weights* plus its device blob and configuration (kept alive here)."""
+
+    def __init__(self, handle, blob, ctx, acfg):
+        self.handle, self.blob, self.ctx, self.acfg = handle, blob, ctx, acfg
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.fh_audio_weights_release(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+def fh_audio_weight_specs(ctx: Context, acfg):
+    """[(name, dtype, shape)] of the front end's tensors for `acfg` on this context."""
+    a = audio_config_struct(acfg)
+    n = lib.fh_audio_weight_count(ctx, ctypes.byref(a))
+    if n <= 0:
+        raise FHError(FH_EINVAL, "invalid audio configuration")
+    out, t = [], fh_tensor()
+    for i in range(n):
+        _check(None, lib.fh_audio_weight_spec(ctx, ctypes.byref(a), i, ctypes.byref(t)))
+        out.append((t.name.decode(), t.dtype, tuple(t.shape[:t.ndim])))
+    return out
+
+
+def fh_audio_weights_bind(ctx: Context, acfg, tensors: dict, device="cuda") -> AudioWeights:
+    a = audio_config_struct(acfg)
+    blob, index, _names = _pack_blob(fh_audio_weight_specs(ctx, acfg), tensors, device)
+    h = ctypes.c_void_p()
+    _check(ctx, lib.fh_audio_weights_bind(ctx, ctypes.byref(a), ctypes.c_void_p(blob.data_ptr()), blob.numel(),
+                                          index, len(index), ctypes.byref(h)))
+    return AudioWeights(h, blob, ctx, a)
+
+
+def fh_audio_workspace_bytes(aw: AudioWeights, batch: int) -> int:
+    return int(lib.fh_audio_workspace_bytes(aw, int(batch)))
+
+
+def audio_workspace(aw: AudioWeights, batch: int, device="cuda"):
+    import torch
+    return torch.empty(fh_audio_workspace_bytes(aw, batch), dtype=torch.uint8, device=device)
+
+
+def fh_audio_project(ctx, aw, states, tokens, ws, stream=None):
+    """states [B, layers, state_frames, channels] -> tokens [B, frames * audio_per_frame, dim]
+    (float32 device tensors; `tokens` written)."""
+    d = _dims(ctx)
+    a = aw.acfg
+    B = states.shape[0]
+    _check(ctx, lib.fh_audio_project(
+        ctx, aw, B, _dev_f32(states, (B, a.layers, a.state_frames, a.channels), "states"),
+        _dev_f32(tokens, (B, d["frames"] * d["audio_per_frame"], d["dim"]), "tokens"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))

@@ -2,6 +2,7 @@
 // the block / slice schedules, HIP graph capture and replay, kernel timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -86,6 +87,14 @@ struct fh_ctx {
   int64_t time_count = 0;
   hipStream_t cap_stream = nullptr;
   std::vector<GraphEntry> graphs;
+};
+
+struct fh_audio_weights {
+  fh_ctx* ctx;
+  fh_audio_config acfg;
+  int V, LF, F;  // video frames, latent frames, feature width
+  const bf16_t *p1_w, *p1vf_w, *p2_w, *p3_w;
+  const float *p1_b, *p1vf_b, *p2_b, *p3_b, *norm_g, *norm_b;
 };
 
 namespace {
@@ -525,6 +534,98 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   return FH_OK;
 }
 
+// Device pointers of every tensor of `specs` in a caller's blob, checked for
+// presence, dtype, shape, 16-byte alignment and bounds.
+int resolve_tensors(fh_ctx* c, const std::vector<Spec>& specs, const void* blob, size_t blob_bytes,
+                    const fh_tensor* index, int n_index, std::unordered_map<std::string, const void*>& ptr) {
+  if (!blob || !index || n_index <= 0) return fail(c, FH_EINVAL, "null blob or empty index");
+  if ((uintptr_t)blob & 15) return fail(c, FH_EWEIGHTS, "blob must be 16-byte aligned");
+  std::unordered_map<std::string, const fh_tensor*> by_name;
+  for (int i = 0; i < n_index; ++i) {
+    if (!index[i].name) return fail(c, FH_EINVAL, "index entry %d has no name", i);
+    by_name[index[i].name] = &index[i];
+  }
+  for (const Spec& s : specs) {
+    auto it = by_name.find(s.name);
+    if (it == by_name.end()) return fail(c, FH_EWEIGHTS, "weight '%s' missing from the index", s.name.c_str());
+    const fh_tensor& t = *it->second;
+    if (t.dtype != s.dtype)
+      return fail(c, FH_EWEIGHTS, "weight '%s' has dtype %d, expected %d", s.name.c_str(), t.dtype, s.dtype);
+    if (t.ndim != s.ndim || t.shape[0] != s.shape[0] || (s.ndim == 2 && t.shape[1] != s.shape[1]))
+      return fail(c, FH_EWEIGHTS, "weight '%s' has the wrong shape", s.name.c_str());
+    const size_t elems = (size_t)s.shape[0] * (s.ndim == 2 ? (size_t)s.shape[1] : 1);
+    const size_t bytes = elems * (s.dtype == FH_DTYPE_BF16 ? 2 : 4);
+    if (t.offset % 16) return fail(c, FH_EWEIGHTS, "weight '%s' offset is not 16-byte aligned", s.name.c_str());
+    if (t.offset > blob_bytes || bytes > blob_bytes - t.offset)
+      return fail(c, FH_EWEIGHTS, "weight '%s' lies outside the blob", s.name.c_str());
+    ptr[s.name] = (const char*)blob + t.offset;
+  }
+  return FH_OK;
+}
+
+// ---- audio projection front end
+int check_audio_cfg(fh_ctx* c, const fh_audio_config* a) {
+  if (!a) return fail(c, FH_EINVAL, "null audio configuration");
+  if (a->layers <= 0 || a->state_frames <= 0 || a->channels <= 0 || a->window <= 0 || a->temporal_stride <= 0 ||
+      a->hidden <= 0)
+    return fail(c, FH_ESHAPE, "audio configuration sizes must be positive");
+  const int64_t F = (int64_t)a->window * a->layers * a->channels;
+  if (F % 64 || F > (1 << 24) || a->hidden % 128 || a->hidden > 8192)
+    return fail(c, FH_EUNSUPPORTED,
+                "audio feature width (window x layers x channels) must be a multiple of 64 and hidden of 128");
+  return FH_OK;
+}
+
+std::vector<Spec> audio_specs(const fh_ctx* c, const fh_audio_config& a) {
+  const int64_t F = (int64_t)a.window * a.layers * a.channels, P = a.hidden,
+                TD = (int64_t)c->cfg.audio_per_frame * c->cfg.dim, D = c->cfg.dim;
+  return {{"proj1.w", FH_DTYPE_BF16, 2, {P, F}},   {"proj1.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj1vf.w", FH_DTYPE_BF16, 2, {P, F}}, {"proj1vf.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj2.w", FH_DTYPE_BF16, 2, {P, P}},   {"proj2.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj3.w", FH_DTYPE_BF16, 2, {TD, P}},  {"proj3.b", FH_DTYPE_F32, 1, {TD, 0}},
+          {"projNorm.g", FH_DTYPE_F32, 1, {D, 0}}, {"projNorm.b", FH_DTYPE_F32, 1, {D, 0}}};
+}
+
+// splits of a split-K GEMM: the largest divisor of the 64-column slabs that
+// keeps the grid within two workgroups per CU
+int audio_splits(int M, int N, int K) {
+  const int slabs = K / 64, tiles = ((M + 63) / 64) * (N / 128);
+  int best = 1;
+  for (int d = 1; d <= slabs && d <= 256; ++d)
+    if (slabs % d == 0 && (int64_t)d * tiles <= 512) best = d;
+  return best;
+}
+
+struct AudioWS {
+  bf16_t *X, *H1, *H2;
+  float *part, *Y;
+  size_t total;
+};
+
+AudioWS carve_audio(const fh_audio_weights* w, int B, char* base) {
+  const fh_config& g = w->ctx->cfg;
+  const size_t LF = w->LF, F = w->F, P = w->acfg.hidden, TD = (size_t)g.audio_per_frame * g.dim;
+  const size_t M = LF * B;
+  size_t parts = (size_t)audio_splits(B, (int)P, (int)F) * B * P;
+  if (LF > 1) parts = std::max(parts, (size_t)audio_splits((int)(M - B), (int)P, (int)F) * (M - B) * P);
+  parts = std::max(parts, (size_t)audio_splits((int)M, (int)P, (int)P) * M * P);
+  parts = std::max(parts, (size_t)audio_splits((int)M, (int)TD, (int)P) * M * TD);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  AudioWS a;
+  a.X = (bf16_t*)take(M * F * 2);
+  a.H1 = (bf16_t*)take(M * P * 2);
+  a.H2 = (bf16_t*)take(M * P * 2);
+  a.part = (float*)take(parts * 4);
+  a.Y = (float*)take(M * TD * 4);
+  a.total = off;
+  return a;
+}
+
 bool check_ws(fh_ctx* c, int B, void* ws, size_t ws_bytes, int* rc) {
   const size_t need = carve(c, B, nullptr).total;
   if (!ws || ((uintptr_t)ws & 255)) {
@@ -601,29 +702,9 @@ int fh_weights_bind(fh_ctx* c, const void* blob, size_t blob_bytes, const fh_ten
   if (!c) return FH_EINVAL;
   if (!out) return fail(c, FH_EINVAL, "out is NULL");
   *out = nullptr;
-  if (!blob || !index || n_index <= 0) return fail(c, FH_EINVAL, "null blob or empty index");
-  if ((uintptr_t)blob & 15) return fail(c, FH_EWEIGHTS, "blob must be 16-byte aligned");
-  std::unordered_map<std::string, const fh_tensor*> by_name;
-  for (int i = 0; i < n_index; ++i) {
-    if (!index[i].name) return fail(c, FH_EINVAL, "index entry %d has no name", i);
-    by_name[index[i].name] = &index[i];
-  }
   std::unordered_map<std::string, const void*> ptr;
-  for (const Spec& s : c->specs) {
-    auto it = by_name.find(s.name);
-    if (it == by_name.end()) return fail(c, FH_EWEIGHTS, "weight '%s' missing from the index", s.name.c_str());
-    const fh_tensor& t = *it->second;
-    if (t.dtype != s.dtype)
-      return fail(c, FH_EWEIGHTS, "weight '%s' has dtype %d, expected %d", s.name.c_str(), t.dtype, s.dtype);
-    if (t.ndim != s.ndim || t.shape[0] != s.shape[0] || (s.ndim == 2 && t.shape[1] != s.shape[1]))
-      return fail(c, FH_EWEIGHTS, "weight '%s' has the wrong shape", s.name.c_str());
-    const size_t elems = (size_t)s.shape[0] * (s.ndim == 2 ? (size_t)s.shape[1] : 1);
-    const size_t bytes = elems * (s.dtype == FH_DTYPE_BF16 ? 2 : 4);
-    if (t.offset % 16) return fail(c, FH_EWEIGHTS, "weight '%s' offset is not 16-byte aligned", s.name.c_str());
-    if (t.offset > blob_bytes || bytes > blob_bytes - t.offset)
-      return fail(c, FH_EWEIGHTS, "weight '%s' lies outside the blob", s.name.c_str());
-    ptr[s.name] = (const char*)blob + t.offset;
-  }
+  const int rc = resolve_tensors(c, c->specs, blob, blob_bytes, index, n_index, ptr);
+  if (rc) return rc;
   fh_weights* w = new fh_weights();
   w->serial = g_weights_serial++;
   w->ctx = c;
@@ -883,6 +964,98 @@ int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t fir
   if (n_groups > 0 && (uint64_t)first_group + (uint64_t)(n_groups - 1) > 0xFFFFFFFFull) return FH_EINVAL;
   const hipError_t e = fh::philox_fill(out, n_groups, first_group, lane, step, seed, (hipStream_t)stream);
   return e == hipSuccess ? FH_OK : FH_EHIP;
+}
+
+int fh_audio_weight_count(const fh_ctx* c, const fh_audio_config* a) {
+  if (!c || !a || check_audio_cfg(nullptr, a) != FH_OK) return 0;
+  return (int)audio_specs(c, *a).size();
+}
+
+int fh_audio_weight_spec(const fh_ctx* c, const fh_audio_config* a, int i, fh_tensor* out) {
+  if (!c || !a || !out) return FH_EINVAL;
+  if (check_audio_cfg(nullptr, a) != FH_OK) return FH_EINVAL;
+  static const char* const names[] = {"proj1.w", "proj1.b", "proj1vf.w", "proj1vf.b", "proj2.w",
+                                      "proj2.b", "proj3.w", "proj3.b", "projNorm.g", "projNorm.b"};
+  const std::vector<Spec> specs = audio_specs(c, *a);
+  if (i < 0 || i >= (int)specs.size()) return FH_EINVAL;
+  out->name = names[i];  // the same names as audio_specs, in its order (static storage)
+  out->dtype = specs[i].dtype;
+  out->ndim = specs[i].ndim;
+  out->shape[0] = specs[i].shape[0];
+  out->shape[1] = specs[i].shape[1];
+  out->shape[2] = out->shape[3] = 0;
+  out->offset = 0;
+  return FH_OK;
+}
+
+int fh_audio_weights_bind(fh_ctx* c, const fh_audio_config* a, const void* blob, size_t blob_bytes,
+                          const fh_tensor* index, int n_index, fh_audio_weights** out) {
+  if (!c) return FH_EINVAL;
+  if (!out) return fail(c, FH_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_audio_cfg(c, a);
+  if (rc) return rc;
+  std::unordered_map<std::string, const void*> ptr;
+  rc = resolve_tensors(c, audio_specs(c, *a), blob, blob_bytes, index, n_index, ptr);
+  if (rc) return rc;
+  fh_audio_weights* w = new fh_audio_weights();
+  w->ctx = c;
+  w->acfg = *a;
+  w->LF = c->cfg.frames;
+  w->V = 1 + (c->cfg.frames - 1) * a->temporal_stride;
+  w->F = a->window * a->layers * a->channels;
+  auto M = [&](const char* n) { return (const bf16_t*)ptr[n]; };
+  auto V = [&](const char* n) { return (const float*)ptr[n]; };
+  w->p1_w = M("proj1.w"); w->p1_b = V("proj1.b");
+  w->p1vf_w = M("proj1vf.w"); w->p1vf_b = V("proj1vf.b");
+  w->p2_w = M("proj2.w"); w->p2_b = V("proj2.b");
+  w->p3_w = M("proj3.w"); w->p3_b = V("proj3.b");
+  w->norm_g = V("projNorm.g"); w->norm_b = V("projNorm.b");
+  *out = w;
+  return FH_OK;
+}
+
+void fh_audio_weights_release(fh_audio_weights* w) { delete w; }
+
+size_t fh_audio_workspace_bytes(const fh_audio_weights* w, int batch) {
+  if (!w || batch <= 0) return 0;
+  return carve_audio(w, batch, nullptr).total;
+}
+
+int fh_audio_project(fh_ctx* c, const fh_audio_weights* w, int batch, const float* states, float* tokens,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!c) return FH_EINVAL;
+  if (!w || w->ctx != c) return fail(c, FH_EINVAL, "audio weights are null or bound to another context");
+  if (batch <= 0) return fail(c, FH_EINVAL, "batch must be positive, got %d", batch);
+  if (!states || !tokens) return fail(c, FH_EINVAL, "null states or tokens");
+  if (!ws || ((uintptr_t)ws & 255)) return fail(c, FH_EWORKSPACE, "workspace must be a non-null 256-byte aligned device pointer");
+  const AudioWS a = carve_audio(w, batch, (char*)ws);
+  if (ws_bytes < a.total)
+    return fail(c, FH_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes batch %d needs", ws_bytes,
+                a.total, batch);
+  const fh_config& g = c->cfg;
+  const fh_audio_config& ac = w->acfg;
+  const int B = batch, LF = w->LF, F = w->F, P = ac.hidden, TD = g.audio_per_frame * g.dim, M = LF * B;
+  hipStream_t s = (hipStream_t)stream;
+  FH_HIP(fh::audio_features(states, B, ac.layers, ac.state_frames, ac.channels, ac.window, w->V,
+                            ac.temporal_stride, LF, a.X, s));
+  auto proj = [&](const bf16_t* A, int lda, const bf16_t* W, const float* bias, int rows, int N, int K, int act,
+                  int group, int ngroups, float* out_f, bf16_t* out_b) -> int {
+    if (rows <= 0) return FH_OK;
+    const int sp = audio_splits(rows, N, K);
+    FH_HIP(fh::gemm_bf16_splitk_n(A, lda, W, K, rows, N, K, sp, a.part, (size_t)sp * rows * N, s));
+    FH_HIP(fh::sum_parts(a.part, sp, rows, N, bias, act, group, ngroups, out_f, out_b, s));
+    return FH_OK;
+  };
+  int rc = proj(a.X, F, w->p1_w, w->p1_b, B, P, F, 1, B, 1, nullptr, a.H1);            // latent frame 0
+  if (!rc) rc = proj(a.X + (size_t)B * F, F, w->p1vf_w, w->p1vf_b, M - B, P, F, 1, M - B, 1, nullptr,
+                     a.H1 + (size_t)B * P);                                                 // the others
+  if (!rc) rc = proj(a.H1, P, w->p2_w, w->p2_b, M, P, P, 1, M, 1, nullptr, a.H2);
+  if (!rc) rc = proj(a.H2, P, w->p3_w, w->p3_b, M, TD, P, 0, B, LF, a.Y, nullptr);         // rows -> lane-major
+  if (rc) return rc;
+  FH_HIP(fh::layernorm_f32(a.Y, tokens, B * c->La, g.dim, c->La, g.eps, nullptr, nullptr, nullptr, nullptr, 0,
+                           w->norm_g, w->norm_b, s));
+  return FH_OK;
 }
 
 int fh_kernel_time(fh_ctx* c, double* total_ms, int64_t* launches) {

@@ -106,6 +106,20 @@ bool gemm_splitk_ok(int M, int N, int K);
 hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                             float* part, size_t part_elems, hipStream_t s);
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s);
+// Split-K partial products of a small-M GEMM: part[s][m][n] = sum over K range s
+// (K / splits columns each) of A[m] . W[n] (64 x 128 tiles; N % 128 == 0,
+// K a multiple of 64 * splits, part_elems >= splits * M * N).
+hipError_t gemm_bf16_splitk_n(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int splits,
+                              float* part, size_t part_elems, hipStream_t s);
+
+// Audio projection front end (audio.hip). Window features with the latent
+// grouping: X[(i * B + b)][(d * L + l) * C + c], bf16, LF = 1 + (V - 1) / stride.
+hipError_t audio_features(const float* states, int B, int L, int T, int C, int W, int V, int stride, int LF,
+                          bf16_t* X, hipStream_t s);
+// out[row(m)][n] = act(sum_s part[s][m][n] + bias[n]) with row(m) = (m % group) * ngroups
+// + m / group (group * ngroups == M); act 0 none, 1 SiLU; float32 out_f or bf16 out_b.
+hipError_t sum_parts(const float* part, int splits, int M, int N, const float* bias, int act, int group,
+                     int ngroups, float* out_f, bf16_t* out_b, hipStream_t s);
 
 // LayerNorm of fp32 rows (width D) to bf16. Modulated form (g == nullptr):
 //   out = LN(x) * (1 + tab_scale + e_scale[lane]) + tab_shift + e_shift[lane]

@@ -686,6 +686,18 @@ hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
   return launch<128, 128, 64, 4>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
 }
 
+hipError_t gemm_bf16_splitk_n(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int splits,
+                              float* part, size_t part_elems, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (N % 128 || splits < 1 || K % (64 * splits) || lda % 8 || ldw % 8 || !part ||
+      part_elems < (size_t)splits * M * N)
+    return hipErrorInvalidValue;
+  EpiArgs ep;
+  ep.part = part;
+  ep.part_elems = part_elems;
+  return launch<64, 128, 64, 4>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, splits);
+}
+
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s) {
   if (M <= 0 || !r.part) return hipSuccess;
   if (N % 4 || ldx % 4 || r.nparts < 1 || (r.gate_tab && r.rows_per_lane <= 0)) return hipErrorInvalidValue;

@@ -96,6 +96,38 @@ def cpu_baseline(cfg, sigmas, budget_s=15.0):
                       f"whole slice"}
 
 
+def audio_front_end(fh, torch, ctx, cfg, B, stream, calls):
+    """Time the audio projection (speech-encoder states -> the slice's audio
+    tokens, once per slice) on its own: HIP events around `calls` calls. It
+    streams its bf16 weights once per call, so its bound is HBM."""
+    import synth
+    acfg = synth.AUDIO_CONFIGS["lite"]
+    Wa = synth.make_audio_weights(acfg)
+    wbytes = sum(a.nbytes for a in Wa.values())
+    aw = fh.fh_audio_weights_bind(ctx, acfg, Wa)
+    del Wa
+    ws = fh.audio_workspace(aw, B)
+    S = torch.from_numpy(synth.audio_states(acfg, B)).cuda()
+    tok = torch.empty(B, cfg.audio_tokens, cfg.dim, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        fh.fh_audio_project(ctx, aw, S, tok, ws, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        fh.fh_audio_project(ctx, aw, S, tok, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    # algorithmic bytes: the weights once, the states once, the tokens written
+    alg = wbytes + S.numel() * 4 + tok.numel() * 4
+    return {"us_per_call": round(us, 2), "calls_timed": calls, "bound": "hbm",
+            "algorithmic_bytes": int(alg), "achieved_GBps": round(alg / (us * 1e-6) / 1e9, 1),
+            "peak_GBps": PEAK_HBM_GBS, "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "workload": f"audio projection, batch {B}: 12 x 200 x 768 states -> {cfg.audio_tokens} tokens of "
+                        f"width {cfg.dim} (proj1/proj1vf 46080 -> 512, proj2, proj3 512 -> 32 x 1536, "
+                        f"LayerNorm)"}
+
+
 def device_info(torch):
     """Name, compute units and L2 size of cuda:0 as the runtime reports them."""
     p = torch.cuda.get_device_properties(0)
@@ -221,6 +253,8 @@ def main():
                           f"{'MX-FP8 e4m3' if fp8 else 'bf16'}, {k_flops / 1e9:.2f} GFLOP per launch)",
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
 
+    front = audio_front_end(fh, torch, ctx, cfg, B, stream, args.steps) if cfg_name == "slice" else None
+
     breakdown = None
     if args.breakdown:
         breakdown = {}
@@ -253,6 +287,8 @@ def main():
         "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),
         "roofline": roofline,
     }
+    if front is not None:
+        line["audio_front_end"] = front
     if breakdown is not None:
         line["kernel_ms_per_slice"] = breakdown
     if not args.no_cpu:

@@ -230,6 +230,57 @@ int fh_mxfp8_quantize(const float* in, int64_t rows, int32_t K, uint8_t* codes, 
 int fh_mxfp8_gemm(const uint8_t* a, const uint16_t* a_scales, const uint8_t* w, const uint16_t* w_scales,
                   int64_t M, int32_t N, int32_t K, const float* bias, float* y, float* part, void* stream);
 
+/* ---- Audio projection front end: speech-encoder states -> the audio tokens
+ * fh_dit_denoise_slice takes. The gizai:flashhead page (overview) makes a
+ * slice's 5 latent frames of 32 audio tokens from 5 states around each of its
+ * 33 frames, out of wav2vec 2.0 base's 12 layers at 200 frames, and names the
+ * layers proj1, proj1vf, proj2, proj3 and projNorm (type FlashHead). The
+ * arrangement is the plain reading of that:
+ *   - states [batch][layers][state_frames][channels], float32; the slice's V =
+ *     1 + (frames - 1) * temporal_stride video frames are the last V state frames;
+ *   - a frame's feature: the `window` states centred on it (offsets -window/2
+ *     .. window - 1 - window/2, clamped to the first and last state), flattened
+ *     in (offset, layer, channel) order, width F = window * layers * channels;
+ *   - latent frame 0 takes video frame 0's feature, latent frame i >= 1 the
+ *     mean of video frames s(i-1)+1 .. s i (s = temporal_stride);
+ *   - proj1 (latent frame 0) / proj1vf (the others): F -> hidden, SiLU; proj2:
+ *     hidden -> hidden, SiLU; proj3: hidden -> audio_per_frame * dim, the
+ *     latent frame's tokens in order; projNorm: LayerNorm over dim with gain
+ *     and bias (eps of the configuration);
+ *   - tokens [batch][frames * audio_per_frame][dim] float32, latent frame by
+ *     latent frame.
+ * Matrices bf16 [out, in] (products with float32 accumulation), vectors f32. */
+typedef struct fh_audio_config {
+  int32_t layers;          /* speech-encoder layers whose states are used (12) */
+  int32_t state_frames;    /* state frames over the encoder's window (200: 8 s at 25 per second) */
+  int32_t channels;        /* state width (768) */
+  int32_t window;          /* states around each video frame (5) */
+  int32_t temporal_stride; /* video frames per latent frame after the first (8) */
+  int32_t hidden;          /* width of proj1, proj1vf and proj2; a multiple of 128 */
+} fh_audio_config;
+typedef struct fh_audio_weights fh_audio_weights;
+
+/* Tensors of the front end for `acfg` on this context's DiT sizes: names
+ * proj1.{w,b} [hidden, F], proj1vf.{w,b} [hidden, F], proj2.{w,b}
+ * [hidden, hidden], proj3.{w,b} [audio_per_frame * dim, hidden], projNorm.{g,b}
+ * [dim]. Count 0 (spec FH_EINVAL) for a null or invalid configuration (sizes
+ * not positive, F not a multiple of 64, hidden not a multiple of 128).       */
+int fh_audio_weight_count(const fh_ctx* ctx, const fh_audio_config* acfg);
+int fh_audio_weight_spec(const fh_ctx* ctx, const fh_audio_config* acfg, int i, fh_tensor* out);
+/* Bind a caller-owned device blob holding those tensors (checks as
+ * fh_weights_bind); the blob must outlive the handle. FH_ESHAPE /
+ * FH_EUNSUPPORTED for a bad configuration, FH_EWEIGHTS for a bad index.     */
+int fh_audio_weights_bind(fh_ctx* ctx, const fh_audio_config* acfg, const void* dev_blob, size_t blob_bytes,
+                          const fh_tensor* index, int n_index, fh_audio_weights** out);
+void fh_audio_weights_release(fh_audio_weights* w);
+/* Device workspace bytes of fh_audio_project for `batch` lanes (0 for batch <= 0). */
+size_t fh_audio_workspace_bytes(const fh_audio_weights* w, int batch);
+/* states (device, layout above) -> tokens (device, layout above), enqueued on
+ * `stream`. FH_EINVAL for null pointers, foreign weights or batch <= 0,
+ * FH_EWORKSPACE for a missing, misaligned (256 bytes) or short workspace.   */
+int fh_audio_project(fh_ctx* ctx, const fh_audio_weights* w, int batch, const float* states, float* tokens,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Seed of FH_SAMPLER_RENOISE's noise (default 0). Returns FH_EINVAL for a null ctx. */
 int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
 

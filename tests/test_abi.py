@@ -252,3 +252,60 @@ def test_fp32_precision_option_and_workspace():
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_BF16) == fh.FH_OK
     assert fh.fh_workspace_bytes(ctx, 1) == base
     fh.lib.fh_weights_release(w)
+
+
+def test_audio_projection_specs_and_argument_errors():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    acfg = synth.AUDIO_CONFIGS["toy"]
+    specs = fh.fh_audio_weight_specs(ctx, acfg)
+    want = [(n, fh.FH_DTYPE_BF16 if k == "matrix" else fh.FH_DTYPE_F32, shape)
+            for n, shape, k in synth.audio_param_specs(acfg)]
+    assert specs == want
+    L, vp = fh.lib, ctypes.c_void_p
+    bad = fh.audio_config_struct(acfg.replace(hidden=100))          # not a multiple of 128
+    assert L.fh_audio_weight_count(ctx, ctypes.byref(bad)) == 0
+    assert L.fh_audio_weight_count(ctx, None) == 0
+    t = fh.fh_tensor()
+    assert L.fh_audio_weight_spec(ctx, ctypes.byref(bad), 0, ctypes.byref(t)) == fh.FH_EINVAL
+    good = fh.audio_config_struct(acfg)
+    assert L.fh_audio_weight_spec(ctx, ctypes.byref(good), 10, ctypes.byref(t)) == fh.FH_EINVAL
+    # binding checks need no device memory: stand-in addresses, a full and a broken index
+    def index(skip=None, shape_fix=None):
+        ents = [(n, d, s) for n, d, s in specs if n != skip]
+        arr = (fh.fh_tensor * len(ents))()
+        keep = []
+        off = 0
+        for i, (n, d, s) in enumerate(ents):
+            nb = n.encode()
+            keep.append(nb)
+            arr[i].name, arr[i].dtype, arr[i].ndim = nb, d, len(s)
+            for j, v in enumerate(shape_fix(n, s) if shape_fix else s):
+                arr[i].shape[j] = v
+            arr[i].offset = off
+            off += (int(np.prod(s)) * (2 if d == fh.FH_DTYPE_BF16 else 4) + 255) // 256 * 256
+        return arr, off, keep
+    h = vp()
+    arr, size, keep = index()
+    blob = vp(1 << 40)
+    assert L.fh_audio_weights_bind(ctx, ctypes.byref(bad), blob, size, arr, len(arr), ctypes.byref(h)) == \
+        fh.FH_EUNSUPPORTED
+    arr2, _, keep2 = index(skip="proj2.b")
+    assert L.fh_audio_weights_bind(ctx, ctypes.byref(good), blob, size, arr2, len(arr2), ctypes.byref(h)) == \
+        fh.FH_EWEIGHTS
+    assert "proj2.b" in fh.fh_last_error(ctx)
+    arr3, _, keep3 = index(shape_fix=lambda n, s: (s[0] + 1,) + s[1:] if n == "proj3.w" else s)
+    assert L.fh_audio_weights_bind(ctx, ctypes.byref(good), blob, size, arr3, len(arr3), ctypes.byref(h)) == \
+        fh.FH_EWEIGHTS
+    assert L.fh_audio_weights_bind(ctx, ctypes.byref(good), blob, size - 256, arr, len(arr), ctypes.byref(h)) == \
+        fh.FH_EWEIGHTS                                            # the last tensor outside the blob
+    assert L.fh_audio_weights_bind(ctx, ctypes.byref(good), blob, size, arr, len(arr), ctypes.byref(h)) == fh.FH_OK
+    need = L.fh_audio_workspace_bytes(h, 2)
+    assert need > 0 and L.fh_audio_workspace_bytes(h, 0) == 0
+    fake = vp(1 << 40)
+    assert L.fh_audio_project(ctx, h, 2, None, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_audio_project(ctx, h, 0, fake, fake, fake, need, None) == fh.FH_EINVAL
+    assert L.fh_audio_project(ctx, h, 2, fake, fake, fake, need - 1, None) == fh.FH_EWORKSPACE
+    assert L.fh_audio_project(ctx, h, 2, fake, fake, vp((1 << 40) + 16), need, None) == fh.FH_EWORKSPACE
+    ctx2 = fh.fh_create(synth.CONFIGS["toy"])
+    assert L.fh_audio_project(ctx2, h, 2, fake, fake, fake, need, None) == fh.FH_EINVAL   # foreign weights
+    L.fh_audio_weights_release(h)

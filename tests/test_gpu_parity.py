@@ -615,3 +615,55 @@ def test_rebinding_weights_never_replays_a_stale_graph(fh):
     fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0)
     np.testing.assert_array_equal(run(w2), a3)
     assert O.rel_err(a3, ref2, cfg.motion_frames) <= TOL_FP8
+
+
+# ------------------------------------------------------------------ audio projection front end
+from oracle import audio as AU  # noqa: E402
+
+
+def _audio_model(fh, name, B):
+    acfg = synth.AUDIO_CONFIGS[name]
+    dcfg = synth.CONFIGS["toy" if name == "toy" else "slice"]
+    ctx = fh.fh_create(dcfg)
+    Wa = synth.make_audio_weights(acfg)
+    aw = fh.fh_audio_weights_bind(ctx, acfg, Wa)
+    return acfg, dcfg, ctx, Wa, aw, fh.audio_workspace(aw, B)
+
+
+@pytest.mark.parametrize("name,B", [("toy", 2), ("lite", 1), ("lite", 3)])
+def test_audio_projection_against_oracle(fh, name, B):
+    acfg, dcfg, ctx, Wa, aw, ws = _audio_model(fh, name, B)
+    S = synth.audio_states(acfg, B)
+    tok = torch.empty(B, dcfg.audio_tokens, dcfg.dim, dtype=torch.float32, device="cuda")
+    say(f"audio projection {name} B={B}")
+    fh.fh_audio_project(ctx, aw, dev(S), tok, ws)
+    torch.cuda.synchronize()
+    got = tok.cpu().numpy()
+    for b in range(B):
+        ref = AU.audio_project(S[b:b + 1], synth.weights_f32(Wa), acfg)
+        err = O.rel_err(got[b:b + 1], ref)
+        say(f"  lane {b} rel err {err:.3e} (bar {TOL})")
+        assert err <= TOL
+
+
+def test_audio_projection_feeds_the_slice(fh):
+    """Front end then slice on the GPU against the oracle's front end then slice."""
+    acfg, dcfg, ctx, Wa, aw, ws_a = _audio_model(fh, "toy", 1)
+    W = synth.make_weights(dcfg)
+    w = fh.fh_weights_bind(ctx, W)
+    ws = fh.workspace(ctx, 1)
+    S = synth.audio_states(acfg, 1)
+    lat, mot, _ = synth.slice_inputs(dcfg, 1)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say("audio projection -> toy slice")
+    tok = torch.empty(1, dcfg.audio_tokens, dcfg.dim, dtype=torch.float32, device="cuda")
+    fh.fh_audio_project(ctx, aw, dev(S), tok, ws_a)
+    L = dev(lat)
+    out = torch.empty_like(L)
+    fh.fh_dit_denoise_slice(ctx, w, L, dev(mot), tok, sig, out, ws)
+    torch.cuda.synchronize()
+    ref_tok = AU.audio_project(S, synth.weights_f32(Wa), acfg)
+    ref = O.denoise_slice(lat, mot, ref_tok, sig, synth.weights_f32(W), dcfg)
+    err = O.rel_err(out.cpu().numpy(), ref, dcfg.motion_frames)
+    say(f"  rel err {err:.3e} (bar {TOL})")
+    assert err <= TOL
