@@ -128,10 +128,11 @@ class Context:
     def __init__(self, handle, cfg):
         self.handle = handle
         self.cfg = cfg
+        self._free = lib.fh_destroy   # kept: module globals may be gone when this object dies
 
     def __del__(self):
         if getattr(self, "handle", None):
-            lib.fh_destroy(self.handle)
+            self._free(self.handle)
             self.handle = None
 
     @property
@@ -144,10 +145,11 @@ class Weights:
 
     def __init__(self, handle, blob, ctx):
         self.handle, self.blob, self.ctx = handle, blob, ctx
+        self._free = lib.fh_weights_release
 
     def __del__(self):
         if getattr(self, "handle", None):
-            lib.fh_weights_release(self.handle)
+            self._free(self.handle)
             self.handle = None
 
     @property
@@ -400,10 +402,11 @@ class AudioWeights:
 
     def __init__(self, handle, blob, ctx, acfg):
         self.handle, self.blob, self.ctx, self.acfg = handle, blob, ctx, acfg
+        self._free = lib.fh_audio_weights_release
 
     def __del__(self):
         if getattr(self, "handle", None):
-            lib.fh_audio_weights_release(self.handle)
+            self._free(self.handle)
             self.handle = None
 
     @property

@@ -667,3 +667,35 @@ def test_audio_projection_feeds_the_slice(fh):
     err = O.rel_err(out.cpu().numpy(), ref, dcfg.motion_frames)
     say(f"  rel err {err:.3e} (bar {TOL})")
     assert err <= TOL
+
+
+# ------------------------------------------------------------------ largest supported sizes
+MAXCFG = synth.CONFIGS["slice"].replace(n_blocks=1, dim=2048, n_heads=16, ffn_dim=8192, in_ch=64, out_ch=64,
+                                        frames=3, height=8, width=12, motion_frames=2, audio_per_frame=64)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp32", "fp8ffn"])
+def test_largest_supported_sizes(fh, precision):
+    """Width 2048 (16 heads), FFN 8192, 64 latent channels, 64 audio tokens per
+    latent frame, 3 x 8 x 12 latent (288 tokens: ragged tiles), batch 2, 2 steps."""
+    cfg = MAXCFG
+    W = synth.make_weights(cfg)
+    Wf = synth.weights_f32(W)
+    prec = {"bf16": None, "fp32": fh.FH_PREC_FP32, "fp8ffn": None}[precision]
+    m = Model(fh, cfg, W, 2, precision=prec)
+    if precision == "fp8ffn":
+        fh.fh_weights_quantize_fp8(m.ctx, m.w)
+        fh.fh_set_option(m.ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.4, 0.0]
+    say(f"largest sizes, {precision}")
+    got = m.slice(lat, mot, aud, sig)
+    if precision == "fp8ffn":
+        ref, bar = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear), TOL_MX
+    else:
+        ref, bar = O.denoise_slice(lat, mot, aud, sig, Wf, cfg), (TOL_F32 if precision == "fp32" else TOL)
+    for b in range(2):
+        err = O.rel_err(got[b:b + 1], ref[b:b + 1], cfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e} (bar {bar})")
+        assert err <= bar
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
