@@ -21,8 +21,9 @@ to +-448 first (x / X < 512 can exceed 448). An all-zero block gets X = 1.
 e4m3 ("FN"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals
 m/8 * 2^-6; no infinities; S.1111.111 is NaN (never produced here).
 
-mx_linear is the FFN product of the FP8 variant of the block
-(``dit_block(..., ffn_linear=mx_linear)``).
+mx_linear is the FFN product of the FP8 variants of the block
+(``dit_block(..., ffn_linear=mx_linear)``) and mx_attention their
+self-attention (``attn=mx_attention``).
 
 Decisions are taken on float32 inputs in float32-exact arithmetic (a power-
 of-two division and a rounding on a power-of-two grid are exact in float64),
@@ -32,9 +33,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .dit import linear
+from .dit import linear, to64
 
-__all__ = ["BLOCK", "e4m3_decode", "e4m3_encode", "mx_quantize", "mx_dequantize", "mx_linear"]
+__all__ = ["BLOCK", "e4m3_decode", "e4m3_encode", "mx_quantize", "mx_dequantize", "mx_linear",
+           "mx_attention"]
 
 BLOCK = 32
 E4M3_MAX = 448.0
@@ -111,3 +113,26 @@ def mx_linear(x, w, b=None):
     xq = mx_dequantize(*mx_quantize(np.asarray(x, dtype=np.float64).astype(np.float32)))
     wq = mx_dequantize(*mx_quantize(np.asarray(w, dtype=np.float64).astype(np.float32)))
     return linear(xq, wq, b)
+
+
+def _mx_round(x):
+    """MX-FP8 round trip of float values along the last axis (float32 decisions)."""
+    return mx_dequantize(*mx_quantize(np.asarray(x, dtype=np.float64).astype(np.float32)))
+
+
+def mx_attention(q, k, v):
+    """Softmax attention on MX-FP8 operands, q/k/v [B, nh, N, dh].
+
+    READING (the page that names FP8 attention does not define it): each
+    product's operands are quantised along that product's contraction axis,
+    as in mx_linear -- q and k along dh for the scores; for the weighted sum
+    the values along the keys (per output dimension) and the probabilities
+    p = exp(s - max_j s) along the keys (per query); the sum in the
+    denominator is of the unquantised p. So
+        out = Q(p) Q(v) / sum_j p,   s = Q(q) Q(k)^T / sqrt(dh).
+    """
+    q, k, v = to64(q), to64(k), to64(v)
+    s = _mx_round(q) @ np.swapaxes(_mx_round(k), -1, -2) / np.sqrt(q.shape[-1])
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    vq = np.swapaxes(_mx_round(np.swapaxes(v, -1, -2)), -1, -2)
+    return (_mx_round(p) @ vq) / p.sum(axis=-1, keepdims=True)

@@ -147,3 +147,91 @@ def test_block_routes_both_ffn_layers_through_the_product_hook():
     np.testing.assert_array_equal(got, ref)
     F = W["blocks.0.ffn1.w"].shape[0]
     assert seen == [(cfg.dim, (F, cfg.dim)), (F, (cfg.dim, F))]
+
+
+def test_mx_attention_uniform_scores_average_the_quantised_values():
+    """q = 0: every score is 0, p = 1 (exactly representable), so the output is
+    the mean over keys of the values quantised along the keys."""
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((1, 2, 64, 32)) * np.exp(rng.uniform(-3, 3, (1, 2, 64, 1)))
+    q = np.zeros((1, 2, 8, 32))
+    k = rng.standard_normal((1, 2, 64, 32))
+    vq = np.swapaxes(Q.mx_dequantize(*Q.mx_quantize(np.swapaxes(v, -1, -2).astype(np.float32))), -1, -2)
+    got = Q.mx_attention(q, k, v)
+    np.testing.assert_allclose(got, np.broadcast_to(vq.mean(axis=2, keepdims=True), got.shape), rtol=1e-12)
+    # the value quantisation runs along the keys: per key it would differ
+    vk = Q.mx_dequantize(*Q.mx_quantize(v.astype(np.float32)))
+    assert not np.allclose(vk.mean(axis=2), vq.mean(axis=2), rtol=1e-6)
+
+
+def test_mx_attention_tracks_exact_attention():
+    """Unit-scale scores: the FP8 result's RMS error against exact attention
+    matches the rounding budget -- about 2.65 % RMS from the values, 2.65 %
+    from the probabilities and sqrt(2) x 2.65 % on the scores (q and k),
+    carried into the weights by the exponential: sqrt(2.65^2 + 2.65^2 +
+    3.7^2) = 5.3 %. A dropped quantisation lowers it, a wrong axis or scale
+    raises it past the band."""
+    import oracle as O
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 3, 64, 128))
+    k = rng.standard_normal((2, 3, 96, 128))
+    v = rng.standard_normal((2, 3, 96, 128))
+    ex, got = O.attention(q, k, v), Q.mx_attention(q, k, v)
+    rms = np.sqrt(((got - ex) ** 2).mean() / (ex ** 2).mean())
+    assert 0.03 < rms < 0.08
+
+
+def test_block_routes_self_attention_through_the_hook():
+    import oracle as O
+    from synth import CONFIGS, make_weights, weights_f32, block_inputs
+    cfg = CONFIGS["toy"]
+    W = weights_f32(make_weights(cfg))
+    x, e, a = block_inputs(cfg, 1)
+    seen = []
+
+    def spy(q, k, v):
+        seen.append(q.shape)
+        return O.attention(q, k, v)
+
+    np.testing.assert_array_equal(O.dit_block_from_temb(x, e, a, W, 0, cfg, attn=spy),
+                                  O.dit_block_from_temb(x, e, a, W, 0, cfg))
+    assert seen == [(1, cfg.n_heads, cfg.tokens, cfg.head_dim)]
+
+
+def _grid_ints(rng, shape):
+    """Entries in {-2, -1, 0, 1, 2}: exact in e4m3 under any block scale."""
+    return rng.integers(-2, 3, shape).astype(np.float64)
+
+
+def test_mx_attention_identity_values_expose_the_probabilities():
+    """v = identity (32 keys x 32 dims, exact under MX), q and k on the MX grid
+    (so the scores are exact): the output is exactly Q(p) / sum(p), with p the
+    unquantised exp(s - max) and Q the MX round trip along the keys."""
+    rng = np.random.default_rng(7)
+    q, k = _grid_ints(rng, (1, 1, 8, 32)), _grid_ints(rng, (1, 1, 32, 32))
+    v = np.eye(32)[None, None]
+    s = q @ np.swapaxes(k, -1, -2) / np.sqrt(32)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    want = Q.mx_dequantize(*Q.mx_quantize(p.astype(np.float32))) / p.sum(-1, keepdims=True)
+    np.testing.assert_allclose(Q.mx_attention(q, k, v), want, rtol=1e-13, atol=0)
+    assert not np.allclose(want * p.sum(-1, keepdims=True), p, rtol=1e-6)   # the rounding is visible
+
+
+@pytest.mark.parametrize("side", ["k", "q"])
+def test_mx_attention_quantises_q_and_k_along_the_head_dim(side):
+    """One operand one-hot (exact), the other off the grid: a score is one
+    entry of the off-grid operand after its MX round trip along dh."""
+    rng = np.random.default_rng(8)
+    off = rng.standard_normal((1, 1, 32, 32)) * 3
+    hot = np.zeros((1, 1, 32, 32))
+    hot[0, 0, np.arange(32), rng.integers(0, 32, 32)] = 1.0
+    q, k = (hot, off) if side == "k" else (off, hot)
+    v = np.eye(32)[None, None]
+    qd = Q.mx_dequantize(*Q.mx_quantize(q.astype(np.float32)))
+    kd = Q.mx_dequantize(*Q.mx_quantize(k.astype(np.float32)))
+    s = qd @ np.swapaxes(kd, -1, -2) / np.sqrt(32)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    want = Q.mx_dequantize(*Q.mx_quantize(p.astype(np.float32))) / p.sum(-1, keepdims=True)
+    np.testing.assert_allclose(Q.mx_attention(q, k, v), want, rtol=1e-13, atol=0)
+    raw = q @ np.swapaxes(k, -1, -2) / np.sqrt(32)
+    assert not np.allclose(s, raw, rtol=1e-6)                              # the round trip mattered
