@@ -231,6 +231,220 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   }
 }
 
+// MX-FP8 self-attention (v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3).
+// Same workgroup shape as flash_attn (64 queries, 2 query groups x 2 key
+// halves, 64-key blocks, double-buffered DMA). Differences:
+//  * S^T = K Q^T takes two scaled MFMAs per 32-key tile (k-steps of 64 dims);
+//    each operand lane-half h supplies bytes [16h, 16h+16) of both 32-wide
+//    blocks of a k-step and the E8M0 scale of its row's block h;
+//  * MFMA row i of a tile reads key kperm_mx(i) = 16 bit2(i) + 4 (i >> 3) +
+//    (i & 3), so lane-half h ends up holding the scores of keys 16h .. 16h+15
+//    in order -- exactly the bytes the P^T operand of the next product wants;
+//  * the probabilities are quantised per query and 32-key tile (block
+//    maximum with one exchange between the lane halves) and O^T = V^T P^T is
+//    one scaled MFMA per 32 output dims;
+//  * the running sum l is of the unquantised probabilities.
+// LDS of a key half per stage: K codes [64 keys][128 B] (chunk swizzle
+// kswz_mx), V^T codes [128 dims][64 B] (vswz_mx), K scales [64][4 B], V
+// scales [128][2 B].
+__device__ __forceinline__ int kperm_mx(int i) { return ((i & 4) << 2) | ((i >> 3) << 2) | (i & 3); }
+// 16-lane fragment reads touch rows {0..7, 16..23} or {8..15, 24..31} of a tile
+// (two 128-byte rows per bank window): these take 16 distinct 16-byte slots
+__device__ __forceinline__ int kswz_mx(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
+__device__ __forceinline__ int vswz_mx(int r) { return (r >> 2) & 3; }
+constexpr int MXK_CODES = 64 * HD;                 // 8 KB
+constexpr int MXV_CODES = HD * 64;                 // 8 KB
+constexpr int MX_HALF = MXK_CODES + MXV_CODES + 1024;  // + K and V scales (256 B each), 1 KB aligned
+constexpr int MX_STAGE = 2 * MX_HALF;
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i_t frag_mx(const char* row, int c_lo, int c_hi) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(row + (c_lo << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(row + (c_hi << 4));
+  return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__global__ __launch_bounds__(256, 1) void flash_attn_mx_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ ks, int ldq, const uint8_t* __restrict__ vt, const uint8_t* __restrict__ vts,
+    bf16_t* __restrict__ o, int ldo, int N, int D, float scale_log2, int n_qt, int n_heads, int n_wg) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * MX_STAGE];
+  const int wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (wg >= n_wg) return;
+  const int qt = wg % n_qt, h = (wg / n_qt) % n_heads, b = wg / (n_qt * n_heads);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 1, kh = wave >> 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int q0 = qt * AQ + qg * 32;
+  const int lds_q = ldq / 32;  // scale bytes per row
+
+  // this lane's query: k-step s holds bytes [64s + 16lh, +16) and [64s + 32 + 16lh, +16)
+  v8i_t qf[2];
+  int qsc[2];
+  {
+    const int qrow = min(q0 + lr, N - 1);
+    const uint8_t* qp = q + ((int64_t)b * N + qrow) * ldq + h * HD;
+    const uint8_t* sp = qs + ((int64_t)b * N + qrow) * lds_q + h * 4;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      qf[s2] = frag_mx(reinterpret_cast<const char*>(qp + 64 * s2), lh, 2 + lh);
+      qsc[s2] = sp[2 * s2 + lh];
+    }
+  }
+
+  const int nkb = N / 64;
+  const int nh0 = (nkb + 1) / 2;
+  const uint8_t* kbase = k + (int64_t)b * N * ldq + h * HD;
+  const uint8_t* ksbase = ks + (int64_t)b * N * lds_q + h * 4;
+  const uint8_t* vbase = vt + ((int64_t)b * D + h * HD) * N;
+  const uint8_t* vsbase = vts + (int64_t)b * (N / 64) * D * 2 + h * HD * 2;
+  // DMA d = 9 wave + i of 36 per stage: half d / 18; e = d % 18: K code rows 8e..8e+7 (e < 8),
+  // V^T code rows 16(e-8)..+15 (e < 16), the K scales (e = 16), the V scales (e = 17)
+  auto issue = [&](int buf, int j) {
+    char* stg = smem + buf * MX_STAGE;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int d = 9 * wave + i, c = d / 18, e = d % 18;
+      const int kb = min(c == 0 ? j : nh0 + j, nkb - 1);
+      char* hp = stg + c * MX_HALF;
+      if (e < 8) {
+        const int row = 8 * e + (lane >> 3);
+        const int ch = (lane & 7) ^ kswz_mx(row);
+        dma16(kbase + (int64_t)(kb * 64 + row) * ldq + ch * 16, hp + e * 1024);
+      } else if (e < 16) {
+        const int row = 16 * (e - 8) + (lane >> 2);
+        const int ch = (lane & 3) ^ vswz_mx(row);
+        dma16(vbase + (int64_t)row * N + kb * 64 + ch * 16, hp + MXK_CODES + (e - 8) * 1024);
+      } else if (e == 16) {
+        __builtin_amdgcn_global_load_lds((gbl_void*)(ksbase + (int64_t)(kb * 64 + lane) * lds_q),
+                                         (lds_void*)(hp + MXK_CODES + MXV_CODES), 4, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vsbase + ((int64_t)kb * D + 2 * lane) * 2),
+                                         (lds_void*)(hp + MXK_CODES + MXV_CODES + 256), 4, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow_l = kperm_mx(lr);
+
+  issue(0, 0);
+  for (int j = 0; j < nh0; ++j) {
+    wait_vm<0>();
+    barrier();
+    if (j + 1 < nh0) issue((j + 1) & 1, j + 1);
+    const int kb = kh == 0 ? j : nh0 + j;
+    if (kb >= nkb) continue;
+    const char* hp = smem + (j & 1) * MX_STAGE + kh * MX_HALF;
+    const char* kp = hp;
+    const char* vp = hp + MXK_CODES;
+    const uint8_t* ksp = reinterpret_cast<const uint8_t*>(hp + MXK_CODES + MXV_CODES);
+    const uint8_t* vsp = ksp + 256;
+
+    f32x16 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+      const int row = 32 * t + krow_l;
+      const int x = kswz_mx(row);
+      const char* rp = kp + row * HD;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const v8i_t kf = frag_mx(rp, (4 * s2 + lh) ^ x, (4 * s2 + 2 + lh) ^ x);
+        const int ksc = ksp[row * 4 + 2 * s2 + lh];
+        st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[s2], st[t], 0, 0, 0, ksc, 0, qsc[s2]);
+      }
+    }
+    // st[t][r] is the score of key kb*64 + 32t + 16lh + r
+    if ((kb + 1) * 64 > N) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 64 + 32 * t + 16 * lh + r >= N) st[t][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__any(mx > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+    float ps = 0.f;
+    int pex[2];
+    u32x4 pc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float amax = 0.f;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(st[t][r], scale_log2, -m_run));
+        ps += p[r];
+        amax = fmaxf(amax, p[r]);
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the tile's 32 keys of this query
+      pex[t] = mx_shared_exp(amax);
+      const float inv = mx_inv_scale(pex[t]);
+      const u32x2 a = pack8_e4m3(p, inv), c = pack8_e4m3(p + 8, inv);
+      pc[t] = u32x4{a.x, a.y, c.x, c.y};
+    }
+    l_run += ps;
+    const v8i_t pf = {(int)pc[0].x, (int)pc[0].y, (int)pc[0].z, (int)pc[0].w,
+                      (int)pc[1].x, (int)pc[1].y, (int)pc[1].z, (int)pc[1].w};
+    const int psc = (lh ? pex[1] : pex[0]) + 127;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int row = 32 * dt + lr;
+      const int x = vswz_mx(row);
+      const v8i_t vf = frag_mx(vp + row * 64, lh ^ x, (2 + lh) ^ x);
+      const int vsc = vsp[row * 2 + lh];
+      acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, acc[dt], 0, 0, 0, vsc, 0, psc);
+    }
+  }
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // merge the key halves as flash_attn does
+  barrier();
+  float* mg = reinterpret_cast<float*>(smem) + qg * (66 * 64);
+  if (kh == 1) {
+    mg[lane] = m_run;
+    mg[64 + lane] = l_run;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mg[(2 + dt * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = mg[lane], l1 = mg[64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float inv = 1.f / (l_run * a0 + l1 * a1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * a0 + mg[(2 + dt * 16 + r) * 64 + lane] * a1;
+    if (q0 + lr < N) store_o(o + ((int64_t)b * N + q0 + lr) * ldo + h * HD, acc, inv, lh);
+  }
+}
+
 // Cross-attention: one wave (workgroup) per 32 queries of one (lane, head),
 // so a slice launches one wave per 32 tokens and head across the whole chip.
 // Keys are the audio tokens of the query's latent frame (or all of them);
@@ -353,6 +567,18 @@ hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const 
   const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
   flash_attn_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, ldq, k, ldk, vt, o, ldo, N, n_heads * HD,
                                                        scale_log2, n_qt, n_heads, n_wg);
+  return hipGetLastError();
+}
+
+hipError_t flash_attn_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k, const uint8_t* ks, int ldq,
+                         const uint8_t* vt, const uint8_t* vts, bf16_t* o, int ldo, int B, int N, int n_heads,
+                         float scale, hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  if (N % 64 || ldq % 32 || ldq < n_heads * HD || ldo % 4 || !qs || !ks || !vts) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
+  flash_attn_mx_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, qs, k, ks, ldq, vt, vts, o, ldo, N, n_heads * HD,
+                                                          scale_log2, n_qt, n_heads, n_wg);
   return hipGetLastError();
 }
 

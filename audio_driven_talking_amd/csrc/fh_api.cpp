@@ -50,6 +50,9 @@ struct WS {
   // float32 activations of FH_PREC_FP32 (carved only for that precision)
   float *fh = nullptr, *fqkv = nullptr, *fao = nullptr, *fqc = nullptr, *fu = nullptr, *fkc = nullptr,
         *fvc = nullptr;
+  // MX-FP8 self-attention operands of FH_PREC_FP8_ATTN (carved only for it): q and k codes [B*N][2D]
+  // and scales [B*N][2D/32]; V^T codes [B][D][N] and scales [B][N/64][D][2]
+  uint8_t *qkq = nullptr, *qks = nullptr, *vq = nullptr, *vs = nullptr;
   size_t total;
 };
 
@@ -179,6 +182,12 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.hs = (uint16_t*)take((D / 64) * B * N * 2);
   w.uq = (uint8_t*)take(B * N * Fd);
   w.us = (uint16_t*)take((Fd / 64) * B * N * 2);
+  if (c->precision == FH_PREC_FP8_ATTN) {
+    w.qkq = (uint8_t*)take(B * N * 2 * D);
+    w.qks = (uint8_t*)take(B * N * 2 * D / 32);
+    w.vq = (uint8_t*)take(B * D * N);
+    w.vs = (uint8_t*)take(B * (N / 64) * D * 2);
+  }
   if (c->precision == FH_PREC_FP32) {
     w.fh = (float*)take(B * N * D * 4);
     w.fqkv = (float*)take(B * N * 3 * D * 4);
@@ -265,6 +274,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
                               nullptr, nullptr, pend_in, s));
   }
+  const bool mx_attn = c->precision == FH_PREC_FP8_ATTN;
   {
     Timed t(c, FH_K_GEMM_QKV, s);
     fh::EpiArgs ep;
@@ -275,16 +285,25 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.out_t = ws.vt;
     ep.t_cols = D;
     ep.rows_per_lane = N;
-    FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
+    if (mx_attn) {  // values straight to MX-FP8 along the tokens
+      ep.out_q = ws.vq;
+      ep.q_scale_b = ws.vs;
+    }
+    FH_HIP(fh::gemm_bf16(mx_attn ? fh::EPI_SPLIT_T_MX : fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
   }
   {
     Timed t(c, FH_K_RMSNORM_ROPE, s);
     FH_HIP(fh::rmsnorm_rope_bf16(ws.qk, 2 * D, M, D, 2, wb.norm_q, wb.norm_k, ws.rcos, ws.rsin, N,
-                                 g.head_dim, g.eps, s));
+                                 g.head_dim, g.eps, s, mx_attn ? ws.qkq : nullptr, mx_attn ? ws.qks : nullptr,
+                                 2 * D));
   }
   {
     Timed t(c, FH_K_ATTN, s);
-    FH_HIP(fh::flash_attn(ws.qk, 2 * D, ws.qk + D, 2 * D, ws.vt, ws.ao, D, B, N, g.n_heads, scale, s));
+    if (mx_attn)
+      FH_HIP(fh::flash_attn_mx(ws.qkq, ws.qks, ws.qkq + D, ws.qks + D / 32, 2 * D, ws.vq, ws.vs, ws.ao, D, B, N,
+                               g.n_heads, scale, s));
+    else
+      FH_HIP(fh::flash_attn(ws.qk, 2 * D, ws.qk + D, 2 * D, ws.vt, ws.ao, D, B, N, g.n_heads, scale, s));
   }
   {
     Timed t(c, FH_K_GEMM_O, s);
@@ -328,7 +347,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.ldx = D;
     FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
   }
-  const bool fp8 = c->precision == FH_PREC_FP8_FFN;
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D,
@@ -626,6 +645,15 @@ AudioWS carve_audio(const fh_audio_weights* w, int B, char* base) {
   return a;
 }
 
+int check_precision(fh_ctx* c, const fh_weights* w) {
+  if (c->precision == FH_PREC_FP8_ATTN && c->N % 64)
+    return fail(c, FH_EUNSUPPORTED, "FP8 self-attention needs tokens per lane a multiple of 64 (have %d)", c->N);
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN;
+  if (fp8 && !w->fp8)
+    return fail(c, FH_EINVAL, "FP8 precision needs fh_weights_quantize_fp8 on these weights");
+  return FH_OK;
+}
+
 bool check_ws(fh_ctx* c, int B, void* ws, size_t ws_bytes, int* rc) {
   const size_t need = carve(c, B, nullptr).total;
   if (!ws || ((uintptr_t)ws & 255)) {
@@ -752,8 +780,8 @@ int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, f
   if (!x || !temb || !audio) return fail(c, FH_EINVAL, "null x, temb or audio");
   int rc = FH_OK;
   if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
-  if (c->precision == FH_PREC_FP8_FFN && !w->fp8)
-    return fail(c, FH_EINVAL, "FH_PREC_FP8_FFN needs fh_weights_quantize_fp8 on these weights");
+  rc = check_precision(c, w);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const fh_config& g = c->cfg;
   const int D = g.dim;
@@ -795,8 +823,8 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
     if (!std::isfinite(sigmas[i])) return fail(c, FH_EINVAL, "sigma[%d] is not finite", i);
   int rc = FH_OK;
   if (!check_ws(c, batch, ws, ws_bytes, &rc)) return rc;
-  if (c->precision == FH_PREC_FP8_FFN && !w->fp8)
-    return fail(c, FH_EINVAL, "FH_PREC_FP8_FFN needs fh_weights_quantize_fp8 on these weights");
+  rc = check_precision(c, w);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   WS wsp = carve(c, batch, (char*)ws);
 
@@ -857,7 +885,7 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     return FH_OK;
   }
   if (option == FH_OPT_PRECISION) {
-    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32)
+    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32 && value != FH_PREC_FP8_ATTN)
       return fail(c, FH_EINVAL, "unknown precision %d", value);
     c->precision = value;
     return FH_OK;

@@ -26,6 +26,9 @@ enum Epi {
                       // values of row m in column group p (gemm_ssq_groups(M, N, K) groups)
   EPI_GELU_MX = 7,    // gelu_tanh(C + bias) quantised to MX-FP8: out_q[m, n] codes, q_scale
                       // (MX scale layout below, rows = M)
+  EPI_SPLIT_T_MX = 8, // n < split as EPI_SPLIT_T; n >= split: C + bias as MX-FP8 along the rows of
+                      // each lane (rows a multiple of 64): codes out_q[lane][n - split][m mod rows],
+                      // E8M0 scales q_scale_b[lane][(m mod rows) / 64][n - split][block 0 | 1]
 };
 
 // MX-FP8 operand layout used by the FP8 GEMM: codes [rows][K] (e4m3 bytes,
@@ -52,6 +55,7 @@ struct EpiArgs {
   uint8_t* out_q = nullptr;          // EPI_GELU_MX: codes [M][ldq bytes]
   int ldq = 0;
   uint16_t* q_scale = nullptr;       // EPI_GELU_MX: scales [N / 64][M]
+  uint8_t* q_scale_b = nullptr;      // EPI_SPLIT_T_MX: scales of the transposed part
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -137,14 +141,27 @@ hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_l
 // with nparts == 2 also columns [D, 2D) with gain g1. If cos_t != nullptr the
 // normalised values are rotated pairwise: pair j of a head (adjacent dims)
 // turns by the angle table [tokens, head_dim/2] row (row mod rows_per_lane).
+// With out_q non-null the normalised (and rotated) values are written as
+// MX-FP8 instead: codes out_q[row * ldq + part * D + col], E8M0 scales
+// q_scale[row * (ldq / 32) + (part * D + col) / 32] (32 columns per block).
 hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, const float* g0,
                              const float* g1, const float* cos_t, const float* sin_t,
-                             int rows_per_lane, int head_dim, float eps, hipStream_t s);
+                             int rows_per_lane, int head_dim, float eps, hipStream_t s, uint8_t* out_q = nullptr,
+                             uint8_t* q_scale = nullptr, int ldq = 0);
 
 // softmax(q k^T * scale) v over all N keys of the same lane; q/k rows of
 // stride ldq/ldk (head h at column h*128), values transposed vt[lane][D][N].
 hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const bf16_t* vt,
                       bf16_t* o, int ldo, int B, int N, int n_heads, float scale, hipStream_t s);
+
+// MX-FP8 form of flash_attn: q and k as MX-FP8 along the head dim (codes
+// [rows][ldq] bytes, head h at column h*128, scales [rows][ldq/32] bytes), the
+// values transposed as MX-FP8 along the keys (codes [lane][D][N], scales
+// [lane][N/64][D] byte pairs, as EPI_SPLIT_T_MX writes them); probabilities
+// quantised per query and 32-key block; N a multiple of 64.
+hipError_t flash_attn_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k, const uint8_t* ks, int ldq,
+                         const uint8_t* vt, const uint8_t* vts, bf16_t* o, int ldo, int B, int N, int n_heads,
+                         float scale, hipStream_t s);
 
 // Audio cross-attention with short key ranges: queries of latent frame f =
 // row / hw see keys [f*apf, f*apf + apf) (full != 0: all La keys). With ssq

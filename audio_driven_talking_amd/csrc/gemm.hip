@@ -108,7 +108,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
   char* st = smem + wave * ST::BYTES;
   const int nw = n0 + wn * C;  // first column of this wave's sub-tile
   // the transposed form applies to a whole sub-tile (split is a multiple of BN)
-  const bool transposed = EPI == EPI_SPLIT_T && nw >= ep.split;
+  const bool transposed = (EPI == EPI_SPLIT_T || EPI == EPI_SPLIT_T_MX) && nw >= ep.split;
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
     const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
@@ -188,6 +188,49 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
           reinterpret_cast<uint8_t*>(ep.q_scale)[((int64_t)(n / 64) * M + m) * 2 + ((n / 32) & 1)] =
               (uint8_t)(ex + 127);
         }
+      }
+      lds_fence();
+    } else if (EPI == EPI_SPLIT_T_MX && transposed) {
+      // values as MX-FP8 along the tokens: f32 sums -> LDS [32 rows][C]; then
+      // one lane per column: bias, the column's 32-token block maximum, 32
+      // codes into out_q[lane][column][token] and the block's scale byte
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(st + lr * ST::PF + (i * 32 + 8 * g + 4 * lh) * 4) = v;
+        }
+      lds_fence();
+      const int bl = mb / ep.rows_per_lane, t0 = mb - bl * ep.rows_per_lane;  // a block never spans lanes
+#pragma unroll
+      for (int cc = 0; cc < C / 64; ++cc) {
+        const int col = cc * 64 + lane, n = nw + col;
+        const float bias = ep.bias[n];
+        float y[32];
+        float amax = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          // rows past M repeat row M-1: they are not stored, and a copy cannot raise the maximum
+          const int rr = mb + r < M ? r : M - 1 - mb;
+          y[r] = *reinterpret_cast<const float*>(st + rr * ST::PF + col * 4) + bias;
+          amax = fmaxf(amax, fabsf(y[r]));
+        }
+        const int ex = mx_shared_exp(amax);
+        const float inv = mx_inv_scale(ex);
+        u32x4 w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2 a = pack8_e4m3(y + 16 * h, inv), b = pack8_e4m3(y + 16 * h + 8, inv);
+          w[h] = u32x4{a.x, a.y, b.x, b.y};
+        }
+        const int64_t vrow = (int64_t)bl * ep.t_cols + (n - ep.split);
+        u32x4* op = reinterpret_cast<u32x4*>(ep.out_q + vrow * ep.rows_per_lane + t0);
+        op[0] = w[0];
+        op[1] = w[1];
+        // scales [lane][rows / 64][t_cols] as byte pairs (32-row blocks 2s, 2s+1)
+        ep.q_scale_b[(((int64_t)bl * (ep.rows_per_lane / 64) + t0 / 64) * ep.t_cols + (n - ep.split)) * 2 +
+                     ((t0 / 32) & 1)] = (uint8_t)(ex + 127);
       }
       lds_fence();
     } else {
@@ -635,6 +678,9 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
   if (epi == EPI_SPLIT_T && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8))
     return hipErrorInvalidValue;
+  if (epi == EPI_SPLIT_T_MX && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 64 || M % ep.rows_per_lane ||
+                                !ep.out_q || !ep.q_scale_b || (BN / 2) % 64))
+    return hipErrorInvalidValue;
   if (epi == EPI_GATED_RES && ep.rows_per_lane <= 0) return hipErrorInvalidValue;
   if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
     return hipErrorInvalidValue;
@@ -648,6 +694,7 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
     case EPI_GATED_RES: FH_GEMM(EPI_GATED_RES); break;
     case EPI_RES: FH_GEMM(EPI_RES); break;
     case EPI_SPLIT_T: FH_GEMM(EPI_SPLIT_T); break;
+    case EPI_SPLIT_T_MX: FH_GEMM(EPI_SPLIT_T_MX); break;
     case EPI_PARTIAL: FH_GEMM(EPI_PARTIAL); break;
     case EPI_BF16_SSQ: FH_GEMM(EPI_BF16_SSQ); break;
     default: return hipErrorInvalidValue;

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
 __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
     bf16_t* __restrict__ p, int ld, int D, int tpp, const float* __restrict__ g0,
     const float* __restrict__ g1, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-    int rows_per_lane, int head_dim, float eps) {
+    int rows_per_lane, int head_dim, float eps, uint8_t* __restrict__ out_q, uint8_t* __restrict__ q_scale,
+    int ldq) {
   __shared__ float red[8];
   const int row = blockIdx.x;
   const int part = threadIdx.x / tpp, tp = threadIdx.x % tpp;
@@ -140,6 +141,19 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
       y[2 * e + 1] = a * sn + bb * cs;
     }
   }
+  if (out_q) {
+    // MX-FP8 along the row: a 32-column block is 4 consecutive threads (lanes)
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ex = mx_shared_exp(amax);
+    const int col = part * D + c;
+    *reinterpret_cast<u32x2*>(out_q + (int64_t)row * ldq + col) = pack8_e4m3(y, mx_inv_scale(ex));
+    if ((tp & 3) == 0) q_scale[(int64_t)row * (ldq / 32) + col / 32] = (uint8_t)(ex + 127);
+    return;
+  }
   u16x8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = f2bf(y[e]);
@@ -170,13 +184,15 @@ hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_l
 
 hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, const float* g0,
                              const float* g1, const float* cos_t, const float* sin_t,
-                             int rows_per_lane, int head_dim, float eps, hipStream_t s) {
+                             int rows_per_lane, int head_dim, float eps, hipStream_t s, uint8_t* out_q,
+                             uint8_t* q_scale, int ldq) {
   if (rows <= 0) return hipSuccess;
   const int tpp = threads_for(D);
   if (D % 8 || ld % 8 || head_dim % 8 || nparts < 1 || nparts > 2 || tpp * nparts > 512)
     return hipErrorInvalidValue;
+  if (out_q && (D % 32 || !q_scale || ldq % 32 || ldq < nparts * D)) return hipErrorInvalidValue;
   rmsnorm_rope_kernel<<<rows, tpp * nparts, 0, s>>>(p, ld, D, tpp, g0, g1, cos_t, sin_t, rows_per_lane,
-                                                     head_dim, eps);
+                                                     head_dim, eps, out_q, q_scale, ldq);
   return hipGetLastError();
 }
 

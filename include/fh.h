@@ -191,7 +191,14 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       the block structure to ~1e-5. Slow. fh_workspace_bytes grows under
  *       this precision (float32 activations and audio K/V), so query it after
  *       setting the option; a smaller workspace is FH_EWORKSPACE.          */
-enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2 };
+/*     FH_PREC_FP8_ATTN: FH_PREC_FP8_FFN and the self-attention on MX-FP8
+ *       too: q and k quantised along the head dim by the q/k norm, the values
+ *       along the tokens by the QKV projection, the probabilities per query
+ *       and 32-key block; both products on the block-scaled MFMA; sums and
+ *       softmax in float32. Needs fh_weights_quantize_fp8 and tokens per lane
+ *       a multiple of 64 (FH_EUNSUPPORTED otherwise); the workspace grows
+ *       (query fh_workspace_bytes after setting it).                        */
+enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2, FH_PREC_FP8_ATTN = 3 };
 enum {
   FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
   FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,

@@ -234,7 +234,7 @@ def test_fp32_precision_option_and_workspace():
     ctx = fh.fh_create(synth.CONFIGS["toy"])
     L = fh.lib
     base = fh.fh_workspace_bytes(ctx, 1)
-    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 3) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 4) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP32) == fh.FH_OK
     c = synth.CONFIGS["toy"]
     N, D, Fd, La = c.frames * c.height * c.width, c.dim, c.ffn_dim, c.frames * c.audio_per_frame
@@ -309,3 +309,27 @@ def test_audio_projection_specs_and_argument_errors():
     ctx2 = fh.fh_create(synth.CONFIGS["toy"])
     assert L.fh_audio_project(ctx2, h, 2, fake, fake, fake, need, None) == fh.FH_EINVAL   # foreign weights
     L.fh_audio_weights_release(h)
+
+
+def test_fp8_attention_precision_checks():
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    L = fh.lib
+    base = fh.fh_workspace_bytes(ctx, 1)
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_ATTN) == fh.FH_OK
+    c = synth.CONFIGS["toy"]
+    N, D = c.frames * c.height * c.width, c.dim
+    r = lambda b: (b + 255) // 256 * 256
+    assert fh.fh_workspace_bytes(ctx, 1) == base + r(N * 2 * D) + r(N * 2 * D // 32) + r(D * N) + r(N // 64 * D * 2)
+    # tokens per lane not a multiple of 64: refused before any launch
+    ragged = synth.CONFIGS["slice"].replace(n_blocks=1, width=10)      # 800 tokens
+    ctx2 = fh.fh_create(ragged)
+    st, w = _bind(ctx2)
+    assert st == fh.FH_OK
+    assert L.fh_set_option(ctx2, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_ATTN) == fh.FH_OK
+    fake = ctypes.c_void_p(1 << 40)
+    need = fh.fh_workspace_bytes(ctx2, 1)
+    sig = (ctypes.c_float * 2)(1.0, 0.0)
+    assert L.fh_dit_denoise_slice(ctx2, w, 1, fake, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EUNSUPPORTED
+    assert "multiple of 64" in fh.fh_last_error(ctx2)
+    assert L.fh_dit_block_forward(ctx2, w, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EUNSUPPORTED
+    fh.lib.fh_weights_release(w)

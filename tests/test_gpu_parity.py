@@ -699,3 +699,88 @@ def test_largest_supported_sizes(fh, precision):
         say(f"  lane {b} rel err {err:.3e} (bar {bar})")
         assert err <= bar
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+
+
+# ------------------------------------------------------------------ MX-FP8 self-attention
+# With FH_PREC_FP8_ATTN the FFN GEMMs and the self-attention run on MX-FP8.
+# Against the oracle with both MX-FP8 forms the bar is TOL_MX as for the FFN
+# (flipped codes dominate). The attention alone: quantisation moves the
+# self-attention-only update of a full-width block by 1.1e-2 against exact
+# attention; the kernel quantises P against the online softmax's running
+# maximum instead of the row maximum, which changes rounding decisions only --
+# the oracle with P quantised against a randomly lowered maximum (up to 2^8)
+# moves by 7.2e-3 -- so the self-attention-only block is held to TOL.
+def _fp8_attn_model(fh, cfg, W, B):
+    m = Model(fh, cfg, W, B, precision=fh.FH_PREC_FP8_ATTN)
+    fh.fh_weights_quantize_fp8(m.ctx, m.w)
+    return m
+
+
+def test_fp8_attn_toy_slice(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = _fp8_attn_model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say("toy slice, FP8 FFN and self-attention, 4 steps")
+    got = m.slice(lat, mot, aud, sig)
+    Wf = synth.weights_f32(W)
+    ref_q = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear, attn=Q.mx_attention)
+    ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
+    err_q, err = O.rel_err(got, ref_q, cfg.motion_frames), O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs the exact oracle {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL_MX and err <= TOL_FP8
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig, graph=False), got)
+
+
+def test_fp8_attn_self_attention_only_block(fh):
+    """Full-width block with the FFN and cross-attention outputs zeroed: the
+    update is the self-attention branch alone."""
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    for k in ("ffn2.w", "co.w"):
+        W["blocks.0." + k] = np.zeros_like(W["blocks.0." + k])
+    for k in ("ffn2.b", "co.b"):
+        W["blocks.0." + k] = np.zeros_like(W["blocks.0." + k])
+    m = _fp8_attn_model(fh, cfg, W, 1)
+    x, e, a = synth.block_inputs(cfg, 1)
+    say("full-width block, self-attention only, FP8")
+    got = m.block(0, x, e, a)
+    Wf = synth.weights_f32(W)
+    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, attn=Q.mx_attention), x)
+    err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
+    say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL}), vs exact {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL and err <= TOL_FP8
+
+
+def test_fp8_attn_block(fh):
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    m = _fp8_attn_model(fh, cfg, W, 1)
+    x, e, a = synth.block_inputs(cfg, 1)
+    say("full-width block, FP8 FFN and self-attention")
+    got = m.block(0, x, e, a)
+    Wf = synth.weights_f32(W)
+    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, ffn_linear=Q.mx_linear,
+                                                 attn=Q.mx_attention), x)
+    err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
+    say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs exact {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL_MX and err <= TOL_FP8
+
+
+def test_fp8_attn_full_slice(fh):
+    path = os.path.join(GOLDEN, "slice_b1.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path, allow_pickle=False)
+    cfg = synth.CONFIGS[str(g["config"])]
+    W = synth.make_weights(cfg)
+    assert synth.weights_digest(W) == str(g["digest"])
+    m = _fp8_attn_model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    say("full slice B=1, FP8 FFN and self-attention, against slice_b1")
+    got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
+    err = O.rel_err(got, g["out"], cfg.motion_frames)
+    say(f"  rel err {err:.3e} (bar {TOL_FP8})")
+    assert err <= TOL_FP8
