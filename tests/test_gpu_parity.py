@@ -769,18 +769,34 @@ def test_fp8_attn_block(fh):
     assert err_q <= TOL_MX and err <= TOL_FP8
 
 
-def test_fp8_attn_full_slice(fh):
-    path = os.path.join(GOLDEN, "slice_b1.npz")
+@pytest.mark.parametrize("precision,case", [
+    ("fp8attn", "slice_b1"), ("fp8attn", "slice_b3"), ("fp8attn", "slice768"),
+    ("fp8ffn", "slice_b3"), ("fp8ffn", "slice768"),
+    ("fp32", "slice_b3"), ("fp32", "slice768")])
+def test_other_precisions_on_stored_full_slices(fh, precision, case):
+    """The full 30-block, 4-step workloads (batch 1 and 3, 1280 and 2880 tokens --
+    the latter an odd number of 64-key blocks) in FP8 or float32 precision
+    against the stored exact float64 outputs, lane by lane."""
+    path = os.path.join(GOLDEN, case + ".npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated")
     g = np.load(path, allow_pickle=False)
     cfg = synth.CONFIGS[str(g["config"])]
+    B = int(g["batch"])
     W = synth.make_weights(cfg)
     assert synth.weights_digest(W) == str(g["digest"])
-    m = _fp8_attn_model(fh, cfg, W, 1)
-    lat, mot, aud = synth.slice_inputs(cfg, 1)
-    say("full slice B=1, FP8 FFN and self-attention, against slice_b1")
+    if precision == "fp8attn":
+        m = _fp8_attn_model(fh, cfg, W, B)
+    elif precision == "fp8ffn":
+        m = _fp8_model(fh, cfg, W, B)
+    else:
+        m = Model(fh, cfg, W, B, precision=fh.FH_PREC_FP32)
+    bar = TOL_F32 if precision == "fp32" else TOL_FP8
+    lat, mot, aud = synth.slice_inputs(cfg, B)
+    say(f"{case}: full slice B={B}, {precision}")
     got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
-    err = O.rel_err(got, g["out"], cfg.motion_frames)
-    say(f"  rel err {err:.3e} (bar {TOL_FP8})")
-    assert err <= TOL_FP8
+    for b in range(B):
+        err = O.rel_err(got[b:b + 1], g["out"][b:b + 1], cfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e} (bar {bar})")
+        assert err <= bar
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
