@@ -66,7 +66,7 @@ def _load():
     # (same soname), since it receives torch's device pointers and streams.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m audio_driven_talking_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built: run `python audio_driven_talking_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     sig = {

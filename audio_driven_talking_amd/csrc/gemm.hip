@@ -775,7 +775,8 @@ hipError_t gemm_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const
                    const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (N % 128 || K % 64 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
-  if (N % 256 == 0 && N >= 4096) return launch_mx<192, 256, 4>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
+  // stage counts from a same-process A/B of the FP8 slice (3 beat 4 and 5 here; 4 beat 3, 6 and 8 for split K)
+  if (N % 256 == 0 && N >= 4096) return launch_mx<192, 256, 3>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
   return launch_mx<192, 128, 5>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
 }
 
@@ -786,7 +787,7 @@ hipError_t gemm_mx_splitk(const uint8_t* A, int lda, const uint16_t* As, const u
   EpiArgs ep;
   ep.part = part;
   ep.part_elems = part_elems;
-  return launch_mx<128, 128, 6>(EPI_PARTIAL, A, lda, As, W, ldw, Ws, M, N, K, ep, s, 2);
+  return launch_mx<128, 128, 4>(EPI_PARTIAL, A, lda, As, W, ldw, Ws, M, N, K, ep, s, 2);
 }
 
 hipError_t mx_quantize(const float* in_f, const bf16_t* in_b, int64_t rows, int K, uint8_t* codes,
