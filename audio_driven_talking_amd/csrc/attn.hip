@@ -370,12 +370,17 @@ __global__ __launch_bounds__(256, 1) void flash_attn_mx_kernel(
         for (int r = 0; r < 16; ++r)
           if (kb * 64 + 32 * t + 16 * lh + r >= N) st[t][r] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // per-tile score maxima (the row maximum is their maximum): the largest
+    // probability of a tile is exp2 of its largest scaled score, exp2 being monotonic
+    float tmax[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      float v = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, st[t][r]);
+      tmax[t] = fmaxf(v, __shfl_xor(v, 32, 64)) * scale_log2;  // the tile's 32 keys of this query
+    }
+    const float mx = fmaxf(tmax[0], tmax[1]);
     if (__any(mx > m_run + TAU)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -386,26 +391,30 @@ __global__ __launch_bounds__(256, 1) void flash_attn_mx_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
-    float ps = 0.f;
     int pex[2];
     u32x4 pc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float amax = 0.f;
-      float p[16];
+      pex[t] = mx_shared_exp(__builtin_amdgcn_exp2f(tmax[t] - m_run));
+      // exp2(y - e) = p * 2^-e: the codes' operands straight from the exponential;
+      // they stay below 512 (p <= 2^(e+9)), only the e4m3 range needs a clamp
+      const float moff = -m_run - (float)pex[t];
+      float q[16], qs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(st[t][r], scale_log2, -m_run));
-        ps += p[r];
-        amax = fmaxf(amax, p[r]);
+        const float v = __builtin_amdgcn_exp2f(fmaf(st[t][r], scale_log2, moff));
+        qs += v;
+        q[r] = fminf(v, 448.f);
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the tile's 32 keys of this query
-      pex[t] = mx_shared_exp(amax);
-      const float inv = mx_inv_scale(pex[t]);
-      const u32x2 a = pack8_e4m3(p, inv), c = pack8_e4m3(p + 8, inv);
-      pc[t] = u32x4{a.x, a.y, c.x, c.y};
+      l_run += qs * __uint_as_float((uint32_t)(pex[t] + 127) << 23);  // sum of p = 2^e * sum of p 2^-e
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // four codes per word: low half, then high half
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * e], q[4 * e + 1], 0, false);
+        w[e] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * e + 2], q[4 * e + 3], lo, true);
+      }
+      pc[t] = w;
     }
-    l_run += ps;
     const v8i_t pf = {(int)pc[0].x, (int)pc[0].y, (int)pc[0].z, (int)pc[0].w,
                       (int)pc[1].x, (int)pc[1].y, (int)pc[1].z, (int)pc[1].w};
     const int psc = (lh ? pex[1] : pex[0]) + 127;
