@@ -8,7 +8,10 @@
 //
 // Workgroup tile BM x BN (BM, BN multiples of 64), K-slabs of BK = 32 or 64,
 // 256 threads = 4 waves in 2x2, each wave (BM/2) x (BN/2) of MFMA 32x32x16
-// blocks. Operand slabs go global -> LDS directly (global_load_lds_dwordx4:
+// blocks; or (KW = 2) two such groups of 4 waves, each taking half of every
+// slab's k-steps, which puts two waves on each SIMD (one wave alone cannot
+// issue LDS fragment reads fast enough to feed a 64 x 64 wave tile) and adds
+// the groups' sums through LDS before the epilogue. Operand slabs go global -> LDS directly (global_load_lds_dwordx4:
 // each wave instruction fills 1 KB of whole rows), NS slabs deep, one barrier
 // per slab. A slab's fragments are read into registers during the previous
 // slab's MFMAs, and the DMA and LDS-read instructions are spread between the
@@ -303,19 +306,21 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS>
-__global__ __launch_bounds__(256, (smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
+template <int EPI, int BM, int BN, int BK, int NS, int KW>
+__global__ __launch_bounds__(256 * KW, (KW == 1 && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
                   int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
+  constexpr int NW = 4 * KW;           // waves: KW groups of 2 x 2, group g takes k-steps g KK/KW ..
   constexpr int ROWB = BK * 2;         // bytes per LDS row of a slab
   constexpr int CH = BK / 8;           // 16-byte chunks per row
   constexpr int RG = 64 / CH;          // rows per 1 KB DMA group
   constexpr int MI = BM / 64;          // 32-row activation blocks per wave
   constexpr int NI = BN / 64;          // 32-row weight blocks per wave
-  constexpr int GA = BM / RG / 4;      // 1 KB DMA groups per wave per slab, activations
-  constexpr int GW = BN / RG / 4;      // ... weights
+  constexpr int GA = BM / RG / NW;     // 1 KB DMA groups per wave per slab, activations
+  constexpr int GW = BN / RG / NW;     // ... weights
   constexpr int SLAB = (BM + BN) * ROWB;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && GA * RG * 4 == BM && GW * RG * 4 == BN, "tile shape");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && GA * RG * NW == BM && GW * RG * NW == BN, "tile shape");
+  static_assert(KW == 1 || KW == 2, "one or two wave groups along K");
   static_assert(NS >= 2 && (NS - 1) * (GA + GW) < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
 
@@ -334,30 +339,32 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int kg = wave >> 2;                    // wave group along K
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
 
   // DMA: lane fills LDS row r = RG g + lane/CH, physical chunk lane%CH, which
-  // holds logical chunk (lane%CH) ^ swz(r)
+  // holds logical chunk (lane%CH) ^ swz(r); every wave of both groups takes
+  // its share of the slab's 1 KB groups
   const int drow = lane / CH;
   const bf16_t* ga[GA];
   const bf16_t* gw[GW];
 #pragma unroll
   for (int i = 0; i < GA; ++i) {
-    const int r = RG * (wave + 4 * i) + drow;
+    const int r = RG * (wave + NW * i) + drow;
     ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + ((lane % CH) ^ swz<BK>(r)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
-    const int r = RG * (wave + 4 * i) + drow;
+    const int r = RG * (wave + NW * i) + drow;
     gw[i] = W + (int64_t)(n0 + r) * ldw + ((lane % CH) ^ swz<BK>(r)) * 8;
   }
 
   // one DMA instruction d of a slab: d < GA an activation group, else a weight group
   auto dma_one = [&](int d, int buf, int k0) {
     char* sa = smem + buf * SLAB;
-    if (d < GA) dma16(ga[d] + k0, sa + (wave + 4 * d) * 1024);
-    else dma16(gw[d - GA] + k0, sa + BM * ROWB + (wave + 4 * (d - GA)) * 1024);
+    if (d < GA) dma16(ga[d] + k0, sa + (wave + NW * d) * 1024);
+    else dma16(gw[d - GA] + k0, sa + BM * ROWB + (wave + NW * (d - GA)) * 1024);
   };
 
   f32x16 acc[NI][MI];
@@ -371,8 +378,10 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   // Fragments of a whole slab are held in registers, in two sets: while the
   // MFMAs of slab kt run on one set, the fragments of slab kt + 1 are read
   // into the other. Rows: activations wm*BM/2 + 32 j + lr, weights
-  // wn*BN/2 + 32 i + lr; k-step kk covers the slab's k-columns 16 kk .. +15.
-  constexpr int KK = BK / 16, P = NI * MI, NR = NI + MI, DPS = GA + GW;
+  // wn*BN/2 + 32 i + lr; the wave's k-step kk covers the slab's k-columns
+  // 16 (kg KK + kk) .. +15 (KK k-steps per wave group).
+  constexpr int KK = BK / 16 / KW, P = NI * MI, NR = NI + MI, DPS = GA + GW;
+  static_assert(KK * 16 * KW == BK, "slab splits evenly between the wave groups");
   constexpr int SLOTS = KK * P, READS = KK * NR;
   const int xr = swz<BK>(lr);
   const int a_row = (wm * (BM / 2) + lr) * ROWB, w_row = BM * ROWB + (wn * (BN / 2) + lr) * ROWB;
@@ -380,7 +389,7 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   // fragment read r of a slab: k-step r / NR; r % NR < NI a weight block, else activations
   auto read_one = [&](int r, int set, int buf) {
     const int kk = r / NR, q = r % NR;
-    const char* sb = smem + buf * SLAB + (((2 * kk + lh) ^ xr) * 16);
+    const char* sb = smem + buf * SLAB + (((2 * (kg * KK + kk) + lh) ^ xr) * 16);
     if (q < NI) wf[set][kk][q] = *reinterpret_cast<const bf16x8*>(sb + w_row + q * 32 * ROWB);
     else af[set][kk][q - NI] = *reinterpret_cast<const bf16x8*>(sb + a_row + (q - NI) * 32 * ROWB);
   };
@@ -441,6 +450,37 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   static_assert(4 * Stage<BN / 2>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
   wait_lgkm0();
   barrier();  // every wave is done with the slab buffers (its DMAs landed above)
+  if constexpr (KW == 2) {
+    // group 1 hands its sums to group 0 through LDS past the four epilogue
+    // staging regions (lane-contiguous 16-byte pieces), then leaves
+    constexpr int RED = (4 * Stage<BN / 2>::BYTES + 255) / 256 * 256;
+    static_assert(RED + 4 * P * 16 * 64 * 4 <= NS * SLAB, "hand-over buffer must fit the slab buffers");
+    float4* red = reinterpret_cast<float4*>(smem + RED) + (wave & 3) * P * 4 * 64 + lane;
+    if (kg) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            red[((i * MI + j) * 4 + q) * 64] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+    barrier();
+    if (kg) return;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < MI; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = red[((i * MI + j) * 4 + q) * 64];
+          acc[i][j][4 * q] += v.x;
+          acc[i][j][4 * q + 1] += v.y;
+          acc[i][j][4 * q + 2] += v.z;
+          acc[i][j][4 * q + 3] += v.w;
+        }
+  }
   store_tile<EPI, BM, BN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
 }
 
@@ -672,7 +712,7 @@ __global__ __launch_bounds__(256) void residual_from_parts_kernel(float* __restr
   *xp = apply_pending(r, *xp, m, n, M, N);
 }
 
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, int KW = 1>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                   const EpiArgs& ep, hipStream_t s, int splits = 1) {
   if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
@@ -686,8 +726,8 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
     return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
-  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
-#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256 * KW);
+#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
   switch (epi) {
     case EPI_BF16: FH_GEMM(EPI_BF16); break;
     case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;
@@ -730,7 +770,8 @@ hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, 
   EpiArgs ep;
   ep.part = part;
   ep.part_elems = part_elems;
-  return launch<128, 128, 64, 4>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
+  // two wave groups along K: 2.3 % faster than one group on the FFN down-projection at 1280 tokens
+  return launch<128, 128, 64, 4, 2>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
 }
 
 hipError_t gemm_bf16_splitk_n(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int splits,
