@@ -461,17 +461,14 @@ __global__ __launch_bounds__(256, 1) void flash_attn_mx_kernel(
 // global memory (they are small and shared through L2), before the scores.
 constexpr int MAXG = 64;  // most column groups of the query sums of squares
 
-__global__ __launch_bounds__(64) void cross_attn_kernel(
-    const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc, int ldk,
-    const bf16_t* __restrict__ vct, bf16_t* __restrict__ o, int ldo, int N, int La, int D, int hw,
-    int apf, int full, float scale_log2, const float* __restrict__ ssq, int groups,
-    const float* __restrict__ g, float eps) {
-  const int b = blockIdx.z, h = blockIdx.y;
+// The MFMA B-operand fragments of 32 query rows q0 .. q0+31 of head h (row
+// lr of lane half lh: dims 16 s + 8 lh .. +7 in qf[s]), with the query
+// RMSNorm over the full width applied when ssq is given.
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[8], const bf16_t* __restrict__ q, int ldq, int b, int h,
+                                             int q0, int N, int D, const float* __restrict__ ssq, int groups,
+                                             const float* __restrict__ g, float eps) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
-  const int q0 = blockIdx.x * 32;
-
-  bf16x8 qf[8];
   {
     const int qrow = min(q0 + lr, N - 1);
     const bf16_t* qp = q + ((int64_t)b * N + qrow) * ldq + h * HD + 8 * lh;
@@ -508,6 +505,20 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(
       }
     }
   }
+}
+
+__global__ __launch_bounds__(64) void cross_attn_kernel(
+    const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc, int ldk,
+    const bf16_t* __restrict__ vct, bf16_t* __restrict__ o, int ldo, int N, int La, int D, int hw,
+    int apf, int full, float scale_log2, const float* __restrict__ ssq, int groups,
+    const float* __restrict__ g, float eps) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int q0 = blockIdx.x * 32;
+
+  bf16x8 qf[8];
+  load_q_frags(qf, q, ldq, b, h, q0, N, D, ssq, groups, g, eps);
   const int k_lo = full ? 0 : (q0 / hw) * apf;
   const int k_hi = full ? La : k_lo + apf;
 
@@ -566,6 +577,70 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(
   if (q0 + lr < N) store_o(o + ((int64_t)b * N + q0 + lr) * ldo + h * HD, acc, 1.f / l_run, lh);
 }
 
+// Frame-local cross-attention probabilities: for 32 queries of one (lane,
+// head), the softmax over the apf audio tokens of their latent frame (at most
+// MAXKB blocks of 32, scores kept in registers), written normalised as bf16 to
+// p[row][h apf + j]. The value product and the output projection then run as
+// one GEMM against per-frame products of the values with that projection.
+constexpr int MAXKB = 4;
+
+__global__ __launch_bounds__(64) void cross_probs_kernel(
+    const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ kc, int ldk, bf16_t* __restrict__ p,
+    int ldp, int N, int La, int D, int hw, int apf, float scale_log2, const float* __restrict__ ssq, int groups,
+    const float* __restrict__ g, float eps) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int q0 = blockIdx.x * 32;
+
+  bf16x8 qf[8];
+  load_q_frags(qf, q, ldq, b, h, q0, N, D, ssq, groups, g, eps);
+  const int k_lo = (q0 / hw) * apf, nkb = apf / 32;
+
+  // S^T blocks: lane (lr, lh) holds query lr's scores of keys 8 (r/4) + 4 lh + r%4
+  f32x16 st[MAXKB];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < MAXKB; ++kb) {
+    if (kb >= nkb) break;
+    bf16x8 kf[8];
+    const bf16_t* kp = kc + ((int64_t)b * La + k_lo + 32 * kb + lr) * ldk + h * HD + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], st[kb], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r] * scale_log2);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float l = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < MAXKB; ++kb) {
+    if (kb >= nkb) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      st[kb][r] = exp2f(fmaf(st[kb][r], scale_log2, -mx));
+      l += st[kb][r];
+    }
+  }
+  l += __shfl_xor(l, 32, 64);
+  const float inv = 1.f / l;
+  if (q0 + lr >= N) return;
+  bf16_t* pr = p + ((int64_t)b * N + q0 + lr) * ldp + h * apf + 4 * lh;
+#pragma unroll
+  for (int kb = 0; kb < MAXKB; ++kb) {
+    if (kb >= nkb) break;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const u32x2 w = {pack2bf(st[kb][4 * a] * inv, st[kb][4 * a + 1] * inv),
+                       pack2bf(st[kb][4 * a + 2] * inv, st[kb][4 * a + 3] * inv)};
+      *reinterpret_cast<u32x2*>(pr + 32 * kb + 8 * a) = w;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const bf16_t* vt,
@@ -588,6 +663,21 @@ hipError_t flash_attn_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k, 
   const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
   flash_attn_mx_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, qs, k, ks, ldq, vt, vts, o, ldo, N, n_heads * HD,
                                                           scale_log2, n_qt, n_heads, n_wg);
+  return hipGetLastError();
+}
+
+hipError_t cross_probs(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, bf16_t* p, int ldp, int B, int N,
+                       int La, int hw, int apf, int n_heads, float scale, const float* ssq, int groups,
+                       const float* g, float eps, hipStream_t s) {
+  if (B <= 0 || N <= 0) return hipSuccess;
+  if (N % 32 || hw % 32 || apf % 32 || apf > 32 * MAXKB || La % 32 || ldq % 8 || ldk % 8 || ldp % 4 ||
+      ldp < n_heads * apf || (N / hw) * apf > La || !p)
+    return hipErrorInvalidValue;
+  if (ssq && (groups < 4 || groups > MAXG || groups % 4 || !g)) return hipErrorInvalidValue;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid(N / 32, n_heads, B);
+  cross_probs_kernel<<<grid, 64, 0, s>>>(q, ldq, kc, ldk, p, ldp, N, La, n_heads * HD, hw, apf, scale_log2, ssq,
+                                         groups, g, eps);
   return hipGetLastError();
 }
 

@@ -78,6 +78,9 @@ static std::atomic<uint64_t> g_weights_serial{1};
 struct fh_ctx {
   fh_config cfg;
   int N, HW, La;
+  // frame-local cross-attention with the value product folded into the output
+  // projection (per-frame V' = v W_co^T per head, once per slice)
+  bool fold_co = false;
   std::vector<Spec> specs;
   std::string err;
   bool use_graph = true;
@@ -149,6 +152,15 @@ std::vector<Spec> make_specs(const fh_config& g) {
   return s;
 }
 
+// per-block audio cache: plain form k [B La][D] and V^T [B][D][La]; folded
+// form [k | v] [B La][2D] and V' [B F][D][n_heads apf]
+size_t slot_elems(const fh_ctx* c, int B) { return (size_t)B * c->La * c->cfg.dim; }
+size_t kslot(const fh_ctx* c, int B) { return (c->fold_co ? 2 : 1) * slot_elems(c, B); }
+size_t vslot(const fh_ctx* c, int B) {
+  return c->fold_co ? (size_t)B * c->cfg.frames * c->cfg.dim * c->cfg.n_heads * c->cfg.audio_per_frame
+                    : slot_elems(c, B);
+}
+
 WS carve(const fh_ctx* c, int B, char* base) {
   const fh_config& g = c->cfg;
   const size_t N = c->N, D = g.dim, La = c->La, Fd = g.ffn_dim, nb = g.n_blocks;
@@ -168,8 +180,8 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.qc = (bf16_t*)take(B * N * D * 2);
   w.u = (bf16_t*)take(B * N * Fd * 2);
   w.aud = (bf16_t*)take(B * La * D * 2);
-  w.kc = (bf16_t*)take(nb * B * La * D * 2);
-  w.vct = (bf16_t*)take(nb * B * La * D * 2);
+  w.kc = (bf16_t*)take(nb * kslot(c, B) * 2);
+  w.vct = (bf16_t*)take(nb * vslot(c, B) * 2);
   w.emb = (float*)take(R * g.freq_dim * 4);
   w.t1 = (float*)take(R * D * 4);
   w.e = (float*)take(R * D * 4);
@@ -241,11 +253,25 @@ struct Timed {
   }
 };
 
-size_t slot_elems(const fh_ctx* c, int B) { return (size_t)B * c->La * c->cfg.dim; }
 
 int audio_kv(fh_ctx* c, const WBlock& wb, int B, bf16_t* kc, bf16_t* vct, const WS& ws, hipStream_t s) {
   const fh_config& g = c->cfg;
   const int D = g.dim;
+  if (c->fold_co) {
+    // [k | v] row-major, k RMS-normalised in place; then per head h the product
+    // v[:, h] W_co[:, h]^T of every latent frame's apf tokens, stored as
+    // V'[(lane, frame)][n][h apf + j] for the grouped output projection
+    const int apf = g.audio_per_frame, KH = g.n_heads * apf;
+    fh::EpiArgs ep;
+    ep.bias = wb.ckv_b;
+    ep.out_bf = kc;
+    ep.ldo = 2 * D;
+    FH_HIP(fh::gemm_bf16(fh::EPI_BF16, ws.aud, D, wb.ckv_w, D, B * c->La, 2 * D, D, ep, s));
+    FH_HIP(fh::rmsnorm_rope_bf16(kc, 2 * D, B * c->La, D, 1, wb.norm_ck, nullptr, nullptr, nullptr, c->La,
+                                 g.head_dim, g.eps, s));
+    FH_HIP(fh::gemm_bf16_heads(kc + D, 2 * D, wb.co_w, D, B * c->La, D, D, g.n_heads, vct, apf, KH, s));
+    return FH_OK;
+  }
   fh::EpiArgs ep;
   ep.bias = wb.ckv_b;
   ep.out_bf = kc;
@@ -333,19 +359,38 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.ssq = ws.ssq;
     FH_HIP(fh::gemm_bf16(fh::EPI_BF16_SSQ, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
   }
-  {
-    Timed t(c, FH_K_CROSS_ATTN, s);
-    FH_HIP(fh::cross_attn(ws.qc, D, kc, D, vct, ws.ao, D, B, N, c->La, c->HW, g.audio_per_frame,
-                          g.cross_full, g.n_heads, scale, ws.ssq, fh::gemm_ssq_groups(M, D, D),
-                          wb.norm_cq, g.eps, s));
-  }
-  {
-    Timed t(c, FH_K_GEMM_CO, s);
-    fh::EpiArgs ep;
-    ep.bias = wb.co_b;
-    ep.x = x;
-    ep.ldx = D;
-    FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
+  if (c->fold_co) {
+    // probabilities P [M][n_heads apf] (in ao), then x += P V'_frame + b: the value
+    // product and the output projection in one GEMM of depth n_heads apf
+    const int apf = g.audio_per_frame, KH = g.n_heads * apf;
+    {
+      Timed t(c, FH_K_CROSS_ATTN, s);
+      FH_HIP(fh::cross_probs(ws.qc, D, kc, 2 * D, ws.ao, KH, B, N, c->La, c->HW, apf, g.n_heads, scale, ws.ssq,
+                             fh::gemm_ssq_groups(M, D, D), wb.norm_cq, g.eps, s));
+    }
+    {
+      Timed t(c, FH_K_GEMM_CO, s);
+      fh::EpiArgs ep;
+      ep.bias = wb.co_b;
+      ep.x = x;
+      ep.ldx = D;
+      FH_HIP(fh::gemm_bf16_grouped(fh::EPI_RES, ws.ao, KH, vct, KH, M, D, KH, c->HW, (int64_t)D * KH, ep, s));
+    }
+  } else {
+    {
+      Timed t(c, FH_K_CROSS_ATTN, s);
+      FH_HIP(fh::cross_attn(ws.qc, D, kc, D, vct, ws.ao, D, B, N, c->La, c->HW, g.audio_per_frame,
+                            g.cross_full, g.n_heads, scale, ws.ssq, fh::gemm_ssq_groups(M, D, D),
+                            wb.norm_cq, g.eps, s));
+    }
+    {
+      Timed t(c, FH_K_GEMM_CO, s);
+      fh::EpiArgs ep;
+      ep.bias = wb.co_b;
+      ep.x = x;
+      ep.ldx = D;
+      FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
+    }
   }
   const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN;
   {
@@ -501,7 +546,7 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   for (int i = 0; i < g.n_blocks; ++i) {
     int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
                                 ws.fvc + i * slot_elems(c, B), s)
-                 : audio_kv(c, w->blk[i], B, ws.kc + i * slot_elems(c, B), ws.vct + i * slot_elems(c, B), ws, s);
+                 : audio_kv(c, w->blk[i], B, ws.kc + i * kslot(c, B), ws.vct + i * vslot(c, B), ws, s);
     if (rc) return rc;
   }
   for (int c0 = 0; c0 < n_steps; c0 += GEMV_ROWS) {
@@ -538,8 +583,8 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       fh::PendingRes pend;
       for (int i = 0; i < g.n_blocks; ++i) {
         fh::PendingRes next;
-        int rc = run_block(c, w->blk[i], B, ws.x, e0, 0, ws.kc + i * slot_elems(c, B),
-                           ws.vct + i * slot_elems(c, B), ws, s, &pend, &next);
+        int rc = run_block(c, w->blk[i], B, ws.x, e0, 0, ws.kc + i * kslot(c, B),
+                           ws.vct + i * vslot(c, B), ws, s, &pend, &next);
         if (rc) return rc;
         pend = next;
       }
@@ -694,6 +739,8 @@ int fh_create(const fh_config* cfg, fh_ctx** out) {
   ctx->HW = g.height * g.width;
   ctx->N = g.frames * ctx->HW;
   ctx->La = g.frames * g.audio_per_frame;
+  ctx->fold_co = !g.cross_full && ctx->HW % 64 == 0 && g.audio_per_frame <= 128 &&
+                 (g.n_heads * g.audio_per_frame) % 64 == 0;
   ctx->specs = make_specs(g);
   *out = ctx;
   return FH_OK;

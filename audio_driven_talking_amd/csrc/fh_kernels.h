@@ -56,10 +56,23 @@ struct EpiArgs {
   int ldq = 0;
   uint16_t* q_scale = nullptr;       // EPI_GELU_MX: scales [N / 64][M]
   uint8_t* q_scale_b = nullptr;      // EPI_SPLIT_T_MX: scales of the transposed part
+  int ldt = 0;                       // EPI_SPLIT_T: pitch of a transposed row (0: rows_per_lane)
+  // row-grouped weights (gemm_bf16_grouped): rows [g R, (g+1) R) of A take W + g * w_group_stride
+  int w_group_rows = 0;
+  int64_t w_group_stride = 0;
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                      const EpiArgs& ep, hipStream_t s);
+// Block-diagonal product, one per head: for h < heads, C_h = A[:, h Kh .. +Kh] W[:, h Kh .. +Kh]^T
+// (Kh = K / heads), stored transposed: row m = lane l, token t of C_h goes to
+// out[(l t_cols + n) ldt + h rows_per_lane + t] (EPI_SPLIT_T with split 0, no bias unless given).
+hipError_t gemm_bf16_heads(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int heads,
+                           bf16_t* out, int rows_per_lane, int ldt, hipStream_t s);
+// EPI_RES / EPI_GATED_RES / EPI_BF16 GEMM whose weights change every group_rows rows of A:
+// rows [g R, (g+1) R) use W + g * group_stride (R a multiple of 64)
+hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                             int group_rows, int64_t group_stride, const EpiArgs& ep, hipStream_t s);
 // number of column groups of EPI_BF16_SSQ's per-row partial sums for this shape
 int gemm_ssq_groups(int M, int N, int K);
 
@@ -173,6 +186,12 @@ hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const
                       bf16_t* o, int ldo, int B, int N, int La, int hw, int apf, int full,
                       int n_heads, float scale, const float* ssq, int groups, const float* g, float eps,
                       hipStream_t s);
+// Frame-local cross-attention probabilities softmax(q k^T scale) over the apf
+// audio tokens of each query's latent frame (apf a multiple of 32, at most 128),
+// normalised, bf16, at p[(b N + n) ldp + h apf + j]; query RMSNorm as cross_attn.
+hipError_t cross_probs(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, bf16_t* p, int ldp, int B, int N,
+                       int La, int hw, int apf, int n_heads, float scale, const float* ssq, int groups,
+                       const float* g, float eps, hipStream_t s);
 
 // Rotary angle tables [N, head_dim/2] (cos, sin), computed in float64.
 hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,

@@ -282,7 +282,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int nl = i * 32 + 8 * g + 4 * lh;
-            const float4 b = *reinterpret_cast<const float4*>(ep.bias + nw + nl);
+            const float4 b = ep.bias ? *reinterpret_cast<const float4*>(ep.bias + nw + nl) : make_float4(0.f, 0.f, 0.f, 0.f);
             bf16_t* sp = reinterpret_cast<bf16_t*>(st + nl * ST::PT) + lr;
             sp[0] = f2bf(acc[i][j][4 * g] + b.x);
             sp[ST::PT / 2] = f2bf(acc[i][j][4 * g + 1] + b.y);
@@ -290,13 +290,16 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
             sp[3 * ST::PT / 2] = f2bf(acc[i][j][4 * g + 3] + b.w);
           }
         lds_fence();
+        // transposed rows of pitch ldt; a head-split product (split index ks) starts at column ks rows_per_lane
+        const int ldt = ep.ldt ? ep.ldt : ep.rows_per_lane;
 #pragma unroll
         for (int it = 0; it < C * 4 / 64; ++it) {
           const int c = it * 64 + lane, nl = c / 4, t8 = (c % 4) * 8;
           const int m = mb + t8;  // 8 rows, never across a lane: rows_per_lane % 8 == 0
           if (m < M) {
             const int bl = m / ep.rows_per_lane, t = m - bl * ep.rows_per_lane;
-            bf16_t* o = ep.out_t + ((int64_t)bl * ep.t_cols + (nw + nl - ep.split)) * ep.rows_per_lane + t;
+            bf16_t* o = ep.out_t + ((int64_t)bl * ep.t_cols + (nw + nl - ep.split)) * ldt +
+                        (int64_t)ks * ep.rows_per_lane + t;
             *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(st + nl * ST::PT + t8 * 2);
           }
         }
@@ -335,6 +338,7 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   K /= splits;
   A += (int64_t)ks * K;
   W += (int64_t)ks * K;
+  if (ep.w_group_rows) W += (int64_t)(m0 / ep.w_group_rows) * ep.w_group_stride;  // a tile is in one group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -682,6 +686,7 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
                      const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s,
                      int splits = 1) {
   if (N % BN || splits < 1 || K % (splits * 64) || lda % 16 || ldw % 16 || M % 2) return hipErrorInvalidValue;
+  if (ep.w_group_rows || ep.ldt) return hipErrorInvalidValue;  // bf16 kernel only
   if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
     return hipErrorInvalidValue;
   if (epi == EPI_GELU_MX && (!ep.out_q || !ep.q_scale || ep.ldq % 16)) return hipErrorInvalidValue;
@@ -722,8 +727,13 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
                                 !ep.out_q || !ep.q_scale_b || (BN / 2) % 64))
     return hipErrorInvalidValue;
   if (epi == EPI_GATED_RES && ep.rows_per_lane <= 0) return hipErrorInvalidValue;
-  if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
+  // splits > 1: K halves summed through f32 parts, or (EPI_SPLIT_T, all columns transposed) one
+  // separate product per split placed side by side in rows of pitch ldt
+  const bool head_split = epi == EPI_SPLIT_T && ep.split == 0 && ep.ldt >= splits * ep.rows_per_lane;
+  if (splits > 1 && !head_split && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
     return hipErrorInvalidValue;
+  if (epi == EPI_SPLIT_T && ep.ldt && (ep.ldt < ep.rows_per_lane || ep.ldt % 8)) return hipErrorInvalidValue;
+  if (ep.w_group_rows && (ep.w_group_rows % BM || ep.w_group_stride <= 0)) return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles * splits + 7) / 8 * 8), block(256 * KW);
@@ -784,6 +794,36 @@ hipError_t gemm_bf16_splitk_n(const bf16_t* A, int lda, const bf16_t* W, int ldw
   ep.part = part;
   ep.part_elems = part_elems;
   return launch<64, 128, 64, 4>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, splits);
+}
+
+hipError_t gemm_bf16_heads(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int heads,
+                           bf16_t* out, int rows_per_lane, int ldt, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (heads < 1 || K % (64 * heads) || N % 128 || lda % 8 || ldw % 8 || !out || rows_per_lane <= 0 ||
+      rows_per_lane % 8 || M % rows_per_lane || ldt < heads * rows_per_lane)
+    return hipErrorInvalidValue;
+  EpiArgs ep;
+  ep.out_t = out;
+  ep.split = 0;
+  ep.t_cols = N;
+  ep.rows_per_lane = rows_per_lane;
+  ep.ldt = ldt;
+  if (M <= 256) return launch<64, 128, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
+  return launch<128, 64, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
+}
+
+hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
+                             int group_rows, int64_t group_stride, const EpiArgs& ep_in, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if ((epi != EPI_RES && epi != EPI_GATED_RES && epi != EPI_BF16) || N % 128 || K % KALIGN || lda % 8 ||
+      ldw % 8 || group_rows <= 0 || group_rows % 64 || group_stride <= 0)
+    return hipErrorInvalidValue;
+  EpiArgs ep = ep_in;
+  ep.w_group_rows = group_rows;
+  ep.w_group_stride = group_stride;
+  // a tile never spans two groups: 128-row tiles where the groups allow, else 64
+  if (group_rows % 128 == 0) return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+  return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
 }
 
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s) {
