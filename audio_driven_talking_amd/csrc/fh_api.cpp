@@ -53,6 +53,8 @@ struct WS {
   // MX-FP8 self-attention operands of FH_PREC_FP8_ATTN (carved only for it): q and k codes [B*N][2D]
   // and scales [B*N][2D/32]; V^T codes [B][D][N] and scales [B][N/64][D][2]
   uint8_t *qkq = nullptr, *qks = nullptr, *vq = nullptr, *vs = nullptr;
+  // per-block pointer tables of the block-batched audio K/V launches
+  fh::BatchEntry *tab_kv = nullptr, *tab_co = nullptr;
   size_t total;
 };
 
@@ -194,6 +196,8 @@ WS carve(const fh_ctx* c, int B, char* base) {
   w.hs = (uint16_t*)take((D / 64) * B * N * 2);
   w.uq = (uint8_t*)take(B * N * Fd);
   w.us = (uint16_t*)take((Fd / 64) * B * N * 2);
+  w.tab_kv = (fh::BatchEntry*)take(fh::MAX_BATCH_TABLE * sizeof(fh::BatchEntry));
+  w.tab_co = (fh::BatchEntry*)take(fh::MAX_BATCH_TABLE * sizeof(fh::BatchEntry));
   if (c->precision == FH_PREC_FP8_ATTN) {
     w.qkq = (uint8_t*)take(B * N * 2 * D);
     w.qks = (uint8_t*)take(B * N * 2 * D / 32);
@@ -283,6 +287,38 @@ int audio_kv(fh_ctx* c, const WBlock& wb, int B, bf16_t* kc, bf16_t* vct, const 
   FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.aud, D, wb.ckv_w, D, B * c->La, 2 * D, D, ep, s));
   FH_HIP(fh::rmsnorm_rope_bf16(kc, D, B * c->La, D, 1, wb.norm_ck, nullptr, nullptr, nullptr, c->La,
                                g.head_dim, g.eps, s));
+  return FH_OK;
+}
+
+// The folded audio K/V of every block in three launches (the per-block form
+// of audio_kv, batched over a table of the blocks' weights): [k | v] of all
+// blocks, the k RMSNorm of all blocks, V' of all blocks.
+int audio_kv_all(fh_ctx* c, const fh_weights* w, int B, const WS& ws, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const int D = g.dim, nb = g.n_blocks, apf = g.audio_per_frame, Ma = B * c->La;
+  fh::BatchTableArgs kv{}, co{};
+  kv.n = co.n = nb;
+  for (int i = 0; i < nb; ++i) {
+    kv.w[i] = w->blk[i].ckv_w;
+    kv.b[i] = w->blk[i].ckv_b;
+    kv.g[i] = w->blk[i].norm_ck;
+    co.w[i] = w->blk[i].co_w;
+  }
+  FH_HIP(fh::fill_batch_table(ws.tab_kv, kv, s));
+  FH_HIP(fh::fill_batch_table(ws.tab_co, co, s));
+  fh::EpiArgs ep;
+  ep.out_bf = ws.kc;
+  ep.ldo = 2 * D;
+  FH_HIP(fh::gemm_bf16_batched(fh::EPI_BF16, ws.aud, D, 0, ws.tab_kv, nb, D, Ma, 2 * D, D, 1, ep, kslot(c, B), s));
+  FH_HIP(fh::rmsnorm_bf16_table(ws.kc, 2 * D, nb * Ma, D, ws.tab_kv, Ma, g.eps, s));
+  fh::EpiArgs et;
+  et.out_t = ws.vct;
+  et.split = 0;
+  et.t_cols = D;
+  et.rows_per_lane = apf;
+  et.ldt = g.n_heads * apf;
+  FH_HIP(fh::gemm_bf16_batched(fh::EPI_SPLIT_T, ws.kc + D, 2 * D, kslot(c, B), ws.tab_co, nb, D, Ma, D, D,
+                               g.n_heads, et, vslot(c, B), s));
   return FH_OK;
 }
 
@@ -543,11 +579,16 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   FH_HIP(fh::rope_table(ws.rcos, ws.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
   const bool f32 = c->precision == FH_PREC_FP32;
   if (!f32) FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
-  for (int i = 0; i < g.n_blocks; ++i) {
-    int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
-                                ws.fvc + i * slot_elems(c, B), s)
-                 : audio_kv(c, w->blk[i], B, ws.kc + i * kslot(c, B), ws.vct + i * vslot(c, B), ws, s);
+  if (!f32 && c->fold_co && g.n_blocks <= fh::MAX_BATCH_TABLE) {
+    int rc = audio_kv_all(c, w, B, ws, s);
     if (rc) return rc;
+  } else {
+    for (int i = 0; i < g.n_blocks; ++i) {
+      int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
+                                  ws.fvc + i * slot_elems(c, B), s)
+                   : audio_kv(c, w->blk[i], B, ws.kc + i * kslot(c, B), ws.vct + i * vslot(c, B), ws, s);
+      if (rc) return rc;
+    }
   }
   for (int c0 = 0; c0 < n_steps; c0 += GEMV_ROWS) {
     // time embedding of up to GEMV_ROWS steps at once (the weights are read once)

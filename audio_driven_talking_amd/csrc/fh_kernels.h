@@ -36,6 +36,23 @@ enum Epi {
 // 64-element slab: scale[s][row] = uint16 with block 2s in the low byte and
 // block 2s+1 in the high byte (s < K / 64).
 
+// Per-entry pointers of a block-batched launch (the audio K/V of every DiT
+// block at once): weights, bias and a norm gain, in device memory.
+struct BatchEntry {
+  const bf16_t* W;
+  const float* bias;
+  const float* g;
+};
+constexpr int MAX_BATCH_TABLE = 64;
+struct BatchTableArgs {
+  const void* w[MAX_BATCH_TABLE];
+  const void* b[MAX_BATCH_TABLE];
+  const void* g[MAX_BATCH_TABLE];
+  int n;
+};
+// write n entries of args into dst (device), on the stream (capturable)
+hipError_t fill_batch_table(BatchEntry* dst, const BatchTableArgs& args, hipStream_t s);
+
 struct EpiArgs {
   const float* bias = nullptr;
   bf16_t* out_bf = nullptr;
@@ -60,6 +77,11 @@ struct EpiArgs {
   // row-grouped weights (gemm_bf16_grouped): rows [g R, (g+1) R) of A take W + g * w_group_stride
   int w_group_rows = 0;
   int64_t w_group_stride = 0;
+  // block-batched launch (gemm_bf16_batched): entry e of batch takes W, bias from batch[e],
+  // A + e batch_a_stride and out_bf / out_t + e batch_out_stride
+  const BatchEntry* batch = nullptr;
+  int batch_n = 1;
+  int64_t batch_a_stride = 0, batch_out_stride = 0;
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -69,6 +91,12 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
 // out[(l t_cols + n) ldt + h rows_per_lane + t] (EPI_SPLIT_T with split 0, no bias unless given).
 hipError_t gemm_bf16_heads(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K, int heads,
                            bf16_t* out, int rows_per_lane, int ldt, hipStream_t s);
+// The same product for nb entries of a table in one launch (EPI_BF16, or the head-split
+// EPI_SPLIT_T of gemm_bf16_heads with heads > 1): entry e computes
+// (A + e a_stride)(W_e)^T (+ bias_e) into out + e out_stride; ep carries the output form.
+hipError_t gemm_bf16_batched(int epi, const bf16_t* A, int lda, int64_t a_stride, const BatchEntry* tab, int nb,
+                             int ldw, int M, int N, int K, int heads, const EpiArgs& ep, int64_t out_stride,
+                             hipStream_t s);
 // EPI_RES / EPI_GATED_RES / EPI_BF16 GEMM whose weights change every group_rows rows of A:
 // rows [g R, (g+1) R) use W + g * group_stride (R a multiple of 64)
 hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -192,6 +220,10 @@ hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const
 hipError_t cross_probs(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, bf16_t* p, int ldp, int B, int N,
                        int La, int hw, int apf, int n_heads, float scale, const float* ssq, int groups,
                        const float* g, float eps, hipStream_t s);
+
+// RMSNorm of rows [rows][D] (pitch ld) in place, row r scaled by tab[r / rows_per_entry].g
+hipError_t rmsnorm_bf16_table(bf16_t* p, int ld, int rows, int D, const BatchEntry* tab, int rows_per_entry,
+                              float eps, hipStream_t s);
 
 // Rotary angle tables [N, head_dim/2] (cos, sin), computed in float64.
 hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_dim, double theta,

@@ -309,7 +309,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS, int KW>
+template <int EPI, int BM, int BN, int BK, int NS, int KW, bool BATCH>
 __global__ __launch_bounds__(256 * KW, (KW == 1 && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
                   int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
@@ -330,7 +330,18 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
   bid = (bid & 7) * per_xcd + (bid >> 3);
-  if (bid >= tiles * splits) return;
+  if (bid >= tiles * splits * (BATCH ? ep.batch_n : 1)) return;
+  if constexpr (BATCH) {
+    // entry e of the table: its weights and bias, its rows of A and its output
+    const int e = bid / (tiles * splits);
+    bid -= e * tiles * splits;
+    const BatchEntry be = ep.batch[e];
+    W = be.W;
+    ep.bias = be.bias;
+    A += (int64_t)e * ep.batch_a_stride;
+    if (ep.out_bf) ep.out_bf += (int64_t)e * ep.batch_out_stride;
+    if (ep.out_t) ep.out_t += (int64_t)e * ep.batch_out_stride;
+  }
   // split ks of K (splits > 1 only with EPI_PARTIAL) covers columns [ks K/splits, (ks+1) K/splits)
   const int ks = bid / tiles, tile = bid - ks * tiles;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
@@ -717,7 +728,7 @@ __global__ __launch_bounds__(256) void residual_from_parts_kernel(float* __restr
   *xp = apply_pending(r, *xp, m, n, M, N);
 }
 
-template <int BM, int BN, int BK, int NS, int KW = 1>
+template <int BM, int BN, int BK, int NS, int KW = 1, bool BATCH = false>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                   const EpiArgs& ep, hipStream_t s, int splits = 1) {
   if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
@@ -734,10 +745,13 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
     return hipErrorInvalidValue;
   if (epi == EPI_SPLIT_T && ep.ldt && (ep.ldt < ep.rows_per_lane || ep.ldt % 8)) return hipErrorInvalidValue;
   if (ep.w_group_rows && (ep.w_group_rows % BM || ep.w_group_stride <= 0)) return hipErrorInvalidValue;
+  if (BATCH != (ep.batch != nullptr) || ep.batch_n < 1) return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
-  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256 * KW);
-#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
+  const int64_t wgs = (int64_t)tiles * splits * ep.batch_n;
+  if (wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256 * KW);
+#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
   switch (epi) {
     case EPI_BF16: FH_GEMM(EPI_BF16); break;
     case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;
@@ -810,6 +824,67 @@ hipError_t gemm_bf16_heads(const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   ep.ldt = ldt;
   if (M <= 256) return launch<64, 128, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
   return launch<128, 64, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
+}
+
+template <int BM, int BN, int NS>
+hipError_t launch_batched(int epi, const bf16_t* A, int lda, int ldw, int M, int N, int K, const EpiArgs& ep,
+                          hipStream_t s, int splits) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = tiles_m * (N / BN);
+  const int64_t wgs = (int64_t)tiles * splits * ep.batch_n;
+  if (N % BN || K % (splits * 64) || wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256);
+  // W comes from the table; the argument only fills the slot
+  if (epi == EPI_BF16)
+    launch_gemm(gemm_bf16_nt<EPI_BF16, BM, BN, 64, NS, 1, true>, grid, block, s, A, lda, (const bf16_t*)nullptr,
+                ldw, M, N, K, tiles_m, tiles, splits, ep);
+  else
+    launch_gemm(gemm_bf16_nt<EPI_SPLIT_T, BM, BN, 64, NS, 1, true>, grid, block, s, A, lda, (const bf16_t*)nullptr,
+                ldw, M, N, K, tiles_m, tiles, splits, ep);
+  return hipGetLastError();
+}
+
+hipError_t gemm_bf16_batched(int epi, const bf16_t* A, int lda, int64_t a_stride, const BatchEntry* tab, int nb,
+                             int ldw, int M, int N, int K, int heads, const EpiArgs& ep_in, int64_t out_stride,
+                             hipStream_t s) {
+  if (M <= 0 || nb <= 0) return hipSuccess;
+  if (!tab || heads < 1 || lda % 8 || ldw % 8 || K % (64 * heads) || a_stride < 0 || out_stride < 0)
+    return hipErrorInvalidValue;
+  EpiArgs ep = ep_in;
+  ep.batch = tab;
+  ep.batch_n = nb;
+  ep.batch_a_stride = a_stride;
+  ep.batch_out_stride = out_stride;
+  if (epi == EPI_BF16) {
+    if (heads != 1 || !ep.out_bf || ep.ldo % 8) return hipErrorInvalidValue;
+  } else if (epi == EPI_SPLIT_T) {
+    if (ep.split != 0 || !ep.out_t || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8 || M % ep.rows_per_lane ||
+        ep.ldt < heads * ep.rows_per_lane || ep.ldt % 8 || ep.t_cols != N)
+      return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  // a head-split product runs two 64-deep slabs per workgroup: two stages, so nothing is fetched twice
+  // and up to three workgroups share a CU
+  if (heads > 1 && K / heads == 128) {
+    if (M <= 256) return launch_batched<64, 128, 2>(epi, A, lda, ldw, M, N, K, ep, s, heads);
+    return launch_batched<128, 64, 2>(epi, A, lda, ldw, M, N, K, ep, s, heads);
+  }
+  if (M <= 256) return launch_batched<64, 128, 4>(epi, A, lda, ldw, M, N, K, ep, s, heads);
+  return launch_batched<128, 64, 4>(epi, A, lda, ldw, M, N, K, ep, s, heads);
+}
+
+namespace {
+__global__ void fill_batch_table_kernel(BatchEntry* dst, BatchTableArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.n) dst[i] = BatchEntry{(const bf16_t*)a.w[i], (const float*)a.b[i], (const float*)a.g[i]};
+}
+}  // namespace
+
+hipError_t fill_batch_table(BatchEntry* dst, const BatchTableArgs& args, hipStream_t s) {
+  if (!dst || args.n < 1 || args.n > MAX_BATCH_TABLE) return hipErrorInvalidValue;
+  fill_batch_table_kernel<<<1, MAX_BATCH_TABLE, 0, s>>>(dst, args);
+  return hipGetLastError();
 }
 
 hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
     bf16_t* __restrict__ p, int ld, int D, int tpp, const float* __restrict__ g0,
     const float* __restrict__ g1, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     int rows_per_lane, int head_dim, float eps, uint8_t* __restrict__ out_q, uint8_t* __restrict__ q_scale,
-    int ldq) {
+    int ldq, const BatchEntry* __restrict__ tab, int tab_rows) {
   __shared__ float red[8];
   const int row = blockIdx.x;
   const int part = threadIdx.x / tpp, tp = threadIdx.x % tpp;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
   const float tot = group_sum(ss, red, part * wpp, wpp);
   if (!on) return;
   const float rs = rsqrtf(tot / (float)D + eps);
-  const float* g = part ? g1 : g0;
+  const float* g = tab ? tab[row / tab_rows].g : part ? g1 : g0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] *= rs * g[c + e];
   if (cos_t) {
@@ -192,7 +192,17 @@ hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, con
     return hipErrorInvalidValue;
   if (out_q && (D % 32 || !q_scale || ldq % 32 || ldq < nparts * D)) return hipErrorInvalidValue;
   rmsnorm_rope_kernel<<<rows, tpp * nparts, 0, s>>>(p, ld, D, tpp, g0, g1, cos_t, sin_t, rows_per_lane,
-                                                     head_dim, eps, out_q, q_scale, ldq);
+                                                     head_dim, eps, out_q, q_scale, ldq, nullptr, 1);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bf16_table(bf16_t* p, int ld, int rows, int D, const BatchEntry* tab, int rows_per_entry,
+                              float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int tpp = threads_for(D);
+  if (D % 8 || ld % 8 || ld < D || tpp > 512 || !tab || rows_per_entry <= 0) return hipErrorInvalidValue;
+  rmsnorm_rope_kernel<<<rows, tpp, 0, s>>>(p, ld, D, tpp, nullptr, nullptr, nullptr, nullptr, 1, 8, eps, nullptr,
+                                           nullptr, 0, tab, rows_per_entry);
   return hipGetLastError();
 }
 
