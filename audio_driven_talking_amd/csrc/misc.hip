@@ -42,6 +42,10 @@ __global__ void sinusoid_kernel(float* __restrict__ out, Times ts, int R, int di
 }
 
 // 16 outputs per 256-thread workgroup (4 per wave); the R input rows sit in LDS.
+// A wave requests the weights of its 4 rows for a 2048-deep chunk of K at once
+// (16 bytes per lane and row, 4 chunks of 512), then forms the products.
+constexpr int GV_OPW = 4, GV_KC = 4;
+
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int R, int K,
                                                    const bf16_t* __restrict__ W,
                                                    const float* __restrict__ b, float* __restrict__ y,
@@ -53,27 +57,56 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = 0; o < 4; ++o) {
-    const int n = blockIdx.x * 16 + wave * 4 + o;
-    if (n >= N) break;
-    float acc[MAXR];
+  const int n0 = blockIdx.x * 16 + wave * GV_OPW;
+  float acc[GV_OPW][MAXR];
 #pragma unroll
-    for (int r = 0; r < MAXR; ++r) acc[r] = 0.f;
-    const u16x8* wr = reinterpret_cast<const u16x8*>(W + (int64_t)n * K);
-    for (int kc = lane; kc < K / 8; kc += 64) {
-      const u16x8 w = wr[kc];
+  for (int o = 0; o < GV_OPW; ++o)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wf = bf2f(w[e]);
+    for (int r = 0; r < MAXR; ++r) acc[o][r] = 0.f;
+  const int KC = K / 8;  // 8-element chunks per row
+  for (int c0 = 0; c0 < KC; c0 += 64 * GV_KC) {
+    u16x8 w[GV_OPW][GV_KC];
 #pragma unroll
-        for (int r = 0; r < MAXR; ++r)
-          if (r < R) acc[r] += wf * sx[r * K + kc * 8 + e];
+    for (int o = 0; o < GV_OPW; ++o)
+#pragma unroll
+      for (int i = 0; i < GV_KC; ++i) {
+        const int kc = c0 + 64 * i + lane;
+        if (n0 + o < N && kc < KC) w[o][i] = reinterpret_cast<const u16x8*>(W + (int64_t)(n0 + o) * K)[kc];
+        else w[o][i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int i = 0; i < GV_KC; ++i) {
+      const int kc = c0 + 64 * i + lane;
+      if (kc >= KC) break;
+#pragma unroll
+      for (int r = 0; r < MAXR; ++r) {
+        if (r >= R) break;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sx + r * K + kc * 8);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(sx + r * K + kc * 8 + 4);
+#pragma unroll
+        for (int o = 0; o < GV_OPW; ++o) {
+          float t = acc[o][r];
+          t += bf2f(w[o][i][0]) * a[0];
+          t += bf2f(w[o][i][1]) * a[1];
+          t += bf2f(w[o][i][2]) * a[2];
+          t += bf2f(w[o][i][3]) * a[3];
+          t += bf2f(w[o][i][4]) * c[0];
+          t += bf2f(w[o][i][5]) * c[1];
+          t += bf2f(w[o][i][6]) * c[2];
+          t += bf2f(w[o][i][7]) * c[3];
+          acc[o][r] = t;
+        }
       }
     }
+  }
+#pragma unroll
+  for (int o = 0; o < GV_OPW; ++o) {
+    const int n = n0 + o;
+    if (n >= N) break;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r)
       if (r < R) {
-        const float s = wave_sum(acc[r]);
+        const float s = wave_sum(acc[o][r]);
         if (lane == 0) {
           const float v = s + b[n];
           y[(int64_t)r * N + n] = act_out ? silu(v) : v;
