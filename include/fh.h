@@ -116,7 +116,11 @@ void fh_weights_release(fh_weights* w);
  * `batch` independent lanes: activations, the audio keys/values of every
  * block, the rotary tables and the time embedding (the FlashHead type's
  * `work` scratch), for the context's current precision (FH_PREC_FP32 needs
- * more). 0 for batch <= 0 or a null ctx.                                     */
+ * more). With frame-local cross-attention the per-block audio cache also
+ * holds the values already multiplied into the cross-attention output
+ * projection, per latent frame and head (frames x dim x heads x
+ * audio_per_frame bf16 per lane and block: 5.9 MB per block at the Lite
+ * sizes). 0 for batch <= 0 or a null ctx.                                    */
 size_t fh_workspace_bytes(const fh_ctx* ctx, int batch);
 
 /* One DiT block (block index `block`) on the residual stream, in place.
