@@ -822,6 +822,11 @@ hipError_t gemm_bf16_heads(const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   ep.t_cols = N;
   ep.rows_per_lane = rows_per_lane;
   ep.ldt = ldt;
+  // two stages when each workgroup has only two 64-deep slabs (K / heads = 128), as in the batched form
+  if (K / heads == 128) {
+    if (M <= 256) return launch<64, 128, 64, 2>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
+    return launch<128, 64, 64, 2>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
+  }
   if (M <= 256) return launch<64, 128, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
   return launch<128, 64, 64, 4>(EPI_SPLIT_T, A, lda, W, ldw, M, N, K, ep, s, heads);
 }
