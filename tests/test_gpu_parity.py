@@ -126,6 +126,22 @@ def test_toy_full_cross_attention(fh):
     assert err <= TOL
 
 
+def test_toy_more_blocks_than_the_batched_audio_table(fh):
+    """66 blocks: past the 64-entry pointer table the per-slice audio keys and
+    values (and the folded cross-attention values) are formed block by block."""
+    cfg = synth.CONFIGS["toy"].replace(n_blocks=66)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.TOY_SIGMAS)
+    say("toy slice, 66 blocks")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"toy 66-block rel err {err:.3e}")
+    assert err <= TOL
+
+
 # ------------------------------------------------------------------ one real block
 @pytest.fixture(scope="module")
 def block_model(fh):
