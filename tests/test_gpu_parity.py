@@ -142,6 +142,24 @@ def test_toy_more_blocks_than_the_batched_audio_table(fh):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("apf", [64, 128, 160])
+def test_toy_audio_tokens_per_frame(fh, apf):
+    """Frame-local cross-attention over 64 and 128 audio tokens per latent frame
+    (2 and 4 blocks of 32 in the probabilities kernel, folded output) and over
+    160 (beyond the fold's limit: the plain path)."""
+    cfg = synth.CONFIGS["toy"].replace(audio_per_frame=apf)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = list(synth.TOY_SIGMAS)
+    say(f"toy slice, {apf} audio tokens per frame, B=2")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
 # ------------------------------------------------------------------ one real block
 @pytest.fixture(scope="module")
 def block_model(fh):
