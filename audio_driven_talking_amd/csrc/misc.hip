@@ -198,30 +198,55 @@ __global__ void philox_fill_kernel(uint32_t* __restrict__ out, int64_t n, uint32
 }
 
 // Output head on the modulated, normalised rows h (bf16 [B*N, D]) fused with
-// the sampler update: MFMA 16x16x32, one wave per 16 tokens and 16 channels;
-// lane l holds token (l % 16) and channels 4 (l / 16) + {0..3} of its group.
-// Euler: x' = x + (s' - s) v. Re-noising: x' = (1 - s') (x - s v) + s' eps,
-// eps from latent_noise (element index c * N + token within the lane).
+// the sampler update: MFMA 16x16x32, one workgroup per 16 tokens, its 4 waves
+// each taking a quarter of the D-long dot products (all of a wave's operand
+// loads requested before its MFMAs), the quarters added in wave order through
+// LDS; lane l holds token (l % 16) and channels 4 (l / 16) + {0..3} of a
+// 16-channel group. Euler: x' = x + (s' - s) v. Re-noising: x' = (1 - s')
+// (x - s v) + s' eps, eps from latent_noise (element index c * N + token
+// within the lane).
+constexpr int HE_KQ = 12;  // 32-deep k-steps a wave requests at once
+
 __global__ __launch_bounds__(256) void head_euler_kernel(
     const bf16_t* __restrict__ h, int B, int N, int D, const bf16_t* __restrict__ Wh,
     const float* __restrict__ bh, int Co, const float* lat_cur, float* lat_next,
     const float* __restrict__ motion, int nmt, float sigma, float sigma_next, SamplerArgs sa) {
+  __shared__ f32x4 part[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * 16;
-  if (t0 >= B * N) return;
+  const int t0 = blockIdx.x * 16;
   const int lr = lane & 15, lq = lane >> 4;
   const int row = min(t0 + lr, B * N - 1);
-  const bf16_t* hp = h + (int64_t)row * D + 8 * lq;
+  const int kq = D / 4;  // this wave's k range [wave kq, (wave + 1) kq)
+  const bf16_t* hp = h + (int64_t)row * D + wave * kq + 8 * lq;
   const float dsig = sigma_next - sigma;
   for (int cg = 0; cg < Co; cg += 16) {
-    const bf16_t* wp = Wh + (int64_t)(cg + lr) * D + 8 * lq;
+    const bf16_t* wp = Wh + (int64_t)(cg + lr) * D + wave * kq + 8 * lq;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 32)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(wp + k0),
-                                                    *reinterpret_cast<const bf16x8*>(hp + k0), acc, 0, 0, 0);
+    for (int k0 = 0; k0 < kq; k0 += 32 * HE_KQ) {
+      bf16x8 a[HE_KQ], w[HE_KQ];
+#pragma unroll
+      for (int i = 0; i < HE_KQ; ++i)
+        if (k0 + 32 * i < kq) {
+          w[i] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * i);
+          a[i] = *reinterpret_cast<const bf16x8*>(hp + k0 + 32 * i);
+        }
+#pragma unroll
+      for (int i = 0; i < HE_KQ; ++i)
+        if (k0 + 32 * i < kq) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], a[i], acc, 0, 0, 0);
+    }
     mfma_drain(acc);
-    if (t0 + lr < B * N) {
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && t0 + lr < B * N) {
+      f32x4 v4 = part[0][lane];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        const f32x4 p = part[q][lane];
+        v4[0] += p[0];
+        v4[1] += p[1];
+        v4[2] += p[2];
+        v4[3] += p[3];
+      }
       const int b = (t0 + lr) / N, tok = (t0 + lr) % N;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(256) void head_euler_kernel(
         if (tok < nmt) {
           lat_next[idx] = motion[((int64_t)b * Co + co) * nmt + tok];
         } else {
-          const float v = acc[i] + bh[co];
+          const float v = v4[i] + bh[co];
           if (sa.renoise) {
             const float eps = latent_noise((uint32_t)(co * N + tok), (uint32_t)b, sa.step, sa.k0, sa.k1);
             lat_next[idx] = (1.f - sigma_next) * (lat_cur[idx] - sigma * v) + sigma_next * eps;
@@ -240,6 +265,7 @@ __global__ __launch_bounds__(256) void head_euler_kernel(
         }
       }
     }
+    __syncthreads();  // part[] is reused by the next channel group
   }
 }
 
@@ -330,8 +356,8 @@ hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, 
 hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
                       float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s) {
-  if (D % 32 || Co % 16) return hipErrorInvalidValue;
-  head_euler_kernel<<<(B * N + 63) / 64, 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
+  if (D % 128 || Co % 16) return hipErrorInvalidValue;
+  head_euler_kernel<<<(B * N + 15) / 16, 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
                                                       n_motion_tok, sigma, sigma_next, sa);
   return hipGetLastError();
 }
