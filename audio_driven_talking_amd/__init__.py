@@ -17,7 +17,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfh.so")
+# FH_DEBUG=1: the debug build (synchronises after every launch, no graphs)
+LIB_PATH = os.path.join(_HERE, "libfh_debug.so" if os.environ.get("FH_DEBUG") == "1" else "libfh.so")
 
 FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHTS = range(7)
 FH_DTYPE_BF16, FH_DTYPE_F32 = 1, 2
@@ -66,7 +67,8 @@ def _load():
     # (same soname), since it receives torch's device pointers and streams.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python audio_driven_talking_amd/build.py`")
+        debug = "FH_DEBUG=1 " if LIB_PATH.endswith("_debug.so") else ""
+        raise ImportError(f"{LIB_PATH} is not built: run `{debug}python audio_driven_talking_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     sig = {

@@ -119,11 +119,26 @@ int fail(fh_ctx* c, int code, const char* fmt, ...) {
   return code;
 }
 
+#ifdef FH_DEBUG
+// Debug build: every HIP call of the runtime is followed by a device
+// synchronisation, so a kernel fault is reported, with the launching call's
+// text, by the library call that launched it (graphs are off in this build).
+#define FH_HIP(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ == hipSuccess) e_ = hipDeviceSynchronize();                                      \
+    if (e_ == hipSuccess) e_ = hipGetLastError();                                           \
+    if (e_ != hipSuccess) return fail(c, FH_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+constexpr bool kDebugBuild = true;
+#else
 #define FH_HIP(expr)                                                                        \
   do {                                                                                      \
     hipError_t e_ = (expr);                                                                 \
     if (e_ != hipSuccess) return fail(c, FH_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+constexpr bool kDebugBuild = false;
+#endif
 
 std::vector<Spec> make_specs(const fh_config& g) {
   const int64_t D = g.dim, Fd = g.ffn_dim, C = g.in_ch, Co = g.out_ch, Fq = g.freq_dim;
@@ -783,6 +798,7 @@ int fh_create(const fh_config* cfg, fh_ctx** out) {
   ctx->fold_co = !g.cross_full && ctx->HW % 64 == 0 && g.audio_per_frame <= 128 &&
                  (g.n_heads * g.audio_per_frame) % 64 == 0;
   ctx->specs = make_specs(g);
+  ctx->use_graph = !kDebugBuild;  // the debug build synchronises after every launch: no capture
   *out = ctx;
   return FH_OK;
 }
@@ -964,7 +980,7 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
 int fh_set_option(fh_ctx* c, int option, int value) {
   if (!c) return FH_EINVAL;
   if (option == FH_OPT_GRAPH) {
-    c->use_graph = value != 0;
+    c->use_graph = value != 0 && !kDebugBuild;
     return FH_OK;
   }
   if (option == FH_OPT_TIME_KERNEL) {

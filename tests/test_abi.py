@@ -333,3 +333,18 @@ def test_fp8_attention_precision_checks():
     assert "multiple of 64" in fh.fh_last_error(ctx2)
     assert L.fh_dit_block_forward(ctx2, w, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EUNSUPPORTED
     fh.lib.fh_weights_release(w)
+
+
+def test_debug_runtime_compiles():
+    """The FH_DEBUG runtime (a device synchronisation after every HIP call, no
+    graph capture) still compiles: syntax-only pass over its source."""
+    import importlib.util
+    import subprocess
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "audio_driven_talking_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("fh_build_check", path)
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    cmd = [b.HIPCC, *b.FLAGS, "-DFH_DEBUG", "-fsyntax-only", os.path.join(b.CSRC, "fh_api.cpp")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
