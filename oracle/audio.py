@@ -15,7 +15,7 @@ READINGS (the plainest ones the rest supports; every size is a parameter):
      (768 for wav2vec 2.0 base);
   A2 the slice's V video frames are the window's last V frames: frame f sits
      at state frame T - V + f;
-  A3 "5 states around" a frame: offsets -2 .. +2, clamped to [0, T - 1];
+  A3 a frame's five states are those at offsets -2 .. +2 from it, clamped to [0, T - 1];
      a frame's feature is those states flattened in (offset, layer, channel)
      order, width 5 L C;
   A4 latent frames follow the video VAE's temporal stride s (8 for LTX):
