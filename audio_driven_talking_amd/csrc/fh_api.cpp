@@ -28,9 +28,9 @@ struct WBlock {
   const bf16_t *qkv_w, *o_w, *cq_w, *ckv_w, *co_w, *ffn1_w, *ffn2_w;
   const float *mod, *qkv_b, *norm_q, *norm_k, *o_b, *norm3_g, *norm3_b, *cq_b, *ckv_b, *norm_cq,
       *norm_ck, *co_b, *ffn1_b, *ffn2_b;
-  // MX-FP8 copies of the FFN matrices (fh_weights_quantize_fp8), else null
-  const uint8_t *ffn1_q = nullptr, *ffn2_q = nullptr;
-  const uint16_t *ffn1_s = nullptr, *ffn2_s = nullptr;
+  // MX-FP8 copies of the FFN and QKV matrices (fh_weights_quantize_fp8), else null
+  const uint8_t *ffn1_q = nullptr, *ffn2_q = nullptr, *qkv_q = nullptr;
+  const uint16_t *ffn1_s = nullptr, *ffn2_s = nullptr, *qkv_s = nullptr;
 };
 
 struct GraphEntry {
@@ -346,12 +346,14 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
   const fh_config& g = c->cfg;
   const int N = c->N, D = g.dim, M = B * N, Fd = g.ffn_dim;
   const float scale = 1.0f / std::sqrt((float)g.head_dim);
+  // FP8 self-attention: the QKV projection too runs on MX-FP8 operands (the
+  // LayerNorm writes codes and scales for it)
+  const bool mx_attn = c->precision == FH_PREC_FP8_ATTN;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
-                              nullptr, nullptr, pend_in, s));
+                              nullptr, nullptr, pend_in, s, mx_attn ? ws.hq : nullptr, mx_attn ? ws.hs : nullptr));
   }
-  const bool mx_attn = c->precision == FH_PREC_FP8_ATTN;
   {
     Timed t(c, FH_K_GEMM_QKV, s);
     fh::EpiArgs ep;
@@ -365,8 +367,10 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     if (mx_attn) {  // values straight to MX-FP8 along the tokens
       ep.out_q = ws.vq;
       ep.q_scale_b = ws.vs;
+      FH_HIP(fh::gemm_mx(fh::EPI_SPLIT_T_MX, ws.hq, D, ws.hs, wb.qkv_q, D, wb.qkv_s, M, 3 * D, D, ep, s));
+    } else {
+      FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
     }
-    FH_HIP(fh::gemm_bf16(mx_attn ? fh::EPI_SPLIT_T_MX : fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
   }
   {
     Timed t(c, FH_K_RMSNORM_ROPE, s);
@@ -1015,7 +1019,7 @@ namespace {
 size_t fp8_block_bytes(const fh_config& g) {
   auto r = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t D = g.dim, Fd = g.ffn_dim;
-  return r(Fd * D) + r(D * Fd) + r(D / 64 * Fd * 2) + r(Fd / 64 * D * 2);
+  return r(Fd * D) + r(D * Fd) + r(D / 64 * Fd * 2) + r(Fd / 64 * D * 2) + r(3 * D * D) + r(D / 64 * 3 * D * 2);
 }
 }  // namespace
 
@@ -1041,9 +1045,12 @@ int fh_weights_quantize_fp8(fh_ctx* c, fh_weights* w, void* buf, size_t bytes, v
     uint8_t* q2 = q1 + r((size_t)Fd * D);
     uint16_t* s1 = (uint16_t*)(q2 + r((size_t)D * Fd));
     uint16_t* s2 = (uint16_t*)((char*)s1 + r((size_t)D / 64 * Fd * 2));
+    uint8_t* q3 = (uint8_t*)((char*)s2 + r((size_t)Fd / 64 * D * 2));
+    uint16_t* s3 = (uint16_t*)(q3 + r((size_t)3 * D * D));
     FH_HIP(fh::mx_quantize(nullptr, b.ffn1_w, Fd, D, q1, s1, s));
     FH_HIP(fh::mx_quantize(nullptr, b.ffn2_w, D, Fd, q2, s2, s));
-    b.ffn1_q = q1; b.ffn1_s = s1; b.ffn2_q = q2; b.ffn2_s = s2;
+    FH_HIP(fh::mx_quantize(nullptr, b.qkv_w, 3 * D, D, q3, s3, s));
+    b.ffn1_q = q1; b.ffn1_s = s1; b.ffn2_q = q2; b.ffn2_s = s2; b.qkv_q = q3; b.qkv_s = s3;
     p += fp8_block_bytes(g);
   }
   w->fp8 = true;

@@ -701,6 +701,11 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
   if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
     return hipErrorInvalidValue;
   if (epi == EPI_GELU_MX && (!ep.out_q || !ep.q_scale || ep.ldq % 16)) return hipErrorInvalidValue;
+  if ((epi == EPI_SPLIT_T || epi == EPI_SPLIT_T_MX) && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8))
+    return hipErrorInvalidValue;
+  if (epi == EPI_SPLIT_T_MX && (ep.rows_per_lane % 64 || M % ep.rows_per_lane || !ep.out_q || !ep.q_scale_b ||
+                                (BN / 2) % 64))
+    return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
@@ -711,6 +716,8 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
     case EPI_GATED_RES: FH_MX(EPI_GATED_RES); break;
     case EPI_RES: FH_MX(EPI_RES); break;
     case EPI_PARTIAL: FH_MX(EPI_PARTIAL); break;
+    case EPI_SPLIT_T: FH_MX(EPI_SPLIT_T); break;
+    case EPI_SPLIT_T_MX: FH_MX(EPI_SPLIT_T_MX); break;
     default: return hipErrorInvalidValue;
   }
 #undef FH_MX
@@ -936,8 +943,11 @@ hipError_t gemm_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const
                    const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (N % 128 || K % 64 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
-  // stage counts from a same-process A/B of the FP8 slice (3 beat 4 and 5 here; 4 beat 3, 6 and 8 for split K)
-  if (N % 256 == 0 && N >= 4096) return launch_mx<192, 256, 3>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
+  // stage counts from a same-process A/B of the FP8 slice (3 beat 4 and 5 here; 4 beat 3, 6 and 8 for split K);
+  // 192 x 256 tiles only where they still give most CUs a tile (FFN up: 245 at 1280 tokens; QKV: 126 -> 192 x 128)
+  const int64_t tiles_wide = (int64_t)((M + 191) / 192) * (N / 256);
+  if (N % 256 == 0 && N >= 4096 && tiles_wide >= 200)
+    return launch_mx<192, 256, 3>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
   return launch_mx<192, 128, 5>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
 }
 

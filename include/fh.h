@@ -196,7 +196,9 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       this precision (float32 activations and audio K/V), so query it after
  *       setting the option; a smaller workspace is FH_EWORKSPACE.          */
 /*     FH_PREC_FP8_ATTN: FH_PREC_FP8_FFN and the self-attention on MX-FP8
- *       too: q and k quantised along the head dim by the q/k norm, the values
+ *       too: the QKV projection on MX-FP8 operands (its LayerNorm writes
+ *       codes and scales), q and k quantised along the head dim by the q/k
+ *       norm, the values
  *       along the tokens by the QKV projection, the probabilities per query
  *       and 32-key block; both products on the block-scaled MFMA; sums and
  *       softmax in float32. Needs fh_weights_quantize_fp8 and tokens per lane
@@ -211,7 +213,7 @@ enum {
 int fh_set_option(fh_ctx* ctx, int option, int value);
 /* Bytes of the device buffer fh_weights_quantize_fp8 fills (0 for a null ctx). */
 size_t fh_fp8_weight_bytes(const fh_ctx* ctx);
-/* Quantise the FFN matrices of bound weights to MX-FP8 into a caller-owned
+/* Quantise the FFN and QKV matrices of bound weights to MX-FP8 into a caller-owned
  * device buffer (256-byte aligned, fh_fp8_weight_bytes bytes; it must outlive
  * w) and attach them to w. Enqueued on `stream`. FH_EINVAL for a null,
  * foreign or misaligned argument or a short buffer; FH_EHIP on launch errors. */

@@ -207,12 +207,13 @@ def merge_heads(x):
     return x.transpose(0, 2, 1, 3).reshape(B, N, nh * dh)
 
 
-def self_attention(h, Wb, ang, cfg, attn=attention):
-    """QKV projection, q/k RMSNorm (full width), 3-D rotary, softmax attention
-    (``attn``: ``attention`` here, or the FP8 form of oracle/mxfp8.py).
-    Returns the head-merged output before the output projection, [B, N, D]."""
+def self_attention(h, Wb, ang, cfg, attn=attention, qkv_linear=linear):
+    """QKV projection (``qkv_linear``), q/k RMSNorm (full width), 3-D rotary,
+    softmax attention (``attn``: ``attention`` here, or the FP8 forms of
+    oracle/mxfp8.py for both). Returns the head-merged output before the
+    output projection, [B, N, D]."""
     D, nh = cfg.dim, cfg.n_heads
-    qkv = linear(h, Wb["qkv.w"], Wb["qkv.b"])
+    qkv = qkv_linear(h, Wb["qkv.w"], Wb["qkv.b"])
     q, k, v = qkv[..., :D], qkv[..., D:2 * D], qkv[..., 2 * D:]
     q = rms_norm(q, Wb["norm_q.g"], cfg.eps)
     k = rms_norm(k, Wb["norm_k.g"], cfg.eps)
@@ -258,7 +259,7 @@ def block_weights(W, i):
     return {k[len(p):]: v for k, v in W.items() if k.startswith(p)}
 
 
-def dit_block(x, e0, audio, Wb, cfg, ang, ffn_linear=linear, attn=attention):
+def dit_block(x, e0, audio, Wb, cfg, ang, ffn_linear=linear, attn=attention, qkv_linear=linear):
     """One Wan-style block on the residual stream x [B, N, D].
 
     mods = table + e0 ([B, 6, D]): shift/scale/gate for self-attention, then
@@ -267,14 +268,15 @@ def dit_block(x, e0, audio, Wb, cfg, ang, ffn_linear=linear, attn=attention):
       x += CO(CA(LN_affine(x), audio))           (ungated)
       x += gate_ff * FFN(LN(x)(1+scale_ff)+shift_ff)
 
-    ffn_linear is the product used for the FFN's two layers and attn the
-    self-attention: ``linear`` and ``attention`` here, or the block-scaled FP8
-    forms of oracle/mxfp8.py for the FP8 variants.
+    ffn_linear is the product used for the FFN's two layers, attn the
+    self-attention and qkv_linear its input projection: ``linear`` and
+    ``attention`` here, or the block-scaled FP8 forms of oracle/mxfp8.py for
+    the FP8 variants.
     """
     x = to64(x)
     m = to64(Wb["mod"])[None] + to64(e0)
     h = modulate(layer_norm(x, cfg.eps), m[:, 0], m[:, 1])
-    x = x + m[:, 2][:, None, :] * linear(self_attention(h, Wb, ang, cfg, attn), Wb["o.w"], Wb["o.b"])
+    x = x + m[:, 2][:, None, :] * linear(self_attention(h, Wb, ang, cfg, attn, qkv_linear), Wb["o.w"], Wb["o.b"])
     h3 = layer_norm(x, cfg.eps, Wb["norm3.g"], Wb["norm3.b"])
     kc, vc = audio_kv(audio, Wb, cfg)
     x = x + linear(cross_attention(h3, kc, vc, Wb, cfg), Wb["co.w"], Wb["co.b"])
@@ -283,11 +285,11 @@ def dit_block(x, e0, audio, Wb, cfg, ang, ffn_linear=linear, attn=attention):
     return x + m[:, 5][:, None, :] * ffn_linear(u, Wb["ffn2.w"], Wb["ffn2.b"])
 
 
-def dit_block_from_temb(x, e, audio, W, i, cfg, ffn_linear=linear, attn=attention):
+def dit_block_from_temb(x, e, audio, W, i, cfg, ffn_linear=linear, attn=attention, qkv_linear=linear):
     """Block i with its modulation derived from a time embedding e [B, D]:
     e0 = Linear(SiLU(e)) (the shared time projection)."""
     e0 = linear(silu(e), W["time_proj.w"], W["time_proj.b"]).reshape(-1, 6, cfg.dim)
-    return dit_block(x, e0, audio, block_weights(W, i), cfg, rope_angles(cfg), ffn_linear, attn)
+    return dit_block(x, e0, audio, block_weights(W, i), cfg, rope_angles(cfg), ffn_linear, attn, qkv_linear)
 
 
 def patchify(latent):
@@ -303,14 +305,14 @@ def unpatchify(tokens, cfg):
     return np.moveaxis(t, -1, 1)
 
 
-def dit_flow(latent, sigma, audio, W, cfg, blocks=None, ffn_linear=linear, attn=attention):
+def dit_flow(latent, sigma, audio, W, cfg, blocks=None, ffn_linear=linear, attn=attention, qkv_linear=linear):
     """Flow prediction v [B, C, F, H, W] of the DiT at noise level sigma (scalar)."""
     B = latent.shape[0]
     e, e0 = time_embedding(np.full(B, sigma, dtype=np.float64), W, cfg)
     ang = rope_angles(cfg)
     x = linear(patchify(latent), W["patch.w"], W["patch.b"])
     for i in (range(cfg.n_blocks) if blocks is None else blocks):
-        x = dit_block(x, e0, audio, block_weights(W, i), cfg, ang, ffn_linear, attn)
+        x = dit_block(x, e0, audio, block_weights(W, i), cfg, ang, ffn_linear, attn, qkv_linear)
     hm = to64(W["head.mod"])[None] + e[:, None, :]          # [B, 2, D]: shift, scale
     h = modulate(layer_norm(x, cfg.eps), hm[:, 0], hm[:, 1])
     return unpatchify(linear(h, W["head.w"], W["head.b"]), cfg)
@@ -335,12 +337,12 @@ def euler_step(latent, v, sigma, sigma_next):
     return to64(latent) + (float(sigma_next) - float(sigma)) * to64(v)
 
 
-def denoise_slice(noise, motion, audio, sigmas, W, cfg, ffn_linear=linear, attn=attention):
+def denoise_slice(noise, motion, audio, sigmas, W, cfg, ffn_linear=linear, attn=attention, qkv_linear=linear):
     """Noise latent [B,C,F,H,W] -> denoised latent after len(sigmas)-1 steps,
     the motion frames pinned before the first step and after every step."""
     x = pin_motion(noise, motion)
     for i in range(len(sigmas) - 1):
-        v = dit_flow(x, sigmas[i], audio, W, cfg, ffn_linear=ffn_linear, attn=attn)
+        v = dit_flow(x, sigmas[i], audio, W, cfg, ffn_linear=ffn_linear, attn=attn, qkv_linear=qkv_linear)
         x = pin_motion(euler_step(x, v, sigmas[i], sigmas[i + 1]), motion)
     return x
 

@@ -180,7 +180,8 @@ def test_fp8_precision_argument_errors():
     L, vp = fh.lib, ctypes.c_void_p
     c = synth.CONFIGS["toy"]
     r = lambda b: (b + 255) // 256 * 256
-    per = r(c.ffn_dim * c.dim) * 2 + r(c.dim // 64 * c.ffn_dim * 2) + r(c.ffn_dim // 64 * c.dim * 2)
+    per = (r(c.ffn_dim * c.dim) * 2 + r(c.dim // 64 * c.ffn_dim * 2) + r(c.ffn_dim // 64 * c.dim * 2)
+           + r(3 * c.dim * c.dim) + r(c.dim // 64 * 3 * c.dim * 2))   # FFN and QKV codes + scales
     assert fh.fh_fp8_weight_bytes(ctx) == per * c.n_blocks
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 7) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN) == fh.FH_OK

@@ -759,7 +759,8 @@ def test_fp8_attn_toy_slice(fh):
     say("toy slice, FP8 FFN and self-attention, 4 steps")
     got = m.slice(lat, mot, aud, sig)
     Wf = synth.weights_f32(W)
-    ref_q = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear, attn=Q.mx_attention)
+    ref_q = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear, attn=Q.mx_attention,
+                            qkv_linear=Q.mx_linear)
     ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
     err_q, err = O.rel_err(got, ref_q, cfg.motion_frames), O.rel_err(got, ref, cfg.motion_frames)
     say(f"  rel err vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs the exact oracle {err:.3e} (bar {TOL_FP8})")
@@ -770,7 +771,8 @@ def test_fp8_attn_toy_slice(fh):
 
 def test_fp8_attn_self_attention_only_block(fh):
     """Full-width block with the FFN and cross-attention outputs zeroed: the
-    update is the self-attention branch alone."""
+    update is the self-attention branch alone (MX-FP8 QKV projection and
+    attention), held to the bf16 bar against the MX-FP8 oracle."""
     cfg = synth.CONFIGS["block"]
     W = synth.make_weights(cfg)
     for k in ("ffn2.w", "co.w"):
@@ -782,7 +784,8 @@ def test_fp8_attn_self_attention_only_block(fh):
     say("full-width block, self-attention only, FP8")
     got = m.block(0, x, e, a)
     Wf = synth.weights_f32(W)
-    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, attn=Q.mx_attention), x)
+    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, attn=Q.mx_attention,
+                                                 qkv_linear=Q.mx_linear), x)
     err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
     say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL}), vs exact {err:.3e} (bar {TOL_FP8})")
     assert err_q <= TOL and err <= TOL_FP8
@@ -797,7 +800,7 @@ def test_fp8_attn_block(fh):
     got = m.block(0, x, e, a)
     Wf = synth.weights_f32(W)
     err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, ffn_linear=Q.mx_linear,
-                                                 attn=Q.mx_attention), x)
+                                                 attn=Q.mx_attention, qkv_linear=Q.mx_linear), x)
     err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
     say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs exact {err:.3e} (bar {TOL_FP8})")
     assert err_q <= TOL_MX and err <= TOL_FP8

@@ -198,6 +198,26 @@ def test_block_routes_self_attention_through_the_hook():
     assert seen == [(1, cfg.n_heads, cfg.tokens, cfg.head_dim)]
 
 
+def test_qkv_hook_is_the_self_attention_input_projection():
+    """The qkv_linear hook takes the QKV projection and nothing else: once per
+    block, [B, N, D] -> [B, N, 3D] with the block's qkv weights; the default
+    hook gives the plain oracle bitwise."""
+    import oracle as O
+    from synth import CONFIGS, make_weights, weights_f32, block_inputs
+    cfg = CONFIGS["toy"]
+    W = weights_f32(make_weights(cfg))
+    x, e, a = block_inputs(cfg, 1)
+    seen = []
+
+    def spy(h, w, b):
+        seen.append((h.shape, w.shape))
+        return O.linear(h, w, b)
+
+    np.testing.assert_array_equal(O.dit_block_from_temb(x, e, a, W, 0, cfg, qkv_linear=spy),
+                                  O.dit_block_from_temb(x, e, a, W, 0, cfg))
+    assert seen == [((1, cfg.tokens, cfg.dim), (3 * cfg.dim, cfg.dim))]
+
+
 def _grid_ints(rng, shape):
     """Entries in {-2, -1, 0, 1, 2}: exact in e4m3 under any block scale."""
     return rng.integers(-2, 3, shape).astype(np.float64)
