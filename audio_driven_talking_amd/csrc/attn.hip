@@ -14,6 +14,9 @@
 // V^T blocks are DMA'd into XOR-swizzled LDS, double-buffered.
 // cross_attn: short key ranges (32 audio tokens per latent frame, or all of
 // them), fragments loaded straight from global memory, no LDS.
+// cross_probs: the frame-local softmax probabilities alone (the value
+// product is folded into the output projection's GEMM).
+// flash_attn_mx: the self-attention on MX-FP8 operands (block-scaled MFMA).
 #include "fh_common.h"
 #include "fh_kernels.h"
 

@@ -11,9 +11,9 @@
 // blocks; or (KW = 2) two such groups of 4 waves, each taking half of every
 // slab's k-steps, which puts two waves on each SIMD (one wave alone cannot
 // issue LDS fragment reads fast enough to feed a 64 x 64 wave tile) and adds
-// the groups' sums through LDS before the epilogue. Operand slabs go global -> LDS directly (global_load_lds_dwordx4:
-// each wave instruction fills 1 KB of whole rows), NS slabs deep, one barrier
-// per slab. A slab's fragments are read into registers during the previous
+// the groups' sums through LDS before the epilogue. Operand slabs go global
+// -> LDS directly (global_load_lds_dwordx4: each wave instruction fills 1 KB
+// of whole rows), NS slabs deep, one barrier per slab. A slab's fragments are read into registers during the previous
 // slab's MFMAs, and the DMA and LDS-read instructions are spread between the
 // MFMAs, so neither the address unit nor the LDS stalls the matrix core in
 // bursts. The 16-byte chunks of an LDS row are XOR-swizzled so that the
@@ -23,6 +23,11 @@
 // Tile order is XCD-aware: the grid is padded to a multiple of the 8 XCDs and
 // each XCD gets a contiguous run of tiles, M fastest, so the tiles sharing a
 // weight slab share an L2.
+// Other forms of the same kernel: split K (f32 parts per K range), K ranges
+// multiplied separately and stored side by side (one product per attention
+// head), weights chosen per group of rows (one weight matrix per latent
+// frame), and a launch over a table of weight pointers (one product per DiT
+// block). An MX-FP8 form on the block-scaled MFMA follows below.
 #include <type_traits>
 
 #include "fh_common.h"
