@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -135,10 +136,23 @@ def device_info(torch):
             "gcn_arch": getattr(p, "gcnArchName", ""), "l2_bytes": getattr(p, "L2_cache_size", None)}
 
 
+def kernel_code_hash(path):
+    """SHA-256 of a kernel source's code: // comments, trailing blanks and empty
+    lines removed, so an edit of comments alone keeps counters taken on the
+    same code valid."""
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = re.sub(r"//.*$", "", line).rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def traffic_from_profile(kernel_src_hash, name):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3
     counter summary profiles/<name> (FETCH_SIZE and WRITE_SIZE scaled by a copy
-    kernel of known size), if it was taken on the current kernel source; else None."""
+    kernel of known size), if it was taken on the current kernel code
+    (kernel_code_hash); else None."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -146,7 +160,7 @@ def traffic_from_profile(kernel_src_hash, name):
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("source_sha256") != kernel_src_hash:
+    if d.get("code_sha256") != kernel_src_hash:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -246,11 +260,11 @@ def main():
     k_avg_s = kms / 1e3 / max(kn, 1)
     achieved = k_flops / k_avg_s / 1e12
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
-    src = open(os.path.join(ROOT, "audio_driven_talking_amd", "csrc", "gemm.hip"), "rb").read()
+    code_hash = kernel_code_hash(os.path.join(ROOT, "audio_driven_talking_amd", "csrc", "gemm.hip"))
     counters = "gemm_mx_ffn2_slice_b1_counters.json" if fp8 else "gemm_ffn2_slice_b1_counters.json"
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_from_profile(hashlib.sha256(src).hexdigest(), counters),
+                "traffic": traffic_from_profile(code_hash, counters),
                 "kernel": f"{ROOF_KERNEL} (M={M}, N={cfg.dim}, K={cfg.ffn_dim}, "
                           f"{'MX-FP8 e4m3' if fp8 else 'bf16'}, {k_flops / 1e9:.2f} GFLOP per launch)",
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
