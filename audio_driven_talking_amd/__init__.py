@@ -323,7 +323,7 @@ def fh_fp8_weight_bytes(ctx):
 
 
 def fh_weights_quantize_fp8(ctx, w, stream=None, device="cuda"):
-    """Quantise w's FFN matrices to MX-FP8 into a new device buffer kept on w."""
+    """Quantise w's FFN and QKV matrices to MX-FP8 into a new device buffer kept on w."""
     import torch
     buf = torch.empty(fh_fp8_weight_bytes(ctx) + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
