@@ -20,3 +20,4 @@ from .dit import *  # noqa: F401,F403
 from . import renoise  # noqa: F401
 from . import mxfp8  # noqa: F401
 from . import audio  # noqa: F401
+from . import color  # noqa: F401
