@@ -12,7 +12,10 @@ sRGB's transfer curve and BT.709 primaries with the D65 white (IEC 61966-2-1),
 CIELAB (CIE 15) relative to that white.
 
 READINGS (the plainest ones the rest supports):
-  C1 frames and picture are sRGB values in [0, 1], [F, H, W, 3] and [H, W, 3];
+  C1 frames and picture are sRGB values in [0, 1] held as RGB planes: the
+     picture [3, H, W] as the gizai:flashhead page's FlashHead.picture makes
+     it, the decoded frames [3, F, H, W] (channels first, as a video VAE
+     emits them);
   C2 the statistics are per frame and per Lab channel: mean and standard
      deviation (population) over the frame's pixels, and the same over the
      picture;
@@ -94,9 +97,13 @@ def lab_to_rgb(lab):
 
 
 def lab_stats(lab):
-    """Per-channel mean and population standard deviation over all pixels of [..., 3]."""
+    """Per-channel mean and population standard deviation over all pixels of
+    [..., 3]. A channel whose values are all equal has deviation exactly 0
+    (floating-point summation could leave a residue of ~1e-14 that C3's
+    division would blow up)."""
     v = lab.reshape(-1, 3)
-    return v.mean(axis=0), v.std(axis=0)
+    flat = np.ptp(v, axis=0) == 0
+    return np.where(flat, v[0], v.mean(axis=0)), np.where(flat, 0.0, v.std(axis=0))
 
 
 def match_lab(lab, mu, sd, mu_ref, sd_ref, strength):
@@ -107,12 +114,13 @@ def match_lab(lab, mu, sd, mu_ref, sd_ref, strength):
 
 
 def color_match(frames, picture, strength=1.0):
-    """Frames [F, H, W, 3] matched to picture [H', W', 3] (C1-C5), float64."""
-    ref = rgb_to_lab(picture)
+    """Frames [3, F, H, W] matched to picture [3, H', W'] (C1-C5), float64."""
+    ref = rgb_to_lab(np.moveaxis(np.asarray(picture, dtype=np.float64), 0, -1))
     mu_ref, sd_ref = lab_stats(ref)
-    out = np.empty(np.shape(frames), dtype=np.float64)
-    for i, fr in enumerate(np.asarray(frames)):
-        lab = rgb_to_lab(fr)
+    fr = np.moveaxis(np.asarray(frames, dtype=np.float64), 0, -1)      # [F, H, W, 3]
+    out = np.empty(fr.shape, dtype=np.float64)
+    for i in range(fr.shape[0]):
+        lab = rgb_to_lab(fr[i])
         mu, sd = lab_stats(lab)
         out[i] = np.clip(lab_to_rgb(match_lab(lab, mu, sd, mu_ref, sd_ref, strength)), 0.0, 1.0)
-    return out
+    return np.moveaxis(out, -1, 0)

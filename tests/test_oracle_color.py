@@ -72,9 +72,21 @@ def test_flat_frame_takes_the_picture_mean():
     np.testing.assert_allclose(out, np.tile([[55.0, -1.0, 4.0]], (16, 1)), atol=1e-12)
 
 
+def test_flat_frame_in_color_match_takes_the_picture_mean_colour():
+    """A frame of one colour has deviation 0 in every channel (C3): it becomes
+    the picture's mean Lab colour, whatever residue summation leaves."""
+    rng = np.random.default_rng(4)
+    pic = rng.uniform(0.2, 0.8, (3, 9, 7))
+    frames = np.broadcast_to(np.array([0.3, 0.6, 0.2])[:, None, None, None], (3, 2, 16, 12)).copy()
+    out = C.color_match(frames, pic, 1.0)
+    mu_ref = C.rgb_to_lab(np.moveaxis(pic, 0, -1)).reshape(-1, 3).mean(axis=0)
+    np.testing.assert_allclose(C.rgb_to_lab(np.moveaxis(out, 0, -1)).reshape(-1, 3), np.tile(mu_ref, (2 * 16 * 12, 1)),
+                               atol=1e-9)
+
+
 def test_zero_strength_returns_the_frames():
     rng = np.random.default_rng(2)
-    frames, pic = rng.random((2, 5, 6, 3)), rng.random((7, 4, 3))
+    frames, pic = rng.random((3, 2, 5, 6)), rng.random((3, 7, 4))
     np.testing.assert_allclose(C.color_match(frames, pic, 0.0), frames, atol=1e-12)
 
 
@@ -98,21 +110,22 @@ def _rgb_scalar(L, a, b):
 
 def test_color_match_equals_a_scalar_loop():
     rng = np.random.default_rng(3)
-    frames, pic, s = rng.random((2, 3, 4, 3)), rng.random((5, 3, 3)), 0.7
-    ref = [_lab_scalar(*p) for p in pic.reshape(-1, 3)]
+    frames, pic, s = rng.random((3, 2, 3, 4)), rng.random((3, 5, 3)), 0.7   # RGB planes
+    ref = [_lab_scalar(pic[0, y, x], pic[1, y, x], pic[2, y, x]) for y in range(5) for x in range(3)]
     n = len(ref)
     mr = [sum(v[c] for v in ref) / n for c in range(3)]
     sr = [math.sqrt(sum((v[c] - mr[c]) ** 2 for v in ref) / n) for c in range(3)]
     want = np.empty_like(frames)
-    for f in range(frames.shape[0]):
-        lab = [_lab_scalar(*p) for p in frames[f].reshape(-1, 3)]
+    for f in range(frames.shape[1]):
+        lab = [_lab_scalar(frames[0, f, y, x], frames[1, f, y, x], frames[2, f, y, x])
+               for y in range(3) for x in range(4)]
         m = [sum(v[c] for v in lab) / len(lab) for c in range(3)]
         sd = [math.sqrt(sum((v[c] - m[c]) ** 2 for v in lab) / len(lab)) for c in range(3)]
         outs = []
         for v in lab:
             w = [v[c] + s * (mr[c] + (v[c] - m[c]) * sr[c] / sd[c] - v[c]) for c in range(3)]
             outs.append(_rgb_scalar(*w))
-        want[f] = np.array(outs).reshape(frames.shape[1:])
+        want[:, f] = np.array(outs).T.reshape(3, 3, 4)
     np.testing.assert_allclose(C.color_match(frames, pic, s), want, atol=1e-12)
 
 
