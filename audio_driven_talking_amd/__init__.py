@@ -36,7 +36,7 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
            "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
            "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
-           "fh_kernel_time", "fh_last_error", "fh_status_str"]
+           "fh_color_match_workspace_bytes", "fh_color_match", "fh_kernel_time", "fh_last_error", "fh_status_str"]
 
 
 class fh_config(ctypes.Structure):
@@ -96,6 +96,8 @@ def _load():
         "fh_audio_project": (i32, [vp, vp, i32, vp, vp, vp, sz, vp]),
         "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                      ctypes.c_int64, vp, vp]),
+        "fh_color_match_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "fh_color_match": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp, sz, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
         "fh_status_str": (ctypes.c_char_p, [i32]),
@@ -316,6 +318,36 @@ def fh_philox4x32_fill(seed, lane, step, first_group, out, stream=None):
                                 out.numel() // 4, ctypes.c_void_p(out.data_ptr()), _stream(stream))
     if st != FH_OK:
         raise FHError(st, f"fh_philox4x32_fill: {fh_status_str(st)}")
+
+
+def fh_color_match_workspace_bytes(n_frames, height, width, ref_height, ref_width):
+    return int(lib.fh_color_match_workspace_bytes(n_frames, height, width, ref_height, ref_width))
+
+
+def fh_color_match(frames, picture, strength=1.0, out=None, workspace=None, stream=None):
+    """Lab colour match of float32 device planes frames [3, F, H, W] to
+    picture [3, H', W'] (see include/fh.h). Returns out (a new tensor unless
+    given; it may be frames for an in-place call)."""
+    import torch
+    for name, t, nd in (("frames", frames, 4), ("picture", picture, 3)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.dim() != nd \
+                or not t.is_contiguous() or t.shape[0] != 3:
+            raise ValueError(f"{name} must be a contiguous float32 device tensor [3, ...] of {nd} dims")
+    _, F, H, W = frames.shape
+    _, Hr, Wr = picture.shape
+    if out is None:
+        out = torch.empty_like(frames)
+    elif out.shape != frames.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like frames")
+    if workspace is None:
+        workspace = torch.empty(max(fh_color_match_workspace_bytes(F, H, W, Hr, Wr), 1), dtype=torch.uint8,
+                                device=frames.device)
+    st = lib.fh_color_match(ctypes.c_void_p(frames.data_ptr()), F, H, W, ctypes.c_void_p(picture.data_ptr()),
+                            Hr, Wr, float(strength), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_color_match: {fh_status_str(st)}")
+    return out
 
 
 def fh_fp8_weight_bytes(ctx):

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfh.so")
-SOURCES = ["gemm.hip", "norm.hip", "attn.hip", "misc.hip", "debug_f32.hip", "audio.hip", "fh_api.cpp"]
+SOURCES = ["gemm.hip", "norm.hip", "attn.hip", "misc.hip", "debug_f32.hip", "audio.hip", "color.hip", "fh_api.cpp"]
 # attention keeps its MFMA accumulators in VGPRs: the online softmax rescales
 # and reads them with VALU every key block, and AGPR copies would dominate.
 EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

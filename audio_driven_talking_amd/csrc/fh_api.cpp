@@ -1105,6 +1105,43 @@ int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t fir
   return e == hipSuccess ? FH_OK : FH_EHIP;
 }
 
+namespace {
+bool color_sizes_ok(int32_t F, int32_t H, int32_t W, int32_t Hr, int32_t Wr) {
+  if (F < 0 || F > 65534 || H <= 0 || W <= 0 || Hr <= 0 || Wr <= 0) return false;
+  const int64_t npix = (int64_t)H * W, nref = (int64_t)Hr * Wr;
+  // one thread per pixel at most, 2^31 workgroups of 256
+  return npix <= (1ll << 32) && nref <= (1ll << 32) && (int64_t)F * npix < (1ll << 38);
+}
+}  // namespace
+
+size_t fh_color_match_workspace_bytes(int32_t n_frames, int32_t height, int32_t width, int32_t ref_height,
+                                      int32_t ref_width) {
+  if (!color_sizes_ok(n_frames, height, width, ref_height, ref_width) || n_frames == 0) return 0;
+  return fh::color_match_workspace(n_frames, (int64_t)height * width, (int64_t)ref_height * ref_width);
+}
+
+int fh_color_match(const float* frames, int32_t n_frames, int32_t height, int32_t width, const float* picture,
+                   int32_t ref_height, int32_t ref_width, float strength, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!color_sizes_ok(n_frames, height, width, ref_height, ref_width) || !std::isfinite(strength)) return FH_EINVAL;
+  if (n_frames == 0) return FH_OK;
+  if (!frames || !picture || !out || ((uintptr_t)frames & 3) || ((uintptr_t)picture & 3) || ((uintptr_t)out & 3))
+    return FH_EINVAL;
+  const int64_t npix = (int64_t)height * width, nref = (int64_t)ref_height * ref_width;
+  const size_t bytes = (size_t)n_frames * npix * 3 * sizeof(float);
+  if (out != frames && (const char*)out < (const char*)frames + bytes && (const char*)frames < (const char*)out + bytes)
+    return FH_EINVAL;  // partial overlap
+  const hipStream_t s = (hipStream_t)stream;
+  if (strength == 0.0f) {  // correction disabled: the frames unchanged
+    if (out == frames) return FH_OK;
+    return hipMemcpyAsync(out, frames, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess ? FH_OK : FH_EHIP;
+  }
+  if (!workspace || ((uintptr_t)workspace & 255)) return FH_EINVAL;
+  if (workspace_bytes < fh::color_match_workspace(n_frames, npix, nref)) return FH_EWORKSPACE;
+  const hipError_t e = fh::color_match(frames, n_frames, npix, picture, nref, strength, out, workspace, s);
+  return e == hipSuccess ? FH_OK : FH_EHIP;
+}
+
 int fh_audio_weight_count(const fh_ctx* c, const fh_audio_config* a) {
   if (!c || !a || check_audio_cfg(nullptr, a) != FH_OK) return 0;
   return (int)audio_specs(c, *a).size();

@@ -305,4 +305,12 @@ hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh,
                           const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
                           float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s);
 
+// Lab colour match of F frames of npix pixels (planes [3][F][npix]) to a picture
+// of npix_ref pixels (planes [3][npix_ref]); out may equal frames. The
+// workspace (color_match_workspace bytes, 256-byte aligned) holds the partial
+// sums and the per-frame coefficients. Needs 1 <= F <= 65534, npix, npix_ref >= 1.
+size_t color_match_workspace(int F, int64_t npix, int64_t npix_ref);
+hipError_t color_match(const float* frames, int F, int64_t npix, const float* pic, int64_t npix_ref, float strength,
+                       float* out, void* ws, hipStream_t s);
+
 }  // namespace fh

@@ -15,6 +15,9 @@ Extra objects on the line:
   cpu_baseline  the float64 numpy oracle timed on this host on a bounded
                 sample of the same workload (some of the slice's block-steps),
                 scaled to frames/s.
+  audio_front_end, color_correction
+                the audio projection before the denoise and the Lab colour
+                match after the decode, each timed on its own.
 """
 from __future__ import annotations
 
@@ -127,6 +130,36 @@ def audio_front_end(fh, torch, ctx, cfg, B, stream, calls):
             "workload": f"audio projection, batch {B}: 12 x 200 x 768 states -> {cfg.audio_tokens} tokens of "
                         f"width {cfg.dim} (proj1/proj1vf 46080 -> 512, proj2, proj3 512 -> 32 x 1536, "
                         f"LayerNorm)"}
+
+
+def color_correction(fh, torch, stream, calls):
+    """Time the Lab colour match of one slice's decoded frames (33 of 512 x 512,
+    RGB planes) to the 512 x 512 picture, strength 1: HIP events around
+    `calls` calls on the launch stream. Algorithmic bytes: the frames read
+    once and written once, the picture read once (the statistics must see
+    every pixel before any output, so the kernels read the frames twice)."""
+    import synth
+    F, H, W, Hr, Wr = synth.COLOR_SHAPES["slice"]
+    fr, pic = synth.color_inputs(F, H, W, Hr, Wr)
+    Fd, Pd = torch.from_numpy(fr).cuda(), torch.from_numpy(pic).cuda()
+    out = torch.empty_like(Fd)
+    ws = torch.empty(fh.fh_color_match_workspace_bytes(F, H, W, Hr, Wr), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        fh.fh_color_match(Fd, Pd, 1.0, out=out, workspace=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        fh.fh_color_match(Fd, Pd, 1.0, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    alg = 4 * (2 * fr.size + pic.size)
+    gbs = alg / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 2), "calls_timed": calls, "bound": "hbm", "algorithmic_bytes": int(alg),
+            "achieved_GBps": round(gbs, 1), "peak_GBps": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "frames_per_s": round(F * calls / (e0.elapsed_time(e1) * 1e-3), 1),
+            "workload": f"Lab colour match, strength 1: {F} decoded frames of {H}x{W} (float32 RGB planes) "
+                        f"to the {Hr}x{Wr} picture"}
 
 
 def device_info(torch):
@@ -270,6 +303,7 @@ def main():
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
 
     front = audio_front_end(fh, torch, ctx, cfg, B, stream, args.steps) if cfg_name == "slice" else None
+    color = color_correction(fh, torch, stream, args.steps) if cfg_name == "slice" else None
 
     breakdown = None
     if args.breakdown:
@@ -306,6 +340,8 @@ def main():
     }
     if front is not None:
         line["audio_front_end"] = front
+    if color is not None:
+        line["color_correction"] = color
     if breakdown is not None:
         line["kernel_ms_per_slice"] = breakdown
     if not args.no_cpu:

@@ -306,6 +306,39 @@ int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
  * launch fails.                                                             */
 int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t first_group, int64_t n_groups,
                        uint32_t* out, void* stream);
+/* ---- Colour correction after the decode -----------------------------------
+ * The decoded frames' colours matched to the reference picture's (gizai:
+ * flashhead reference page, overview paragraph: Lab means and deviations;
+ * audio-cpp page "SoulX-FlashHead", section "Generate": the correction
+ * strength, 1 by default, 0 disabling it; section "Variant boundaries":
+ * colour processing in F32 on the device). Per frame f and Lab channel c,
+ * with mu, sd the frame's mean and population deviation and mu_r, sd_r the
+ * picture's:  v' = mu_r + (v - mu) sd_r / sd  (mu_r where sd = 0), then
+ * v + strength (v' - v), back to sRGB and clamped to [0, 1]. sRGB is
+ * IEC 61966-2-1's (BT.709 primaries, its transfer curve, the D65 white at
+ * x, y = 0.3127, 0.3290); CIELAB is CIE 15's relative to that white.
+ *
+ * frames: [3][n_frames][height][width] float32 RGB planes in [0, 1] (a video
+ * decoder's channels-first output); picture: [3][ref_height][ref_width]
+ * float32 planes, as the reference page's FlashHead.picture makes it; out:
+ * like frames, and may be frames itself (in place), but may not overlap it
+ * otherwise. Pixel arithmetic is float32, the statistics' sums float64 in a
+ * fixed order (deterministic). Device pointers, 4-byte aligned (16-byte
+ * aligned with height*width and ref_height*ref_width multiples of 4 takes
+ * the vector path), enqueued on `stream`. workspace: caller-owned device
+ * memory of fh_color_match_workspace_bytes, 256-byte aligned, unused when
+ * strength == 0 (then out is a copy of frames, bit for bit).
+ * n_frames == 0 does nothing. FH_EINVAL: sizes out of range (n_frames above
+ * 65534, a side <= 0), a non-finite strength, a null or misaligned pointer,
+ * partial overlap; FH_EWORKSPACE: workspace too small; FH_EHIP: launch error.
+ * fh_color_match_workspace_bytes returns 0 for sizes fh_color_match rejects
+ * or n_frames == 0.                                                          */
+size_t fh_color_match_workspace_bytes(int32_t n_frames, int32_t height, int32_t width, int32_t ref_height,
+                                      int32_t ref_width);
+int fh_color_match(const float* frames, int32_t n_frames, int32_t height, int32_t width, const float* picture,
+                   int32_t ref_height, int32_t ref_width, float strength, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
 

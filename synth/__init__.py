@@ -265,3 +265,47 @@ def audio_states(acfg: AudioProjConfig, batch: int = 1):
     draws from seed 46 + 100 b."""
     return np.stack([normal((acfg.layers, acfg.state_frames, acfg.channels), STATES_SEED + LANE_SEED_STRIDE * b)
                      for b in range(batch)])
+
+
+# ---------------------------------------------------------------- colour match
+COLOR_SEED = 47
+# (frames, height, width, picture height, picture width): the Lite slice decodes
+# 33 frames of 512 x 512 and matches them to the 512 x 512 picture (gizai:flashhead
+# reference page, overview paragraph and FlashHead.picture)
+COLOR_SHAPES = {"toy": (5, 24, 40, 32, 20), "ragged": (3, 7, 9, 5, 11), "slice": (33, 512, 512, 512, 512)}
+
+
+def _color_field(rng, h, w):
+    """A smooth [3, h, w] colour field in about [0.1, 0.9]: a few low-frequency
+    cosines per channel on the unit square, so fields drawn at other sizes
+    from the same generator state look alike."""
+    y, x = np.meshgrid(np.linspace(0.0, 1.0, h), np.linspace(0.0, 1.0, w), indexing="ij")
+    out = np.empty((3, h, w))
+    for c in range(3):
+        f = np.full((h, w), 0.5)
+        for _ in range(4):
+            ky, kx, ph, amp = rng.uniform(0.5, 4.0), rng.uniform(0.5, 4.0), rng.uniform(0, 2 * np.pi), 0.1
+            f += amp * np.cos(2 * np.pi * (ky * y + kx * x) + ph)
+        out[c] = f
+    return out
+
+
+def color_inputs(n_frames, height, width, ref_height, ref_width, seed: int = COLOR_SEED):
+    """Decoded frames [3, F, H, W] and the picture [3, H', W'], float32 sRGB
+    values in [0, 1].
+
+    Recipe (not on the pages; stated once here): the picture is a smooth
+    colour field; frame f is the same field drawn at the frames' size, with a
+    per-frame, per-channel gain U(0.8, 1.2) and offset U(-0.1, 0.1) (a colour
+    cast for the correction to remove) and N(0, 0.02) noise, clipped to
+    [0, 1], so bright and dark corners saturate exactly at 0 and 1.
+    """
+    rng = np.random.default_rng([seed, n_frames, height, width, ref_height, ref_width])
+    state = rng.bit_generator.state
+    pic = np.clip(_color_field(rng, ref_height, ref_width), 0.0, 1.0)
+    rng.bit_generator.state = state
+    base = _color_field(rng, height, width)
+    gain = rng.uniform(0.8, 1.2, (3, n_frames, 1, 1))
+    off = rng.uniform(-0.1, 0.1, (3, n_frames, 1, 1))
+    frames = base[:, None] * gain + off + rng.normal(0.0, 0.02, (3, n_frames, height, width))
+    return np.clip(frames, 0.0, 1.0).astype(np.float32), pic.astype(np.float32)

@@ -349,3 +349,30 @@ def test_debug_runtime_compiles():
     cmd = [b.HIPCC, *b.FLAGS, "-DFH_DEBUG", "-fsyntax-only", os.path.join(b.CSRC, "fh_api.cpp")]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_color_match_workspace_and_argument_errors():
+    W = fh.fh_color_match_workspace_bytes
+    # (F + 1) chunks of 2048 pixels x 6 float64 sums, rounded to 256 bytes, then 9 floats per frame
+    chunks = (512 * 512 + 2047) // 2048
+    assert W(33, 512, 512, 512, 512) == ((34 * chunks * 48 + 255) // 256) * 256 + 33 * 36
+    assert W(5, 24, 40, 7, 300) == ((6 * 2 * 48 + 255) // 256) * 256 + 5 * 36   # the picture sets the chunks
+    assert W(0, 4, 4, 4, 4) == 0 and W(-1, 4, 4, 4, 4) == 0 and W(65535, 4, 4, 4, 4) == 0
+    assert W(1, 0, 4, 4, 4) == 0 and W(1, 4, 4, 4, -4) == 0
+    L, vp = fh.lib, ctypes.c_void_p
+    a, b, o, ws = vp(1 << 40), vp((1 << 40) + (1 << 30)), vp((1 << 40) + (2 << 30)), vp((1 << 40) + (3 << 30))
+    need = W(2, 8, 8, 8, 8)
+    call = lambda fr, F, H, Wd, pic, s, out, w, nb: L.fh_color_match(fr, F, H, Wd, pic, 8, 8, s, out, w, nb, None)
+    assert call(None, 0, 8, 8, None, 1.0, None, None, 0) == fh.FH_OK               # nothing to do
+    assert call(a, -1, 8, 8, b, 1.0, o, ws, need) == fh.FH_EINVAL
+    assert call(a, 2, 0, 8, b, 1.0, o, ws, need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, b, float("nan"), o, ws, need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, b, float("inf"), o, ws, need) == fh.FH_EINVAL
+    assert call(None, 2, 8, 8, b, 1.0, o, ws, need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, None, 1.0, o, ws, need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, b, 1.0, None, ws, need) == fh.FH_EINVAL
+    assert call(vp((1 << 40) + 2), 2, 8, 8, b, 1.0, o, ws, need) == fh.FH_EINVAL     # misaligned frames
+    assert call(a, 2, 8, 8, b, 1.0, vp((1 << 40) + 64), ws, need) == fh.FH_EINVAL   # partial overlap
+    assert call(a, 2, 8, 8, b, 1.0, o, None, need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, b, 1.0, o, vp((1 << 40) + (3 << 30) + 16), need) == fh.FH_EINVAL
+    assert call(a, 2, 8, 8, b, 1.0, o, ws, need - 1) == fh.FH_EWORKSPACE
