@@ -1109,8 +1109,9 @@ namespace {
 bool color_sizes_ok(int32_t F, int32_t H, int32_t W, int32_t Hr, int32_t Wr) {
   if (F < 0 || F > 65534 || H <= 0 || W <= 0 || Hr <= 0 || Wr <= 0) return false;
   const int64_t npix = (int64_t)H * W, nref = (int64_t)Hr * Wr;
-  // one thread per pixel at most, 2^31 workgroups of 256
-  return npix <= (1ll << 32) && nref <= (1ll << 32) && (int64_t)F * npix < (1ll << 38);
+  // the transfer launches up to one thread per frame pixel, and a launch
+  // holds at most 2^32 - 1 work-items
+  return npix <= (1ll << 32) && nref <= (1ll << 32) && (int64_t)F * npix <= (1ll << 32) - 256;
 }
 }  // namespace
 

@@ -329,7 +329,8 @@ int fh_philox4x32_fill(uint64_t seed, uint32_t lane, uint32_t step, uint32_t fir
  * memory of fh_color_match_workspace_bytes, 256-byte aligned, unused when
  * strength == 0 (then out is a copy of frames, bit for bit).
  * n_frames == 0 does nothing. FH_EINVAL: sizes out of range (n_frames above
- * 65534, a side <= 0), a non-finite strength, a null or misaligned pointer,
+ * 65534, a side <= 0, more than 2^32 - 256 frame pixels in all, either
+ * image above 2^32 pixels), a non-finite strength, a null or misaligned pointer,
  * partial overlap; FH_EWORKSPACE: workspace too small; FH_EHIP: launch error.
  * fh_color_match_workspace_bytes returns 0 for sizes fh_color_match rejects
  * or n_frames == 0.                                                          */

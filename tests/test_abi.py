@@ -359,6 +359,7 @@ def test_color_match_workspace_and_argument_errors():
     assert W(5, 24, 40, 7, 300) == ((6 * 2 * 48 + 255) // 256) * 256 + 5 * 36   # the picture sets the chunks
     assert W(0, 4, 4, 4, 4) == 0 and W(-1, 4, 4, 4, 4) == 0 and W(65535, 4, 4, 4, 4) == 0
     assert W(1, 0, 4, 4, 4) == 0 and W(1, 4, 4, 4, -4) == 0
+    assert W(16384, 512, 512, 4, 4) == 0 and W(16383, 512, 512, 4, 4) > 0   # 2^32 - 256 frame pixels at most
     L, vp = fh.lib, ctypes.c_void_p
     a, b, o, ws = vp(1 << 40), vp((1 << 40) + (1 << 30)), vp((1 << 40) + (2 << 30)), vp((1 << 40) + (3 << 30))
     need = W(2, 8, 8, 8, 8)
