@@ -1,8 +1,9 @@
 // Colour correction after the VAE decode: each decoded frame's colours are
-// moved to the reference picture's CIELAB statistics (the gizai:flashhead
-// page's overview: Lab means and deviations; the audio-cpp page's request
-// options: a strength, 1 by default, 0 disabling it; its variant boundaries:
-// colour processing in F32).
+// moved to the reference picture's CIELAB statistics (gizai:flashhead
+// reference page, overview paragraph: Lab means and deviations; audio-cpp
+// page "SoulX-FlashHead", section Generate: a strength, 1 by default, 0
+// disabling it; section Variant boundaries: colour processing on the device
+// in F32).
 //
 // sRGB in [0, 1] -> linear (the sRGB curve) -> XYZ (BT.709 primaries, D65 at
 // the sRGB chromaticity 0.3127, 0.3290) -> CIELAB relative to that white.
