@@ -36,7 +36,7 @@ def run(fh, frames, pic, strength, out=None):
 
 
 @pytest.mark.parametrize("shape", ["toy", "ragged", "slice"])
-@pytest.mark.parametrize("strength", [1.0, 0.35])
+@pytest.mark.parametrize("strength", [1.0, 0.35, 1.5])
 def test_color_match_against_oracle(fh, shape, strength):
     say(f"color_match {shape} {synth.COLOR_SHAPES[shape]} strength {strength}")
     fr, pic = synth.color_inputs(*synth.COLOR_SHAPES[shape])
