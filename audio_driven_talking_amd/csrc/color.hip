@@ -196,8 +196,13 @@ __device__ void image_stats(const double* partial, int nchunks, int img, int64_t
   __syncthreads();  // red is reused
 }
 
+// A channel whose deviation is below this many Lab units counts as flat: on
+// a grey frame a* and b* hold only rounding noise (about 1e-5 in float32),
+// which sd_ref / sd would turn into arbitrary chroma.
+constexpr double FLAT_SD = 1e-3;
+
 // coef[f][9]: per Lab channel the frame's mean, the picture's mean and the
-// scale sd_ref / sd (0 where sd = 0). One workgroup of 256 per frame; each
+// scale sd_ref / sd (0 where sd < FLAT_SD). One workgroup of 256 per frame; each
 // also reduces the picture's partials.
 __global__ __launch_bounds__(256) void color_finalize_kernel(const float* __restrict__ frames, int64_t npix,
                                                              const float* __restrict__ pic, int64_t npix_ref,
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(256) void color_finalize_kernel(const float* __rest
     for (int c = 0; c < 3; ++c) {
       coef[f * 9 + c] = (float)mu[c];
       coef[f * 9 + 3 + c] = (float)mur[c];
-      coef[f * 9 + 6 + c] = sd[c] > 0.0 ? (float)(sdr[c] / sd[c]) : 0.0f;
+      coef[f * 9 + 6 + c] = sd[c] >= FLAT_SD ? (float)(sdr[c] / sd[c]) : 0.0f;
     }
 }
 

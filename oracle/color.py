@@ -20,21 +20,29 @@ READINGS (the plainest ones the rest supports):
      deviation (population) over the frame's pixels, and the same over the
      picture;
   C3 matching moves each channel to the picture's statistics,
-     v' = mu_ref + (v - mu) * sd_ref / sd   (v' = mu_ref where sd = 0);
+     v' = mu_ref + (v - mu) * sd_ref / sd   (v' = mu_ref where sd = 0, C7);
   C4 the strength s blends in Lab: v'' = v + s (v' - v) (s = 0 leaves the
      frame as it was, s = 1 is the full match);
   C5 back to sRGB through the inverse transforms, clamped to [0, 1];
   C6 one white for both the RGB -> XYZ matrix and the Lab reference: D65 at
      the chromaticity the sRGB standard gives (0.3127, 0.3290), so sRGB white
      is exactly L* = 100, a* = b* = 0 (CIE's tabulated D65 differs in the
-     fourth decimal of X and Z, which moves Lab values by under 0.01).
+     fourth decimal of X and Z, which moves Lab values by under 0.01);
+  C7 a channel whose deviation is below FLAT_SD = 1e-3 Lab units counts as
+     flat (C3's sd = 0 rule): on a grey frame (R = G = B) a* and b* carry only
+     rounding noise (about 1e-14 here, 1e-5 in float32), which sd_ref / sd
+     would blow up into arbitrary chroma; a thousandth of a Lab unit is far
+     below anything visible (one RGB24 level is about 0.4 L* units).
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["RGB_TO_XYZ", "WHITE", "srgb_to_linear", "linear_to_srgb", "rgb_to_lab", "lab_to_rgb",
+__all__ = ["FLAT_SD", "RGB_TO_XYZ", "WHITE", "srgb_to_linear", "linear_to_srgb", "rgb_to_lab", "lab_to_rgb",
            "lab_stats", "match_lab", "color_match"]
+
+# C7: deviations below this (Lab units) count as a flat channel
+FLAT_SD = 1e-3
 
 # BT.709 primaries and the D65 white point (xy chromaticities)
 _PRIMARIES = np.array([[0.64, 0.33], [0.30, 0.60], [0.15, 0.06]])
@@ -107,8 +115,9 @@ def lab_stats(lab):
 
 
 def match_lab(lab, mu, sd, mu_ref, sd_ref, strength):
-    """C3 and C4 on one frame's Lab values."""
-    scale = np.divide(sd_ref, sd, out=np.zeros(3), where=sd > 0)
+    """C3 and C4 on one frame's Lab values (C7: a channel with sd below FLAT_SD
+    is flat and takes mu_ref)."""
+    scale = np.divide(sd_ref, sd, out=np.zeros(3), where=sd >= FLAT_SD)
     matched = mu_ref + (lab - mu) * scale
     return lab + strength * (matched - lab)
 

@@ -82,6 +82,21 @@ def test_flat_black_and_one_pixel_picture(fh):
     np.testing.assert_allclose(got.reshape(3, -1), np.repeat([[0.9], [0.1], [0.4]], got[0].size, 1), atol=TOL_COLOR)
 
 
+def test_grey_frames_take_the_picture_chroma(fh):
+    """A grey frame's a* and b* deviations are rounding noise (~1e-5 in
+    float32, ~1e-14 in the oracle): both sides treat them as flat (below 1e-3
+    Lab units), so they agree to the bar instead of amplifying different noise."""
+    fr, pic = synth.color_inputs(3, 16, 12, 8, 8)
+    fr[1] = fr[0]
+    fr[2] = fr[0]                               # R = G = B in every frame
+    for s in (1.0, 0.5):
+        got = run(fh, fr, pic, s).cpu().numpy()
+        want = C.color_match(fr.astype(np.float64), pic.astype(np.float64), s)
+        err = np.abs(got - want).max()
+        say(f"  grey frames strength {s}: max abs err {err:.3e}")
+        assert err <= TOL_COLOR
+
+
 def test_scalar_path_on_misaligned_planes(fh):
     """Planes that start off a 16-byte boundary take the one-pixel path; it
     matches the oracle to the same bar."""

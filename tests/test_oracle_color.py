@@ -84,6 +84,29 @@ def test_flat_frame_in_color_match_takes_the_picture_mean_colour():
                                atol=1e-9)
 
 
+def test_grey_frame_takes_the_picture_chroma():
+    """C7: on a grey frame (R = G = B, greys varying) a* and b* hold only
+    rounding noise; they count as flat and take the picture's mean chroma,
+    while L* is matched as usual. Without the threshold sd_ref / sd amplifies
+    the noise into arbitrary chroma."""
+    rng = np.random.default_rng(5)
+    pic = rng.uniform(0.2, 0.8, (3, 9, 7))
+    g = rng.uniform(0.1, 0.9, (1, 2, 16, 12))
+    frames = np.repeat(g, 3, axis=0)
+    out = C.color_match(frames, pic, 1.0)
+    ref = C.rgb_to_lab(np.moveaxis(pic, 0, -1)).reshape(-1, 3)
+    for f in range(2):
+        lab = C.rgb_to_lab(np.moveaxis(out[:, f], 0, -1)).reshape(-1, 3)
+        clipped = np.any((out[:, f] <= 0) | (out[:, f] >= 1), axis=0).reshape(-1)
+        np.testing.assert_allclose(lab[~clipped, 1:], np.tile(ref.mean(axis=0)[1:], ((~clipped).sum(), 1)),
+                                   atol=1e-6)
+        src = C.rgb_to_lab(np.moveaxis(frames[:, f], 0, -1)).reshape(-1, 3)
+        assert np.abs(src[:, 1:]).max() < 1e-9 and src[:, 0].std() > 1.0   # grey in, real L* spread
+    # the decision sits far from the noise on either side
+    sd = C.lab_stats(C.rgb_to_lab(np.moveaxis(frames[:, 0], 0, -1)))[1]
+    assert sd[1] < 1e-9 < C.FLAT_SD < 1.0 < sd[0]
+
+
 def test_zero_strength_returns_the_frames():
     rng = np.random.default_rng(2)
     frames, pic = rng.random((3, 2, 5, 6)), rng.random((3, 7, 4))
