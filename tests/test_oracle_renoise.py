@@ -179,3 +179,18 @@ def test_philox_is_ten_keyed_rounds():
     one = R.philox4x32(np.array([[1, 2, 3, 4]], np.uint64), np.array([5, 6], np.uint64), rounds=1)[0]
     p0, p1 = 0xD2511F53 * 1, 0xCD9E8D57 * 3
     assert list(one) == [(p1 >> 32) ^ 2 ^ 5, p1 & 0xFFFFFFFF, (p0 >> 32) ^ 4 ^ 6, p0 & 0xFFFFFFFF]
+
+
+def test_philox_matches_the_published_known_answer_vectors():
+    """The generator equals Random123's published Philox-4x32-10 known-answer
+    vectors (tests/golden/philox4x32_10_kat.txt): all-zero and all-ones
+    counter/key, and the digits-of-pi case."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox4x32_10_kat.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        v = [int(t, 16) for t in r]
+        ctr, key, want = v[0:4], v[4:6], v[6:10]
+        got = R.philox4x32(np.array([ctr], dtype=np.uint32), np.array(key, dtype=np.uint32))
+        assert [int(x) for x in np.asarray(got).ravel()] == want
