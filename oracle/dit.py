@@ -28,14 +28,20 @@ cross-attention; q/k RMSNorm over the full width; 3-D rotary on adjacent
 dimension pairs; tanh-GELU FFN; sinusoidal timestep embedding through a
 two-layer SiLU MLP, projected to six modulation rows per block.
 
-Arithmetic is float64 throughout; bf16 matrices arrive as exact float values.
+Arithmetic is float64 throughout by default; bf16 matrices arrive as exact
+float values. ``working_dtype(np.float32)`` runs the same statements in
+float32 (the plain fp32 CPU model timed as a baseline); tests pin it to the
+float64 path on small inputs.
 """
 from __future__ import annotations
+
+import contextlib
+import math
 
 import numpy as np
 
 __all__ = [
-    "linear", "silu", "sinusoid", "time_embedding", "layer_norm", "modulate",
+    "working_dtype", "linear", "silu", "sinusoid", "time_embedding", "layer_norm", "modulate",
     "rms_norm", "gelu_tanh", "token_positions", "rope_pair_split", "rope_angles",
     "apply_rope", "softmax", "attention", "split_heads", "merge_heads",
     "self_attention", "audio_kv", "cross_attention", "dit_block",
@@ -44,8 +50,23 @@ __all__ = [
 ]
 
 
+_WORK = np.dtype(np.float64)
+
+
+@contextlib.contextmanager
+def working_dtype(dtype):
+    """Run the oracle's arithmetic in `dtype` (float64 outside this scope)."""
+    global _WORK
+    old, _WORK = _WORK, np.dtype(dtype)
+    try:
+        yield
+    finally:
+        _WORK = old
+
+
 def to64(a):
-    return np.asarray(a, dtype=np.float64)
+    """a as an array of the working dtype (float64 unless working_dtype says otherwise)."""
+    return np.asarray(a, dtype=_WORK)
 
 
 # ----------------------------------------------------------------------------
@@ -68,7 +89,7 @@ def gelu_tanh(z):
     """READING (the FFN activation is not on the pages): tanh-approximated GELU,
     0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
     z = to64(z)
-    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
 
 
 def layer_norm(x, eps, g=None, b=None):
@@ -178,8 +199,8 @@ def apply_rope(x, ang):
     (a, b) -> (a cos - b sin, a sin + b cos)."""
     x = to64(x)
     a, b = x[..., 0::2], x[..., 1::2]
-    c = np.cos(ang)[None, :, None, :]
-    s = np.sin(ang)[None, :, None, :]
+    c = to64(np.cos(ang))[None, :, None, :]
+    s = to64(np.sin(ang))[None, :, None, :]
     out = np.empty_like(x)
     out[..., 0::2] = a * c - b * s
     out[..., 1::2] = a * s + b * c
@@ -193,7 +214,7 @@ def attention(q, k, v):
     """softmax(q k^T / sqrt(dh)) v per (batch, head); q [B,nh,Nq,dh], k/v [B,nh,Nk,dh].
     The full score matrix, no mask (READING: a slice is denoised jointly)."""
     q, k, v = to64(q), to64(k), to64(v)
-    s = q @ np.swapaxes(k, -1, -2) / np.sqrt(q.shape[-1])
+    s = q @ np.swapaxes(k, -1, -2) / math.sqrt(q.shape[-1])
     return softmax(s, axis=-1) @ v
 
 

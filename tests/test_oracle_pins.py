@@ -413,3 +413,30 @@ def test_rel_err_excludes_motion_frames():
     g[:, :, 0] += 5.0
     assert O.rel_err(g, r, motion_frames=1) == 0.0
     assert O.rel_err(g, r) == 5.0
+
+
+def test_float32_working_dtype_follows_the_float64_path():
+    """working_dtype(np.float32) (the fp32 CPU baseline) runs every statement in
+    float32 -- no silent promotion back to float64 -- and agrees with the
+    float64 path to float32 rounding on a small slice and on one block of the
+    real width. The default outside the scope stays float64."""
+    cfg, W, noise, mot, a = _sampler_case()
+    sig = [1.0, 0.5, 0.0]
+    ref = O.denoise_slice(noise, mot, a, sig, W, cfg)
+    with O.working_dtype(np.float32):
+        got = O.denoise_slice(noise, mot, a, sig, W, cfg)
+        v = O.dit_flow(O.pin_motion(noise, mot), 1.0, a, W, cfg)
+    assert got.dtype == np.float32 and v.dtype == np.float32
+    assert O.rel_err(got, ref, cfg.motion_frames) < 1e-5
+    assert O.denoise_slice(noise, mot, a, sig, W, cfg).dtype == np.float64
+    # one block at width 256 with 2 heads of 128 (the toy DiT's block)
+    tc = synth.CONFIGS["toy"]
+    Wt = synth.weights_f32(synth.make_weights(tc, blocks=[0]))
+    x = rng.standard_normal((1, tc.tokens, tc.dim))
+    e = rng.standard_normal((1, tc.dim))
+    aud = rng.standard_normal((1, tc.audio_tokens, tc.dim))
+    want = O.dit_block_from_temb(x, e, aud, Wt, 0, tc)
+    with O.working_dtype(np.float32):
+        have = O.dit_block_from_temb(x, e, aud, Wt, 0, tc)
+    assert have.dtype == np.float32
+    assert O.rel_err(have - x, want - x) < 1e-5
