@@ -83,6 +83,30 @@ def test_toy_slice(fh):
     np.testing.assert_array_equal(got3, got)          # deterministic
 
 
+def test_graph_cache_eviction_while_graphs_run(fh):
+    """Eleven slices on eleven new sets of buffers with no synchronisation
+    between the calls: every call captures a graph, and from the ninth on the
+    oldest cached graph is evicted while it may still be running on the
+    stream. Every output must equal the synchronised single call, bitwise."""
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.TOY_SIGMAS)
+    want = m.slice(lat, mot, aud, sig)
+    fh.fh_set_option(m.ctx, fh.FH_OPT_GRAPH, 1)
+    bufs = []
+    say("11 slices on new pointers, no sync between them")
+    for _ in range(11):
+        L, Mo, A = dev(lat), dev(mot), dev(aud)
+        o = torch.full_like(L, float("nan"))
+        fh.fh_dit_denoise_slice(m.ctx, m.w, L, Mo, A, sig, o, m.ws)
+        bufs.append((L, Mo, A, o))
+    torch.cuda.synchronize()
+    for i, (_, _, _, o) in enumerate(bufs):
+        np.testing.assert_array_equal(o.cpu().numpy(), want, err_msg=f"call {i}")
+
+
 def test_toy_multi_step_and_edge_cases(fh):
     cfg = synth.CONFIGS["toy"]
     W = synth.make_weights(cfg)
@@ -359,6 +383,16 @@ TOL_MX = 5e-2
 # 5.8 % RMS, 5.4 % in the max norm, on the full-width block). The max-norm
 # ratio tracks the RMS ratio for these near-Gaussian errors; margin about 1.7.
 TOL_FP8 = 1e-1
+# Full 30-block, 4-step slices average the block-level code flips over 120
+# block-steps and end on the head's small update: measured on MI355X 6.2e-3
+# against the MX-FP8 oracle (slice_b1_fp8ffn) and 1.07-1.17e-2 against the
+# exact oracle (FP8 FFN, and FFN + QKV + self-attention; batch 1, 3 and
+# 768x768, lane by lane). The kernels are deterministic, so these numbers
+# move only when the code changes the order or place of a rounding; the
+# bars keep a margin of about 2 over them, so a real regression (a wrong
+# scale, a dropped block, a layout slip: >= 1/64 of a product) still fails.
+TOL_FP8_SLICE_MX = 1.5e-2
+TOL_FP8_SLICE = 2.5e-2
 
 
 def _scales_to_rows(sc, rows, K):
@@ -499,7 +533,7 @@ def test_fp8_ffn_block(fh):
     assert err_q <= TOL_MX and err <= TOL_FP8
 
 
-@pytest.mark.parametrize("case,bar", [("slice_b1_fp8ffn", TOL_MX), ("slice_b1", TOL_FP8)])
+@pytest.mark.parametrize("case,bar", [("slice_b1_fp8ffn", TOL_FP8_SLICE_MX), ("slice_b1", TOL_FP8_SLICE)])
 def test_fp8_ffn_full_slice(fh, case, bar):
     path = os.path.join(GOLDEN, case + ".npz")
     if not os.path.exists(path):
@@ -828,7 +862,7 @@ def test_other_precisions_on_stored_full_slices(fh, precision, case):
         m = _fp8_model(fh, cfg, W, B)
     else:
         m = Model(fh, cfg, W, B, precision=fh.FH_PREC_FP32)
-    bar = TOL_F32 if precision == "fp32" else TOL_FP8
+    bar = TOL_F32 if precision == "fp32" else TOL_FP8_SLICE
     lat, mot, aud = synth.slice_inputs(cfg, B)
     say(f"{case}: full slice B={B}, {precision}")
     got = m.slice(lat, mot, aud, [float(s) for s in g["sigmas"]])
