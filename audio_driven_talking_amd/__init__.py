@@ -26,7 +26,7 @@ FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER, FH_OPT_PRECISION = 1, 2, 3, 4
 FH_SAMPLER_EULER, FH_SAMPLER_RENOISE = 0, 1
 FH_PREC_BF16, FH_PREC_FP8_FFN, FH_PREC_FP32, FH_PREC_FP8_ATTN = 0, 1, 2, 3
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn",
-                  "cross_attn", "layernorm", "rmsnorm_rope"]
+                  "cross_attn", "layernorm", "rmsnorm_rope", "audio_kv"]
 FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}
 
 # every symbol include/fh.h declares
@@ -36,7 +36,8 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
            "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
            "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
-           "fh_color_match_workspace_bytes", "fh_color_match", "fh_kernel_time", "fh_last_error", "fh_status_str"]
+           "fh_color_match_workspace_bytes", "fh_color_match", "fh_kernel_time", "fh_shader_clock",
+           "fh_last_error", "fh_status_str"]
 
 
 class fh_config(ctypes.Structure):
@@ -99,6 +100,7 @@ def _load():
         "fh_color_match_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "fh_color_match": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp, sz, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+        "fh_shader_clock": (i32, [vp, ctypes.c_size_t, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
         "fh_status_str": (ctypes.c_char_p, [i32]),
     }
@@ -411,6 +413,19 @@ def fh_kernel_time(ctx):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(ctx, lib.fh_kernel_time(ctx, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def fh_shader_clock(n_wg=1024, iters=20000, stream=None):
+    """Median shader clock (MHz) of n_wg workgroups running back-to-back bf16
+    MFMAs (a measurement aid; waits for the probe)."""
+    import torch
+    buf = torch.empty(32 * n_wg, dtype=torch.uint8, device="cuda")
+    mhz = ctypes.c_double()
+    st = lib.fh_shader_clock(ctypes.c_void_p(buf.data_ptr()), buf.numel(), int(n_wg), int(iters), _stream(stream),
+                             ctypes.byref(mhz))
+    if st != FH_OK:
+        raise FHError(st, f"fh_shader_clock: {fh_status_str(st)}")
+    return mhz.value
 
 
 def fh_last_error(ctx):

@@ -37,7 +37,22 @@ struct GraphEntry {
   std::vector<uint64_t> key;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  // recorded on the caller's stream after every launch of exec: an exec may
+  // still run when it is evicted or the context is destroyed, so those wait
+  // on this event before destroying it
+  hipEvent_t done = nullptr;
 };
+
+// wait until the last launch of a cached graph has finished, then free it
+void release_graph(GraphEntry& ge) {
+  if (ge.done) {
+    hipEventSynchronize(ge.done);
+    hipEventDestroy(ge.done);
+  }
+  if (ge.exec) hipGraphExecDestroy(ge.exec);
+  if (ge.graph) hipGraphDestroy(ge.graph);
+  ge = GraphEntry();
+}
 
 struct WS {
   float* x;
@@ -598,15 +613,18 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   FH_HIP(fh::rope_table(ws.rcos, ws.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
   const bool f32 = c->precision == FH_PREC_FP32;
   if (!f32) FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
-  if (!f32 && c->fold_co && g.n_blocks <= fh::MAX_BATCH_TABLE) {
-    int rc = audio_kv_all(c, w, B, ws, s);
-    if (rc) return rc;
-  } else {
-    for (int i = 0; i < g.n_blocks; ++i) {
-      int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
-                                  ws.fvc + i * slot_elems(c, B), s)
-                   : audio_kv(c, w->blk[i], B, ws.kc + i * kslot(c, B), ws.vct + i * vslot(c, B), ws, s);
+  {
+    Timed t(c, FH_K_AUDIO_KV, s);
+    if (!f32 && c->fold_co && g.n_blocks <= fh::MAX_BATCH_TABLE) {
+      int rc = audio_kv_all(c, w, B, ws, s);
       if (rc) return rc;
+    } else {
+      for (int i = 0; i < g.n_blocks; ++i) {
+        int rc = f32 ? audio_kv_f32(c, w->blk[i], B, audio, ws.fkc + i * slot_elems(c, B),
+                                    ws.fvc + i * slot_elems(c, B), s)
+                     : audio_kv(c, w->blk[i], B, ws.kc + i * kslot(c, B), ws.vct + i * vslot(c, B), ws, s);
+        if (rc) return rc;
+      }
     }
   }
   for (int c0 = 0; c0 < n_steps; c0 += GEMV_ROWS) {
@@ -790,9 +808,13 @@ int fh_create(const fh_config* cfg, fh_ctx** out) {
     return FH_ESHAPE;
   if (g.dim != g.n_heads * g.head_dim || g.in_ch != g.out_ch || g.motion_frames >= g.frames)
     return FH_ESHAPE;
+  // n_heads even: the cross-attention query's sums of squares come in column
+  // groups of 64 for some tile shapes (dim / 64 of them), which the kernels
+  // take four at a time. freq_dim <= 2048: the time-embedding GEMV holds up to
+  // 8 rows of its input in 64 KiB of LDS.
   if (g.head_dim != 128 || g.dim % 128 || g.ffn_dim % 128 || g.dim > 2048 || g.in_ch > 64 ||
-      g.in_ch % 16 ||
-      g.freq_dim % 8 || g.freq_dim * 4 > 65536 || (g.height * g.width) % 32 || g.audio_per_frame % 32)
+      g.in_ch % 16 || g.n_heads % 2 ||
+      g.freq_dim % 8 || g.freq_dim > 2048 || (g.height * g.width) % 32 || g.audio_per_frame % 32)
     return FH_EUNSUPPORTED;
   fh_ctx* ctx = new fh_ctx();
   ctx->cfg = g;
@@ -809,10 +831,7 @@ int fh_create(const fh_config* cfg, fh_ctx** out) {
 
 void fh_destroy(fh_ctx* c) {
   if (!c) return;
-  for (auto& ge : c->graphs) {
-    if (ge.exec) hipGraphExecDestroy(ge.exec);
-    if (ge.graph) hipGraphDestroy(ge.graph);
-  }
+  for (auto& ge : c->graphs) release_graph(ge);
   for (auto& e : c->ev_free) { hipEventDestroy(e.first); hipEventDestroy(e.second); }
   for (auto& e : c->ev_pending) { hipEventDestroy(e.first); hipEventDestroy(e.second); }
   if (c->cap_stream) hipStreamDestroy(c->cap_stream);
@@ -952,6 +971,7 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   for (auto& ge : c->graphs)
     if (ge.key == key) {
       FH_HIP(hipGraphLaunch(ge.exec, s));
+      FH_HIP(hipEventRecord(ge.done, s));
       return FH_OK;
     }
   if (!c->cap_stream) FH_HIP(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
@@ -965,19 +985,24 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
     return rc;
   }
   if (ce != hipSuccess) return fail(c, FH_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(ce));
-  hipGraphExec_t exec = nullptr;
-  hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  GraphEntry ge;
+  ge.key = key;
+  ge.graph = graph;
+  hipError_t ie = hipGraphInstantiate(&ge.exec, graph, nullptr, nullptr, 0);
+  if (ie == hipSuccess) ie = hipEventCreateWithFlags(&ge.done, hipEventDisableTiming);
   if (ie != hipSuccess) {
-    hipGraphDestroy(graph);
+    release_graph(ge);
     return fail(c, FH_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(ie));
   }
   if ((int)c->graphs.size() >= MAX_GRAPHS) {
-    hipGraphExecDestroy(c->graphs.front().exec);
-    hipGraphDestroy(c->graphs.front().graph);
+    // the oldest graph may still be running from an earlier call: its event
+    // waits for that launch before the exec is destroyed
+    release_graph(c->graphs.front());
     c->graphs.erase(c->graphs.begin());
   }
-  c->graphs.push_back({key, graph, exec});
-  FH_HIP(hipGraphLaunch(exec, s));
+  c->graphs.push_back(ge);
+  FH_HIP(hipGraphLaunch(ge.exec, s));
+  FH_HIP(hipEventRecord(ge.done, s));
   return FH_OK;
 }
 
@@ -1232,6 +1257,31 @@ int fh_audio_project(fh_ctx* c, const fh_audio_weights* w, int batch, const floa
   if (rc) return rc;
   FH_HIP(fh::layernorm_f32(a.Y, tokens, B * c->La, g.dim, c->La, g.eps, nullptr, nullptr, nullptr, nullptr, 0,
                            w->norm_g, w->norm_b, s));
+  return FH_OK;
+}
+
+int fh_shader_clock(void* dev_buf, size_t bytes, int n_wg, int iters, void* stream, double* mhz) {
+  if (!dev_buf || !mhz || n_wg < 1 || n_wg > 65536 || iters < 1 || iters > (1 << 20) ||
+      bytes < (size_t)32 * n_wg)
+    return FH_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (fh::clock_probe((uint64_t*)dev_buf, n_wg, iters, s) != hipSuccess) return FH_EHIP;
+  std::vector<uint64_t> h((size_t)4 * n_wg);
+  if (hipMemcpyAsync(h.data(), dev_buf, h.size() * 8, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return FH_EHIP;
+  int dev = 0, wall_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wall_khz <= 0)
+    return FH_EHIP;
+  std::vector<double> f;
+  for (int i = 0; i < n_wg; ++i) {
+    const uint64_t dt = h[4 * i + 1] - h[4 * i], dr = h[4 * i + 3] - h[4 * i + 2];
+    if (dr > 0) f.push_back((double)dt / (double)dr * wall_khz / 1000.0);
+  }
+  if (f.empty()) return FH_EHIP;
+  std::sort(f.begin(), f.end());
+  *mhz = f[f.size() / 2];
   return FH_OK;
 }
 

@@ -263,6 +263,8 @@ hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC,
                       int n_motion_tok, hipStream_t s);
 
 hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s);
+// shader-clock probe: n_wg workgroups of MFMA loops, 4 counters each into out
+hipError_t clock_probe(uint64_t* out, int n_wg, int iters, hipStream_t s);
 
 // ---- float32 debug path (FH_PREC_FP32): activations and products in float32 ----
 enum EpiF32 {

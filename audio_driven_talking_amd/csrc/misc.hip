@@ -309,7 +309,61 @@ __global__ void f32_to_bf16_kernel(const float* __restrict__ in, bf16_t* __restr
   if (i < n) out[i] = f2bf(in[i]);
 }
 
+// Clock probe: every wave issues `iters` groups of four independent bf16
+// MFMAs (so the matrix core never waits on a result); wave 0 reads the shader
+// cycle counter and the constant-rate wall clock before and after the
+// workgroup's loops. out[4 wg + {0,1,2,3}] = cycles start, end, wall start,
+// end. The accumulators are stored only when `sink` is set (never by the
+// host), which keeps the MFMAs from being removed.
+__global__ __launch_bounds__(256) void clock_probe_kernel(uint64_t* __restrict__ out, int iters, int sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)(lane + e));
+    b[e] = (__bf16)(0.002f * (float)(lane - e));
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k][r] = 0.f;
+  __syncthreads();
+  uint64_t t0 = 0, r0 = 0;
+  if (threadIdx.x == 0) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  mfma_drain(acc[3]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    out[4 * blockIdx.x] = t0;
+    out[4 * blockIdx.x + 1] = t1;
+    out[4 * blockIdx.x + 2] = r0;
+    out[4 * blockIdx.x + 3] = r1;
+  }
+  if (sink) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v += acc[k][r];
+    reinterpret_cast<float*>(out)[threadIdx.x] = v;
+  }
+}
+
 }  // namespace
+
+hipError_t clock_probe(uint64_t* out, int n_wg, int iters, hipStream_t s) {
+  if (!out || n_wg < 1 || iters < 1) return hipErrorInvalidValue;
+  clock_probe_kernel<<<n_wg, 256, 0, s>>>(out, iters, 0);
+  return hipGetLastError();
+}
 
 hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh, const float* bh, int Co,
                           const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,

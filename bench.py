@@ -12,9 +12,18 @@ Extra objects on the line:
                 two halves): algorithmic FLOPs per launch / its mean duration,
                 timed with HIP events on the launch stream over a second pass
                 of the same K steps.
-  cpu_baseline  the float64 numpy oracle timed on this host on a bounded
-                sample of the same workload (some of the slice's block-steps),
-                scaled to frames/s.
+  hot_mfma_frac the method's FLOPs of every GEMM and attention kernel class
+                (QKV, O, cross-q, cross-out, FFN up/down, self- and
+                cross-attention, the per-slice audio K/V) / the sum of their
+                kernel times / the 2.5 PF bf16 peak; per-class figures under
+                "hot".
+  shader_clock_mhz
+                the clock every CU holds while it runs back-to-back MFMAs.
+  workloads     batch 3 (three streams) and 768x768 (2880 tokens): frames/s,
+                ms per call and their own hot-kernel fractions.
+  cpu_baseline  the fp32 numpy oracle on this host: one real-shape block
+                (1280 tokens, its audio K/V and modulation) three times,
+                median, scaled to the slice's 120 block-steps.
   audio_front_end, color_correction
                 the audio projection before the denoise and the Lab colour
                 match after the decode, each timed on its own.
@@ -65,26 +74,79 @@ def flops_per_slice(cfg, B, n_steps):
         n_steps * cfg.n_blocks * (gemm + attn)
 
 
-def cpu_baseline(cfg, sigmas, budget_s=15.0):
-    """Time the float64 oracle on block-steps of the first step, scale to a slice."""
+# kernel classes of the hot path (GEMMs and attention) and the method's FLOPs
+# of each per slice call
+HOT_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn", "cross_attn",
+               "audio_kv"]
+
+
+def hot_flops_per_class(cfg, B, n_steps):
+    """Algorithmic FLOPs per slice call of each hot kernel class. The folded
+    cross-attention output executes fewer FLOPs than 2 M D D; the method's
+    count is what the rate is quoted on."""
+    N, D, Fd, La = cfg.tokens, cfg.dim, cfg.ffn_dim, cfg.audio_tokens
+    M, bs = B * N, n_steps * cfg.n_blocks
+    keys = La if cfg.cross_full else cfg.audio_per_frame
+    return {"gemm_qkv": bs * 2 * M * D * 3 * D, "gemm_o": bs * 2 * M * D * D, "gemm_cq": bs * 2 * M * D * D,
+            "gemm_co": bs * 2 * M * D * D, "gemm_ffn1": bs * 2 * M * D * Fd, "gemm_ffn2": bs * 2 * M * Fd * D,
+            "attn": bs * 4 * B * N * N * D, "cross_attn": bs * 4 * M * keys * D,
+            "audio_kv": cfg.n_blocks * 2 * B * La * D * 2 * D}
+
+
+def hot_fraction(per_class_ms, flops):
+    """(hot TF/s, fraction of the bf16 peak) from per-slice ms and FLOPs of the classes."""
+    t = sum(per_class_ms[k] for k in flops) * 1e-3
+    f = sum(flops.values())
+    return f / t / 1e12, f / t / 1e12 / PEAK_BF16_TFLOPS
+
+
+def time_classes(fh, ctx, step, torch, classes, passes):
+    """ms per slice call and launches per call of each kernel class: HIP events
+    around its launches over `passes` calls (direct launches)."""
+    out = {}
+    for name in classes:
+        fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, fh.FH_K[name])
+        step()
+        torch.cuda.synchronize()
+        fh.fh_kernel_time(ctx)
+        for _ in range(passes):
+            step()
+        torch.cuda.synchronize()
+        ms, n = fh.fh_kernel_time(ctx)
+        out[name] = (ms / passes, n / passes)
+    fh.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, -1)
+    return out
+
+
+def hot_report(timed, flops):
+    per = {}
+    for k, f in flops.items():
+        ms, n = timed[k]
+        tf = f / (ms * 1e-3) / 1e12
+        per[k] = {"ms_per_call": round(ms, 4), "launches_per_call": round(n, 2), "gflop_per_call": round(f / 1e9, 2),
+                  "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    tf, frac = hot_fraction({k: v[0] for k, v in timed.items()}, flops)
+    return per, round(tf, 1), round(frac, 4), round(sum(timed[k][0] for k in flops), 4)
+
+
+def cpu_baseline(cfg, sigmas, repeats=3):
+    """The fp32 numpy oracle on one real-shape block (1280 tokens: modulation
+    from a time embedding, the block's audio K/V, the block), `repeats` times;
+    the median, times the slice's block-steps, gives the slice time."""
     import threadpoolctl
     import oracle
     import synth
-    W = synth.weights_f32(synth.make_weights(cfg, blocks=list(range(min(cfg.n_blocks, 8)))))
-    lat, mot, aud = synth.slice_inputs(cfg, 1)
-    x0 = oracle.pin_motion(lat, mot)
-    e, e0 = oracle.time_embedding(np.array([sigmas[0]]), W, cfg)
-    ang = oracle.rope_angles(cfg)
-    x = oracle.linear(oracle.patchify(x0), W["patch.w"], W["patch.b"])
-    t0 = time.perf_counter()
-    k = 0
-    while k < min(cfg.n_blocks, 8):
-        x = oracle.dit_block(x, e0, aud, oracle.block_weights(W, k), cfg, ang)
-        k += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    t_block = (time.perf_counter() - t0) / k
-    t_slice = t_block * cfg.n_blocks * (len(sigmas) - 1)
+    W = synth.weights_f32(synth.make_weights(cfg, blocks=[0]))
+    x, e, a = synth.block_inputs(cfg, 1)
+    ts = []
+    with oracle.working_dtype(np.float32):
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            oracle.dit_block_from_temb(x, e, a, W, 0, cfg)
+            ts.append(time.perf_counter() - t0)
+    t_block = sorted(ts)[len(ts) // 2]
+    block_steps = cfg.n_blocks * (len(sigmas) - 1)
+    t_slice = t_block * block_steps
     blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] or [1])
     cpu = "unknown"
@@ -92,12 +154,15 @@ def cpu_baseline(cfg, sigmas, budget_s=15.0):
         cpu = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
+    flops = sum(hot_flops_per_class(cfg, 1, len(sigmas) - 1).values()) / block_steps
     return {"value": FRAMES_PER_SLICE / t_slice, "unit": "frames/s", "cores": int(threads),
             "kind": "oracle", "cpu": cpu,
             "blas": ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in blas})),
-            "sample": f"{k} of the {cfg.n_blocks * (len(sigmas) - 1)} block-steps of one batch-1 "
-                      f"slice (float64 numpy oracle, {t_block:.3f} s per block-step), scaled to the "
-                      f"whole slice"}
+            "block_s_median": round(t_block, 4), "block_s_all": [round(t, 4) for t in ts],
+            "gflops": round(flops / t_block / 1e9, 1),
+            "sample": f"one real-shape block (1280 tokens, width {cfg.dim}, its audio K/V and modulation) run "
+                      f"{repeats} times by the float32 numpy oracle, median {t_block:.3f} s, times the "
+                      f"{block_steps} block-steps of a batch-1 slice"}
 
 
 def audio_front_end(fh, torch, ctx, cfg, B, stream, calls):
@@ -162,6 +227,42 @@ def color_correction(fh, torch, stream, calls):
                         f"to the {Hr}x{Wr} picture"}
 
 
+def other_workload(fh, torch, synth, W, name, stream, steps, hot_passes, no_graph):
+    """frames/s, ms per call and the hot-kernel fraction of another workload of
+    the metric's configuration list (batch 3, 768x768), on the same weights."""
+    cfg_name, B, desc = WORKLOADS[name]
+    cfg = synth.CONFIGS[cfg_name]
+    sig = list(synth.SLICE_SIGMAS)
+    ctx = fh.fh_create(cfg)
+    w = fh.fh_weights_bind(ctx, W)
+    ws = fh.workspace(ctx, B)
+    L, Mo, A = (torch.from_numpy(a).cuda() for a in synth.slice_inputs(cfg, B))
+    out = torch.empty_like(L)
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0 if no_graph else 1)
+
+    def step():
+        fh.fh_dit_denoise_slice(ctx, w, L, Mo, A, sig, out, ws, stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    T = time.perf_counter() - t0
+    total, _ = flops_per_slice(cfg, B, len(sig) - 1)
+    timed = time_classes(fh, ctx, step, torch, HOT_CLASSES, hot_passes)
+    per, tf, frac, ms_hot = hot_report(timed, hot_flops_per_class(cfg, B, len(sig) - 1))
+    res = {"workload": desc, "batch": B, "tokens": cfg.tokens, "steps": steps,
+           "frames_per_s": round(FRAMES_PER_SLICE * B * steps / T, 2), "ms_per_call": round(1e3 * T / steps, 4),
+           "tflops_end_to_end": round(total / (T / steps) / 1e12, 2), "hot_mfma_frac": frac, "hot_tflops": tf,
+           "hot_ms_per_call": ms_hot, "attn": per["attn"], "gemm_ffn2": per["gemm_ffn2"]}
+    del w, ws, L, Mo, A, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def device_info(torch):
     """Name, compute units and L2 size of cuda:0 as the runtime reports them."""
     p = torch.cuda.get_device_properties(0)
@@ -213,6 +314,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the batch-3 and 768x768 workloads and the per-class hot-kernel timing")
+    ap.add_argument("--hot-passes", type=int, default=3, help="slice calls per timed kernel class")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one elementwise copy of 256 MiB (read + write) first; rocprofv3 "
                          "counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes")
@@ -234,7 +338,6 @@ def main():
     W = synth.make_weights(cfg)
     ctx = fh.fh_create(cfg)
     w = fh.fh_weights_bind(ctx, W)
-    del W
     fp8 = args.precision in ("fp8ffn", "fp8attn")
     if fp8:
         fh.fh_weights_quantize_fp8(ctx, w)
@@ -302,6 +405,22 @@ def main():
                           f"{'MX-FP8 e4m3' if fp8 else 'bf16'}, {k_flops / 1e9:.2f} GFLOP per launch)",
                 "avg_us": round(k_avg_s * 1e6, 2), "launches_timed": kn}
 
+    # every GEMM and attention class: the hot-path fraction of the MFMA peak
+    hot = None
+    if not args.no_extra and not fp8:
+        timed = time_classes(fh, ctx, step, torch, [k for k in HOT_CLASSES if k != ROOF_KERNEL], args.hot_passes)
+        timed[ROOF_KERNEL] = (kms / max(args.steps, 1), kn / max(args.steps, 1))
+        hot = hot_report(timed, hot_flops_per_class(cfg, B, n_steps))
+    clock = fh.fh_shader_clock(stream=stream)
+
+    # the other workloads of the metric's configuration list, same weights
+    extra = {}
+    if not args.no_extra and args.workload == "slice" and not fp8 and args.sampler == "euler":
+        for name in ("slice_b3", "slice768"):
+            extra[name] = other_workload(fh, torch, synth, W, name, stream, max(3, args.steps // 2),
+                                         args.hot_passes, args.no_graph)
+    del W
+
     front = audio_front_end(fh, torch, ctx, cfg, B, stream, args.steps) if cfg_name == "slice" else None
     color = color_correction(fh, torch, stream, args.steps) if cfg_name == "slice" else None
 
@@ -337,7 +456,17 @@ def main():
         "mfma_frac_end_to_end": round(total_flops / (T / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tflops_end_to_end": round(total_flops / (T / args.steps) / 1e12, 2),
         "roofline": roofline,
+        "shader_clock_mhz": round(clock, 1),
     }
+    if hot is not None:
+        per, tf, frac, ms_hot = hot
+        line["hot_mfma_frac"] = frac
+        line["hot_tflops"] = tf
+        line["hot"] = {"classes": per, "ms_per_call": ms_hot, "ms_per_call_all_kernels_wall": round(ms, 4),
+                       "peak_tflops": PEAK_BF16_TFLOPS,
+                       "peak_at_measured_clock_tflops": round(PEAK_BF16_TFLOPS * clock / 2400.0, 1)}
+    if extra:
+        line["workloads"] = extra
     if front is not None:
         line["audio_front_end"] = front
     if color is not None:

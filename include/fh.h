@@ -50,8 +50,8 @@ enum { FH_DTYPE_BF16 = 1, FH_DTYPE_F32 = 2 };
 
 /* Sizes of the DiT and of one slice latent. Every dimension is a runtime value
  * (audio-cpp page, "Variant boundaries"). The kernels implement:
- *   head_dim == 128, dim == n_heads * 128, dim % 128 == 0, ffn_dim % 128 == 0,
- *   dim <= 2048, in_ch == out_ch <= 64, freq_dim % 8 == 0, frames*height*width
+ *   head_dim == 128, dim == n_heads * 128, n_heads even, ffn_dim % 128 == 0,
+ *   dim <= 2048, in_ch == out_ch <= 64, freq_dim % 8 == 0, freq_dim <= 2048, frames*height*width
  *   a multiple of 32, height*width a multiple of 32, in_ch a multiple of 16, audio_per_frame a
  *   multiple of 32, 0 <= motion_frames < frames.                                */
 typedef struct fh_config {
@@ -205,10 +205,12 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       a multiple of 64 (FH_EUNSUPPORTED otherwise); the workspace grows
  *       (query fh_workspace_bytes after setting it).                        */
 enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2, FH_PREC_FP8_ATTN = 3 };
+/* Kernel classes of FH_OPT_TIME_KERNEL. FH_K_AUDIO_KV is the once-per-slice
+ * audio keys and values of every block (all of its launches as one sample). */
 enum {
   FH_K_GEMM_QKV = 0, FH_K_GEMM_O = 1, FH_K_GEMM_CQ = 2, FH_K_GEMM_CO = 3, FH_K_GEMM_FFN1 = 4,
   FH_K_GEMM_FFN2 = 5, FH_K_ATTN = 6, FH_K_CROSS_ATTN = 7, FH_K_LAYERNORM = 8, FH_K_RMSNORM_ROPE = 9,
-  FH_K_COUNT = 10
+  FH_K_AUDIO_KV = 10, FH_K_COUNT = 11
 };
 int fh_set_option(fh_ctx* ctx, int option, int value);
 /* Bytes of the device buffer fh_weights_quantize_fp8 fills (0 for a null ctx). */
@@ -342,6 +344,17 @@ int fh_color_match(const float* frames, int32_t n_frames, int32_t height, int32_
 
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
+
+/* Measurement aid (not a step of the method): the shader clock while every
+ * compute unit runs back-to-back bf16 MFMAs, in MHz. Launches n_wg
+ * workgroups of 256 threads, each timing `iters` MFMA groups with the shader
+ * cycle counter against the constant-rate wall clock (hipDeviceAttribute-
+ * WallClockRate), on `stream`, and waits for them. dev_buf: caller-owned
+ * device buffer of at least 32 * n_wg bytes (4 counters per workgroup).
+ * *mhz receives the median over workgroups. FH_EINVAL for null or short
+ * arguments, n_wg outside [1, 65536] or iters outside [1, 1 << 20];
+ * FH_EHIP on runtime errors.                                                 */
+int fh_shader_clock(void* dev_buf, size_t bytes, int n_wg, int iters, void* stream, double* mhz);
 
 /* Human-readable text of the last error on ctx (never NULL), and of a code.  */
 const char* fh_last_error(const fh_ctx* ctx);

@@ -49,6 +49,8 @@ def cfg_dict(name="slice", **kw):
     (dict(n_blocks=0), fh.FH_ESHAPE),
     (dict(eps=float("nan")), fh.FH_ESHAPE),
     (dict(cross_full=2), fh.FH_ESHAPE),
+    (dict(n_heads=3, dim=384), fh.FH_EUNSUPPORTED),     # odd head count: query sums in groups of 4
+    (dict(freq_dim=2056), fh.FH_EUNSUPPORTED),          # 8 GEMV rows of it must fit 64 KiB of LDS
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(fh.FHError) as e:
@@ -59,6 +61,8 @@ def test_create_rejects(kw, status):
 def test_create_accepts_workloads():
     for name in synth.CONFIGS:
         fh.fh_create(synth.CONFIGS[name])
+    fh.fh_create(cfg_dict(freq_dim=2048))
+    fh.fh_create(cfg_dict(n_heads=2, dim=256))
     fh.fh_create(synth.CONFIGS["slice"].replace(cross_full=True))
 
 
@@ -152,7 +156,7 @@ def test_call_argument_errors_before_any_launch():
     assert L.fh_dit_block_forward(ctx, None, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, 99, 0) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, fh.FH_K["attn"]) == fh.FH_OK
-    assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, 10) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_TIME_KERNEL, len(fh.KERNEL_CLASSES)) == fh.FH_EINVAL
     fh.lib.fh_weights_release(w)
     assert fh.fh_status_str(fh.FH_EWORKSPACE).startswith("workspace")
 
@@ -377,3 +381,15 @@ def test_color_match_workspace_and_argument_errors():
     assert call(a, 2, 8, 8, b, 1.0, o, None, need) == fh.FH_EINVAL
     assert call(a, 2, 8, 8, b, 1.0, o, vp((1 << 40) + (3 << 30) + 16), need) == fh.FH_EINVAL
     assert call(a, 2, 8, 8, b, 1.0, o, ws, need - 1) == fh.FH_EWORKSPACE
+
+
+def test_shader_clock_argument_errors():
+    """The clock probe rejects null or short buffers and out-of-range sizes
+    before any launch."""
+    L, fake, mhz = fh.lib, ctypes.c_void_p(1 << 40), ctypes.c_double()
+    assert L.fh_shader_clock(None, 1 << 20, 16, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
+    assert L.fh_shader_clock(fake, 1 << 20, 16, 100, None, None) == fh.FH_EINVAL
+    assert L.fh_shader_clock(fake, 32 * 16 - 1, 16, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
+    assert L.fh_shader_clock(fake, 1 << 30, 0, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
+    assert L.fh_shader_clock(fake, 1 << 30, 65537, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
+    assert L.fh_shader_clock(fake, 1 << 30, 16, 0, None, ctypes.byref(mhz)) == fh.FH_EINVAL

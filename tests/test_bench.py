@@ -60,3 +60,21 @@ def test_committed_counter_summaries_match_the_kernel_code():
         if d.get("code_sha256") != h:
             pytest.xfail(f"profiles/{name} predates the current gemm.hip code: re-take the counters")
         assert d["hbm_bytes_per_launch"] > d["algorithmic_bytes_per_launch"] > 0
+
+
+def test_hot_class_flops_add_up():
+    """The per-class FLOPs of the hot kernels add up to the slice's GEMM and
+    attention FLOPs plus the cross-attention and the per-slice audio K/V; the
+    hot fraction divides them by the summed class times."""
+    cfg = synth.CONFIGS["slice"]
+    per = bench.hot_flops_per_class(cfg, 1, 4)
+    assert set(per) == set(bench.HOT_CLASSES)
+    total, hot = bench.flops_per_slice(cfg, 1, 4)
+    D, N, M = cfg.dim, cfg.tokens, cfg.tokens
+    cross = 4 * 30 * 4 * M * cfg.audio_per_frame * D
+    audio_kv = 30 * 2 * cfg.audio_tokens * D * 2 * D
+    assert sum(per.values()) == hot + cross + audio_kv
+    assert per["attn"] == 4 * 30 * 4 * N * N * D
+    tf, frac = bench.hot_fraction({k: 1.0 for k in per}, per)   # 1 ms per class
+    assert abs(tf - sum(per.values()) / (len(per) * 1e-3) / 1e12) < 1e-6
+    assert abs(frac - tf / bench.PEAK_BF16_TFLOPS) < 1e-12
