@@ -36,7 +36,8 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
            "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
            "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
-           "fh_color_match_workspace_bytes", "fh_color_match", "fh_kernel_time", "fh_shader_clock",
+           "fh_color_match_workspace_bytes", "fh_color_match", "fh_color_match_noalloc",
+           "fh_color_match_noalloc_max_bytes", "fh_kernel_time", "fh_shader_clock",
            "fh_last_error", "fh_status_str"]
 
 
@@ -99,6 +100,8 @@ def _load():
                                      ctypes.c_int64, vp, vp]),
         "fh_color_match_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "fh_color_match": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp, sz, vp]),
+        "fh_color_match_noalloc": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp]),
+        "fh_color_match_noalloc_max_bytes": (sz, []),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "fh_shader_clock": (i32, [vp, ctypes.c_size_t, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
@@ -349,6 +352,27 @@ def fh_color_match(frames, picture, strength=1.0, out=None, workspace=None, stre
                             ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream))
     if st != FH_OK:
         raise FHError(st, f"fh_color_match: {fh_status_str(st)}")
+    return out
+
+
+def fh_color_match_noalloc(frames, picture, strength=1.0, out=None, stream=None):
+    """fh_color_match with its statistics in the library's static device
+    scratch: no workspace argument (see include/fh.h). Returns out."""
+    import torch
+    for name, t, nd in (("frames", frames, 4), ("picture", picture, 3)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.dim() != nd \
+                or not t.is_contiguous() or t.shape[0] != 3:
+            raise ValueError(f"{name} must be a contiguous float32 device tensor [3, ...] of {nd} dims")
+    _, F, H, W = frames.shape
+    _, Hr, Wr = picture.shape
+    if out is None:
+        out = torch.empty_like(frames)
+    elif out.shape != frames.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like frames")
+    st = lib.fh_color_match_noalloc(ctypes.c_void_p(frames.data_ptr()), F, H, W, ctypes.c_void_p(picture.data_ptr()),
+                                    Hr, Wr, float(strength), ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_color_match_noalloc: {fh_status_str(st)}")
     return out
 
 

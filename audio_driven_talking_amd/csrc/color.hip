@@ -16,6 +16,8 @@
 // the chunks in index order to the transfer coefficients, and the per-pixel
 // transfer in float32. The frames are read twice and written once; the sRGB
 // curve's powers dominate the arithmetic.
+#include <mutex>
+
 #include "fh_common.h"
 #include "fh_kernels.h"
 
@@ -358,6 +360,40 @@ hipError_t color_match(const float* frames, int F, int64_t npix, const float* pi
   else
     color_apply_kernel<false><<<agrid, 256, 0, s>>>(frames, npix, F, coef, strength, T, out);
   return hipGetLastError();
+}
+
+
+// ---- statistics scratch in a static device array, for callers that cannot
+// allocate (fh_color_match_noalloc). Every GPU the library runs on holds its
+// own copy of the array until the process ends. In host code `scratch` names
+// a host-side stand-in, not device memory: the device address of each GPU's
+// copy comes from hipGetSymbolAddress, once per device, and only that address
+// is ever passed to a kernel.
+namespace {
+constexpr size_t COLOR_SCRATCH_BYTES = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[COLOR_SCRATCH_BYTES];
+constexpr int MAX_SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[MAX_SCRATCH_DEVICES] = {};
+}  // namespace
+
+size_t color_scratch_bytes() { return COLOR_SCRATCH_BYTES; }
+
+hipError_t color_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace fh

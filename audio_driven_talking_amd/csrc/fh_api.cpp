@@ -1168,6 +1168,32 @@ int fh_color_match(const float* frames, int32_t n_frames, int32_t height, int32_
   return e == hipSuccess ? FH_OK : FH_EHIP;
 }
 
+int fh_color_match_noalloc(const float* frames, int32_t n_frames, int32_t height, int32_t width,
+                           const float* picture, int32_t ref_height, int32_t ref_width, float strength, float* out,
+                           void* stream) {
+  if (!color_sizes_ok(n_frames, height, width, ref_height, ref_width) || !std::isfinite(strength)) return FH_EINVAL;
+  if (n_frames == 0) return FH_OK;
+  if (!frames || !picture || !out || ((uintptr_t)frames & 3) || ((uintptr_t)picture & 3) || ((uintptr_t)out & 3))
+    return FH_EINVAL;
+  const int64_t npix = (int64_t)height * width, nref = (int64_t)ref_height * ref_width;
+  const size_t bytes = (size_t)n_frames * npix * 3 * sizeof(float);
+  if (out != frames && (const char*)out < (const char*)frames + bytes && (const char*)frames < (const char*)out + bytes)
+    return FH_EINVAL;  // partial overlap
+  const hipStream_t s = (hipStream_t)stream;
+  if (strength == 0.0f) {  // correction disabled: the frames unchanged
+    if (out == frames) return FH_OK;
+    return hipMemcpyAsync(out, frames, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess ? FH_OK : FH_EHIP;
+  }
+  // the statistics of this call must fit the static scratch
+  if (fh::color_match_workspace(n_frames, npix, nref) > fh::color_scratch_bytes()) return FH_EWORKSPACE;
+  void* scratch = nullptr;
+  if (fh::color_scratch(&scratch) != hipSuccess) return FH_EHIP;
+  const hipError_t e = fh::color_match(frames, n_frames, npix, picture, nref, strength, out, scratch, s);
+  return e == hipSuccess ? FH_OK : FH_EHIP;
+}
+
+size_t fh_color_match_noalloc_max_bytes(void) { return fh::color_scratch_bytes(); }
+
 int fh_audio_weight_count(const fh_ctx* c, const fh_audio_config* a) {
   if (!c || !a || check_audio_cfg(nullptr, a) != FH_OK) return 0;
   return (int)audio_specs(c, *a).size();

@@ -312,6 +312,10 @@ hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh,
 // workspace (color_match_workspace bytes, 256-byte aligned) holds the partial
 // sums and the per-frame coefficients. Needs 1 <= F <= 65534, npix, npix_ref >= 1.
 size_t color_match_workspace(int F, int64_t npix, int64_t npix_ref);
+// the static statistics scratch of the allocation-free colour match: its size,
+// and the current device's address of it (looked up once per device)
+size_t color_scratch_bytes();
+hipError_t color_scratch(void** ptr);
 hipError_t color_match(const float* frames, int F, int64_t npix, const float* pic, int64_t npix_ref, float strength,
                        float* out, void* ws, hipStream_t s);
 

@@ -342,6 +342,26 @@ int fh_color_match(const float* frames, int32_t n_frames, int32_t height, int32_
                    int32_t ref_height, int32_t ref_width, float strength, float* out, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* fh_color_match without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The same kernels and results, bit for
+ * bit, as fh_color_match; the statistics' partial sums live in a static
+ * device array of fh_color_match_noalloc_max_bytes() bytes (4 MiB) that each
+ * GPU holds until the process ends. The call allocates nothing. Every call
+ * on one GPU shares that array, and a call overwrites every element it reads
+ * before reading it, so nothing needs clearing; calls whose work overlaps on
+ * one GPU (two streams, or a call and a replay of a graph that captured one)
+ * race on it and must be ordered by the caller. Arguments and errors as
+ * fh_color_match, except: FH_EWORKSPACE when the call's statistics need more
+ * than the array holds (fh_color_match_workspace_bytes of the sizes above
+ * fh_color_match_noalloc_max_bytes(): for example 33 frames of 1920 x 1080
+ * fit, 33 frames of 3840 x 2160 do not); FH_EHIP if the array's device
+ * address cannot be looked up.                                               */
+int fh_color_match_noalloc(const float* frames, int32_t n_frames, int32_t height, int32_t width,
+                           const float* picture, int32_t ref_height, int32_t ref_width, float strength, float* out,
+                           void* stream);
+size_t fh_color_match_noalloc_max_bytes(void);
+
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
 
