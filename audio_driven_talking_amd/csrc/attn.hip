@@ -652,8 +652,8 @@ hipError_t flash_attn(const bf16_t* q, int ldq, const bf16_t* k, int ldk, const 
   if (N % 32 || ldq % 8 || ldk % 8 || ldo % 4) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
-  flash_attn_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, ldq, k, ldk, vt, o, ldo, N, n_heads * HD,
-                                                       scale_log2, n_qt, n_heads, n_wg);
+  launch_timed(flash_attn_kernel, dim3((n_wg + 7) / 8 * 8), dim3(256), s, q, ldq, k, ldk, vt, o, ldo, N,
+               n_heads * HD, scale_log2, n_qt, n_heads, n_wg);
   return hipGetLastError();
 }
 
@@ -664,8 +664,8 @@ hipError_t flash_attn_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k, 
   if (N % 64 || ldq % 32 || ldq < n_heads * HD || ldo % 4 || !qs || !ks || !vts) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int n_qt = (N + AQ - 1) / AQ, n_wg = n_qt * n_heads * B;
-  flash_attn_mx_kernel<<<(n_wg + 7) / 8 * 8, 256, 0, s>>>(q, qs, k, ks, ldq, vt, vts, o, ldo, N, n_heads * HD,
-                                                          scale_log2, n_qt, n_heads, n_wg);
+  launch_timed(flash_attn_mx_kernel, dim3((n_wg + 7) / 8 * 8), dim3(256), s, q, qs, k, ks, ldq, vt, vts, o, ldo, N,
+               n_heads * HD, scale_log2, n_qt, n_heads, n_wg);
   return hipGetLastError();
 }
 
@@ -679,8 +679,8 @@ hipError_t cross_probs(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, bf16
   if (ssq && (groups < 4 || groups > MAXG || groups % 4 || !g)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(N / 32, n_heads, B);
-  cross_probs_kernel<<<grid, 64, 0, s>>>(q, ldq, kc, ldk, p, ldp, N, La, n_heads * HD, hw, apf, scale_log2, ssq,
-                                         groups, g, eps);
+  launch_timed(cross_probs_kernel, grid, dim3(64), s, q, ldq, kc, ldk, p, ldp, N, La, n_heads * HD, hw, apf,
+               scale_log2, ssq, groups, g, eps);
   return hipGetLastError();
 }
 
@@ -695,8 +695,8 @@ hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const
   if (ssq && (groups < 4 || groups > MAXG || groups % 4 || !g)) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(N / 32, n_heads, B);
-  cross_attn_kernel<<<grid, 64, 0, s>>>(q, ldq, kc, ldk, vct, o, ldo, N, La, n_heads * HD, hw, apf,
-                                        full, scale_log2, ssq, groups, g, eps);
+  launch_timed(cross_attn_kernel, grid, dim3(64), s, q, ldq, kc, ldk, vct, o, ldo, N, La, n_heads * HD, hw, apf,
+               full, scale_log2, ssq, groups, g, eps);
   return hipGetLastError();
 }
 

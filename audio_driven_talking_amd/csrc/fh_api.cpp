@@ -269,7 +269,7 @@ struct Timed {
       }
     }
     at_launch = cls == FH_K_GEMM_QKV || cls == FH_K_GEMM_O || cls == FH_K_GEMM_CQ || cls == FH_K_GEMM_CO ||
-                cls == FH_K_GEMM_FFN1 || cls == FH_K_GEMM_FFN2;
+                cls == FH_K_GEMM_FFN1 || cls == FH_K_GEMM_FFN2 || cls == FH_K_ATTN || cls == FH_K_CROSS_ATTN;
     if (at_launch) fh::arm_launch_events(ev.first, ev.second);
     else hipEventRecord(ev.first, s);
   }

@@ -1,5 +1,6 @@
 // Host-side launchers of the libfh HIP kernels (internal to the library).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -7,11 +8,30 @@
 
 namespace fh {
 
-// Kernel timing: arm_launch_events(start, stop) makes the next GEMM launch on
-// this thread record start and stop from its own dispatch (hipExtLaunchKernel);
-// launch_events_used() then tells (and resets) whether a launch took them.
+// Kernel timing: arm_launch_events(start, stop) makes the next timed launch
+// (GEMM, attention) on this thread record start and stop from its own
+// dispatch (hipExtLaunchKernel); launch_events_used() then tells (and
+// resets) whether a launch took them.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);
 bool launch_events_used();
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents& armed_launch_events();  // this thread's
+
+// a kernel launch that takes the armed events, if any
+template <typename Kern, typename... Args>
+void launch_timed(Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchEvents& e = armed_launch_events();
+  if (e.start) {
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e.start, e.stop, 0, args...);
+    e.start = e.stop = nullptr;
+    e.used = true;
+  } else {
+    kern<<<grid, block, 0, s>>>(args...);
+  }
+}
 
 // Epilogues of the bf16 GEMM C[M,N] = A[M,K] * W[N,K]^T (+ bias[N]).
 enum Epi {

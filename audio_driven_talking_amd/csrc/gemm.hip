@@ -31,32 +31,22 @@
 #include <type_traits>
 
 #include "fh_common.h"
-#include <hip/hip_ext.h>
 
 #include "fh_kernels.h"
 
 namespace fh {
 
 namespace {
-struct LaunchEvents {
-  hipEvent_t start = nullptr, stop = nullptr;
-  bool used = false;
-};
 thread_local LaunchEvents t_launch_ev;
 
 // a GEMM launch: through hipExtLaunchKernelGGL with the armed events, if any
 template <typename Kern, typename... Args>
 void launch_gemm(Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
-  LaunchEvents& e = t_launch_ev;
-  if (e.start) {
-    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e.start, e.stop, 0, args...);
-    e.start = e.stop = nullptr;
-    e.used = true;
-  } else {
-    kern<<<grid, block, 0, s>>>(args...);
-  }
+  launch_timed(kern, grid, block, s, args...);
 }
 }  // namespace
+
+LaunchEvents& armed_launch_events() { return t_launch_ev; }
 
 void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
   t_launch_ev.start = start;

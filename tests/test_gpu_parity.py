@@ -237,6 +237,35 @@ def test_block_single_branch(fh, keep):
     assert err <= TOL
 
 
+# ------------------------------------------------------------------ self-attention kernels
+ATTN_SHAPES = {
+    # 128 tokens: two 64-key blocks, one per key half
+    "toy": synth.CONFIGS["toy"],
+    # 96 tokens: a ragged second 64-key block (32 keys) and a half query tile
+    "n96": synth.CONFIGS["toy"].replace(frames=3, height=4, width=8, motion_frames=1),
+    # 2880 tokens: 45 key blocks, halves of 23 and 22
+    "n2880": synth.CONFIGS["slice768"].replace(n_blocks=1),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(ATTN_SHAPES))
+def test_self_attention_token_counts(fh, shape):
+    """The self-attention at token counts that leave a key half with fewer
+    blocks than the other, a half query tile, or an odd number of 64-key
+    blocks."""
+    cfg = ATTN_SHAPES[shape]
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = [1.0, 0.5, 0.0]
+    say(f"{shape} ({cfg.tokens} tokens) slice")
+    got = m.slice(lat, mot, aud, sig)
+    ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
+    err = O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
 # ------------------------------------------------------------------ slices
 def test_slice_two_blocks_full_width(fh):
     cfg = synth.CONFIGS["slice"].replace(n_blocks=2)
