@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfh_debug.so" if os.environ.get("FH_DEBUG") == "1" else "libfh.so")
 
 FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHTS = range(7)
-FH_DTYPE_BF16, FH_DTYPE_F32 = 1, 2
+FH_DTYPE_BF16, FH_DTYPE_F32, FH_DTYPE_F16 = 1, 2, 3
 FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER, FH_OPT_PRECISION = 1, 2, 3, 4
 FH_SAMPLER_EULER, FH_SAMPLER_RENOISE = 0, 1
 FH_PREC_BF16, FH_PREC_FP8_FFN, FH_PREC_FP32, FH_PREC_FP8_ATTN = 0, 1, 2, 3
@@ -37,7 +37,8 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
            "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
            "fh_color_match_workspace_bytes", "fh_color_match", "fh_color_match_noalloc",
-           "fh_color_match_noalloc_max_bytes", "fh_kernel_time", "fh_shader_clock",
+           "fh_color_match_noalloc_max_bytes", "fh_vae_weight_count", "fh_vae_weight_spec", "fh_vae_weights_bind",
+           "fh_vae_weights_release", "fh_vae_workspace_bytes", "fh_vae_decode", "fh_kernel_time", "fh_shader_clock",
            "fh_last_error", "fh_status_str"]
 
 
@@ -102,6 +103,12 @@ def _load():
         "fh_color_match": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp, sz, vp]),
         "fh_color_match_noalloc": (i32, [vp, i32, i32, i32, vp, i32, i32, ctypes.c_float, vp, vp]),
         "fh_color_match_noalloc_max_bytes": (sz, []),
+        "fh_vae_weight_count": (i32, [vp]),
+        "fh_vae_weight_spec": (i32, [vp, i32, ctypes.POINTER(fh_tensor)]),
+        "fh_vae_weights_bind": (i32, [vp, vp, sz, ctypes.POINTER(fh_tensor), i32, ctypes.POINTER(vp)]),
+        "fh_vae_weights_release": (None, [vp]),
+        "fh_vae_workspace_bytes": (sz, [vp]),
+        "fh_vae_decode": (i32, [vp, vp, vp, vp, sz, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "fh_shader_clock": (i32, [vp, ctypes.c_size_t, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
@@ -195,6 +202,8 @@ def _host_bytes(a):
                 return t.view(torch.int16).numpy().view(np.uint8), FH_DTYPE_BF16
             if t.dtype == torch.float32:
                 return t.numpy().view(np.uint8), FH_DTYPE_F32
+            if t.dtype == torch.float16:
+                return t.numpy().view(np.uint8), FH_DTYPE_F16
             raise TypeError(f"unsupported tensor dtype {t.dtype}")
     except ImportError:
         pass
@@ -203,6 +212,8 @@ def _host_bytes(a):
         return a.view(np.uint8).reshape(-1), FH_DTYPE_BF16
     if a.dtype == np.float32:
         return a.view(np.uint8).reshape(-1), FH_DTYPE_F32
+    if a.dtype == np.float16:
+        return a.view(np.uint8).reshape(-1), FH_DTYPE_F16
     raise TypeError(f"unsupported array dtype {a.dtype}")
 
 
@@ -528,3 +539,89 @@ def fh_audio_project(ctx, aw, states, tokens, ws, stream=None):
         ctx, aw, B, _dev_f32(states, (B, a.layers, a.state_frames, a.channels), "states"),
         _dev_f32(tokens, (B, d["frames"] * d["audio_per_frame"], d["dim"]), "tokens"),
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- video decoder
+class fh_vae_config(ctypes.Structure):
+    _fields_ = [("latent_ch", ctypes.c_int32), ("frames", ctypes.c_int32), ("height", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("widths", ctypes.c_int32 * 4), ("out_ch", ctypes.c_int32),
+                ("patch", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+def vae_config_struct(vc):
+    """fh_vae_config from an object with the same fields (e.g. synth.VaeConfig)."""
+    if isinstance(vc, fh_vae_config):
+        return vc
+    return fh_vae_config(vc.latent_ch, vc.frames, vc.height, vc.width, (ctypes.c_int32 * 4)(*vc.widths),
+                         vc.out_ch, vc.patch, vc.eps)
+
+
+class VaeWeights:
+    """An fh_vae_weights* plus its device blob and configuration (kept alive here)."""
+
+    def __init__(self, handle, blob, cfg):
+        self.handle, self.blob, self.cfg = handle, blob, cfg
+        self._free = lib.fh_vae_weights_release
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self._free(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+
+def fh_vae_weight_specs(vc):
+    """[(name, dtype, shape)] of a decoder's tensors."""
+    v = vae_config_struct(vc)
+    n = lib.fh_vae_weight_count(ctypes.byref(v))
+    if n <= 0:
+        raise FHError(FH_EINVAL, "unsupported decoder configuration")
+    out, t = [], fh_tensor()
+    for i in range(n):
+        _check(None, lib.fh_vae_weight_spec(ctypes.byref(v), i, ctypes.byref(t)))
+        out.append((t.name.decode(), t.dtype, tuple(t.shape[:t.ndim])))
+    return out
+
+
+def fh_vae_weights_bind(vc, tensors: dict, device="cuda") -> VaeWeights:
+    """Pack the decoder's tensors (kernels as float16 arrays, or uint16 arrays of
+    float16 bits, any shape of the right size; biases and gains float32) into
+    one device blob and bind it."""
+    v = vae_config_struct(vc)
+    ts = {k: (a.view(np.float16) if isinstance(a, np.ndarray) and a.dtype == np.uint16 else a)
+          for k, a in tensors.items()}
+    blob, index, _names = _pack_blob(fh_vae_weight_specs(v), ts, device)
+    h = ctypes.c_void_p()
+    _check(None, lib.fh_vae_weights_bind(ctypes.byref(v), ctypes.c_void_p(blob.data_ptr()), blob.numel(), index,
+                                         len(index), ctypes.byref(h)))
+    return VaeWeights(h, blob, v)
+
+
+def fh_vae_workspace_bytes(vc) -> int:
+    return int(lib.fh_vae_workspace_bytes(ctypes.byref(vae_config_struct(vc))))
+
+
+def fh_vae_decode(vw: VaeWeights, latent, frames=None, workspace=None, stream=None):
+    """Decode a float32 device latent [latent_ch, F, H, W] to frames
+    [out_ch, 8 (F - 1) + 1, 32 H, 32 W] in [0, 1] (see include/fh.h)."""
+    import torch
+    v = vw.cfg
+    shape = (v.latent_ch, v.frames, v.height, v.width)
+    out_shape = (v.out_ch, 8 * (v.frames - 1) + 1, 8 * v.patch * v.height, 8 * v.patch * v.width)
+    if not isinstance(latent, torch.Tensor) or not latent.is_cuda or latent.dtype != torch.float32 \
+            or not latent.is_contiguous() or tuple(latent.shape) != shape:
+        raise ValueError(f"latent must be a contiguous float32 device tensor of shape {shape}")
+    if frames is None:
+        frames = torch.empty(out_shape, dtype=torch.float32, device=latent.device)
+    elif tuple(frames.shape) != out_shape or frames.dtype != torch.float32 or not frames.is_contiguous():
+        raise ValueError(f"frames must be a contiguous float32 tensor of shape {out_shape}")
+    if workspace is None:
+        workspace = torch.empty(fh_vae_workspace_bytes(v), dtype=torch.uint8, device=latent.device)
+    st = lib.fh_vae_decode(vw, ctypes.c_void_p(latent.data_ptr()), ctypes.c_void_p(frames.data_ptr()),
+                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream))
+    if st != FH_OK:
+        raise FHError(st, f"fh_vae_decode: {fh_status_str(st)}")
+    return frames

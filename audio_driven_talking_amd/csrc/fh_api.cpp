@@ -696,7 +696,7 @@ int resolve_tensors(fh_ctx* c, const std::vector<Spec>& specs, const void* blob,
     if (t.ndim != s.ndim || t.shape[0] != s.shape[0] || (s.ndim == 2 && t.shape[1] != s.shape[1]))
       return fail(c, FH_EWEIGHTS, "weight '%s' has the wrong shape", s.name.c_str());
     const size_t elems = (size_t)s.shape[0] * (s.ndim == 2 ? (size_t)s.shape[1] : 1);
-    const size_t bytes = elems * (s.dtype == FH_DTYPE_BF16 ? 2 : 4);
+    const size_t bytes = elems * (s.dtype == FH_DTYPE_F32 ? 4 : 2);
     if (t.offset % 16) return fail(c, FH_EWEIGHTS, "weight '%s' offset is not 16-byte aligned", s.name.c_str());
     if (t.offset > blob_bytes || bytes > blob_bytes - t.offset)
       return fail(c, FH_EWEIGHTS, "weight '%s' lies outside the blob", s.name.c_str());
@@ -791,7 +791,82 @@ bool check_ws(fh_ctx* c, int B, void* ws, size_t ws_bytes, int* rc) {
   return true;
 }
 
+// ---- video decoder
+bool vae_cfg_ok(const fh_vae_config* v) {
+  auto pow2 = [](int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; };
+  if (!v || !pow2(v->latent_ch, 8, 512) || v->frames < 1 || v->height < 1 || v->width < 1 || v->patch != 4 ||
+      v->out_ch < 1 || (v->out_ch * v->patch * v->patch) % 16 || !(v->eps > 0.f) || !std::isfinite(v->eps))
+    return false;
+  for (int i = 0; i < 4; ++i)
+    if (!pow2(v->widths[i], 32, 512)) return false;
+  // every layer's output positions (the largest is the last resolution) within 2^30
+  const int64_t T = 8 * (int64_t)(v->frames - 1) + 1, H = 8 * (int64_t)v->height, W = 8 * (int64_t)v->width;
+  return T * H * W <= ((int64_t)1 << 30) && v->frames <= 4096 && v->height <= 4096 && v->width <= 4096;
+}
+
+std::vector<Spec> vae_specs(const fh_vae_config& v) {
+  std::vector<Spec> s;
+  auto conv = [&](const std::string& n, int64_t co, int64_t ci) {
+    s.push_back({n + ".w", FH_DTYPE_F16, 2, {co, 27 * ci}});
+    s.push_back({n + ".b", FH_DTYPE_F32, 1, {co, 0}});
+  };
+  auto vec = [&](const std::string& n, int64_t a) { s.push_back({n, FH_DTYPE_F32, 1, {a, 0}}); };
+  conv("conv_in", v.widths[0], v.latent_ch);
+  for (int i = 0; i < 3; ++i) {
+    const std::string p = "up" + std::to_string(i) + ".";
+    vec(p + "norm1.g", v.widths[i]);
+    conv(p + "conv1", v.widths[i], v.widths[i]);
+    vec(p + "norm2.g", v.widths[i]);
+    conv(p + "conv2", v.widths[i], v.widths[i]);
+    conv(p + "up", 8 * v.widths[i + 1], v.widths[i]);
+  }
+  vec("norm_out.g", v.widths[3]);
+  conv("conv_out", v.out_ch * v.patch * v.patch, v.widths[3]);
+  return s;
+}
+
+struct VaeWS {
+  _Float16 *zero, *x0, *a, *b, *c;
+  size_t total;
+};
+
+VaeWS carve_vae(const fh_vae_config& v, char* base) {
+  int64_t T = v.frames, H = v.height, W = v.width, act = T * H * W * v.widths[0];
+  for (int i = 0; i < 3; ++i) {
+    act = std::max(act, T * H * W * v.widths[i]);
+    T = 2 * T - 1;
+    H *= 2;
+    W *= 2;
+    act = std::max(act, T * H * W * v.widths[i + 1]);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return (_Float16*)p;
+  };
+  VaeWS w;
+  w.zero = take(256);
+  w.x0 = take((size_t)v.latent_ch * v.frames * v.height * v.width * 2);
+  w.a = take((size_t)act * 2);
+  w.b = take((size_t)act * 2);
+  w.c = take((size_t)act * 2);
+  w.total = off;
+  return w;
+}
+
+int log2i(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
 }  // namespace
+
+struct fh_vae_weights {
+  fh_vae_config cfg;
+  std::unordered_map<std::string, const void*> ptr;
+};
 
 extern "C" {
 
@@ -1193,6 +1268,90 @@ int fh_color_match_noalloc(const float* frames, int32_t n_frames, int32_t height
 }
 
 size_t fh_color_match_noalloc_max_bytes(void) { return fh::color_scratch_bytes(); }
+
+int fh_vae_weight_count(const fh_vae_config* v) { return vae_cfg_ok(v) ? (int)vae_specs(*v).size() : 0; }
+
+int fh_vae_weight_spec(const fh_vae_config* v, int i, fh_tensor* out) {
+  if (!out || !vae_cfg_ok(v)) return FH_EINVAL;
+  static thread_local std::vector<Spec> specs;  // keeps the returned names alive until the next call
+  specs = vae_specs(*v);
+  if (i < 0 || i >= (int)specs.size()) return FH_EINVAL;
+  std::memset(out, 0, sizeof *out);
+  out->name = specs[i].name.c_str();
+  out->dtype = specs[i].dtype;
+  out->ndim = specs[i].ndim;
+  out->shape[0] = specs[i].shape[0];
+  out->shape[1] = specs[i].shape[1];
+  return FH_OK;
+}
+
+int fh_vae_weights_bind(const fh_vae_config* v, const void* blob, size_t blob_bytes, const fh_tensor* index,
+                        int n_index, fh_vae_weights** out) {
+  if (!out) return FH_EINVAL;
+  *out = nullptr;
+  if (!vae_cfg_ok(v)) return FH_EINVAL;
+  std::unordered_map<std::string, const void*> ptr;
+  const int rc = resolve_tensors(nullptr, vae_specs(*v), blob, blob_bytes, index, n_index, ptr);
+  if (rc) return rc;
+  fh_vae_weights* w = new fh_vae_weights();
+  w->cfg = *v;
+  w->ptr = std::move(ptr);
+  *out = w;
+  return FH_OK;
+}
+
+void fh_vae_weights_release(fh_vae_weights* w) { delete w; }
+
+size_t fh_vae_workspace_bytes(const fh_vae_config* v) { return vae_cfg_ok(v) ? carve_vae(*v, nullptr).total : 0; }
+
+int fh_vae_decode(const fh_vae_weights* w, const float* latent, float* frames, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!w || !latent || !frames || ((uintptr_t)latent & 15) || ((uintptr_t)frames & 15)) return FH_EINVAL;
+  const fh_vae_config& v = w->cfg;
+  const VaeWS ws = carve_vae(v, (char*)workspace);
+  if (!workspace || ((uintptr_t)workspace & 255)) return FH_EINVAL;
+  if (workspace_bytes < ws.total) return FH_EWORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  auto P = [&](const std::string& n) { return w->ptr.at(n); };
+  fh_ctx* c = nullptr;  // FH_HIP reports through c (none here)
+  int T = v.frames, H = v.height, W = v.width;
+  FH_HIP(fh::latent_to_f16(latent, v.latent_ch, (int64_t)T * H * W, ws.x0, ws.zero, s));
+  auto conv = [&](int epi, const _Float16* in, int cin, const std::string& name, int cout, _Float16* out,
+                  const _Float16* res, float* fr) {
+    fh::ConvArgs a;
+    a.in = in;
+    a.T = T;
+    a.H = H;
+    a.W = W;
+    a.cin_log2 = log2i(cin);
+    a.w = (const _Float16*)P(name + ".w");
+    a.bias = (const float*)P(name + ".b");
+    a.cout = cout;
+    a.zero = ws.zero;
+    a.out = out;
+    a.res = res;
+    a.frames = fr;
+    return fh::conv3d_f16(epi, a, s);
+  };
+  FH_HIP(conv(fh::CONV_PLAIN, ws.x0, v.latent_ch, "conv_in", v.widths[0], ws.a, nullptr, nullptr));
+  for (int i = 0; i < 3; ++i) {
+    const std::string p = "up" + std::to_string(i) + ".";
+    const int C = v.widths[i];
+    const int64_t M = (int64_t)T * H * W;
+    FH_HIP(fh::norm_silu_f16(ws.a, (const float*)P(p + "norm1.g"), ws.b, M, C, v.eps, s));
+    FH_HIP(conv(fh::CONV_PLAIN, ws.b, C, p + "conv1", C, ws.c, nullptr, nullptr));
+    FH_HIP(fh::norm_silu_f16(ws.c, (const float*)P(p + "norm2.g"), ws.b, M, C, v.eps, s));
+    FH_HIP(conv(fh::CONV_RES, ws.b, C, p + "conv2", C, ws.c, ws.a, nullptr));
+    FH_HIP(conv(fh::CONV_UP, ws.c, C, p + "up", 8 * v.widths[i + 1], ws.a, nullptr, nullptr));
+    T = 2 * T - 1;
+    H *= 2;
+    W *= 2;
+  }
+  FH_HIP(fh::norm_silu_f16(ws.a, (const float*)P("norm_out.g"), ws.b, (int64_t)T * H * W, v.widths[3], v.eps, s));
+  FH_HIP(conv(fh::CONV_FRAMES, ws.b, v.widths[3], "conv_out", v.out_ch * v.patch * v.patch, nullptr, nullptr,
+              frames));
+  return FH_OK;
+}
 
 int fh_audio_weight_count(const fh_ctx* c, const fh_audio_config* a) {
   if (!c || !a || check_audio_cfg(nullptr, a) != FH_OK) return 0;

@@ -283,6 +283,33 @@ hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC,
                       int n_motion_tok, hipStream_t s);
 
 hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s);
+// Video decoder (vae.hip). A causal 3 x 3 x 3 convolution on channels-last F16
+// activations in[T][H][W][C_in] (C_in = 2^cin_log2) with kernels w[C_out][27 C_in]
+// (tap-major) and F32 bias: F16 sum, + bias in F32, F16 store, then
+//   CONV_PLAIN  out[T][H][W][C_out]
+//   CONV_RES    out = F16(that + res) (res like out)
+//   CONV_UP     depth to space: channel s C' + c (C' = C_out / 8, s = 4 dt + 2 dh + dw) to
+//               out[2t + dt - 1][2h + dh][2w + dw][c], frame 2t + dt = 0 dropped
+//   CONV_FRAMES channel c 16 + 4 py + px to frames[c][t][4h + py][4w + px] = clamp((v + 1) / 2, 0, 1)
+// zero: 16 or more bytes of zeros (the padding row).
+enum ConvEpi { CONV_PLAIN = 0, CONV_RES = 1, CONV_UP = 2, CONV_FRAMES = 3 };
+struct ConvArgs {
+  const _Float16* in = nullptr;
+  int T = 0, H = 0, W = 0, cin_log2 = 0;
+  const _Float16* w = nullptr;
+  const float* bias = nullptr;
+  int cout = 0;
+  const _Float16* zero = nullptr;
+  _Float16* out = nullptr;
+  const _Float16* res = nullptr;
+  float* frames = nullptr;
+};
+hipError_t conv3d_f16(int epi, const ConvArgs& a, hipStream_t s);
+// RMS norm over the C channels of each of M positions (F32 sums), gain g, SiLU, F16 out
+hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t M, int C, float eps, hipStream_t s);
+// latent [C][F H W] float32 -> channels-last F16; also clears 256 bytes at zero
+hipError_t latent_to_f16(const float* lat, int C, int64_t FHW, _Float16* out, _Float16* zero, hipStream_t s);
+
 // shader-clock probe: n_wg workgroups of MFMA loops, 4 counters each into out
 hipError_t clock_probe(uint64_t* out, int n_wg, int iters, hipStream_t s);
 

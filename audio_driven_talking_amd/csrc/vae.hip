@@ -1,0 +1,284 @@
+// Video decoder after the denoiser on gfx950: the slice latent to 33 RGB
+// frames through causal 3 x 3 x 3 convolutions (an assumed LTX-style layout:
+// conv_in, three stages of a residual block and a depth-to-space up-sampling
+// convolution, norm + SiLU, conv_out unfolded into 4 x 4 pixels).
+//
+// Numerics follow the audio-cpp page "SoulX-FlashHead", section "Variant
+// boundaries": convolutions take F16 operands with F32 accumulation and
+// store F16, the channel bias added in F32 to the F16-rounded sum before the
+// final F16 cast; residual sums are stored in F16; the channel RMS norm
+// accumulates in F32 and stores F16; the public latent and frames are F32.
+//
+// Activations are channels-last F16, [T][H][W][C]. A convolution is an
+// implicit GEMM on the F16 MFMA (32x32x16): rows are output positions
+// (M = T H W), columns output channels, and K = 27 C_in runs tap-major
+// (tap = 9 dt + 3 dh + dw, then the input channel), which is exactly the
+// kernel's [C_out][3][3][3][C_in] layout, so the weights are the B operand as
+// stored. Each K-slab of 32 is DMA'd to LDS: every lane computes the source
+// of its own 16-byte chunk (its output position shifted by the chunk's tap:
+// frames before 0 clamp to frame 0, the causal padding; positions outside
+// the frame read a zero row), so the shifted input is never materialised.
+// The epilogue rounds and stores in the layer's own form: plain, plus a
+// residual, depth to space into the next resolution, or the final pixels.
+#include "fh_common.h"
+#include "fh_kernels.h"
+
+namespace fh {
+namespace {
+
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CBM = 128;   // output positions per tile
+constexpr int CBK = 32;    // K per slab (64-byte LDS rows)
+constexpr int CNS = 4;     // slab stages
+
+// 16-byte chunk swizzle of 64-byte rows: the 16 rows a fragment read touches
+// at one logical chunk take 16 distinct 16-byte slots of a 256-byte bank
+// window (the quarter from row & 3, the XOR from (row >> 2) & 3)
+__device__ __forceinline__ int cswz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ float round16(float x) { return (float)(f16_t)x; }
+
+template <int BN, int EPI>
+__global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, int n_tiles) {
+  constexpr int ROWB = CBK * 2;
+  constexpr int SLAB = (CBM + BN) * ROWB;
+  constexpr int GA = CBM / 64;   // 1 KB A-DMAs per wave per slab (16 rows of 64 B each)
+  constexpr int GW = BN / 64;    // ... weights
+  constexpr int DPS = GA + GW;
+  constexpr int MI = CBM / 64, NI = BN / 64;  // 32-row MFMA blocks per wave (activations, weights)
+  static_assert((CNS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char smem[CNS * SLAB];
+
+  int bid = blockIdx.x;
+  bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
+  if (bid >= n_tiles) return;
+  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const int m0 = tm * CBM, n0 = tn * BN;
+  const int HW = a.H * a.W, M = a.T * HW;
+  const int Cin = 1 << a.cin_log2, K = 27 * Cin, KT = (K + CBK - 1) / CBK;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // DMA roles: instruction i of this wave fills slab rows 16 (wave + 4 i) + lane / 4,
+  // physical chunk lane & 3, which holds logical chunk (lane & 3) ^ cswz(row)
+  int pt[GA], ph[GA], pw[GA], ca[GA];
+#pragma unroll
+  for (int i = 0; i < GA; ++i) {
+    const int r = 16 * (wave + 4 * i) + (lane >> 2);
+    const int m = min(m0 + r, M - 1);
+    pt[i] = m / HW;
+    ph[i] = (m - pt[i] * HW) / a.W;
+    pw[i] = m - pt[i] * HW - ph[i] * a.W;
+    ca[i] = (lane & 3) ^ cswz(r);
+  }
+  const f16_t* wr[GW];
+  int cw[GW];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int r = 16 * (wave + 4 * i) + (lane >> 2);
+    wr[i] = a.w + (int64_t)min(n0 + r, a.cout - 1) * K;
+    cw[i] = (lane & 3) ^ cswz(r);
+  }
+  // the source of this lane's chunk of activation row i in the slab at k0
+  auto a_src = [&](int i, int k0) -> const f16_t* {
+    const int k = k0 + 8 * ca[i];
+    if (k >= K) return a.zero;
+    const int tap = k >> a.cin_log2, c = k & (Cin - 1);
+    const int dt = tap / 9, dh = (tap / 3) % 3, dw = tap % 3;
+    const int t = max(pt[i] + dt - 2, 0), h = ph[i] + dh - 1, w = pw[i] + dw - 1;
+    if (h < 0 || h >= a.H || w < 0 || w >= a.W) return a.zero;
+    return a.in + ((int64_t)(t * a.H + h) * a.W + w) * Cin + c;
+  };
+  auto dma_slab = [&](int buf, int kt) {
+    char* sb = smem + buf * SLAB;
+    const int k0 = min(kt, KT - 1) * CBK;
+#pragma unroll
+    for (int i = 0; i < GA; ++i) dma16(a_src(i, k0), sb + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int k = k0 + 8 * cw[i];
+      dma16(wr[i] + (k < K ? k : 0), sb + CBM * ROWB + (wave + 4 * i) * 1024);  // past K: A is zero there
+    }
+  };
+
+  f32x16 acc[NI][MI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // slab kt lives in buffer kt % CNS; slabs 0 .. CNS-2 are fetched up front
+#pragma unroll
+  for (int s = 0; s < CNS - 1; ++s) dma_slab(s, s);
+  const int arow = wm * (CBM / 2) + lr, wrow = CBM + wn * (BN / 2) + lr;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vm<(CNS - 2) * DPS>();  // this wave's DMAs of slab kt have landed
+    barrier();                   // everyone's have, and slab kt - 1's buffer is read out
+    dma_slab((kt + CNS - 1) % CNS, kt + CNS - 1);
+    const char* sb = smem + (kt % CNS) * SLAB;
+#pragma unroll
+    for (int kk = 0; kk < CBK / 16; ++kk) {
+      f16x8 af[MI], wf[NI];
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        const int r = arow + 32 * j;
+        af[j] = *reinterpret_cast<const f16x8*>(sb + r * ROWB + (((2 * kk + lh) ^ cswz(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = wrow + 32 * i;
+        wf[i] = *reinterpret_cast<const f16x8*>(sb + r * ROWB + (((2 * kk + lh) ^ cswz(r - CBM)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vm<0>();
+  mfma_drain(acc[NI - 1][MI - 1]);
+
+  // epilogue: lane (lr, lh) of block (i, j) holds output channels
+  // n0 + wn BN/2 + 32 i + 8 g + 4 lh + e (e = 0..3) of position m0 + wm CBM/2 + 32 j + lr
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int m = m0 + wm * (CBM / 2) + 32 * j + lr;
+    if (m >= M) continue;
+    const int t = m / HW, h = (m - t * HW) / a.W, w = m - t * HW - h * a.W;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * (BN / 2) + 32 * i + 8 * g + 4 * lh;
+        if (n >= a.cout) continue;
+        const f32x4 b = *reinterpret_cast<const f32x4*>(a.bias + n);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = round16(round16(acc[i][j][4 * g + e]) + b[e]);
+        if constexpr (EPI == CONV_PLAIN || EPI == CONV_RES) {
+          f16_t* o = a.out + (int64_t)m * a.cout + n;
+          if constexpr (EPI == CONV_RES) {
+            const f16x4 r = *reinterpret_cast<const f16x4*>(a.res + (int64_t)m * a.cout + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = v[e] + (float)r[e];
+          }
+          const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
+          *reinterpret_cast<f16x4*>(o) = y;
+        } else if constexpr (EPI == CONV_UP) {
+          // channel n = s C' + c (C' a multiple of 4: the 4 channels share s)
+          const int cp = a.cout >> 3, s = n / cp, c = n - s * cp;
+          const int t2 = 2 * t + (s >> 2) - 1, h2 = 2 * h + ((s >> 1) & 1), w2 = 2 * w + (s & 1);
+          if (t2 >= 0) {
+            f16_t* o = a.out + ((int64_t)(t2 * 2 * a.H + h2) * 2 * a.W + w2) * cp + c;
+            const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
+            *reinterpret_cast<f16x4*>(o) = y;
+          }
+        } else {
+          // CONV_FRAMES: channel n = c 16 + 4 py + px -> pixel (4 h + py, 4 w + px) of colour c,
+          // value (v + 1) / 2 clamped to [0, 1]
+          const int c = n >> 4, py = (n >> 2) & 3;
+          float* o = a.frames + ((int64_t)(c * a.T + t) * 4 * a.H + 4 * h + py) * 4 * a.W + 4 * w;
+          f32x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf((v[e] + 1.f) * 0.5f, 0.f), 1.f);
+          *reinterpret_cast<f32x4*>(o) = y;
+        }
+      }
+  }
+}
+
+// RMS norm over the C channels of each position (F32 sums), gain, SiLU, F16
+// store. C / 8 threads per position, 8 channels (16 bytes) each.
+__global__ __launch_bounds__(256) void norm_silu_kernel(const f16_t* __restrict__ x, const float* __restrict__ g,
+                                                        f16_t* __restrict__ y, int64_t M, int C, float eps) {
+  const int tpp = C >> 3;
+  const int64_t p = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpp;
+  const int c = (threadIdx.x % tpp) * 8;
+  const bool on = p < M;
+  f16x8 v = {};
+  if (on) v = *reinterpret_cast<const f16x8*>(x + p * C + c);
+  float f[8], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[e] = (float)v[e];
+    ss += f[e] * f[e];
+  }
+  for (int o = 1; o < tpp; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  if (!on) return;
+  const float rs = rsqrtf(ss / (float)C + eps);
+  f16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float z = f[e] * rs * g[c + e];
+    out[e] = (f16_t)(z / (1.f + __expf(-z)));
+  }
+  *reinterpret_cast<f16x8*>(y + p * C + c) = out;
+}
+
+// latent [C][F][H][W] float32 -> channels-last F16 [F][H][W][C]; the first
+// 128 threads also clear the decoder's zero row
+__global__ __launch_bounds__(256) void latent_f16_kernel(const float* __restrict__ lat, int C, int64_t FHW,
+                                                         f16_t* __restrict__ out, f16_t* __restrict__ zero) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < 128) zero[i] = (f16_t)0.f;
+  if (i >= (int64_t)C * FHW) return;
+  const int64_t pos = i / C;
+  const int c = (int)(i - pos * C);
+  out[i] = (f16_t)lat[(int64_t)c * FHW + pos];
+}
+
+template <int BN>
+hipError_t launch_conv(int epi, const ConvArgs& a, hipStream_t s) {
+  const int64_t M = (int64_t)a.T * a.H * a.W;
+  const int tiles_m = (int)((M + CBM - 1) / CBM);
+  const int tiles = tiles_m * ((a.cout + BN - 1) / BN);
+  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  switch (epi) {
+    case CONV_PLAIN: launch_timed(conv3d_kernel<BN, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_RES: launch_timed(conv3d_kernel<BN, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_UP: launch_timed(conv3d_kernel<BN, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_FRAMES: launch_timed(conv3d_kernel<BN, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t conv3d_f16(int epi, const ConvArgs& a, hipStream_t s) {
+  const int64_t M = (int64_t)a.T * a.H * a.W;
+  if (M <= 0) return hipSuccess;
+  if (M > (1 << 30) || a.cin_log2 < 3 || a.cin_log2 > 10 || a.cout % 16 || !a.in || !a.w || !a.bias || !a.zero)
+    return hipErrorInvalidValue;
+  if ((epi == CONV_PLAIN || epi == CONV_RES || epi == CONV_UP) && !a.out) return hipErrorInvalidValue;
+  if (epi == CONV_RES && !a.res) return hipErrorInvalidValue;
+  if (epi == CONV_UP && (a.cout % 32)) return hipErrorInvalidValue;  // 8 sub-positions x a multiple of 4 channels
+  if (epi == CONV_FRAMES && (!a.frames || a.cout % 16)) return hipErrorInvalidValue;
+  // 128 output channels per tile where there are that many, else 64
+  return a.cout >= 128 ? launch_conv<128>(epi, a, s) : launch_conv<64>(epi, a, s);
+}
+
+hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t M, int C, float eps, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (C < 8 || C > 512 || (C & (C - 1))) return hipErrorInvalidValue;
+  const int64_t threads = M * (C / 8);
+  norm_silu_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(x, g, y, M, C, eps);
+  return hipGetLastError();
+}
+
+hipError_t latent_to_f16(const float* lat, int C, int64_t FHW, _Float16* out, _Float16* zero, hipStream_t s) {
+  const int64_t n = (int64_t)C * FHW;
+  const int64_t total = n > 128 ? n : 128;
+  latent_f16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(lat, C, FHW, out, zero);
+  return hipGetLastError();
+}
+
+}  // namespace fh

@@ -24,9 +24,10 @@ Extra objects on the line:
   cpu_baseline  the fp32 numpy oracle on this host: one real-shape block
                 (1280 tokens, its audio K/V and modulation) three times,
                 median, scaled to the slice's 120 block-steps.
-  audio_front_end, color_correction
-                the audio projection before the denoise and the Lab colour
-                match after the decode, each timed on its own.
+  audio_front_end, vae_decode, color_correction
+                the audio projection before the denoise, the video decoder
+                after it and the Lab colour match after the decode, each
+                timed on its own.
 """
 from __future__ import annotations
 
@@ -263,6 +264,46 @@ def other_workload(fh, torch, synth, W, name, stream, steps, hot_passes, no_grap
     return res
 
 
+def vae_flops(vc):
+    """Algorithmic FLOPs of one decode: 2 x 27 C_in C_out per output position of
+    every convolution (the norms, SiLU and depth to space are bytes, not FLOPs)."""
+    T, H, W, w = vc.frames, vc.height, vc.width, vc.widths
+    f = 2 * 27 * vc.latent_ch * w[0] * T * H * W
+    for i in range(3):
+        f += 2 * (2 * 27 * w[i] * w[i] * T * H * W) + 2 * 27 * w[i] * 8 * w[i + 1] * T * H * W
+        T, H, W = 2 * T - 1, 2 * H, 2 * W
+    return f + 2 * 27 * w[3] * vc.out_ch * vc.patch ** 2 * T * H * W
+
+
+def vae_decode(fh, torch, synth, stream, calls):
+    """Time the video decoder on one slice latent (5 x 16 x 16 -> 33 frames of
+    512 x 512): HIP events around `calls` calls on the launch stream; its
+    convolutions are F16 MFMA contractions, priced against the 2.5 PF dense
+    F16/bf16 peak."""
+    vc = synth.VAE_CONFIGS["slice"]
+    vw = fh.fh_vae_weights_bind(vc, synth.make_vae_weights(vc))
+    z = torch.from_numpy(synth.vae_latent(vc)).cuda()
+    out = torch.empty(3, vc.out_frames, vc.out_height, vc.out_width, device="cuda")
+    ws = torch.empty(fh.fh_vae_workspace_bytes(vc), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        fh.fh_vae_decode(vw, z, out, ws, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        fh.fh_vae_decode(vw, z, out, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    fl = vae_flops(vc)
+    tf = fl / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 1), "calls_timed": calls, "bound": "mfma", "gflop_per_call": round(fl / 1e9, 2),
+            "tflops": round(tf, 1), "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "frames_per_s": round(vc.out_frames * calls / (e0.elapsed_time(e1) * 1e-3), 1),
+            "workload": f"video decoder, one slice latent {vc.latent_ch}x{vc.frames}x{vc.height}x{vc.width} -> "
+                        f"{vc.out_frames} frames of {vc.out_height}x{vc.out_width}, widths {list(vc.widths)}, "
+                        "F16 operands, F32 sums"}
+
+
 def device_info(torch):
     """Name, compute units and L2 size of cuda:0 as the runtime reports them."""
     p = torch.cuda.get_device_properties(0)
@@ -423,6 +464,7 @@ def main():
 
     front = audio_front_end(fh, torch, ctx, cfg, B, stream, args.steps) if cfg_name == "slice" else None
     color = color_correction(fh, torch, stream, args.steps) if cfg_name == "slice" else None
+    vae = vae_decode(fh, torch, synth, stream, max(5, args.steps // 2)) if cfg_name == "slice" else None
 
     breakdown = None
     if args.breakdown:
@@ -469,6 +511,8 @@ def main():
         line["workloads"] = extra
     if front is not None:
         line["audio_front_end"] = front
+    if vae is not None:
+        line["vae_decode"] = vae
     if color is not None:
         line["color_correction"] = color
     if breakdown is not None:

@@ -46,7 +46,7 @@ enum {
   FH_EWEIGHTS = 6       /* a required weight tensor is missing, misaligned or of the wrong dtype */
 };
 
-enum { FH_DTYPE_BF16 = 1, FH_DTYPE_F32 = 2 };
+enum { FH_DTYPE_BF16 = 1, FH_DTYPE_F32 = 2, FH_DTYPE_F16 = 3 };
 
 /* Sizes of the DiT and of one slice latent. Every dimension is a runtime value
  * (audio-cpp page, "Variant boundaries"). The kernels implement:
@@ -74,7 +74,7 @@ typedef struct fh_config {
 /* One entry of a weight index: a tensor inside the caller's device blob. */
 typedef struct fh_tensor {
   const char* name;   /* e.g. "blocks.3.qkv.w" (see fh_weight_spec) */
-  int32_t dtype;      /* FH_DTYPE_BF16 for matrices, FH_DTYPE_F32 for the rest */
+  int32_t dtype;      /* FH_DTYPE_BF16 for DiT matrices, FH_DTYPE_F16 for decoder kernels, FH_DTYPE_F32 for the rest */
   int32_t ndim;       /* 1 or 2 */
   int64_t shape[4];
   uint64_t offset;    /* bytes from the blob start; multiple of 16 */
@@ -361,6 +361,68 @@ int fh_color_match_noalloc(const float* frames, int32_t n_frames, int32_t height
                            const float* picture, int32_t ref_height, int32_t ref_width, float strength, float* out,
                            void* stream);
 size_t fh_color_match_noalloc_max_bytes(void);
+
+/* ---- Video decoder after the denoiser (an assumed LTX-style layout) --------
+ * The gizai:flashhead page (overview paragraph) has the VAE decode the slice
+ * latent to 33 frames whose colours are then matched to the picture; the
+ * toolkit page gives Lite's LTX stride 32 in space (33 = 1 + 4 x 8 frames from
+ * 5 latent frames: stride 8 in time). The layers are not on the pages; this
+ * decoder is: conv_in (latent_ch -> widths[0]); three stages of a residual
+ * block (x + conv2(SiLU(norm2(conv1(SiLU(norm1(x))))))) and an up-sampling
+ * convolution to 8 widths[i+1] channels with depth to space 2 x 2 x 2 that
+ * drops the first of the doubled frames (T -> 2T - 1); RMS norm, SiLU,
+ * conv_out to out_ch x patch x patch channels unfolded into patch x patch
+ * pixels; the result v in [-1, 1] returned as (v + 1) / 2 clamped to [0, 1].
+ * Every convolution is 3 x 3 x 3, time padded causally (frame 0 repeated
+ * twice before it), space with a zero border; norms are RMS over channels
+ * with a gain, eps `eps`. Numerics as the audio-cpp page's "Variant
+ * boundaries" section states them for Lite's Conv3D: F16 operands, F32
+ * accumulation, F16 output storage with the bias added in F32 to the F16
+ * result before the final F16 cast, F16 residual storage, norms accumulated
+ * in F32 with F16 output; the latent and the frames are F32.
+ * Implemented sizes: latent_ch a power of two in [8, 512]; widths powers of
+ * two in [32, 512]; out_ch * patch * patch a multiple of 16 with patch == 4;
+ * frames, height, width >= 1, and at most 2^30 output positions per layer.  */
+typedef struct fh_vae_config {
+  int32_t latent_ch;  /* 16 */
+  int32_t frames;     /* latent frames: 5 (-> 33 frames) */
+  int32_t height;     /* latent rows: 16 (-> 512) */
+  int32_t width;      /* latent columns: 16 (-> 512) */
+  int32_t widths[4];  /* decoder channels at the latent resolution and after each up-sampling */
+  int32_t out_ch;     /* 3 */
+  int32_t patch;      /* 4 */
+  float eps;          /* 1e-6 */
+} fh_vae_config;
+typedef struct fh_vae_weights fh_vae_weights;
+
+/* Tensors of a decoder: count (0 for a configuration outside the implemented
+ * sizes) and entry i in blob order. Names: conv_in.{w,b}; up{0,1,2}.norm1.g,
+ * .conv1.{w,b}, .norm2.g, .conv2.{w,b}, .up.{w,b}; norm_out.g;
+ * conv_out.{w,b}. Kernels are FH_DTYPE_F16 [C_out, 27 C_in] ([C_out][3][3][3]
+ * [C_in] row-major: time, row, column taps, then the input channel); biases
+ * and gains FH_DTYPE_F32 [C_out]. The up-sampling convolutions' output
+ * channel s C' + c (s = 4 dt + 2 dh + dw) fills sub-position (dt, dh, dw) of
+ * channel c; conv_out's channel c p^2 + py p + px is pixel (py, px) of
+ * colour c. FH_EINVAL for a null argument or i out of range.                 */
+int fh_vae_weight_count(const fh_vae_config* cfg);
+int fh_vae_weight_spec(const fh_vae_config* cfg, int i, fh_tensor* out);
+/* Bind a caller-owned device blob (no copy; it must outlive the binding):
+ * every tensor present with its dtype and shape, 16-byte aligned, inside the
+ * blob. FH_EINVAL (null arguments or an unsupported configuration),
+ * FH_EWEIGHTS (a missing, misplaced or mistyped tensor).                     */
+int fh_vae_weights_bind(const fh_vae_config* cfg, const void* blob, size_t blob_bytes, const fh_tensor* index,
+                        int n_index, fh_vae_weights** out);
+void fh_vae_weights_release(fh_vae_weights* w);
+/* Device scratch of one fh_vae_decode call (0 for an unsupported configuration). */
+size_t fh_vae_workspace_bytes(const fh_vae_config* cfg);
+/* Decode one latent: latent device f32 [latent_ch][frames][height][width];
+ * frames device f32 [out_ch][8 (frames - 1) + 1][8 patch height][8 patch width]
+ * (RGB planes, the input fh_color_match takes); workspace device memory of
+ * fh_vae_workspace_bytes, 256-byte aligned. 16-byte aligned pointers.
+ * Enqueued on `stream`. FH_EINVAL (null or misaligned pointers),
+ * FH_EWORKSPACE, FH_EHIP (launch errors).                                    */
+int fh_vae_decode(const fh_vae_weights* w, const float* latent, float* frames, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);

@@ -21,3 +21,4 @@ from . import renoise  # noqa: F401
 from . import mxfp8  # noqa: F401
 from . import audio  # noqa: F401
 from . import color  # noqa: F401
+from . import vae  # noqa: F401

@@ -309,3 +309,109 @@ def color_inputs(n_frames, height, width, ref_height, ref_width, seed: int = COL
     off = rng.uniform(-0.1, 0.1, (3, n_frames, 1, 1))
     frames = base[:, None] * gain + off + rng.normal(0.0, 0.02, (3, n_frames, height, width))
     return np.clip(frames, 0.0, 1.0).astype(np.float32), pic.astype(np.float32)
+
+
+# ---------------------------------------------------------------- video VAE decoder
+VAE_LATENT_SEED = 48
+
+
+@dataclasses.dataclass(frozen=True)
+class VaeConfig:
+    """Sizes of the video decoder that turns a slice latent into frames.
+
+    The pages fix the latent (the gizai:flashhead page, overview paragraph:
+    5 frames of 16 x 16 for a 512 x 512 picture, 33 decoded frames) and the
+    strides (the toolkit page: LTX stride 32 in space; 33 = 1 + 4 x 8 frames
+    from 5 latent frames, stride 8 in time). The layer widths are not on the
+    pages: `widths` are the decoder's channel counts at its four resolutions
+    (latent, x2, x4, x8 in space), a plain choice; `patch` is the last
+    depth-to-space step (4 x 4 pixels per position)."""
+    latent_ch: int = 16
+    frames: int = 5
+    height: int = 16
+    width: int = 16
+    widths: tuple = (256, 128, 64, 32)
+    out_ch: int = 3
+    patch: int = 4
+    eps: float = 1e-6
+
+    @property
+    def out_frames(self) -> int:
+        return 8 * (self.frames - 1) + 1
+
+    @property
+    def out_height(self) -> int:
+        return self.height * 8 * self.patch
+
+    @property
+    def out_width(self) -> int:
+        return self.width * 8 * self.patch
+
+    def replace(self, **kw) -> "VaeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+VAE_CONFIGS = {
+    # small widths, a 2-frame 4 x 4 latent: 9 frames of 128 x 128
+    "toy": VaeConfig(frames=2, height=4, width=4, widths=(64, 32, 32, 32)),
+    # a 3-frame 6 x 10 latent (180 positions: ragged tiles): 17 frames of 192 x 320
+    "ragged": VaeConfig(frames=3, height=6, width=10, widths=(128, 64, 32, 32)),
+    # the Lite slice: 5 x 16 x 16 latent -> 33 frames of 512 x 512
+    "slice": VaeConfig(),
+}
+
+
+def vae_param_specs(vcfg: VaeConfig):
+    """(name, shape, kind) of the decoder's tensors, in blob order. Convolution
+    kernels are [C_out, 3, 3, 3, C_in] (time, row, column taps, input channel
+    fastest); the up-sampling convolutions have 8 C' outputs, ordered
+    (sub-position, channel): output channel s C' + c fills sub-position s of
+    the 2 x 2 x 2 block of channel c; conv_out has out_ch patch^2 outputs,
+    ordered (colour, row, column) of the patch."""
+    w, P = vcfg.widths, vcfg.patch
+    specs = [("conv_in.w", (w[0], 3, 3, 3, vcfg.latent_ch), "conv"), ("conv_in.b", (w[0],), "vector")]
+    for i in range(3):
+        p = f"up{i}."
+        specs += [(p + "norm1.g", (w[i],), "gain"), (p + "conv1.w", (w[i], 3, 3, 3, w[i]), "conv"),
+                  (p + "conv1.b", (w[i],), "vector"), (p + "norm2.g", (w[i],), "gain"),
+                  (p + "conv2.w", (w[i], 3, 3, 3, w[i]), "conv"), (p + "conv2.b", (w[i],), "vector"),
+                  (p + "up.w", (8 * w[i + 1], 3, 3, 3, w[i]), "conv"), (p + "up.b", (8 * w[i + 1],), "vector")]
+    specs += [("norm_out.g", (w[3],), "gain"), ("conv_out.w", (vcfg.out_ch * P * P, 3, 3, 3, w[3]), "conv"),
+              ("conv_out.b", (vcfg.out_ch * P * P,), "vector")]
+    return specs
+
+
+def f16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bits (round to nearest even), as uint16."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def make_vae_weights(vcfg: VaeConfig, seed: int = WEIGHT_SEED):
+    """dict name -> array: convolution kernels as uint16 float16 bits drawn
+    N(0, 1) / sqrt(27 C_in) in float32 (unit gain through a 3 x 3 x 3
+    convolution of unit-RMS inputs); biases N(0, 0.02) and norm gains
+    1 + N(0, 0.02) as float32."""
+    out = {}
+    for name, shape, kind in vae_param_specs(vcfg):
+        if kind == "conv":
+            g = _rng(seed, name)
+            fan_in = 27 * shape[-1]
+            x = g.standard_normal(shape, dtype=np.float32) / np.float32(np.sqrt(fan_in))
+            out[name] = f16_bits(x)
+        else:
+            out[name] = _draw(seed, name, shape, kind)
+    return out
+
+
+def vae_weights_f32(weights: dict) -> dict:
+    """The decoder weights with the float16 kernels widened to float32 (exact)."""
+    return {k: (f16_to_f32(v) if v.dtype == np.uint16 else v) for k, v in weights.items()}
+
+
+def vae_latent(vcfg: VaeConfig, seed: int = VAE_LATENT_SEED):
+    """A denoised slice latent [latent_ch, frames, height, width], N(0, 1) float32."""
+    return normal((vcfg.latent_ch, vcfg.frames, vcfg.height, vcfg.width), seed)

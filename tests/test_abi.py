@@ -393,3 +393,26 @@ def test_shader_clock_argument_errors():
     assert L.fh_shader_clock(fake, 1 << 30, 0, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
     assert L.fh_shader_clock(fake, 1 << 30, 65537, 100, None, ctypes.byref(mhz)) == fh.FH_EINVAL
     assert L.fh_shader_clock(fake, 1 << 30, 16, 0, None, ctypes.byref(mhz)) == fh.FH_EINVAL
+
+
+def test_vae_specs_and_argument_errors():
+    """Decoder configuration checks, tensor specs and call errors, no launch."""
+    vc = synth.VAE_CONFIGS["slice"]
+    specs = fh.fh_vae_weight_specs(vc)
+    ref = synth.vae_param_specs(vc)
+    assert [s[0] for s in specs] == [r[0] for r in ref]
+    for (n, dt, shape), (_, rshape, kind) in zip(specs, ref):
+        assert dt == (fh.FH_DTYPE_F16 if kind == "conv" else fh.FH_DTYPE_F32)
+        assert int(np.prod(shape)) == int(np.prod(rshape))
+    L = fh.lib
+    for bad in (vc.replace(widths=(256, 96, 64, 32)), vc.replace(patch=2), vc.replace(latent_ch=12),
+                vc.replace(frames=0), vc.replace(widths=(1024, 128, 64, 32))):
+        v = fh.vae_config_struct(bad)
+        assert L.fh_vae_weight_count(ctypes.byref(v)) == 0
+        assert L.fh_vae_workspace_bytes(ctypes.byref(v)) == 0
+    v = fh.vae_config_struct(vc)
+    assert L.fh_vae_workspace_bytes(ctypes.byref(v)) > 3 * 33 * 128 * 128 * 32 * 2
+    h = ctypes.c_void_p()
+    assert L.fh_vae_weights_bind(ctypes.byref(v), None, 0, None, 0, ctypes.byref(h)) == fh.FH_EINVAL
+    assert L.fh_vae_decode(None, ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42),
+                           1 << 30, None) == fh.FH_EINVAL

@@ -78,3 +78,11 @@ def test_hot_class_flops_add_up():
     tf, frac = bench.hot_fraction({k: 1.0 for k in per}, per)   # 1 ms per class
     assert abs(tf - sum(per.values()) / (len(per) * 1e-3) / 1e12) < 1e-6
     assert abs(frac - tf / bench.PEAK_BF16_TFLOPS) < 1e-12
+
+
+def test_vae_flops_of_the_slice_decoder():
+    """Per convolution 2 x 27 C_in C_out per output position: conv_in 0.28,
+    stage convolutions 9.06 + 18.12, 16.31 + 32.62, 30.81 + 61.61, conv_out
+    44.84 GFLOP: 213.7 GFLOP per slice decode."""
+    f = bench.vae_flops(synth.VAE_CONFIGS["slice"])
+    assert abs(f / 1e9 - 213.65) < 0.05
