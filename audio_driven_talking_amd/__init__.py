@@ -36,6 +36,7 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_fp8_weight_bytes", "fh_weights_quantize_fp8", "fh_mxfp8_quantize",
            "fh_mxfp8_gemm", "fh_audio_weight_count", "fh_audio_weight_spec", "fh_audio_weights_bind",
            "fh_audio_weights_release", "fh_audio_workspace_bytes", "fh_audio_project",
+           "fh_slice_from_states_workspace_bytes", "fh_dit_denoise_slice_from_states",
            "fh_color_match_workspace_bytes", "fh_color_match", "fh_color_match_noalloc",
            "fh_color_match_noalloc_max_bytes", "fh_vae_weight_count", "fh_vae_weight_spec", "fh_vae_weights_bind",
            "fh_vae_weights_release", "fh_vae_workspace_bytes", "fh_vae_decode", "fh_kernel_time", "fh_shader_clock",
@@ -97,6 +98,9 @@ def _load():
         "fh_audio_weights_release": (None, [vp]),
         "fh_audio_workspace_bytes": (sz, [vp, i32]),
         "fh_audio_project": (i32, [vp, vp, i32, vp, vp, vp, sz, vp]),
+        "fh_slice_from_states_workspace_bytes": (sz, [vp, vp, i32]),
+        "fh_dit_denoise_slice_from_states": (i32, [vp, vp, vp, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_float), i32,
+                                                   vp, vp, sz, vp]),
         "fh_philox4x32_fill": (i32, [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                      ctypes.c_int64, vp, vp]),
         "fh_color_match_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -538,6 +542,32 @@ def fh_audio_project(ctx, aw, states, tokens, ws, stream=None):
     _check(ctx, lib.fh_audio_project(
         ctx, aw, B, _dev_f32(states, (B, a.layers, a.state_frames, a.channels), "states"),
         _dev_f32(tokens, (B, d["frames"] * d["audio_per_frame"], d["dim"]), "tokens"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+def fh_slice_from_states_workspace_bytes(ctx, aw, batch: int) -> int:
+    return int(lib.fh_slice_from_states_workspace_bytes(ctx, aw, int(batch)))
+
+
+def slice_from_states_workspace(ctx, aw, batch: int, device="cuda"):
+    import torch
+    return torch.empty(fh_slice_from_states_workspace_bytes(ctx, aw, batch), dtype=torch.uint8, device=device)
+
+
+def fh_dit_denoise_slice_from_states(ctx, w, aw, latent, motion_latent, states, sigmas, latent_out, ws,
+                                     stream=None):
+    """The slice denoise fed from speech-encoder states [B, layers, state_frames,
+    channels] (the audio projection front end inside the same call)."""
+    d = _dims(ctx)
+    a = aw.acfg
+    B = latent.shape[0]
+    C, F, H, W = d["in_ch"], d["frames"], d["height"], d["width"]
+    sig = (ctypes.c_float * max(len(sigmas), 1))(*[float(s) for s in sigmas])
+    _check(ctx, lib.fh_dit_denoise_slice_from_states(
+        ctx, w, aw, B, _dev_f32(latent, (B, C, F, H, W), "latent"),
+        _dev_f32(motion_latent, (B, C, d["motion_frames"], H, W), "motion_latent"),
+        _dev_f32(states, (B, a.layers, a.state_frames, a.channels), "states"),
+        sig, len(sigmas) - 1, _dev_f32(latent_out, (B, C, F, H, W), "latent_out"),
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
 
 

@@ -46,11 +46,11 @@ struct GraphEntry {
 // wait until the last launch of a cached graph has finished, then free it
 void release_graph(GraphEntry& ge) {
   if (ge.done) {
-    hipEventSynchronize(ge.done);
-    hipEventDestroy(ge.done);
+    (void)hipEventSynchronize(ge.done);
+    (void)hipEventDestroy(ge.done);
   }
-  if (ge.exec) hipGraphExecDestroy(ge.exec);
-  if (ge.graph) hipGraphDestroy(ge.graph);
+  if (ge.exec) (void)hipGraphExecDestroy(ge.exec);
+  if (ge.graph) (void)hipGraphDestroy(ge.graph);
   ge = GraphEntry();
 }
 
@@ -118,6 +118,7 @@ struct fh_audio_weights {
   int V, LF, F;  // video frames, latent frames, feature width
   const bf16_t *p1_w, *p1vf_w, *p2_w, *p3_w;
   const float *p1_b, *p1vf_b, *p2_b, *p3_b, *norm_g, *norm_b;
+  uint64_t serial = 0;  // identity of this binding for the graph cache
 };
 
 namespace {
@@ -600,10 +601,134 @@ int run_block_f32(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0,
   return FH_OK;
 }
 
+// ---- audio projection front end
+int check_audio_cfg(fh_ctx* c, const fh_audio_config* a) {
+  if (!a) return fail(c, FH_EINVAL, "null audio configuration");
+  if (a->layers <= 0 || a->state_frames <= 0 || a->channels <= 0 || a->window <= 0 || a->temporal_stride <= 0 ||
+      a->hidden <= 0)
+    return fail(c, FH_ESHAPE, "audio configuration sizes must be positive");
+  const int64_t F = (int64_t)a->window * a->layers * a->channels;
+  if (F % 64 || F > (1 << 24) || a->hidden % 128 || a->hidden > 8192)
+    return fail(c, FH_EUNSUPPORTED,
+                "audio feature width (window x layers x channels) must be a multiple of 64 and hidden of 128");
+  return FH_OK;
+}
+
+std::vector<Spec> audio_specs(const fh_ctx* c, const fh_audio_config& a) {
+  const int64_t F = (int64_t)a.window * a.layers * a.channels, P = a.hidden,
+                TD = (int64_t)c->cfg.audio_per_frame * c->cfg.dim, D = c->cfg.dim;
+  return {{"proj1.w", FH_DTYPE_BF16, 2, {P, F}},   {"proj1.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj1vf.w", FH_DTYPE_BF16, 2, {P, F}}, {"proj1vf.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj2.w", FH_DTYPE_BF16, 2, {P, P}},   {"proj2.b", FH_DTYPE_F32, 1, {P, 0}},
+          {"proj3.w", FH_DTYPE_BF16, 2, {TD, P}},  {"proj3.b", FH_DTYPE_F32, 1, {TD, 0}},
+          {"projNorm.g", FH_DTYPE_F32, 1, {D, 0}}, {"projNorm.b", FH_DTYPE_F32, 1, {D, 0}}};
+}
+
+// splits of a split-K GEMM: the largest divisor of the 64-column slabs that
+// keeps the grid within two workgroups per CU
+int audio_splits(int M, int N, int K) {
+  const int slabs = K / 64, tiles = ((M + 63) / 64) * (N / 128);
+  int best = 1;
+  for (int d = 1; d <= slabs && d <= 256; ++d)
+    if (slabs % d == 0 && (int64_t)d * tiles <= 512) best = d;
+  return best;
+}
+
+struct AudioWS {
+  bf16_t *X, *H1, *H2;
+  float *part, *Y;
+  size_t total;
+};
+
+AudioWS carve_audio(const fh_audio_weights* w, int B, char* base) {
+  const fh_config& g = w->ctx->cfg;
+  const size_t LF = w->LF, F = w->F, P = w->acfg.hidden, TD = (size_t)g.audio_per_frame * g.dim;
+  const size_t M = LF * B;
+  size_t parts = (size_t)audio_splits(B, (int)P, (int)F) * B * P;
+  if (LF > 1) parts = std::max(parts, (size_t)audio_splits((int)(M - B), (int)P, (int)F) * (M - B) * P);
+  parts = std::max(parts, (size_t)audio_splits((int)M, (int)P, (int)P) * M * P);
+  parts = std::max(parts, (size_t)audio_splits((int)M, (int)TD, (int)P) * M * TD);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  AudioWS a;
+  a.X = (bf16_t*)take(M * F * 2);
+  a.H1 = (bf16_t*)take(M * P * 2);
+  a.H2 = (bf16_t*)take(M * P * 2);
+  a.part = (float*)take(parts * 4);
+  a.Y = (float*)take(M * TD * 4);
+  a.total = off;
+  return a;
+}
+
+// The audio projection front end (speech-encoder states -> the slice's audio
+// tokens, once per slice): features, four split-K projections, projNorm.
+// The tokens go to tokens_f32 ([B][La][D] float32) or, for the DiT's own
+// bf16 audio buffer, to tokens_bf16.
+int enqueue_front(fh_ctx* c, const fh_audio_weights* w, int B, const float* states, const AudioWS& a,
+                  float* tokens_f32, bf16_t* tokens_bf16, hipStream_t s) {
+  const fh_config& g = c->cfg;
+  const fh_audio_config& ac = w->acfg;
+  const int LF = w->LF, F = w->F, P = ac.hidden, TD = g.audio_per_frame * g.dim, M = LF * B;
+  FH_HIP(fh::audio_features(states, B, ac.layers, ac.state_frames, ac.channels, ac.window, w->V,
+                            ac.temporal_stride, LF, a.X, s));
+  auto proj = [&](const bf16_t* A, int lda, const bf16_t* W, const float* bias, int rows, int N, int K, int act,
+                  int group, int ngroups, float* out_f, bf16_t* out_b) -> int {
+    if (rows <= 0) return FH_OK;
+    const int sp = audio_splits(rows, N, K);
+    FH_HIP(fh::gemm_bf16_splitk_n(A, lda, W, K, rows, N, K, sp, a.part, (size_t)sp * rows * N, s));
+    FH_HIP(fh::sum_parts(a.part, sp, rows, N, bias, act, group, ngroups, out_f, out_b, s));
+    return FH_OK;
+  };
+  int rc = proj(a.X, F, w->p1_w, w->p1_b, B, P, F, 1, B, 1, nullptr, a.H1);            // latent frame 0
+  if (!rc) rc = proj(a.X + (size_t)B * F, F, w->p1vf_w, w->p1vf_b, M - B, P, F, 1, M - B, 1, nullptr,
+                     a.H1 + (size_t)B * P);                                                 // the others
+  if (!rc) rc = proj(a.H1, P, w->p2_w, w->p2_b, M, P, P, 1, M, 1, nullptr, a.H2);
+  if (!rc) rc = proj(a.H2, P, w->p3_w, w->p3_b, M, TD, P, 0, B, LF, a.Y, nullptr);         // rows -> lane-major
+  if (rc) return rc;
+  if (tokens_bf16)  // projNorm straight into bf16 rows (the LayerNorm kernel of the blocks, affine form)
+    FH_HIP(fh::layernorm_bf16(a.Y, tokens_bf16, B * c->La, g.dim, c->La, g.eps, nullptr, nullptr, nullptr, nullptr,
+                              0, w->norm_g, w->norm_b, nullptr, s));
+  else
+    FH_HIP(fh::layernorm_f32(a.Y, tokens_f32, B * c->La, g.dim, c->La, g.eps, nullptr, nullptr, nullptr, nullptr, 0,
+                             w->norm_g, w->norm_b, s));
+  return FH_OK;
+}
+
+// A slice fed from speech-encoder states instead of audio tokens.
+struct FrontEnd {
+  const fh_audio_weights* aw;
+  const float* states;
+  AudioWS a;
+  float* tokens;  // float32 tokens, for the float32 precision
+};
+
+// workspace of a slice from states: the slice's own, the front end's, float32 tokens
+struct StatesWS {
+  char* slice;
+  AudioWS front;
+  float* tokens;
+  size_t total;
+};
+
+StatesWS states_ws(const fh_ctx* c, const fh_audio_weights* aw, int B, char* base) {
+  StatesWS w;
+  const size_t s0 = (carve(c, B, nullptr).total + 255) & ~(size_t)255;
+  const size_t s1 = (carve_audio(aw, B, nullptr).total + 255) & ~(size_t)255;
+  w.slice = base;
+  w.front = carve_audio(aw, B, base ? base + s0 : nullptr);
+  w.tokens = base ? (float*)(base + s0 + s1) : nullptr;
+  w.total = s0 + s1 + (size_t)B * c->La * c->cfg.dim * 4;
+  return w;
+}
+
 // The whole slice: audio K/V of every block, motion pin, then per step the
 // time embedding, patch embedding, all blocks and the head + Euler update.
 int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, const float* motion,
-                  const float* audio, const float* sigmas, int n_steps, float* out, const WS& ws,
+                  const float* audio, const FrontEnd* fe, const float* sigmas, int n_steps, float* out, const WS& ws,
                   hipStream_t s) {
   const fh_config& g = c->cfg;
   const int N = c->N, D = g.dim, C = g.in_ch;
@@ -612,7 +737,15 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
   if (n_steps == 0) return FH_OK;
   FH_HIP(fh::rope_table(ws.rcos, ws.rsin, g.frames, g.height, g.width, g.head_dim, g.rope_theta, s));
   const bool f32 = c->precision == FH_PREC_FP32;
-  if (!f32) FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
+  if (fe) {
+    // the audio tokens from the speech-encoder states: bf16 straight into the
+    // blocks' audio buffer (float32 tokens for the float32 precision)
+    int rc = enqueue_front(c, fe->aw, B, fe->states, fe->a, f32 ? fe->tokens : nullptr, f32 ? nullptr : ws.aud, s);
+    if (rc) return rc;
+    audio = fe->tokens;
+  } else if (!f32) {
+    FH_HIP(fh::f32_to_bf16(audio, ws.aud, (int64_t)B * c->La * D, s));
+  }
   {
     Timed t(c, FH_K_AUDIO_KV, s);
     if (!f32 && c->fold_co && g.n_blocks <= fh::MAX_BATCH_TABLE) {
@@ -703,69 +836,6 @@ int resolve_tensors(fh_ctx* c, const std::vector<Spec>& specs, const void* blob,
     ptr[s.name] = (const char*)blob + t.offset;
   }
   return FH_OK;
-}
-
-// ---- audio projection front end
-int check_audio_cfg(fh_ctx* c, const fh_audio_config* a) {
-  if (!a) return fail(c, FH_EINVAL, "null audio configuration");
-  if (a->layers <= 0 || a->state_frames <= 0 || a->channels <= 0 || a->window <= 0 || a->temporal_stride <= 0 ||
-      a->hidden <= 0)
-    return fail(c, FH_ESHAPE, "audio configuration sizes must be positive");
-  const int64_t F = (int64_t)a->window * a->layers * a->channels;
-  if (F % 64 || F > (1 << 24) || a->hidden % 128 || a->hidden > 8192)
-    return fail(c, FH_EUNSUPPORTED,
-                "audio feature width (window x layers x channels) must be a multiple of 64 and hidden of 128");
-  return FH_OK;
-}
-
-std::vector<Spec> audio_specs(const fh_ctx* c, const fh_audio_config& a) {
-  const int64_t F = (int64_t)a.window * a.layers * a.channels, P = a.hidden,
-                TD = (int64_t)c->cfg.audio_per_frame * c->cfg.dim, D = c->cfg.dim;
-  return {{"proj1.w", FH_DTYPE_BF16, 2, {P, F}},   {"proj1.b", FH_DTYPE_F32, 1, {P, 0}},
-          {"proj1vf.w", FH_DTYPE_BF16, 2, {P, F}}, {"proj1vf.b", FH_DTYPE_F32, 1, {P, 0}},
-          {"proj2.w", FH_DTYPE_BF16, 2, {P, P}},   {"proj2.b", FH_DTYPE_F32, 1, {P, 0}},
-          {"proj3.w", FH_DTYPE_BF16, 2, {TD, P}},  {"proj3.b", FH_DTYPE_F32, 1, {TD, 0}},
-          {"projNorm.g", FH_DTYPE_F32, 1, {D, 0}}, {"projNorm.b", FH_DTYPE_F32, 1, {D, 0}}};
-}
-
-// splits of a split-K GEMM: the largest divisor of the 64-column slabs that
-// keeps the grid within two workgroups per CU
-int audio_splits(int M, int N, int K) {
-  const int slabs = K / 64, tiles = ((M + 63) / 64) * (N / 128);
-  int best = 1;
-  for (int d = 1; d <= slabs && d <= 256; ++d)
-    if (slabs % d == 0 && (int64_t)d * tiles <= 512) best = d;
-  return best;
-}
-
-struct AudioWS {
-  bf16_t *X, *H1, *H2;
-  float *part, *Y;
-  size_t total;
-};
-
-AudioWS carve_audio(const fh_audio_weights* w, int B, char* base) {
-  const fh_config& g = w->ctx->cfg;
-  const size_t LF = w->LF, F = w->F, P = w->acfg.hidden, TD = (size_t)g.audio_per_frame * g.dim;
-  const size_t M = LF * B;
-  size_t parts = (size_t)audio_splits(B, (int)P, (int)F) * B * P;
-  if (LF > 1) parts = std::max(parts, (size_t)audio_splits((int)(M - B), (int)P, (int)F) * (M - B) * P);
-  parts = std::max(parts, (size_t)audio_splits((int)M, (int)P, (int)P) * M * P);
-  parts = std::max(parts, (size_t)audio_splits((int)M, (int)TD, (int)P) * M * TD);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    char* p = base ? base + off : nullptr;
-    off += (bytes + 255) & ~(size_t)255;
-    return p;
-  };
-  AudioWS a;
-  a.X = (bf16_t*)take(M * F * 2);
-  a.H1 = (bf16_t*)take(M * P * 2);
-  a.H2 = (bf16_t*)take(M * P * 2);
-  a.part = (float*)take(parts * 4);
-  a.Y = (float*)take(M * TD * 4);
-  a.total = off;
-  return a;
 }
 
 int check_precision(fh_ctx* c, const fh_weights* w) {
@@ -867,6 +937,12 @@ struct fh_vae_weights {
   fh_vae_config cfg;
   std::unordered_map<std::string, const void*> ptr;
 };
+
+namespace {
+int denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float* latent, const float* motion_latent,
+                  const float* audio_tokens, const FrontEnd* fe, const float* sigmas, int n_steps, float* latent_out,
+                  void* ws, size_t ws_bytes, void* stream);
+}  // namespace
 
 extern "C" {
 
@@ -1015,10 +1091,21 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
                          const float* motion_latent, const float* audio_tokens, const float* sigmas,
                          int n_steps, float* latent_out, void* ws, size_t ws_bytes, void* stream) {
   if (!c) return FH_EINVAL;
+  if (!audio_tokens) return fail(c, FH_EINVAL, "null audio tokens");
+  return denoise_slice(c, w, batch, latent, motion_latent, audio_tokens, nullptr, sigmas, n_steps, latent_out, ws,
+                       ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+int denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float* latent, const float* motion_latent,
+                  const float* audio_tokens, const FrontEnd* fe, const float* sigmas, int n_steps, float* latent_out,
+                  void* ws, size_t ws_bytes, void* stream) {
   if (!w || w->ctx != c) return fail(c, FH_EINVAL, "weights are null or bound to another context");
   if (batch <= 0) return fail(c, FH_EINVAL, "batch must be positive, got %d", batch);
   if (n_steps < 0) return fail(c, FH_EINVAL, "n_steps must be >= 0, got %d", n_steps);
-  if (!latent || !latent_out || (!motion_latent && c->cfg.motion_frames > 0) || !audio_tokens ||
+  if (!latent || !latent_out || (!motion_latent && c->cfg.motion_frames > 0) || (!audio_tokens && !fe) ||
       (!sigmas && n_steps > 0))
     return fail(c, FH_EINVAL, "null latent, motion, audio, sigmas or output pointer");
   for (int i = 0; i <= n_steps && n_steps > 0; ++i)
@@ -1031,10 +1118,12 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   WS wsp = carve(c, batch, (char*)ws);
 
   if (!c->use_graph || c->time_class >= 0)
-    return enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, sigmas, n_steps, latent_out, wsp, s);
+    return enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, fe, sigmas, n_steps, latent_out, wsp, s);
 
   std::vector<uint64_t> key = {w->serial, (uint64_t)batch, (uint64_t)(uintptr_t)latent,
                                (uint64_t)(uintptr_t)motion_latent, (uint64_t)(uintptr_t)audio_tokens,
+                               fe ? fe->aw->serial : 0, fe ? (uint64_t)(uintptr_t)fe->states : 0,
+                               fe ? (uint64_t)(uintptr_t)fe->tokens : 0,
                                (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
                                (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed,
                                (uint64_t)c->precision};
@@ -1051,7 +1140,7 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
     }
   if (!c->cap_stream) FH_HIP(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
   FH_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-  rc = enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, sigmas, n_steps, latent_out, wsp,
+  rc = enqueue_slice(c, w, batch, latent, motion_latent, audio_tokens, fe, sigmas, n_steps, latent_out, wsp,
                      c->cap_stream);
   hipGraph_t graph = nullptr;
   hipError_t ce = hipStreamEndCapture(c->cap_stream, &graph);
@@ -1080,6 +1169,9 @@ int fh_dit_denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float*
   FH_HIP(hipEventRecord(ge.done, s));
   return FH_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int fh_set_option(fh_ctx* c, int option, int value) {
   if (!c) return FH_EINVAL;
@@ -1386,6 +1478,7 @@ int fh_audio_weights_bind(fh_ctx* c, const fh_audio_config* a, const void* blob,
   rc = resolve_tensors(c, audio_specs(c, *a), blob, blob_bytes, index, n_index, ptr);
   if (rc) return rc;
   fh_audio_weights* w = new fh_audio_weights();
+  w->serial = g_weights_serial++;
   w->ctx = c;
   w->acfg = *a;
   w->LF = c->cfg.frames;
@@ -1420,29 +1513,31 @@ int fh_audio_project(fh_ctx* c, const fh_audio_weights* w, int batch, const floa
   if (ws_bytes < a.total)
     return fail(c, FH_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes batch %d needs", ws_bytes,
                 a.total, batch);
-  const fh_config& g = c->cfg;
-  const fh_audio_config& ac = w->acfg;
-  const int B = batch, LF = w->LF, F = w->F, P = ac.hidden, TD = g.audio_per_frame * g.dim, M = LF * B;
-  hipStream_t s = (hipStream_t)stream;
-  FH_HIP(fh::audio_features(states, B, ac.layers, ac.state_frames, ac.channels, ac.window, w->V,
-                            ac.temporal_stride, LF, a.X, s));
-  auto proj = [&](const bf16_t* A, int lda, const bf16_t* W, const float* bias, int rows, int N, int K, int act,
-                  int group, int ngroups, float* out_f, bf16_t* out_b) -> int {
-    if (rows <= 0) return FH_OK;
-    const int sp = audio_splits(rows, N, K);
-    FH_HIP(fh::gemm_bf16_splitk_n(A, lda, W, K, rows, N, K, sp, a.part, (size_t)sp * rows * N, s));
-    FH_HIP(fh::sum_parts(a.part, sp, rows, N, bias, act, group, ngroups, out_f, out_b, s));
-    return FH_OK;
-  };
-  int rc = proj(a.X, F, w->p1_w, w->p1_b, B, P, F, 1, B, 1, nullptr, a.H1);            // latent frame 0
-  if (!rc) rc = proj(a.X + (size_t)B * F, F, w->p1vf_w, w->p1vf_b, M - B, P, F, 1, M - B, 1, nullptr,
-                     a.H1 + (size_t)B * P);                                                 // the others
-  if (!rc) rc = proj(a.H1, P, w->p2_w, w->p2_b, M, P, P, 1, M, 1, nullptr, a.H2);
-  if (!rc) rc = proj(a.H2, P, w->p3_w, w->p3_b, M, TD, P, 0, B, LF, a.Y, nullptr);         // rows -> lane-major
-  if (rc) return rc;
-  FH_HIP(fh::layernorm_f32(a.Y, tokens, B * c->La, g.dim, c->La, g.eps, nullptr, nullptr, nullptr, nullptr, 0,
-                           w->norm_g, w->norm_b, s));
-  return FH_OK;
+  return enqueue_front(c, w, batch, states, a, tokens, nullptr, (hipStream_t)stream);
+}
+
+size_t fh_slice_from_states_workspace_bytes(const fh_ctx* c, const fh_audio_weights* w, int batch) {
+  if (!c || !w || w->ctx != c || batch <= 0) return 0;
+  return states_ws(c, w, batch, nullptr).total;
+}
+
+int fh_dit_denoise_slice_from_states(fh_ctx* c, const fh_weights* w, const fh_audio_weights* aw, int batch,
+                                     const float* latent, const float* motion_latent, const float* states,
+                                     const float* sigmas, int n_steps, float* latent_out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!c) return FH_EINVAL;
+  if (!aw || aw->ctx != c) return fail(c, FH_EINVAL, "audio weights are null or bound to another context");
+  if (!states) return fail(c, FH_EINVAL, "null states");
+  if (batch <= 0) return fail(c, FH_EINVAL, "batch must be positive, got %d", batch);
+  if (!ws || ((uintptr_t)ws & 255))
+    return fail(c, FH_EWORKSPACE, "workspace must be a non-null 256-byte aligned device pointer");
+  const StatesWS sw = states_ws(c, aw, batch, (char*)ws);
+  if (ws_bytes < sw.total)
+    return fail(c, FH_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes batch %d needs", ws_bytes,
+                sw.total, batch);
+  FrontEnd fe{aw, states, sw.front, sw.tokens};
+  return denoise_slice(c, w, batch, latent, motion_latent, nullptr, &fe, sigmas, n_steps, latent_out, sw.slice,
+                       carve(c, batch, nullptr).total, stream);
 }
 
 int fh_shader_clock(void* dev_buf, size_t bytes, int n_wg, int iters, void* stream, double* mhz) {

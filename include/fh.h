@@ -296,6 +296,25 @@ size_t fh_audio_workspace_bytes(const fh_audio_weights* w, int batch);
 int fh_audio_project(fh_ctx* ctx, const fh_audio_weights* w, int batch, const float* states, float* tokens,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The slice denoise fed from the speech encoder's states instead of audio
+ * tokens, as one call (and, with graphs on, one captured graph): the audio
+ * projection front end (fh_audio_project's steps) writes the slice's audio
+ * tokens straight into the blocks' bf16 audio buffer, which the per-slice
+ * audio K/V of every block then reads (the gizai:flashhead page, overview
+ * paragraph and type FlashHead: proj1, proj1vf, proj2, proj3, projNorm feed
+ * the blocks' cross-attention). states: device f32 [batch][layers]
+ * [state_frames][channels] as fh_audio_project takes them; the other
+ * arguments as fh_dit_denoise_slice. The workspace holds the slice's, the
+ * front end's and float32 tokens (for FH_PREC_FP32):
+ * fh_slice_from_states_workspace_bytes (0 for null or foreign arguments).
+ * Errors as fh_dit_denoise_slice, and FH_EINVAL for null or foreign audio
+ * weights or states.                                                        */
+size_t fh_slice_from_states_workspace_bytes(const fh_ctx* ctx, const fh_audio_weights* aw, int batch);
+int fh_dit_denoise_slice_from_states(fh_ctx* ctx, const fh_weights* w, const fh_audio_weights* aw, int batch,
+                                     const float* latent, const float* motion_latent, const float* states,
+                                     const float* sigmas, int n_steps, float* latent_out, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 /* Seed of FH_SAMPLER_RENOISE's noise (default 0). Returns FH_EINVAL for a null ctx. */
 int fh_set_noise_seed(fh_ctx* ctx, uint64_t seed);
 

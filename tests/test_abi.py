@@ -416,3 +416,17 @@ def test_vae_specs_and_argument_errors():
     assert L.fh_vae_weights_bind(ctypes.byref(v), None, 0, None, 0, ctypes.byref(h)) == fh.FH_EINVAL
     assert L.fh_vae_decode(None, ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41), ctypes.c_void_p(1 << 42),
                            1 << 30, None) == fh.FH_EINVAL
+
+
+def test_slice_from_states_argument_errors():
+    """The states-fed slice rejects null or foreign audio weights, null states
+    and short workspaces before any launch."""
+    ctx = fh.fh_create(synth.CONFIGS["toy"])
+    st, w = _bind(ctx)
+    assert st == fh.FH_OK
+    L, fake = fh.lib, ctypes.c_void_p(1 << 40)
+    sig = (ctypes.c_float * 2)(1.0, 0.0)
+    assert L.fh_slice_from_states_workspace_bytes(ctx, None, 1) == 0
+    assert L.fh_dit_denoise_slice_from_states(ctx, w, None, 1, fake, fake, fake, sig, 1, fake, fake, 1 << 30,
+                                              None) == fh.FH_EINVAL
+    fh.lib.fh_weights_release(w)

@@ -766,6 +766,75 @@ def test_audio_projection_feeds_the_slice(fh):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("precision", ["bf16", "fp32"])
+def test_slice_from_states(fh, precision):
+    """The one call from speech-encoder states to the denoised slice against
+    the oracle's front end then slice (toy), and against the two calls
+    (fh_audio_project then fh_dit_denoise_slice) on the GPU: the fused path
+    normalises the tokens straight to bf16, so the two differ only where a
+    token's bf16 rounding does."""
+    acfg, dcfg, ctx, Wa, aw, ws_a = _audio_model(fh, "toy", 2)
+    W = synth.make_weights(dcfg)
+    w = fh.fh_weights_bind(ctx, W)
+    if precision == "fp32":
+        fh.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP32)
+    ws = fh.workspace(ctx, 2)
+    ws_s = fh.slice_from_states_workspace(ctx, aw, 2)
+    S = synth.audio_states(acfg, 2)
+    lat, mot, _ = synth.slice_inputs(dcfg, 2)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say(f"states -> toy slice in one call, B=2, {precision}")
+    out = torch.empty_like(dev(lat))
+    fh.fh_dit_denoise_slice_from_states(ctx, w, aw, dev(lat), dev(mot), dev(S), sig, out, ws_s)
+    tok = torch.empty(2, dcfg.audio_tokens, dcfg.dim, dtype=torch.float32, device="cuda")
+    fh.fh_audio_project(ctx, aw, dev(S), tok, ws_a)
+    two = torch.empty_like(out)
+    fh.fh_dit_denoise_slice(ctx, w, dev(lat), dev(mot), tok, sig, two, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bar = TOL_F32 if precision == "fp32" else TOL
+    for b in range(2):
+        ref_tok = AU.audio_project(S[b:b + 1], synth.weights_f32(Wa), acfg)
+        ref = O.denoise_slice(lat[b:b + 1], mot[b:b + 1], ref_tok, sig, synth.weights_f32(W), dcfg)
+        err = O.rel_err(got[b:b + 1], ref, dcfg.motion_frames)
+        say(f"  lane {b} rel err {err:.3e} (bar {bar})")
+        assert err <= bar
+    diff = O.rel_err(got, two.cpu().numpy(), dcfg.motion_frames)
+    say(f"  one call vs two calls {diff:.3e}")
+    if precision == "fp32":
+        np.testing.assert_array_equal(got, two.cpu().numpy())   # the same float32 kernels on the same tokens
+    else:
+        assert diff <= 5e-3
+    again = torch.empty_like(out)
+    fh.fh_dit_denoise_slice_from_states(ctx, w, aw, dev(lat), dev(mot), dev(S), sig, again, ws_s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(again.cpu().numpy(), got)
+
+
+def test_slice_from_states_lite_size(fh):
+    """The Lite front end (12 x 200 x 768 states, 46080-wide features) into the
+    full-width 30-block slice, one call against the two calls."""
+    acfg, dcfg, ctx, Wa, aw, ws_a = _audio_model(fh, "lite", 1)
+    W = synth.make_weights(dcfg)
+    w = fh.fh_weights_bind(ctx, W)
+    ws = fh.workspace(ctx, 1)
+    ws_s = fh.slice_from_states_workspace(ctx, aw, 1)
+    S = synth.audio_states(acfg, 1)
+    lat, mot, _ = synth.slice_inputs(dcfg, 1)
+    sig = list(synth.SLICE_SIGMAS)
+    say("states -> Lite slice in one call")
+    out = torch.empty_like(dev(lat))
+    fh.fh_dit_denoise_slice_from_states(ctx, w, aw, dev(lat), dev(mot), dev(S), sig, out, ws_s)
+    tok = torch.empty(1, dcfg.audio_tokens, dcfg.dim, dtype=torch.float32, device="cuda")
+    fh.fh_audio_project(ctx, aw, dev(S), tok, ws_a)
+    two = torch.empty_like(out)
+    fh.fh_dit_denoise_slice(ctx, w, dev(lat), dev(mot), tok, sig, two, ws)
+    torch.cuda.synchronize()
+    diff = O.rel_err(out.cpu().numpy(), two.cpu().numpy(), dcfg.motion_frames)
+    say(f"  one call vs two calls {diff:.3e}")
+    assert diff <= 5e-3
+
+
 # ------------------------------------------------------------------ largest supported sizes
 MAXCFG = synth.CONFIGS["slice"].replace(n_blocks=1, dim=2048, n_heads=16, ffn_dim=8192, in_ch=64, out_ch=64,
                                         frames=3, height=8, width=12, motion_frames=2, audio_per_frame=64)
