@@ -39,7 +39,7 @@ EXPORTS = ["fh_create", "fh_destroy", "fh_weight_count", "fh_weight_spec", "fh_w
            "fh_slice_from_states_workspace_bytes", "fh_dit_denoise_slice_from_states",
            "fh_color_match_workspace_bytes", "fh_color_match", "fh_color_match_noalloc",
            "fh_color_match_noalloc_max_bytes", "fh_vae_weight_count", "fh_vae_weight_spec", "fh_vae_weights_bind",
-           "fh_vae_weights_release", "fh_vae_workspace_bytes", "fh_vae_decode", "fh_kernel_time", "fh_shader_clock",
+           "fh_vae_weights_release", "fh_vae_workspace_bytes", "fh_vae_decode", "fh_kernel_time", "fh_debug_workgroup_order", "fh_shader_clock",
            "fh_last_error", "fh_status_str"]
 
 
@@ -115,6 +115,7 @@ def _load():
         "fh_vae_decode": (i32, [vp, vp, vp, vp, sz, vp]),
         "fh_kernel_time": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "fh_shader_clock": (i32, [vp, ctypes.c_size_t, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]),
+        "fh_debug_workgroup_order": (i32, [i32]),
         "fh_last_error": (ctypes.c_char_p, [vp]),
         "fh_status_str": (ctypes.c_char_p, [i32]),
     }
@@ -465,6 +466,13 @@ def fh_shader_clock(n_wg=1024, iters=20000, stream=None):
     if st != FH_OK:
         raise FHError(st, f"fh_shader_clock: {fh_status_str(st)}")
     return mhz.value
+
+
+def fh_debug_workgroup_order(reversed_order: bool):
+    """Reverse (True) or restore the workgroup order of the LDS-sharing kernels."""
+    st = lib.fh_debug_workgroup_order(int(bool(reversed_order)))
+    if st != FH_OK:
+        raise FHError(st, f"fh_debug_workgroup_order: {fh_status_str(st)}")
 
 
 def fh_last_error(ctx):

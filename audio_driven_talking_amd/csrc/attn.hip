@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   // workgroups are dealt round-robin to the 8 XCDs; give each XCD a run of
   // consecutive (query tile fastest) workgroups so the query tiles of a head
   // share one L2 copy of its keys and values
-  const int wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const unsigned bx = wg_x();
+  const int wg = (bx & 7) * (gridDim.x >> 3) + (bx >> 3);
   if (wg >= n_wg) return;
   const int qt = wg % n_qt, h = (wg / n_qt) % n_heads, b = wg / (n_qt * n_heads);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(256, 1) void flash_attn_mx_kernel(
     const uint8_t* __restrict__ ks, int ldq, const uint8_t* __restrict__ vt, const uint8_t* __restrict__ vts,
     bf16_t* __restrict__ o, int ldo, int N, int D, float scale_log2, int n_qt, int n_heads, int n_wg) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * MX_STAGE];
-  const int wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const unsigned bx = wg_x();
+  const int wg = (bx & 7) * (gridDim.x >> 3) + (bx >> 3);
   if (wg >= n_wg) return;
   const int qt = wg % n_qt, h = (wg / n_qt) % n_heads, b = wg / (n_qt * n_heads);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -699,5 +701,7 @@ hipError_t cross_attn(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, const
                full, scale_log2, ssq, groups, g, eps);
   return hipGetLastError();
 }
+
+hipError_t set_wg_reverse_attn(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void color_stats_kernel(const float* __restric
                                                           const float* __restrict__ pic, int64_t npix_ref,
                                                           int F, ColorTables T, double* __restrict__ partial) {
   __shared__ double red[6][256];
-  const int img = blockIdx.y, chunk = blockIdx.x;
+  const int img = blockIdx.y, chunk = wg_x();
   const bool is_ref = img == F;
   const float* base = is_ref ? pic : frames + (int64_t)img * npix;
   const int64_t ps = is_ref ? npix_ref : (int64_t)F * npix;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void color_finalize_kernel(const float* __rest
                                                              const double* __restrict__ partial, int nchunks, int F,
                                                              ColorTables T, float* __restrict__ coef) {
   __shared__ double red[6][256];
-  const int f = blockIdx.x;
+  const int f = wg_x();
   const int64_t fps = (int64_t)F * npix;
   float kf[3], kr[3];
   {
@@ -395,5 +395,7 @@ hipError_t color_scratch(void** ptr) {
   *ptr = g_scratch_dev[dev];
   return hipSuccess;
 }
+
+hipError_t set_wg_reverse_color(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

@@ -1540,6 +1540,15 @@ int fh_dit_denoise_slice_from_states(fh_ctx* c, const fh_weights* w, const fh_au
                        carve(c, batch, nullptr).total, stream);
 }
 
+int fh_debug_workgroup_order(int reversed) {
+  if (reversed != 0 && reversed != 1) return FH_EINVAL;
+  hipError_t (*const set[])(int) = {fh::set_wg_reverse_gemm, fh::set_wg_reverse_attn, fh::set_wg_reverse_color,
+                                    fh::set_wg_reverse_norm, fh::set_wg_reverse_misc, fh::set_wg_reverse_vae};
+  for (auto f : set)
+    if (f(reversed) != hipSuccess) return FH_EHIP;
+  return FH_OK;
+}
+
 int fh_shader_clock(void* dev_buf, size_t bytes, int n_wg, int iters, void* stream, double* mhz) {
   if (!dev_buf || !mhz || n_wg < 1 || n_wg > 65536 || iters < 1 || iters > (1 << 20) ||
       bytes < (size_t)32 * n_wg)

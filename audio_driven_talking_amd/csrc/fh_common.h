@@ -119,3 +119,12 @@ template <typename T>
 __device__ __forceinline__ void mfma_drain(T& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
 }
+
+// Debugging aid for races through LDS: when set (fh_debug_workgroup_order),
+// the kernels whose waves share LDS take their work in the reverse order of
+// workgroup ids along x, so a scheduling-dependent result shows up as a
+// difference between the two orders. Every source file holds its own copy
+// of the flag; set_wg_reverse() sets the copy of the file that calls it.
+static __constant__ int c_wg_reverse = 0;
+__device__ __forceinline__ unsigned wg_x() { return c_wg_reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x; }
+static inline hipError_t set_wg_reverse(int r) { return hipMemcpyToSymbol(HIP_SYMBOL(c_wg_reverse), &r, sizeof r); }

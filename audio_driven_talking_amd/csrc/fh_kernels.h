@@ -310,6 +310,14 @@ hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t
 // latent [C][F H W] float32 -> channels-last F16; also clears 256 bytes at zero
 hipError_t latent_to_f16(const float* lat, int C, int64_t FHW, _Float16* out, _Float16* zero, hipStream_t s);
 
+// the reversed-workgroup-order flag of each source file (fh_common.h, wg_x)
+hipError_t set_wg_reverse_gemm(int r);
+hipError_t set_wg_reverse_attn(int r);
+hipError_t set_wg_reverse_color(int r);
+hipError_t set_wg_reverse_norm(int r);
+hipError_t set_wg_reverse_misc(int r);
+hipError_t set_wg_reverse_vae(int r);
+
 // shader-clock probe: n_wg workgroups of MFMA loops, 4 counters each into out
 hipError_t clock_probe(uint64_t* out, int n_wg, int iters, hipStream_t s);
 

@@ -322,7 +322,7 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   static_assert(NS >= 2 && (NS - 1) * (GA + GW) < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
 
-  int bid = blockIdx.x;
+  int bid = wg_x();
   const int per_xcd = gridDim.x >> 3;
   bid = (bid & 7) * per_xcd + (bid >> 3);
   if (bid >= tiles * splits * (BATCH ? ep.batch_n : 1)) return;
@@ -529,7 +529,7 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
   static_assert(NS >= 2 && (NS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
 
-  int bid = blockIdx.x;
+  int bid = wg_x();
   const int per_xcd = gridDim.x >> 3;
   bid = (bid & 7) * per_xcd + (bid >> 3);
   if (bid >= tiles * splits) return;
@@ -965,5 +965,7 @@ hipError_t mx_quantize(const float* in_f, const bf16_t* in_b, int64_t rows, int 
   else mx_quantize_kernel<bf16_t><<<grid, 256, 0, s>>>(in_b, rows, K, codes, scales);
   return hipGetLastError();
 }
+
+hipError_t set_wg_reverse_gemm(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16 + wave * GV_OPW;
+  const int n0 = wg_x() * 16 + wave * GV_OPW;
   float acc[GV_OPW][MAXR];
 #pragma unroll
   for (int o = 0; o < GV_OPW; ++o)
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restric
                                                           const float* __restrict__ bp,
                                                           float* __restrict__ x, int D) {
   __shared__ float sl[MAXC * PT];
-  const int b = blockIdx.y, t0 = blockIdx.x * PT;
+  const int b = blockIdx.y, t0 = wg_x() * PT;
   for (int i = threadIdx.x; i < C * PT; i += 256) {
     const int c = i / PT, tt = i % PT;
     sl[i] = t0 + tt < N ? lat[((int64_t)b * C + c) * N + t0 + tt] : 0.f;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void head_euler_kernel(
     const float* __restrict__ motion, int nmt, float sigma, float sigma_next, SamplerArgs sa) {
   __shared__ f32x4 part[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 16;
+  const int t0 = wg_x() * 16;
   const int lr = lane & 15, lq = lane >> 4;
   const int row = min(t0 + lr, B * N - 1);
   const int kq = D / 4;  // this wave's k range [wave kq, (wave + 1) kq)
@@ -437,5 +437,7 @@ hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s) {
   f32_to_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in, out, n);
   return hipGetLastError();
 }
+
+hipError_t set_wg_reverse_misc(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
     const float* __restrict__ g, const float* __restrict__ b, PendingRes pend, uint8_t* __restrict__ out_q,
     uint16_t* __restrict__ q_scale) {
   __shared__ float red[8];
-  const int row = blockIdx.x;
+  const int row = wg_x();
   const int c = threadIdx.x * 8;
   const bool on = c < D;
   float* xr = x + (int64_t)row * D + c;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
     int rows_per_lane, int head_dim, float eps, uint8_t* __restrict__ out_q, uint8_t* __restrict__ q_scale,
     int ldq, const BatchEntry* __restrict__ tab, int tab_rows) {
   __shared__ float red[8];
-  const int row = blockIdx.x;
+  const int row = wg_x();
   const int part = threadIdx.x / tpp, tp = threadIdx.x % tpp;
   const int c = tp * 8;
   const bool on = c < D;
@@ -205,5 +205,7 @@ hipError_t rmsnorm_bf16_table(bf16_t* p, int ld, int rows, int D, const BatchEnt
                                            nullptr, 0, tab, rows_per_entry);
   return hipGetLastError();
 }
+
+hipError_t set_wg_reverse_norm(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

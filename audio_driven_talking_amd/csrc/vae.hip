@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
   static_assert((CNS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[CNS * SLAB];
 
-  int bid = blockIdx.x;
+  int bid = wg_x();
   bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
   if (bid >= n_tiles) return;
   const int tm = bid % tiles_m, tn = bid / tiles_m;
@@ -280,5 +280,7 @@ hipError_t latent_to_f16(const float* lat, int C, int64_t FHW, _Float16* out, _F
   latent_f16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(lat, C, FHW, out, zero);
   return hipGetLastError();
 }
+
+hipError_t set_wg_reverse_vae(int r) { return set_wg_reverse(r); }
 
 }  // namespace fh

@@ -446,6 +446,16 @@ int fh_vae_decode(const fh_vae_weights* w, const float* latent, float* frames, v
 /* Total milliseconds and number of timed launches since the last read.      */
 int fh_kernel_time(fh_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Debugging aid (not a step of the method), process-wide on the current
+ * device: reversed = 1 makes every kernel whose waves share LDS (GEMMs,
+ * attention, norms, head, decoder convolutions, colour statistics) take its
+ * work in the reverse order of workgroup ids, 0 restores the normal order.
+ * No reduction depends on scheduling, so results must be bit-identical in
+ * both orders; a difference would expose a race through LDS or between
+ * workgroups. It waits for the device (a synchronous symbol copy); call it
+ * with no library work in flight. FH_EINVAL for other values, FH_EHIP.      */
+int fh_debug_workgroup_order(int reversed);
+
 /* Measurement aid (not a step of the method): the shader clock while every
  * compute unit runs back-to-back bf16 MFMAs, in MHz. Launches n_wg
  * workgroups of 256 threads, each timing `iters` MFMA groups with the shader

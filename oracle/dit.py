@@ -46,7 +46,7 @@ __all__ = [
     "apply_rope", "softmax", "attention", "split_heads", "merge_heads",
     "self_attention", "audio_kv", "cross_attention", "dit_block",
     "dit_block_from_temb", "patchify", "unpatchify", "dit_flow", "pin_motion",
-    "euler_step", "denoise_slice", "block_weights", "to64", "rel_err",
+    "euler_step", "denoise_slice", "block_weights", "to64", "rel_err", "err_stats",
 ]
 
 
@@ -375,3 +375,16 @@ def rel_err(got, ref, motion_frames=0):
     if motion_frames:
         g, r = g[:, :, motion_frames:], r[:, :, motion_frames:]
     return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-300))
+
+
+def err_stats(got, ref, motion_frames=0):
+    """The comparison metric and its two companions, over the same elements as
+    rel_err: the max-norm error max|g - r| / max|r|, the relative L2 error
+    ||g - r|| / ||r||, and the 99.9th percentile of |g - r| / max|r| (one
+    outlier moves the first, not the other two)."""
+    g, r = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    if motion_frames:
+        g, r = g[:, :, motion_frames:], r[:, :, motion_frames:]
+    d, scale = np.abs(g - r), max(np.abs(r).max(), 1e-300)
+    return {"max": float(d.max() / scale), "rel_l2": float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)),
+            "p999": float(np.percentile(d, 99.9) / scale)}

@@ -430,3 +430,8 @@ def test_slice_from_states_argument_errors():
     assert L.fh_dit_denoise_slice_from_states(ctx, w, None, 1, fake, fake, fake, sig, 1, fake, fake, 1 << 30,
                                               None) == fh.FH_EINVAL
     fh.lib.fh_weights_release(w)
+
+
+def test_debug_workgroup_order_rejects_other_values():
+    assert fh.lib.fh_debug_workgroup_order(2) == fh.FH_EINVAL
+    assert fh.lib.fh_debug_workgroup_order(-1) == fh.FH_EINVAL

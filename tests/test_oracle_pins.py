@@ -440,3 +440,24 @@ def test_float32_working_dtype_follows_the_float64_path():
         have = O.dit_block_from_temb(x, e, aud, Wt, 0, tc)
     assert have.dtype == np.float32
     assert O.rel_err(have - x, want - x) < 1e-5
+
+
+def test_err_stats_closed_forms():
+    """The three error figures on a constructed case: ref = 1 everywhere on
+    non-motion frames, got = ref except one element off by 0.5 and a 1e-3
+    offset on 1 % of the elements."""
+    ref = np.ones((1, 2, 3, 10, 10))
+    got = ref.copy()
+    got[:, :, 0] = 7.0                          # motion frame: ignored
+    flat = got[:, :, 1:].reshape(-1)
+    n = flat.size                                # 400
+    flat_idx = np.arange(n)
+    view = got[:, :, 1:].reshape(-1)
+    view[flat_idx[:4]] += 1e-3                   # 1 %
+    view[n - 1] += 0.5
+    got[:, :, 1:] = view.reshape(got[:, :, 1:].shape)
+    s = O.err_stats(got, ref, 1)
+    assert s["max"] == pytest.approx(0.5)
+    assert s["rel_l2"] == pytest.approx(np.sqrt(4e-6 + 0.25) / np.sqrt(n))
+    assert 1e-3 - 1e-12 <= s["p999"] <= 0.5      # the 99.9th percentile sits between the offsets and the outlier
+    assert O.err_stats(got, ref, 1)["max"] == O.rel_err(got, ref, 1)
