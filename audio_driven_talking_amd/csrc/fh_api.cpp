@@ -897,18 +897,23 @@ std::vector<Spec> vae_specs(const fh_vae_config& v) {
 
 struct VaeWS {
   _Float16 *zero, *x0, *a, *b, *c;
-  size_t total;
+  float* part;  // split-K partial sums of the layers that need them
+  size_t part_elems, total;
 };
 
 VaeWS carve_vae(const fh_vae_config& v, char* base) {
   int64_t T = v.frames, H = v.height, W = v.width, act = T * H * W * v.widths[0];
+  size_t parts = fh::conv_part_elems(T * H * W, v.latent_ch, v.widths[0]);
   for (int i = 0; i < 3; ++i) {
     act = std::max(act, T * H * W * v.widths[i]);
+    parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[i], v.widths[i]));
+    parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[i], 8 * v.widths[i + 1]));
     T = 2 * T - 1;
     H *= 2;
     W *= 2;
     act = std::max(act, T * H * W * v.widths[i + 1]);
   }
+  parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[3], v.out_ch * v.patch * v.patch));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -921,6 +926,8 @@ VaeWS carve_vae(const fh_vae_config& v, char* base) {
   w.a = take((size_t)act * 2);
   w.b = take((size_t)act * 2);
   w.c = take((size_t)act * 2);
+  w.part = (float*)take(parts * 4);
+  w.part_elems = parts;
   w.total = off;
   return w;
 }
@@ -1423,7 +1430,7 @@ int fh_vae_decode(const fh_vae_weights* w, const float* latent, float* frames, v
     a.out = out;
     a.res = res;
     a.frames = fr;
-    return fh::conv3d_f16(epi, a, s);
+    return fh::conv3d_f16(epi, a, ws.part, ws.part_elems, s);
   };
   FH_HIP(conv(fh::CONV_PLAIN, ws.x0, v.latent_ch, "conv_in", v.widths[0], ws.a, nullptr, nullptr));
   for (int i = 0; i < 3; ++i) {

@@ -292,7 +292,10 @@ hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s);
 //               out[2t + dt - 1][2h + dh][2w + dw][c], frame 2t + dt = 0 dropped
 //   CONV_FRAMES channel c 16 + 4 py + px to frames[c][t][4h + py][4w + px] = clamp((v + 1) / 2, 0, 1)
 // zero: 16 or more bytes of zeros (the padding row).
-enum ConvEpi { CONV_PLAIN = 0, CONV_RES = 1, CONV_UP = 2, CONV_FRAMES = 3 };
+// Layers whose tiles cannot fill the chip split K: each split's F32 sums go to
+// part ([splits][M][C_out], conv_part_elems elements), and a second kernel
+// adds them in index order before the same rounding and store.
+enum ConvEpi { CONV_PLAIN = 0, CONV_RES = 1, CONV_UP = 2, CONV_FRAMES = 3, CONV_PART = 4 };
 struct ConvArgs {
   const _Float16* in = nullptr;
   int T = 0, H = 0, W = 0, cin_log2 = 0;
@@ -304,7 +307,8 @@ struct ConvArgs {
   const _Float16* res = nullptr;
   float* frames = nullptr;
 };
-hipError_t conv3d_f16(int epi, const ConvArgs& a, hipStream_t s);
+hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems, hipStream_t s);
+size_t conv_part_elems(int64_t M, int cin, int cout);
 // RMS norm over the C channels of each of M positions (F32 sums), gain g, SiLU, F16 out
 hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t M, int C, float eps, hipStream_t s);
 // latent [C][F H W] float32 -> channels-last F16; also clears 256 bytes at zero

@@ -41,8 +41,51 @@ __device__ __forceinline__ int cswz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ float round16(float x) { return (float)(f16_t)x; }
 
+// The layer's output of 4 consecutive channels n..n+3 of position m from their
+// F32 sums: F16 sum, bias added in F32, F16, then stored in the layer's form.
+template <int EPI>
+__device__ __forceinline__ void store4(const ConvArgs& a, int m, int n, const float (&acc)[4]) {
+  const int HW = a.H * a.W;
+  const int t = m / HW, h = (m - t * HW) / a.W, w = m - t * HW - h * a.W;
+  const f32x4 b = *reinterpret_cast<const f32x4*>(a.bias + n);
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = round16(round16(acc[e]) + b[e]);
+  if constexpr (EPI == CONV_PLAIN || EPI == CONV_RES) {
+    f16_t* o = a.out + (int64_t)m * a.cout + n;
+    if constexpr (EPI == CONV_RES) {
+      const f16x4 r = *reinterpret_cast<const f16x4*>(a.res + (int64_t)m * a.cout + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = v[e] + (float)r[e];
+    }
+    const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
+    *reinterpret_cast<f16x4*>(o) = y;
+  } else if constexpr (EPI == CONV_UP) {
+    // channel n = s C' + c (C' a multiple of 4: the 4 channels share s)
+    const int cp = a.cout >> 3, s = n / cp, c = n - s * cp;
+    const int t2 = 2 * t + (s >> 2) - 1, h2 = 2 * h + ((s >> 1) & 1), w2 = 2 * w + (s & 1);
+    if (t2 >= 0) {
+      f16_t* o = a.out + ((int64_t)(t2 * 2 * a.H + h2) * 2 * a.W + w2) * cp + c;
+      const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
+      *reinterpret_cast<f16x4*>(o) = y;
+    }
+  } else {
+    // CONV_FRAMES: channel n = c 16 + 4 py + px -> pixel (4 h + py, 4 w + px) of colour c,
+    // value (v + 1) / 2 clamped to [0, 1]
+    const int c = n >> 4, py = (n >> 2) & 3;
+    float* o = a.frames + ((int64_t)(c * a.T + t) * 4 * a.H + 4 * h + py) * 4 * a.W + 4 * w;
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf((v[e] + 1.f) * 0.5f, 0.f), 1.f);
+    *reinterpret_cast<f32x4*>(o) = y;
+  }
+}
+
+// EPI == CONV_PART: split K; workgroup split ks multiplies slabs [ks KT / splits,
+// (ks + 1) KT / splits) and writes its raw F32 sums to part[ks][m][n]
 template <int BN, int EPI>
-__global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, int n_tiles) {
+__global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, int n_tiles, int splits,
+                                                     float* __restrict__ part) {
   constexpr int ROWB = CBK * 2;
   constexpr int SLAB = (CBM + BN) * ROWB;
   constexpr int GA = CBM / 64;   // 1 KB A-DMAs per wave per slab (16 rows of 64 B each)
@@ -54,11 +97,14 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
 
   int bid = wg_x();
   bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
-  if (bid >= n_tiles) return;
+  if (bid >= n_tiles * splits) return;
+  const int ks = bid / n_tiles;
+  bid -= ks * n_tiles;
   const int tm = bid % tiles_m, tn = bid / tiles_m;
   const int m0 = tm * CBM, n0 = tn * BN;
   const int HW = a.H * a.W, M = a.T * HW;
-  const int Cin = 1 << a.cin_log2, K = 27 * Cin, KT = (K + CBK - 1) / CBK;
+  const int Cin = 1 << a.cin_log2, K = 27 * Cin, KT_all = (K + CBK - 1) / CBK;
+  const int kt0 = ks * KT_all / splits, KT = (ks + 1) * KT_all / splits - kt0;  // this split's slabs
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -97,7 +143,7 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
   };
   auto dma_slab = [&](int buf, int kt) {
     char* sb = smem + buf * SLAB;
-    const int k0 = min(kt, KT - 1) * CBK;
+    const int k0 = (kt0 + min(kt, KT - 1)) * CBK;
 #pragma unroll
     for (int i = 0; i < GA; ++i) dma16(a_src(i, k0), sb + (wave + 4 * i) * 1024);
 #pragma unroll
@@ -152,47 +198,36 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
   for (int j = 0; j < MI; ++j) {
     const int m = m0 + wm * (CBM / 2) + 32 * j + lr;
     if (m >= M) continue;
-    const int t = m / HW, h = (m - t * HW) / a.W, w = m - t * HW - h * a.W;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * (BN / 2) + 32 * i + 8 * g + 4 * lh;
         if (n >= a.cout) continue;
-        const f32x4 b = *reinterpret_cast<const f32x4*>(a.bias + n);
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = round16(round16(acc[i][j][4 * g + e]) + b[e]);
-        if constexpr (EPI == CONV_PLAIN || EPI == CONV_RES) {
-          f16_t* o = a.out + (int64_t)m * a.cout + n;
-          if constexpr (EPI == CONV_RES) {
-            const f16x4 r = *reinterpret_cast<const f16x4*>(a.res + (int64_t)m * a.cout + n);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = v[e] + (float)r[e];
-          }
-          const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
-          *reinterpret_cast<f16x4*>(o) = y;
-        } else if constexpr (EPI == CONV_UP) {
-          // channel n = s C' + c (C' a multiple of 4: the 4 channels share s)
-          const int cp = a.cout >> 3, s = n / cp, c = n - s * cp;
-          const int t2 = 2 * t + (s >> 2) - 1, h2 = 2 * h + ((s >> 1) & 1), w2 = 2 * w + (s & 1);
-          if (t2 >= 0) {
-            f16_t* o = a.out + ((int64_t)(t2 * 2 * a.H + h2) * 2 * a.W + w2) * cp + c;
-            const f16x4 y = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
-            *reinterpret_cast<f16x4*>(o) = y;
-          }
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if constexpr (EPI == CONV_PART) {
+          const f32x4 y = {v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(part + ((int64_t)ks * M + m) * a.cout + n) = y;
         } else {
-          // CONV_FRAMES: channel n = c 16 + 4 py + px -> pixel (4 h + py, 4 w + px) of colour c,
-          // value (v + 1) / 2 clamped to [0, 1]
-          const int c = n >> 4, py = (n >> 2) & 3;
-          float* o = a.frames + ((int64_t)(c * a.T + t) * 4 * a.H + 4 * h + py) * 4 * a.W + 4 * w;
-          f32x4 y;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf((v[e] + 1.f) * 0.5f, 0.f), 1.f);
-          *reinterpret_cast<f32x4*>(o) = y;
+          store4<EPI>(a, m, n, v);
         }
       }
   }
+}
+
+// The split-K convolution's finish: the parts of 4 consecutive channels added
+// in index order, then the layer's rounding and store (store4).
+template <int EPI>
+__global__ __launch_bounds__(256) void conv_reduce_kernel(ConvArgs a, const float* __restrict__ part, int splits) {
+  const int64_t M = (int64_t)a.T * a.H * a.W;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= M * (a.cout / 4)) return;
+  const int64_t m = q / (a.cout / 4);
+  const int n = (int)(q - m * (a.cout / 4)) * 4;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(part + m * a.cout + n);
+  for (int k = 1; k < splits; ++k) sum = sum + *reinterpret_cast<const f32x4*>(part + (k * M + m) * a.cout + n);
+  const float v[4] = {sum[0], sum[1], sum[2], sum[3]};
+  store4<EPI>(a, (int)m, n, v);
 }
 
 // RMS norm over the C channels of each position (F32 sums), gain, SiLU, F16
@@ -236,16 +271,28 @@ __global__ __launch_bounds__(256) void latent_f16_kernel(const float* __restrict
 }
 
 template <int BN>
-hipError_t launch_conv(int epi, const ConvArgs& a, hipStream_t s) {
+hipError_t launch_conv(int epi, const ConvArgs& a, int splits, float* part, hipStream_t s) {
   const int64_t M = (int64_t)a.T * a.H * a.W;
   const int tiles_m = (int)((M + CBM - 1) / CBM);
   const int tiles = tiles_m * ((a.cout + BN - 1) / BN);
-  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
+  if (splits > 1) {
+    launch_timed(conv3d_kernel<BN, CONV_PART>, grid, block, s, a, tiles_m, tiles, splits, part);
+    const dim3 rgrid((unsigned)((M * (a.cout / 4) + 255) / 256));
+    switch (epi) {
+      case CONV_PLAIN: conv_reduce_kernel<CONV_PLAIN><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_RES: conv_reduce_kernel<CONV_RES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_UP: conv_reduce_kernel<CONV_UP><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_FRAMES: conv_reduce_kernel<CONV_FRAMES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (epi) {
-    case CONV_PLAIN: launch_timed(conv3d_kernel<BN, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_RES: launch_timed(conv3d_kernel<BN, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_UP: launch_timed(conv3d_kernel<BN, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_FRAMES: launch_timed(conv3d_kernel<BN, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_PLAIN: launch_timed(conv3d_kernel<BN, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles, 1, part); break;
+    case CONV_RES: launch_timed(conv3d_kernel<BN, CONV_RES>, grid, block, s, a, tiles_m, tiles, 1, part); break;
+    case CONV_UP: launch_timed(conv3d_kernel<BN, CONV_UP>, grid, block, s, a, tiles_m, tiles, 1, part); break;
+    case CONV_FRAMES: launch_timed(conv3d_kernel<BN, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles, 1, part); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -253,7 +300,24 @@ hipError_t launch_conv(int epi, const ConvArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t conv3d_f16(int epi, const ConvArgs& a, hipStream_t s) {
+int conv_splits(int64_t M, int cin, int cout) {
+  // split K where the output tiles cannot fill the chip: up to 256 workgroups,
+  // at least 8 slabs of 32 per split
+  const int bn = cout >= 128 ? 128 : 64;
+  const int64_t tiles = ((M + CBM - 1) / CBM) * ((cout + bn - 1) / bn);
+  const int kt = (27 * cin + CBK - 1) / CBK;
+  if (tiles >= 128 || kt < 16) return 1;
+  int sp = (int)(256 / tiles);
+  sp = sp < kt / 8 ? sp : kt / 8;
+  return sp < 1 ? 1 : sp;
+}
+
+size_t conv_part_elems(int64_t M, int cin, int cout) {
+  const int sp = conv_splits(M, cin, cout);
+  return sp > 1 ? (size_t)sp * M * cout : 0;
+}
+
+hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems, hipStream_t s) {
   const int64_t M = (int64_t)a.T * a.H * a.W;
   if (M <= 0) return hipSuccess;
   if (M > (1 << 30) || a.cin_log2 < 3 || a.cin_log2 > 10 || a.cout % 16 || !a.in || !a.w || !a.bias || !a.zero)
@@ -262,8 +326,10 @@ hipError_t conv3d_f16(int epi, const ConvArgs& a, hipStream_t s) {
   if (epi == CONV_RES && !a.res) return hipErrorInvalidValue;
   if (epi == CONV_UP && (a.cout % 32)) return hipErrorInvalidValue;  // 8 sub-positions x a multiple of 4 channels
   if (epi == CONV_FRAMES && (!a.frames || a.cout % 16)) return hipErrorInvalidValue;
+  const int splits = conv_splits(M, 1 << a.cin_log2, a.cout);
+  if (splits > 1 && (!part || part_elems < (size_t)splits * M * a.cout)) return hipErrorInvalidValue;
   // 128 output channels per tile where there are that many, else 64
-  return a.cout >= 128 ? launch_conv<128>(epi, a, s) : launch_conv<64>(epi, a, s);
+  return a.cout >= 128 ? launch_conv<128>(epi, a, splits, part, s) : launch_conv<64>(epi, a, splits, part, s);
 }
 
 hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t M, int C, float eps, hipStream_t s) {
