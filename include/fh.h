@@ -203,7 +203,9 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       and 32-key block; both products on the block-scaled MFMA; sums and
  *       softmax in float32. Needs fh_weights_quantize_fp8 and tokens per lane
  *       a multiple of 64 (FH_EUNSUPPORTED otherwise); the workspace grows
- *       (query fh_workspace_bytes after setting it).                        */
+ *       (query fh_workspace_bytes after setting it). The gain over
+ *       FH_PREC_FP8_FFN comes from the FP8 QKV projection: the attention
+ *       kernel itself is softmax-bound and no faster than the bf16 one.    */
 enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2, FH_PREC_FP8_ATTN = 3 };
 /* Kernel classes of FH_OPT_TIME_KERNEL. FH_K_AUDIO_KV is the once-per-slice
  * audio keys and values of every block (all of its launches as one sample). */
