@@ -105,6 +105,7 @@ struct fh_ctx {
   int sampler = FH_SAMPLER_EULER;
   uint64_t noise_seed = 0;
   int precision = FH_PREC_BF16;
+  bool prefetch = true;  // FH_OPT_PREFETCH
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_free, ev_pending;
   double time_ms = 0.0;
   int64_t time_count = 0;
@@ -356,15 +357,28 @@ int audio_kv_all(fh_ctx* c, const fh_weights* w, int B, const WS& ws, hipStream_
 // pend_in: a residual update left pending by the previous block (applied by
 // the first LayerNorm); pend_out: if non-null, the FFN output projection may
 // leave its residual update pending there (split K) instead of applying it.
+// Half i (0, 1) of a block's FFN down-projection weights as a prefetch range:
+// the attention output and cross-attention query GEMMs each read one from HBM
+// while they run, so the down-projection finds its weights in the memory-side
+// cache (a 30-block slice leaves every block's weights cold).
+fh::Prefetch ffn2_half(const WBlock& wb, int D, int Fd, int i) {
+  const int64_t total = (int64_t)D * Fd * 2, half = (total / 2) & ~(int64_t)1023;
+  fh::Prefetch pf;
+  pf.p[0] = reinterpret_cast<const char*>(wb.ffn2_w) + i * half;
+  pf.bytes[0] = i ? total - half : half;
+  return pf;
+}
+
 int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int e0_stride,
               const bf16_t* kc, const bf16_t* vct, const WS& ws, hipStream_t s,
-              const fh::PendingRes* pend_in, fh::PendingRes* pend_out) {
+              const fh::PendingRes* pend_in, fh::PendingRes* pend_out, const WBlock* next) {
   const fh_config& g = c->cfg;
   const int N = c->N, D = g.dim, M = B * N, Fd = g.ffn_dim;
   const float scale = 1.0f / std::sqrt((float)g.head_dim);
   // FP8 self-attention: the QKV projection too runs on MX-FP8 operands (the
   // LayerNorm writes codes and scales for it)
   const bool mx_attn = c->precision == FH_PREC_FP8_ATTN;
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN || mx_attn;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
@@ -412,6 +426,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.gate_e0 = e0 + 2 * D;
     ep.gate_stride = e0_stride;
     ep.rows_per_lane = N;
+    if (c->prefetch && !fp8) ep.pf = ffn2_half(wb, D, Fd, 0);
     FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.ao, D, wb.o_w, D, M, D, D, ep, s));
   }
   {
@@ -428,6 +443,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.out_bf = ws.qc;
     ep.ldo = D;
     ep.ssq = ws.ssq;
+    if (c->prefetch && !fp8) ep.pf = ffn2_half(wb, D, Fd, 1);
     FH_HIP(fh::gemm_bf16(fh::EPI_BF16_SSQ, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
   }
   if (c->fold_co) {
@@ -463,7 +479,6 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
       FH_HIP(fh::gemm_bf16(fh::EPI_RES, ws.ao, D, wb.co_w, D, M, D, D, ep, s));
     }
   }
-  const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod + 3 * D, wb.mod + 4 * D, e0 + 3 * D,
@@ -499,8 +514,17 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
       if (fp8)
         FH_HIP(fh::gemm_mx_splitk(ws.uq, Fd, ws.us, wb.ffn2_q, Fd, wb.ffn2_s, M, D, Fd, ws.part,
                                   (size_t)2 * M * D, s));
-      else
-        FH_HIP(fh::gemm_bf16_splitk(ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ws.part, (size_t)2 * M * D, s));
+      else {
+        // the next block's attention output and cross-attention query weights, read from HBM
+        // meanwhile
+        fh::Prefetch pf;
+        if (c->prefetch && next) {
+          pf.p[0] = next->o_w;
+          pf.p[1] = next->cq_w;
+          pf.bytes[0] = pf.bytes[1] = (int64_t)D * D * 2;
+        }
+        FH_HIP(fh::gemm_bf16_splitk(ws.u, Fd, wb.ffn2_w, Fd, M, D, Fd, ws.part, (size_t)2 * M * D, s, pf));
+      }
       pend_out->part = ws.part;
       pend_out->nparts = 2;
       pend_out->bias = ep.bias;
@@ -794,8 +818,10 @@ int enqueue_slice(fh_ctx* c, const fh_weights* w, int B, const float* latent, co
       fh::PendingRes pend;
       for (int i = 0; i < g.n_blocks; ++i) {
         fh::PendingRes next;
+        // the block after this one: the next of this step, or the first of the next step
+        const WBlock* after = i + 1 < g.n_blocks ? &w->blk[i + 1] : st + 1 < n_steps ? &w->blk[0] : nullptr;
         int rc = run_block(c, w->blk[i], B, ws.x, e0, 0, ws.kc + i * kslot(c, B),
-                           ws.vct + i * vslot(c, B), ws, s, &pend, &next);
+                           ws.vct + i * vslot(c, B), ws, s, &pend, &next, after);
         if (rc) return rc;
         pend = next;
       }
@@ -1088,7 +1114,7 @@ int fh_dit_block_forward(fh_ctx* c, const fh_weights* w, int block, int batch, f
   if (f32) return run_block_f32(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.fkc, wsp.fvc, wsp, s);
   // the same arithmetic as inside a slice: a pending FFN residual is applied at the end
   fh::PendingRes pend;
-  rc = run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s, nullptr, &pend);
+  rc = run_block(c, w->blk[block], batch, x, wsp.e0, 6 * D, wsp.kc, wsp.vct, wsp, s, nullptr, &pend, nullptr);
   if (rc) return rc;
   FH_HIP(fh::residual_from_parts(x, D, pend, batch * c->N, D, s));
   return FH_OK;
@@ -1133,7 +1159,7 @@ int denoise_slice(fh_ctx* c, const fh_weights* w, int batch, const float* latent
                                fe ? (uint64_t)(uintptr_t)fe->tokens : 0,
                                (uint64_t)(uintptr_t)latent_out, (uint64_t)(uintptr_t)ws,
                                (uint64_t)n_steps, (uint64_t)c->sampler, c->noise_seed,
-                               (uint64_t)c->precision};
+                               (uint64_t)c->precision, (uint64_t)c->prefetch};
   for (int i = 0; i <= n_steps && n_steps > 0; ++i) {
     uint32_t b;
     std::memcpy(&b, &sigmas[i], 4);
@@ -1195,6 +1221,10 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32 && value != FH_PREC_FP8_ATTN)
       return fail(c, FH_EINVAL, "unknown precision %d", value);
     c->precision = value;
+    return FH_OK;
+  }
+  if (option == FH_OPT_PREFETCH) {
+    c->prefetch = value != 0;
     return FH_OK;
   }
   if (option == FH_OPT_SAMPLER) {

@@ -73,6 +73,20 @@ struct BatchTableArgs {
 // write n entries of args into dst (device), on the stream (capturable)
 hipError_t fill_batch_table(BatchEntry* dst, const BatchTableArgs& args, hipStream_t s);
 
+// Weights a later kernel will read, to be fetched while this kernel runs: up to
+// three byte ranges. A prefetching GEMM launch carries one more wave per
+// workgroup, which reads its share of the ranges (1 KB pieces, the grid's
+// workgroups taking them in turn) into a scratch area of LDS spread over the
+// main loop. The data then sits in the memory-side cache when its consumer
+// starts, instead of in HBM. Results are unaffected.
+struct Prefetch {
+  static constexpr int R = 3;
+  const void* p[R] = {nullptr, nullptr, nullptr};
+  int64_t bytes[R] = {0, 0, 0};
+  __host__ __device__ int64_t kb(int i) const { return p[i] ? bytes[i] >> 10 : 0; }  // whole KB pieces of range i
+  __host__ __device__ bool any() const { return kb(0) + kb(1) + kb(2) > 0; }
+};
+
 struct EpiArgs {
   const float* bias = nullptr;
   bf16_t* out_bf = nullptr;
@@ -102,6 +116,7 @@ struct EpiArgs {
   const BatchEntry* batch = nullptr;
   int batch_n = 1;
   int64_t batch_a_stride = 0, batch_out_stride = 0;
+  Prefetch pf;  // honoured by the 128 x 64 residual and query launches and by split K
 };
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -169,7 +184,7 @@ __device__ __forceinline__ f32x4 apply_pending(const PendingRes& r, f32x4 x, int
 // Split-K form of the residual GEMMs: the two halves of K into part[0..1].
 bool gemm_splitk_ok(int M, int N, int K);
 hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
-                            float* part, size_t part_elems, hipStream_t s);
+                            float* part, size_t part_elems, hipStream_t s, const Prefetch& pf = Prefetch());
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s);
 // Split-K partial products of a small-M GEMM: part[s][m][n] = sum over K range s
 // (K / splits columns each) of A[m] . W[n] (64 x 128 tiles; N % 128 == 0,

@@ -304,8 +304,43 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
   }
 }
 
-template <int EPI, int BM, int BN, int BK, int NS, int KW, bool BATCH>
-__global__ __launch_bounds__(256 * KW, (KW == 1 && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
+// The prefetch wave of a PF launch: it takes the same workgroup barriers as
+// the compute waves (the prologue's, one per slab, the one after the loop and,
+// with two wave groups, the hand-over's) and between them issues its share of
+// the 1 KB pieces of ep.pf into a scratch KB of LDS, spread evenly over slabs
+// KT/8 .. 3KT/4: after the tiles' own first fetches from HBM, and early enough
+// to land before the tiles end. It never waits on its own loads before a
+// barrier (at most 48 in flight), so it cannot hold the others back.
+template <int KW>
+__device__ __forceinline__ void prefetch_wave(const Prefetch& pf, char* lds, int64_t wg, int64_t n_wg, int KT,
+                                              int lane) {
+  const int64_t n0 = pf.kb(0), n1 = pf.kb(1), n = n0 + n1 + pf.kb(2);
+  const int64_t mine = wg < n ? (n - 1 - wg) / n_wg + 1 : 0;  // pieces wg, wg + n_wg, ...
+  int64_t i = 0;
+  auto issue_to = [&](int64_t end) {
+    for (; i < end; ++i) {
+      const int64_t j = wg + i * n_wg;
+      const char* src = j < n0        ? static_cast<const char*>(pf.p[0]) + (j << 10)
+                        : j < n0 + n1 ? static_cast<const char*>(pf.p[1]) + ((j - n0) << 10)
+                                      : static_cast<const char*>(pf.p[2]) + ((j - n0 - n1) << 10);
+      wait_vm<48>();
+      dma16(src + 16 * lane, lds);
+    }
+  };
+  const int k0 = KT / 8, k1 = max(k0 + 1, 3 * KT / 4);
+  barrier();
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt >= k0) issue_to(mine * min(kt - k0 + 1, k1 - k0) / (k1 - k0));
+    barrier();
+  }
+  barrier();
+  if (KW == 2) barrier();
+  wait_vm<0>();
+}
+
+template <int EPI, int BM, int BN, int BK, int NS, int KW, bool BATCH, bool PF>
+__global__ __launch_bounds__(256 * KW + (PF ? 64 : 0),
+                             (KW == 1 && !PF && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
                   int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
   constexpr int NW = 4 * KW;           // waves: KW groups of 2 x 2, group g takes k-steps g KK/KW ..
@@ -320,7 +355,8 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   static_assert(BM % 64 == 0 && BN % 64 == 0 && GA * RG * NW == BM && GW * RG * NW == BN, "tile shape");
   static_assert(KW == 1 || KW == 2, "one or two wave groups along K");
   static_assert(NS >= 2 && (NS - 1) * (GA + GW) < 64, "DMA wait count must fit vmcnt");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
+  static_assert(!PF || !BATCH, "prefetch only in plain launches");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB + (PF ? 1024 : 0)];
 
   int bid = wg_x();
   const int per_xcd = gridDim.x >> 3;
@@ -352,6 +388,13 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   const int kg = wave >> 2;                    // wave group along K
   const int wm = (wave >> 1) & 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
+  if constexpr (PF) {
+    if (wave == NW) {
+      prefetch_wave<KW>(ep.pf, smem + NS * SLAB, tm + (int64_t)tiles_m * tn + (int64_t)ks * tiles,
+                        (int64_t)tiles * splits, K / BK, lane);
+      return;
+    }
+  }
 
   // DMA: lane fills LDS row r = RG g + lane/CH, physical chunk lane%CH, which
   // holds logical chunk (lane%CH) ^ swz(r); every wave of both groups takes
@@ -730,7 +773,7 @@ __global__ __launch_bounds__(256) void residual_from_parts_kernel(float* __restr
   *xp = apply_pending(r, *xp, m, n, M, N);
 }
 
-template <int BM, int BN, int BK, int NS, int KW = 1, bool BATCH = false>
+template <int BM, int BN, int BK, int NS, int KW = 1, bool BATCH = false, bool PF = false>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                   const EpiArgs& ep, hipStream_t s, int splits = 1) {
   if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
@@ -752,18 +795,27 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   const int tiles = tiles_m * (N / BN);
   const int64_t wgs = (int64_t)tiles * splits * ep.batch_n;
   if (wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256 * KW);
-#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
-  switch (epi) {
-    case EPI_BF16: FH_GEMM(EPI_BF16); break;
-    case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;
-    case EPI_GATED_RES: FH_GEMM(EPI_GATED_RES); break;
-    case EPI_RES: FH_GEMM(EPI_RES); break;
-    case EPI_SPLIT_T: FH_GEMM(EPI_SPLIT_T); break;
-    case EPI_SPLIT_T_MX: FH_GEMM(EPI_SPLIT_T_MX); break;
-    case EPI_PARTIAL: FH_GEMM(EPI_PARTIAL); break;
-    case EPI_BF16_SSQ: FH_GEMM(EPI_BF16_SSQ); break;
-    default: return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256 * KW + (PF ? 64 : 0));
+#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH, PF>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
+  if constexpr (PF) {  // the forms that prefetch: the residual, query and split-K products
+    if (!ep.pf.any()) return hipErrorInvalidValue;
+    if (epi == EPI_GATED_RES) FH_GEMM(EPI_GATED_RES);
+    else if (epi == EPI_RES) FH_GEMM(EPI_RES);
+    else if (epi == EPI_BF16_SSQ) FH_GEMM(EPI_BF16_SSQ);
+    else if (epi == EPI_PARTIAL) FH_GEMM(EPI_PARTIAL);
+    else return hipErrorInvalidValue;
+  } else {
+    switch (epi) {
+      case EPI_BF16: FH_GEMM(EPI_BF16); break;
+      case EPI_GELU_BF16: FH_GEMM(EPI_GELU_BF16); break;
+      case EPI_GATED_RES: FH_GEMM(EPI_GATED_RES); break;
+      case EPI_RES: FH_GEMM(EPI_RES); break;
+      case EPI_SPLIT_T: FH_GEMM(EPI_SPLIT_T); break;
+      case EPI_SPLIT_T_MX: FH_GEMM(EPI_SPLIT_T_MX); break;
+      case EPI_PARTIAL: FH_GEMM(EPI_PARTIAL); break;
+      case EPI_BF16_SSQ: FH_GEMM(EPI_BF16_SSQ); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef FH_GEMM
   return hipGetLastError();
@@ -791,12 +843,14 @@ bool gemm_splitk_ok(int M, int N, int K) {
 }
 
 hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
-                            float* part, size_t part_elems, hipStream_t s) {
+                            float* part, size_t part_elems, hipStream_t s, const Prefetch& pf) {
   if (!gemm_splitk_ok(M, N, K) || lda % 8 || ldw % 8) return hipErrorInvalidValue;
   EpiArgs ep;
   ep.part = part;
   ep.part_elems = part_elems;
+  ep.pf = pf;
   // two wave groups along K: 2.3 % faster than one group on the FFN down-projection at 1280 tokens
+  if (pf.any()) return launch<128, 128, 64, 4, 2, false, true>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
   return launch<128, 128, 64, 4, 2>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
 }
 
@@ -843,10 +897,10 @@ hipError_t launch_batched(int epi, const bf16_t* A, int lda, int ldw, int M, int
   const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256);
   // W comes from the table; the argument only fills the slot
   if (epi == EPI_BF16)
-    launch_gemm(gemm_bf16_nt<EPI_BF16, BM, BN, 64, NS, 1, true>, grid, block, s, A, lda, (const bf16_t*)nullptr,
+    launch_gemm(gemm_bf16_nt<EPI_BF16, BM, BN, 64, NS, 1, true, false>, grid, block, s, A, lda, (const bf16_t*)nullptr,
                 ldw, M, N, K, tiles_m, tiles, splits, ep);
   else
-    launch_gemm(gemm_bf16_nt<EPI_SPLIT_T, BM, BN, 64, NS, 1, true>, grid, block, s, A, lda, (const bf16_t*)nullptr,
+    launch_gemm(gemm_bf16_nt<EPI_SPLIT_T, BM, BN, 64, NS, 1, true, false>, grid, block, s, A, lda, (const bf16_t*)nullptr,
                 ldw, M, N, K, tiles_m, tiles, splits, ep);
   return hipGetLastError();
 }
@@ -904,7 +958,11 @@ hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W,
   ep.w_group_rows = group_rows;
   ep.w_group_stride = group_stride;
   // a tile never spans two groups: 128-row tiles where the groups allow, else 64
-  if (group_rows % 128 == 0) return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+  if (group_rows % 128 == 0) {
+    if (ep.pf.any() && epi != EPI_BF16)
+      return launch<128, 64, 64, 4, 1, false, true>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+  }
   return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
 }
 
@@ -928,7 +986,11 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
   switch (gemm_tile_choice(M, N, K)) {
     case 0: return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 1: return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 2: return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 2:
+      // a fifth wave fits beside these tiles' registers (no spill), so they carry the prefetch
+      if (ep.pf.any() && (epi == EPI_GATED_RES || epi == EPI_RES || epi == EPI_BF16_SSQ))
+        return launch<128, 64, 64, 4, 1, false, true>(epi, A, lda, W, ldw, M, N, K, ep, s);
+      return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 3: return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     default: return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }

@@ -113,6 +113,14 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
   bf16_t* pr = p + (int64_t)row * ld + part * D + c;
   u16x8 raw;
   if (on) raw = *reinterpret_cast<const u16x8*>(pr);
+  // the rotary pairs' cos and sin, fetched with the row so their latency hides under the reduction
+  const int half = head_dim >> 1;
+  f32x4 cs = {1.f, 1.f, 1.f, 1.f}, sn = {0.f, 0.f, 0.f, 0.f};
+  if (cos_t && on) {
+    const int64_t t0 = (int64_t)(row % rows_per_lane) * half + ((c % head_dim) >> 1);
+    cs = *reinterpret_cast<const f32x4*>(cos_t + t0);
+    sn = *reinterpret_cast<const f32x4*>(sin_t + t0);
+  }
   float y[8];
   float ss = 0.f;
 #pragma unroll
@@ -129,16 +137,11 @@ __global__ __launch_bounds__(512) void rmsnorm_rope_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] *= rs * g[c + e];
   if (cos_t) {
-    const int half = head_dim >> 1;
-    const int tok = row % rows_per_lane;
-    const int j0 = (c % head_dim) >> 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float cs = cos_t[(int64_t)tok * half + j0 + e];
-      const float sn = sin_t[(int64_t)tok * half + j0 + e];
       const float a = y[2 * e], bb = y[2 * e + 1];
-      y[2 * e] = a * cs - bb * sn;
-      y[2 * e + 1] = a * sn + bb * cs;
+      y[2 * e] = a * cs[e] - bb * sn[e];
+      y[2 * e + 1] = a * sn[e] + bb * cs[e];
     }
   }
   if (out_q) {

@@ -188,6 +188,9 @@ def test_fp8_precision_argument_errors():
            + r(3 * c.dim * c.dim) + r(c.dim // 64 * 3 * c.dim * 2))   # FFN and QKV codes + scales
     assert fh.fh_fp8_weight_bytes(ctx) == per * c.n_blocks
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 7) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_PREFETCH, 0) == fh.FH_OK
+    assert L.fh_set_option(ctx, fh.FH_OPT_PREFETCH, 1) == fh.FH_OK
+    assert L.fh_set_option(ctx, 99, 0) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN) == fh.FH_OK
     # FP8 asked for before quantised weights exist: rejected before any launch
     fake = vp(1 << 40)

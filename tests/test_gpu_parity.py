@@ -325,6 +325,24 @@ def test_full_slice_against_stored_oracle(fh, case):
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
 
 
+def test_weight_prefetch_changes_nothing(fh):
+    """FH_OPT_PREFETCH only adds loads of weights into the caches: a full slice
+    at 1280 tokens, where the attention output, cross-attention query and
+    split-K FFN down-projection GEMMs carry the prefetch wave, is bit-identical
+    with it on (graph and direct launches) and off."""
+    cfg = synth.CONFIGS["slice"]
+    m = Model(fh, cfg, synth.make_weights(cfg), 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.SLICE_SIGMAS)
+    say("full slice B=1, prefetch on / off / on without the graph")
+    outs = []
+    for pf, graph in ((1, True), (0, True), (1, False)):
+        fh.fh_set_option(m.ctx, fh.FH_OPT_PREFETCH, pf)
+        outs.append(m.slice(lat, mot, aud, sig, graph=graph))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+
+
 # ------------------------------------------------------------------ re-noising sampler
 from oracle import renoise as R  # noqa: E402
 
