@@ -107,6 +107,22 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
   const int nw = n0 + wn * C;  // first column of this wave's sub-tile
   // the transposed form applies to a whole sub-tile (split is a multiple of BN)
   const bool transposed = (EPI == EPI_SPLIT_T || EPI == EPI_SPLIT_T_MX) && nw >= ep.split;
+  // residual forms with few values per lane: every x value this lane will update
+  // is requested before the first block is staged, so the reads' latency is paid
+  // once rather than once per 32-row block
+  constexpr int ITS = 32 * C / 4 / 64;
+  constexpr bool XPRE = (EPI == EPI_GATED_RES || EPI == EPI_RES) && MI * ITS <= 8;
+  f32x4 xv[XPRE ? MI : 1][XPRE ? ITS : 1];
+  if constexpr (XPRE) {
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int it = 0; it < ITS; ++it) {
+        const int c = it * 64 + lane, row = c / (C / 4), c4 = (c % (C / 4)) * 4;
+        const int m = m0 + wm * (BM / 2) + j * 32 + row;
+        if (m < M) xv[j][it] = *reinterpret_cast<const f32x4*>(ep.x + (int64_t)m * ep.ldx + nw + c4);
+      }
+  }
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
     const int mb = m0 + wm * (BM / 2) + j * 32;  // first row of the block
@@ -139,7 +155,8 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char
             u = u * (gt + ge);
           }
           f32x4* xp = reinterpret_cast<f32x4*>(ep.x + (int64_t)m * ep.ldx + n);
-          *xp = *xp + u;
+          if constexpr (XPRE) *xp = xv[j][it] + u;
+          else *xp = *xp + u;
         }
       }
       lds_fence();
