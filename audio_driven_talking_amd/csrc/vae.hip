@@ -215,6 +215,175 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
   }
 }
 
+// Halo-tiled form for frames whose width is a multiple of 32 and inputs of at
+// least 32 channels. A tile is 4 output rows x 32 columns of one frame. Per
+// 32-channel chunk of the input, the tile's whole receptive field -- 3 frames
+// (causal, clamped at frame 0) x 6 rows x 34 columns, zero outside the frame --
+// is DMA'd to LDS once (HALO_ROWS rows of 64 bytes), and the 27 taps read
+// their A fragments from it at shifted rows: per chunk 40 KB of input cross
+// L2 -> LDS instead of the 221 KB of a DMA per tap. K runs as (chunk, tap
+// group of one time and row offset: 3 column taps); each group's weights (3 x
+// BN rows x 32 channels) come through a 3-deep ring. Used where the tiles fill
+// half the chip or more (the wide layers of stages 1 and 2 and the output
+// convolution of a slice); the other layers keep the per-tap kernel above.
+constexpr int HR = 4, HC = 32;                      // output rows x columns per tile
+constexpr int HALO_H = HR + 2, HALO_W = HC + 2;     // 6 x 34 positions per frame of the halo
+constexpr int HALO_ROWS = 3 * HALO_H * HALO_W;      // 612
+constexpr int HALO_DMA = 10;                        // 1 KB DMAs per wave per halo (40 x 16 rows >= 612)
+constexpr int HALO_BYTES = 4 * HALO_DMA * 1024;     // 40 KB per buffer
+constexpr int HNS = 3;                              // weight-group ring depth
+
+template <int BN, int HB>
+constexpr int halo_smem() { return HB * HALO_BYTES + HNS * 3 * BN * 64; }
+
+// HB = 2: the next chunk's halo is fetched during this chunk's groups; HB = 1:
+// one halo buffer, refilled between chunks (a stall that a second workgroup on
+// the CU covers: the smaller LDS footprint lets two share a CU)
+template <int BN, int HB, int EPI>
+__global__ __launch_bounds__(256, ((halo_smem<BN, HB>() <= 80 * 1024) ? 2 : 1))
+void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
+  constexpr int WG_BYTES = 3 * BN * 64;       // one tap group's weights: [3 column taps][BN][32 channels]
+  constexpr int DPS = 3 * BN / 16 / 4;        // weight DMAs per wave per group
+  constexpr int NI = BN / 64;                 // 32-channel MFMA blocks per wave
+  static_assert(DPS + HALO_DMA < 64, "DMA wait count must fit vmcnt");
+  static_assert(HALO_ROWS <= 4 * HALO_DMA * 16, "halo DMAs must cover the halo");
+  static_assert(HB == 1 || HB == 2, "one or two halo buffers");
+  __shared__ __attribute__((aligned(1024))) char smem[halo_smem<BN, HB>()];
+  char* const hbuf = smem;                            // HB halo buffers
+  char* const wbuf = smem + HB * HALO_BYTES;          // HNS weight groups
+
+  int bid = wg_x();
+  bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
+  if (bid >= n_tiles) return;
+  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const int wtiles = a.W / HC, htiles = (a.H + HR - 1) / HR;
+  const int wb = tm % wtiles, hb = (tm / wtiles) % htiles, t0 = tm / (wtiles * htiles);
+  const int h0 = hb * HR, w0 = wb * HC, n0 = tn * BN;
+  const int Cin = 1 << a.cin_log2, K = 27 * Cin, nch = Cin >> 5, KT = nch * 9;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // halo DMA d of this wave fills halo rows 16 (wave + 4 d) + lane / 4, physical
+  // chunk lane & 3 (logical chunk (lane & 3) ^ cswz(row)); its source position
+  // is fixed per tile, the chunk's channels move with the input chunk
+  // (rows outside the frame, and the padding rows past the halo, read the zero row)
+  const f16_t* hsrc[HALO_DMA];
+  int hstep[HALO_DMA];  // 32 (channels per chunk) for a real source, 0 for the zero row
+#pragma unroll
+  for (int d = 0; d < HALO_DMA; ++d) {
+    const int r = 16 * (wave + 4 * d) + (lane >> 2);
+    const int lc = (lane & 3) ^ cswz(r);
+    hsrc[d] = a.zero + 8 * lc;
+    hstep[d] = 0;
+    if (r < HALO_ROWS) {
+      const int dt = r / (HALO_H * HALO_W), rem = r - dt * (HALO_H * HALO_W);
+      const int hh = rem / HALO_W, ww = rem - hh * HALO_W;
+      const int t = max(t0 + dt - 2, 0), h = h0 + hh - 1, w = w0 + ww - 1;
+      if (h >= 0 && h < a.H && w >= 0 && w < a.W) {
+        hsrc[d] = a.in + ((int64_t)(t * a.H + h) * a.W + w) * Cin + 8 * lc;
+        hstep[d] = 32;
+      }
+    }
+  }
+  // weight DMA d fills group rows 16 (wave + 4 d) + lane / 4 = column tap dw, channel row n
+  const f16_t* wsrc[DPS];
+#pragma unroll
+  for (int d = 0; d < DPS; ++d) {
+    const int r = 16 * (wave + 4 * d) + (lane >> 2);
+    const int dw = r / BN, n = r - dw * BN;
+    const int lc = (lane & 3) ^ cswz(r);
+    wsrc[d] = a.w + (int64_t)min(n0 + n, a.cout - 1) * K + dw * Cin + 8 * lc;
+  }
+  auto halo_dma = [&](int buf, int cc) {
+#pragma unroll
+    for (int d = 0; d < HALO_DMA; ++d) dma16(hsrc[d] + hstep[d] * cc, hbuf + buf * HALO_BYTES + (wave + 4 * d) * 1024);
+  };
+  auto w_dma = [&](int buf, int it) {
+    const int cc = it / 9, g = it - 9 * cc;  // group g = 3 dt + dh: taps 3 g + dw
+#pragma unroll
+    for (int d = 0; d < DPS; ++d) dma16(wsrc[d] + 3 * g * Cin + 32 * cc, wbuf + buf * WG_BYTES + (wave + 4 * d) * 1024);
+  };
+  // a halo is fetched at the start of each chunk but the last: for chunk cc + 1
+  auto halo_at = [&](int it) { return HB == 2 && it >= 0 && it % 9 == 0 && it / 9 + 1 < nch; };
+
+  f32x16 acc[NI][2];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  halo_dma(0, 0);
+  w_dma(0, 0);
+  w_dma(1, min(1, KT - 1));
+  for (int it = 0; it < KT; ++it) {
+    // this wave's DMAs of group it have landed (and so has every older one: the
+    // halo of this chunk); DMAs issued after them may still be in flight
+    if (halo_at(it - 1) || halo_at(it - 2)) wait_vm<DPS + HALO_DMA>();
+    else wait_vm<DPS>();
+    barrier();  // everyone's have, and the buffers of group it - 1 (and of chunk cc - 1) are read out
+    w_dma((it + 2) % HNS, min(it + 2, KT - 1));
+    const int cc = it / 9, g = it - 9 * cc, dt = g / 3, dh = g - 3 * dt;
+    if (halo_at(it)) halo_dma((cc + 1) & 1, cc + 1);
+    if (HB == 1 && g == 0 && cc > 0) {  // every wave is past chunk cc - 1: refill the one buffer
+      halo_dma(0, cc);
+      wait_vm<0>();
+      barrier();
+    }
+    const char* hb_ = hbuf + (HB == 2 ? (cc & 1) * HALO_BYTES : 0);
+    const char* wb_ = wbuf + (it % HNS) * WG_BYTES;
+    f16x8 af[3][2][2], wf[3][2][NI];
+#pragma unroll
+    for (int dw = 0; dw < 3; ++dw)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = (dt * HALO_H + 2 * wm + j + dh) * HALO_W + lr + dw;
+          af[dw][ks][j] = *reinterpret_cast<const f16x8*>(hb_ + r * 64 + (((2 * ks + lh) ^ cswz(r)) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r = dw * BN + wn * (BN / 2) + 32 * i + lr;
+          wf[dw][ks][i] = *reinterpret_cast<const f16x8*>(wb_ + r * 64 + (((2 * ks + lh) ^ cswz(r)) << 4));
+        }
+      }
+#pragma unroll
+    for (int dw = 0; dw < 3; ++dw)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[dw][ks][i], af[dw][ks][j], acc[i][j], 0, 0, 0);
+  }
+  wait_vm<0>();
+  mfma_drain(acc[NI - 1][1]);
+
+  // epilogue: lane (lr, lh) of block (i, j) holds channels n0 + wn BN/2 + 32 i + 8 g + 4 lh + e
+  // of position (t0, h0 + 2 wm + j, w0 + lr)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int h = h0 + 2 * wm + j;
+    if (h >= a.H) continue;
+    const int m = (t0 * a.H + h) * a.W + w0 + lr;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * (BN / 2) + 32 * i + 8 * g + 4 * lh;
+        if (n >= a.cout) continue;
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        store4<EPI>(a, m, n, v);
+      }
+  }
+}
+
 // The split-K convolution's finish: the parts of 4 consecutive channels added
 // in index order, then the layer's rounding and store (store4).
 template <int EPI>
@@ -270,6 +439,21 @@ __global__ __launch_bounds__(256) void latent_f16_kernel(const float* __restrict
   out[i] = (f16_t)lat[(int64_t)c * FHW + pos];
 }
 
+template <int BN, int HB>
+hipError_t launch_halo(int epi, const ConvArgs& a, hipStream_t s) {
+  const int tiles_m = a.T * ((a.H + HR - 1) / HR) * (a.W / HC);
+  const int tiles = tiles_m * ((a.cout + BN - 1) / BN);
+  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  switch (epi) {
+    case CONV_PLAIN: launch_timed(conv3d_halo_kernel<BN, HB, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_RES: launch_timed(conv3d_halo_kernel<BN, HB, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_UP: launch_timed(conv3d_halo_kernel<BN, HB, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_FRAMES: launch_timed(conv3d_halo_kernel<BN, HB, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int BN>
 hipError_t launch_conv(int epi, const ConvArgs& a, int splits, float* part, hipStream_t s) {
   const int64_t M = (int64_t)a.T * a.H * a.W;
@@ -300,6 +484,11 @@ hipError_t launch_conv(int epi, const ConvArgs& a, int splits, float* part, hipS
 
 }  // namespace
 
+bool halo_ok(const ConvArgs& a) {
+  const int64_t tiles = (int64_t)a.T * ((a.H + HR - 1) / HR) * (a.W / HC) * ((a.cout + 63) / 64);
+  return a.W % HC == 0 && a.cin_log2 >= 5 && tiles >= 128;
+}
+
 int conv_splits(int64_t M, int cin, int cout) {
   // split K where the output tiles cannot fill the chip: up to 256 workgroups,
   // at least 8 slabs of 32 per split
@@ -326,6 +515,9 @@ hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems
   if (epi == CONV_RES && !a.res) return hipErrorInvalidValue;
   if (epi == CONV_UP && (a.cout % 32)) return hipErrorInvalidValue;  // 8 sub-positions x a multiple of 4 channels
   if (epi == CONV_FRAMES && (!a.frames || a.cout % 16)) return hipErrorInvalidValue;
+  // frames a whole number of 32-column tiles wide, at least one 32-channel input chunk and
+  // tiles for half the CUs or more: the halo-tiled kernel
+  if (halo_ok(a)) return launch_halo<64, 1>(epi, a, s);
   const int splits = conv_splits(M, 1 << a.cin_log2, a.cout);
   if (splits > 1 && (!part || part_elems < (size_t)splits * M * a.cout)) return hipErrorInvalidValue;
   // 128 output channels per tile where there are that many, else 64

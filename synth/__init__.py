@@ -356,6 +356,9 @@ VAE_CONFIGS = {
     "toy": VaeConfig(frames=2, height=4, width=4, widths=(64, 32, 32, 32)),
     # a 3-frame 6 x 10 latent (180 positions: ragged tiles): 17 frames of 192 x 320
     "ragged": VaeConfig(frames=3, height=6, width=10, widths=(128, 64, 32, 32)),
+    # a 5-frame 3 x 64 latent, narrow: the up-sampling into stage 2 runs on frames of
+    # 6 x 128 positions (two 4-row tiles, the second half empty) -> 33 frames of 96 x 2048
+    "ragged_h": VaeConfig(frames=5, height=3, width=64, widths=(32, 32, 32, 32)),
     # the Lite slice: 5 x 16 x 16 latent -> 33 frames of 512 x 512
     "slice": VaeConfig(),
 }

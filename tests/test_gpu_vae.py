@@ -1,5 +1,7 @@
 """GPU parity of the video decoder (fh_vae_decode) against the float64 oracle
-(oracle/vae.py), every output element, at the toy, ragged and slice sizes.
+(oracle/vae.py), every output element, at the toy, ragged and slice sizes
+(the slice and ragged_h sizes run the halo-tiled convolution on their wide
+layers, ragged_h on frames whose rows end mid-tile).
 
 Bar: max |gpu - oracle| <= 4e-3 on the frames in [0, 1] (about one RGB24
 level). Both sides round to F16 at the same points (the audio-cpp page's
@@ -36,7 +38,7 @@ def decode(fh, vc, z=None):
     return out, W, z, vw
 
 
-@pytest.mark.parametrize("name", ["toy", "ragged", "latent8", "slice"])
+@pytest.mark.parametrize("name", ["toy", "ragged", "latent8", "ragged_h", "slice"])
 def test_decoder_against_oracle(fh, name):
     vc = synth.VAE_CONFIGS["toy"].replace(latent_ch=8) if name == "latent8" else synth.VAE_CONFIGS[name]
     say(f"decoder {name}: latent {vc.latent_ch}x{vc.frames}x{vc.height}x{vc.width}, widths {vc.widths}")
