@@ -223,34 +223,32 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
 // their A fragments from it at shifted rows: per chunk 40 KB of input cross
 // L2 -> LDS instead of the 221 KB of a DMA per tap. K runs as (chunk, tap
 // group of one time and row offset: 3 column taps); each group's weights (3 x
-// BN rows x 32 channels) come through a 3-deep ring. Used where the tiles fill
+// BN rows x 32 channels) come through a 3-deep ring. The halo has one buffer,
+// refilled between chunks: the stall is covered by a second workgroup on the
+// CU, which the 76 KB footprint (BN = 64) allows. Used where the tiles fill
 // half the chip or more (the wide layers of stages 1 and 2 and the output
 // convolution of a slice); the other layers keep the per-tap kernel above.
 constexpr int HR = 4, HC = 32;                      // output rows x columns per tile
 constexpr int HALO_H = HR + 2, HALO_W = HC + 2;     // 6 x 34 positions per frame of the halo
 constexpr int HALO_ROWS = 3 * HALO_H * HALO_W;      // 612
 constexpr int HALO_DMA = 10;                        // 1 KB DMAs per wave per halo (40 x 16 rows >= 612)
-constexpr int HALO_BYTES = 4 * HALO_DMA * 1024;     // 40 KB per buffer
+constexpr int HALO_BYTES = 4 * HALO_DMA * 1024;     // 40 KB
 constexpr int HNS = 3;                              // weight-group ring depth
 
-template <int BN, int HB>
-constexpr int halo_smem() { return HB * HALO_BYTES + HNS * 3 * BN * 64; }
+template <int BN>
+constexpr int halo_smem() { return HALO_BYTES + HNS * 3 * BN * 64; }
 
-// HB = 2: the next chunk's halo is fetched during this chunk's groups; HB = 1:
-// one halo buffer, refilled between chunks (a stall that a second workgroup on
-// the CU covers: the smaller LDS footprint lets two share a CU)
-template <int BN, int HB, int EPI>
-__global__ __launch_bounds__(256, ((halo_smem<BN, HB>() <= 80 * 1024) ? 2 : 1))
+template <int BN, int EPI>
+__global__ __launch_bounds__(256, ((halo_smem<BN>() <= 80 * 1024) ? 2 : 1))
 void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
   constexpr int WG_BYTES = 3 * BN * 64;       // one tap group's weights: [3 column taps][BN][32 channels]
   constexpr int DPS = 3 * BN / 16 / 4;        // weight DMAs per wave per group
   constexpr int NI = BN / 64;                 // 32-channel MFMA blocks per wave
-  static_assert(DPS + HALO_DMA < 64, "DMA wait count must fit vmcnt");
+  static_assert((HNS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
   static_assert(HALO_ROWS <= 4 * HALO_DMA * 16, "halo DMAs must cover the halo");
-  static_assert(HB == 1 || HB == 2, "one or two halo buffers");
-  __shared__ __attribute__((aligned(1024))) char smem[halo_smem<BN, HB>()];
-  char* const hbuf = smem;                            // HB halo buffers
-  char* const wbuf = smem + HB * HALO_BYTES;          // HNS weight groups
+  __shared__ __attribute__((aligned(1024))) char smem[halo_smem<BN>()];
+  char* const hbuf = smem;                  // the halo
+  char* const wbuf = smem + HALO_BYTES;     // HNS weight groups
 
   int bid = wg_x();
   bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
@@ -297,17 +295,15 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
     const int lc = (lane & 3) ^ cswz(r);
     wsrc[d] = a.w + (int64_t)min(n0 + n, a.cout - 1) * K + dw * Cin + 8 * lc;
   }
-  auto halo_dma = [&](int buf, int cc) {
+  auto halo_dma = [&](int cc) {
 #pragma unroll
-    for (int d = 0; d < HALO_DMA; ++d) dma16(hsrc[d] + hstep[d] * cc, hbuf + buf * HALO_BYTES + (wave + 4 * d) * 1024);
+    for (int d = 0; d < HALO_DMA; ++d) dma16(hsrc[d] + hstep[d] * cc, hbuf + (wave + 4 * d) * 1024);
   };
   auto w_dma = [&](int buf, int it) {
     const int cc = it / 9, g = it - 9 * cc;  // group g = 3 dt + dh: taps 3 g + dw
 #pragma unroll
     for (int d = 0; d < DPS; ++d) dma16(wsrc[d] + 3 * g * Cin + 32 * cc, wbuf + buf * WG_BYTES + (wave + 4 * d) * 1024);
   };
-  // a halo is fetched at the start of each chunk but the last: for chunk cc + 1
-  auto halo_at = [&](int it) { return HB == 2 && it >= 0 && it % 9 == 0 && it / 9 + 1 < nch; };
 
   f32x16 acc[NI][2];
 #pragma unroll
@@ -317,24 +313,22 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  halo_dma(0, 0);
+  halo_dma(0);
   w_dma(0, 0);
   w_dma(1, min(1, KT - 1));
   for (int it = 0; it < KT; ++it) {
-    // this wave's DMAs of group it have landed (and so has every older one: the
-    // halo of this chunk); DMAs issued after them may still be in flight
-    if (halo_at(it - 1) || halo_at(it - 2)) wait_vm<DPS + HALO_DMA>();
-    else wait_vm<DPS>();
-    barrier();  // everyone's have, and the buffers of group it - 1 (and of chunk cc - 1) are read out
+    // this wave's DMAs of group it have landed (and every older one: the first
+    // chunk's halo); the next group's may still be in flight
+    wait_vm<(HNS - 2) * DPS>();
+    barrier();  // everyone's have, and the buffer of group it - 1 is read out
     w_dma((it + 2) % HNS, min(it + 2, KT - 1));
     const int cc = it / 9, g = it - 9 * cc, dt = g / 3, dh = g - 3 * dt;
-    if (halo_at(it)) halo_dma((cc + 1) & 1, cc + 1);
-    if (HB == 1 && g == 0 && cc > 0) {  // every wave is past chunk cc - 1: refill the one buffer
-      halo_dma(0, cc);
+    if (g == 0 && cc > 0) {  // every wave is past chunk cc - 1: refill the halo
+      halo_dma(cc);
       wait_vm<0>();
       barrier();
     }
-    const char* hb_ = hbuf + (HB == 2 ? (cc & 1) * HALO_BYTES : 0);
+    const char* hb_ = hbuf;
     const char* wb_ = wbuf + (it % HNS) * WG_BYTES;
     f16x8 af[3][2][2], wf[3][2][NI];
 #pragma unroll
@@ -439,16 +433,16 @@ __global__ __launch_bounds__(256) void latent_f16_kernel(const float* __restrict
   out[i] = (f16_t)lat[(int64_t)c * FHW + pos];
 }
 
-template <int BN, int HB>
+template <int BN>
 hipError_t launch_halo(int epi, const ConvArgs& a, hipStream_t s) {
   const int tiles_m = a.T * ((a.H + HR - 1) / HR) * (a.W / HC);
   const int tiles = tiles_m * ((a.cout + BN - 1) / BN);
   const dim3 grid((tiles + 7) / 8 * 8), block(256);
   switch (epi) {
-    case CONV_PLAIN: launch_timed(conv3d_halo_kernel<BN, HB, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_RES: launch_timed(conv3d_halo_kernel<BN, HB, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_UP: launch_timed(conv3d_halo_kernel<BN, HB, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_FRAMES: launch_timed(conv3d_halo_kernel<BN, HB, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_PLAIN: launch_timed(conv3d_halo_kernel<BN, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_RES: launch_timed(conv3d_halo_kernel<BN, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_UP: launch_timed(conv3d_halo_kernel<BN, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_FRAMES: launch_timed(conv3d_halo_kernel<BN, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -517,7 +511,7 @@ hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems
   if (epi == CONV_FRAMES && (!a.frames || a.cout % 16)) return hipErrorInvalidValue;
   // frames a whole number of 32-column tiles wide, at least one 32-channel input chunk and
   // tiles for half the CUs or more: the halo-tiled kernel
-  if (halo_ok(a)) return launch_halo<64, 1>(epi, a, s);
+  if (halo_ok(a)) return launch_halo<64>(epi, a, s);
   const int splits = conv_splits(M, 1 << a.cin_log2, a.cout);
   if (splits > 1 && (!part || part_elems < (size_t)splits * M * a.cout)) return hipErrorInvalidValue;
   // 128 output channels per tile where there are that many, else 64
