@@ -510,7 +510,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.gate_e0 = e0 + 5 * D;
     ep.gate_stride = e0_stride;
     ep.rows_per_lane = N;
-    if (pend_out && fh::gemm_splitk_ok(M, D, Fd)) {
+    if (pend_out && (fh::gemm_splitk_ok(M, D, Fd) || (!fp8 && fh::gemm_splitk_wide_ok(M, D, Fd)))) {
       if (fp8)
         FH_HIP(fh::gemm_mx_splitk(ws.uq, Fd, ws.us, wb.ffn2_q, Fd, wb.ffn2_s, M, D, Fd, ws.part,
                                   (size_t)2 * M * D, s));

@@ -183,6 +183,8 @@ __device__ __forceinline__ f32x4 apply_pending(const PendingRes& r, f32x4 x, int
 
 // Split-K form of the residual GEMMs: the two halves of K into part[0..1].
 bool gemm_splitk_ok(int M, int N, int K);
+// the wider split-K form of gemm_bf16_splitk (192 x 192 tiles, bf16 only) for 1536 < M <= 3072
+bool gemm_splitk_wide_ok(int M, int N, int K);
 hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                             float* part, size_t part_elems, hipStream_t s, const Prefetch& pf = Prefetch());
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s);

@@ -859,12 +859,22 @@ bool gemm_splitk_ok(int M, int N, int K) {
   return M > 0 && M <= 1536 && N % 128 == 0 && N <= 2048 && K >= 4096 && K % 128 == 0;
 }
 
+bool gemm_splitk_wide_ok(int M, int N, int K) {
+  // 1536 < M <= 3072 (a 768 x 768 slice: 2880 tokens): 192 x 192 tiles over two K halves make
+  // 15 x 8 x 2 = 240 workgroups where unsplit 192 x 128 tiles make 180 (at three 1280-token
+  // streams the unsplit tiles already make 240, and 256 x 192 halves lost more in the
+  // LayerNorm that adds the parts than they gained)
+  return M > 1536 && M <= 3072 && N % 192 == 0 && N <= 2048 && K >= 4096 && K % 128 == 0;
+}
+
 hipError_t gemm_bf16_splitk(const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                             float* part, size_t part_elems, hipStream_t s, const Prefetch& pf) {
-  if (!gemm_splitk_ok(M, N, K) || lda % 8 || ldw % 8) return hipErrorInvalidValue;
+  if (lda % 8 || ldw % 8) return hipErrorInvalidValue;
   EpiArgs ep;
   ep.part = part;
   ep.part_elems = part_elems;
+  if (gemm_splitk_wide_ok(M, N, K)) return launch<192, 192, 64, 3>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
+  if (!gemm_splitk_ok(M, N, K)) return hipErrorInvalidValue;
   ep.pf = pf;
   // two wave groups along K: 2.3 % faster than one group on the FFN down-projection at 1280 tokens
   if (pf.any()) return launch<128, 128, 64, 4, 2, false, true>(EPI_PARTIAL, A, lda, W, ldw, M, N, K, ep, s, 2);
