@@ -130,6 +130,44 @@ def hot_report(timed, flops):
     return per, round(tf, 1), round(frac, 4), round(sum(timed[k][0] for k in flops), 4)
 
 
+def blas_threads():
+    import threadpoolctl
+    blas = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    return int(max([p.get("num_threads", 1) for p in blas] or [1]))
+
+
+def oracle_beside(name, gpu_us):
+    """The float64 oracle of a secondary row (audio front end, video decoder,
+    colour match) timed once at the bench's own size on the host, beside the
+    GPU's time: a reported baseline, not a target."""
+    import synth
+    if name == "audio_front_end":
+        from oracle import audio as AU
+        acfg = synth.AUDIO_CONFIGS["lite"]
+        S, Wa = synth.audio_states(acfg, 1), synth.weights_f32(synth.make_audio_weights(acfg))
+        t0 = time.perf_counter()
+        AU.audio_project(S, Wa, acfg)
+        sample = "one batch-1 projection, float64 numpy"
+    elif name == "vae_decode":
+        from oracle import vae as V
+        vc = synth.VAE_CONFIGS["slice"]
+        W = synth.vae_weights_f32(synth.make_vae_weights(vc))
+        z = synth.vae_latent(vc)
+        t0 = time.perf_counter()
+        V.decode(z, W, vc)
+        sample = "one slice decode (33 x 512 x 512), float64 numpy with the F16 storage points"
+    else:
+        from oracle import color as C
+        F, H, W, Hr, Wr = synth.COLOR_SHAPES["slice"]
+        fr, pic = synth.color_inputs(F, H, W, Hr, Wr)
+        t0 = time.perf_counter()
+        C.color_match(fr, pic, 1.0)
+        sample = "one slice colour match (33 frames of 512 x 512), float64 numpy"
+    t = time.perf_counter() - t0
+    return {"s_per_call": round(t, 3), "kind": "oracle", "cores": blas_threads(), "sample": sample,
+            "gpu_speedup": round(t / (gpu_us * 1e-6), 1)}
+
+
 def cpu_baseline(cfg, sigmas, repeats=3):
     """The fp32 numpy oracle on one real-shape block (1280 tokens: modulation
     from a time embedding, the block's audio K/V, the block), `repeats` times;
@@ -519,6 +557,9 @@ def main():
         line["kernel_ms_per_slice"] = breakdown
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, sig)
+        for k in ("audio_front_end", "vae_decode", "color_correction"):
+            if k in line:
+                line[k]["cpu_oracle"] = oracle_beside(k, line[k]["us_per_call"])
     print(json.dumps(line), flush=True)
 
 
