@@ -63,6 +63,30 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict_
   else out_b[o] = f2bf(v);
 }
 
+// The same for many parts: one wave per output element, lane l adding parts
+// l, l + 64, ... in index order, then the 64 lane sums by a fixed butterfly
+// (lane 0's sum is stored), so the loads of all parts are in flight at once
+// instead of one after the other.
+__global__ __launch_bounds__(256) void sum_parts_wide_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                             const float* __restrict__ bias, int act, int group,
+                                                             int ngroups, float* __restrict__ out_f,
+                                                             bf16_t* __restrict__ out_b) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t MN = (int64_t)M * N;
+  if (i >= MN) return;  // whole waves
+  const int lane = threadIdx.x & 63;
+  float v = 0.f;
+  for (int s = lane; s < splits; s += 64) v += part[s * MN + i];
+  v = wave_sum(v);
+  if (lane) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  v += bias[n];
+  if (act == 1) v = v / (1.0f + expf(-v));
+  const int64_t o = ((int64_t)(m % group) * ngroups + m / group) * N + n;
+  if (out_f) out_f[o] = v;
+  else out_b[o] = f2bf(v);
+}
+
 }  // namespace
 
 hipError_t audio_features(const float* states, int B, int L, int T, int C, int W, int V, int stride, int LF,
@@ -80,8 +104,12 @@ hipError_t sum_parts(const float* part, int splits, int M, int N, const float* b
   if (total <= 0) return hipSuccess;
   if (splits < 1 || !bias || (!out_f && !out_b) || group <= 0 || ngroups <= 0 || (int64_t)group * ngroups != M)
     return hipErrorInvalidValue;
-  sum_parts_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, splits, M, N, bias, act, group, ngroups,
-                                                                   out_f, out_b);
+  if (splits >= 16 && total <= ((int64_t)1 << 24))
+    sum_parts_wide_kernel<<<(unsigned)((total * 64 + 255) / 256), 256, 0, s>>>(part, splits, M, N, bias, act, group,
+                                                                               ngroups, out_f, out_b);
+  else
+    sum_parts_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, splits, M, N, bias, act, group, ngroups,
+                                                                     out_f, out_b);
   return hipGetLastError();
 }
 
