@@ -958,6 +958,9 @@ hipError_t gemm_bf16_batched(int epi, const bf16_t* A, int lda, int64_t a_stride
     if (M <= 256) return launch_batched<64, 128, 2>(epi, A, lda, ldw, M, N, K, ep, s, heads);
     return launch_batched<128, 64, 2>(epi, A, lda, ldw, M, N, K, ep, s, heads);
   }
+  // 128 < M <= 192 (one lane's 160 audio tokens): every row in one tile, so each weight slab
+  // crosses L2 -> LDS once instead of once per 64-row tile
+  if (M > 128 && M <= 192) return launch_batched<192, 128, 3>(epi, A, lda, ldw, M, N, K, ep, s, heads);
   if (M <= 256) return launch_batched<64, 128, 4>(epi, A, lda, ldw, M, N, K, ep, s, heads);
   return launch_batched<128, 64, 4>(epi, A, lda, ldw, M, N, K, ep, s, heads);
 }
