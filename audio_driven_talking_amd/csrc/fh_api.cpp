@@ -929,17 +929,17 @@ struct VaeWS {
 
 VaeWS carve_vae(const fh_vae_config& v, char* base) {
   int64_t T = v.frames, H = v.height, W = v.width, act = T * H * W * v.widths[0];
-  size_t parts = fh::conv_part_elems(T * H * W, v.latent_ch, v.widths[0]);
+  size_t parts = fh::conv_part_elems((int)T, (int)H, (int)W, v.latent_ch, v.widths[0]);
   for (int i = 0; i < 3; ++i) {
     act = std::max(act, T * H * W * v.widths[i]);
-    parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[i], v.widths[i]));
-    parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[i], 8 * v.widths[i + 1]));
+    parts = std::max(parts, fh::conv_part_elems((int)T, (int)H, (int)W, v.widths[i], v.widths[i]));
+    parts = std::max(parts, fh::conv_part_elems((int)T, (int)H, (int)W, v.widths[i], 8 * v.widths[i + 1]));
     T = 2 * T - 1;
     H *= 2;
     W *= 2;
     act = std::max(act, T * H * W * v.widths[i + 1]);
   }
-  parts = std::max(parts, fh::conv_part_elems(T * H * W, v.widths[3], v.out_ch * v.patch * v.patch));
+  parts = std::max(parts, fh::conv_part_elems((int)T, (int)H, (int)W, v.widths[3], v.out_ch * v.patch * v.patch));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;

@@ -325,7 +325,7 @@ struct ConvArgs {
   float* frames = nullptr;
 };
 hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems, hipStream_t s);
-size_t conv_part_elems(int64_t M, int cin, int cout);
+size_t conv_part_elems(int T, int H, int W, int cin, int cout);
 // RMS norm over the C channels of each of M positions (F32 sums), gain g, SiLU, F16 out
 hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t M, int C, float eps, hipStream_t s);
 // latent [C][F H W] float32 -> channels-last F16; also clears 256 bytes at zero

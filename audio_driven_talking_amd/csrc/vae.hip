@@ -20,6 +20,8 @@
 // the frame read a zero row), so the shifted input is never materialised.
 // The epilogue rounds and stores in the layer's own form: plain, plus a
 // residual, depth to space into the next resolution, or the final pixels.
+#include <algorithm>
+
 #include "fh_common.h"
 #include "fh_kernels.h"
 
@@ -228,36 +230,50 @@ __global__ __launch_bounds__(256) void conv3d_kernel(ConvArgs a, int tiles_m, in
 // CU, which the 76 KB footprint (BN = 64) allows. Used where the tiles fill
 // half the chip or more (the wide layers of stages 1 and 2 and the output
 // convolution of a slice); the other layers keep the per-tap kernel above.
-constexpr int HR = 4, HC = 32;                      // output rows x columns per tile
-constexpr int HALO_H = HR + 2, HALO_W = HC + 2;     // 6 x 34 positions per frame of the halo
-constexpr int HALO_ROWS = 3 * HALO_H * HALO_W;      // 612
-constexpr int HALO_DMA = 10;                        // 1 KB DMAs per wave per halo (40 x 16 rows >= 612)
+// HC = 32 (4 rows) or 16 (8 rows: a 32-position MFMA block is then two image
+// rows) columns per tile; the halo buffer (40 KB) holds either receptive field.
+constexpr int HALO_DMA = 10;                        // 1 KB DMAs per wave per halo (40 x 16 rows)
 constexpr int HALO_BYTES = 4 * HALO_DMA * 1024;     // 40 KB
 constexpr int HNS = 3;                              // weight-group ring depth
+template <int HC>
+struct HaloShape {
+  static constexpr int HR = 128 / HC;                       // output rows per tile
+  static constexpr int H = HR + 2, W = HC + 2;              // halo positions per frame
+  static constexpr int ROWS = 3 * H * W;                    // 612 (HC 32) or 540 (HC 16)
+};
 
 template <int BN>
 constexpr int halo_smem() { return HALO_BYTES + HNS * 3 * BN * 64; }
 
-template <int BN, int EPI>
+// EPI == CONV_PART: split K by input chunks; workgroup split ks multiplies
+// chunks [ks nch / splits, (ks + 1) nch / splits) and writes raw F32 sums to
+// part[ks][m][n]
+template <int BN, int HC, int EPI>
 __global__ __launch_bounds__(256, ((halo_smem<BN>() <= 80 * 1024) ? 2 : 1))
-void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
+void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles, int splits, float* __restrict__ part) {
+  using HS = HaloShape<HC>;
+  constexpr int HR = HS::HR, HALO_H = HS::H, HALO_W = HS::W, HALO_ROWS = HS::ROWS;
   constexpr int WG_BYTES = 3 * BN * 64;       // one tap group's weights: [3 column taps][BN][32 channels]
   constexpr int DPS = 3 * BN / 16 / 4;        // weight DMAs per wave per group
   constexpr int NI = BN / 64;                 // 32-channel MFMA blocks per wave
   static_assert((HNS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
   static_assert(HALO_ROWS <= 4 * HALO_DMA * 16, "halo DMAs must cover the halo");
+  static_assert(HC == 16 || HC == 32, "16 or 32 columns per tile");
   __shared__ __attribute__((aligned(1024))) char smem[halo_smem<BN>()];
   char* const hbuf = smem;                  // the halo
   char* const wbuf = smem + HALO_BYTES;     // HNS weight groups
 
   int bid = wg_x();
   bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);  // a contiguous run of tiles per XCD
-  if (bid >= n_tiles) return;
+  if (bid >= n_tiles * splits) return;
+  const int ks = bid / n_tiles;
+  bid -= ks * n_tiles;
   const int tm = bid % tiles_m, tn = bid / tiles_m;
   const int wtiles = a.W / HC, htiles = (a.H + HR - 1) / HR;
   const int wb = tm % wtiles, hb = (tm / wtiles) % htiles, t0 = tm / (wtiles * htiles);
   const int h0 = hb * HR, w0 = wb * HC, n0 = tn * BN;
-  const int Cin = 1 << a.cin_log2, K = 27 * Cin, nch = Cin >> 5, KT = nch * 9;
+  const int Cin = 1 << a.cin_log2, K = 27 * Cin, nch = Cin >> 5;
+  const int c0 = ks * nch / splits, KT = ((ks + 1) * nch / splits - c0) * 9;  // this split's chunks x 9 groups
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -300,7 +316,7 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
     for (int d = 0; d < HALO_DMA; ++d) dma16(hsrc[d] + hstep[d] * cc, hbuf + (wave + 4 * d) * 1024);
   };
   auto w_dma = [&](int buf, int it) {
-    const int cc = it / 9, g = it - 9 * cc;  // group g = 3 dt + dh: taps 3 g + dw
+    const int cc = c0 + it / 9, g = it % 9;  // group g = 3 dt + dh: taps 3 g + dw
 #pragma unroll
     for (int d = 0; d < DPS; ++d) dma16(wsrc[d] + 3 * g * Cin + 32 * cc, wbuf + buf * WG_BYTES + (wave + 4 * d) * 1024);
   };
@@ -313,7 +329,7 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  halo_dma(0);
+  halo_dma(c0);
   w_dma(0, 0);
   w_dma(1, min(1, KT - 1));
   for (int it = 0; it < KT; ++it) {
@@ -322,8 +338,8 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
     wait_vm<(HNS - 2) * DPS>();
     barrier();  // everyone's have, and the buffer of group it - 1 is read out
     w_dma((it + 2) % HNS, min(it + 2, KT - 1));
-    const int cc = it / 9, g = it - 9 * cc, dt = g / 3, dh = g - 3 * dt;
-    if (g == 0 && cc > 0) {  // every wave is past chunk cc - 1: refill the halo
+    const int cc = c0 + it / 9, g = it % 9, dt = g / 3, dh = g - 3 * dt;
+    if (g == 0 && cc > c0) {  // every wave is past chunk cc - 1: refill the halo
       halo_dma(cc);
       wait_vm<0>();
       barrier();
@@ -334,38 +350,42 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
 #pragma unroll
     for (int dw = 0; dw < 3; ++dw)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int kq = 0; kq < 2; ++kq) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int r = (dt * HALO_H + 2 * wm + j + dh) * HALO_W + lr + dw;
-          af[dw][ks][j] = *reinterpret_cast<const f16x8*>(hb_ + r * 64 + (((2 * ks + lh) ^ cswz(r)) << 4));
+          // position 32 (2 wm + j) + lr of the tile: row p / HC, column p % HC
+          const int p = 32 * (2 * wm + j) + lr;
+          const int r = (dt * HALO_H + p / HC + dh) * HALO_W + p % HC + dw;
+          af[dw][kq][j] = *reinterpret_cast<const f16x8*>(hb_ + r * 64 + (((2 * kq + lh) ^ cswz(r)) << 4));
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int r = dw * BN + wn * (BN / 2) + 32 * i + lr;
-          wf[dw][ks][i] = *reinterpret_cast<const f16x8*>(wb_ + r * 64 + (((2 * ks + lh) ^ cswz(r)) << 4));
+          wf[dw][kq][i] = *reinterpret_cast<const f16x8*>(wb_ + r * 64 + (((2 * kq + lh) ^ cswz(r)) << 4));
         }
       }
 #pragma unroll
     for (int dw = 0; dw < 3; ++dw)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[dw][ks][i], af[dw][ks][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[dw][kq][i], af[dw][kq][j], acc[i][j], 0, 0, 0);
   }
   wait_vm<0>();
   mfma_drain(acc[NI - 1][1]);
 
   // epilogue: lane (lr, lh) of block (i, j) holds channels n0 + wn BN/2 + 32 i + 8 g + 4 lh + e
-  // of position (t0, h0 + 2 wm + j, w0 + lr)
+  // of tile position p = 32 (2 wm + j) + lr: frame t0, row h0 + p / HC, column w0 + p % HC
+  const int M = a.T * a.H * a.W;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int h = h0 + 2 * wm + j;
+    const int p = 32 * (2 * wm + j) + lr;
+    const int h = h0 + p / HC;
     if (h >= a.H) continue;
-    const int m = (t0 * a.H + h) * a.W + w0 + lr;
+    const int m = (t0 * a.H + h) * a.W + w0 + p % HC;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -373,7 +393,11 @@ void conv3d_halo_kernel(ConvArgs a, int tiles_m, int n_tiles) {
         const int n = n0 + wn * (BN / 2) + 32 * i + 8 * g + 4 * lh;
         if (n >= a.cout) continue;
         const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        store4<EPI>(a, m, n, v);
+        if constexpr (EPI == CONV_PART) {
+          *reinterpret_cast<f32x4*>(part + ((int64_t)ks * M + m) * a.cout + n) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          store4<EPI>(a, m, n, v);
+        }
       }
   }
 }
@@ -433,18 +457,33 @@ __global__ __launch_bounds__(256) void latent_f16_kernel(const float* __restrict
   out[i] = (f16_t)lat[(int64_t)c * FHW + pos];
 }
 
-template <int BN>
-hipError_t launch_halo(int epi, const ConvArgs& a, hipStream_t s) {
-  const int tiles_m = a.T * ((a.H + HR - 1) / HR) * (a.W / HC);
+template <int BN, int HC>
+hipError_t launch_halo(int epi, const ConvArgs& a, int splits, float* part, hipStream_t s) {
+  const int tiles_m = a.T * ((a.H + HaloShape<HC>::HR - 1) / HaloShape<HC>::HR) * (a.W / HC);
   const int tiles = tiles_m * ((a.cout + BN - 1) / BN);
-  const dim3 grid((tiles + 7) / 8 * 8), block(256);
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
+#define FH_HALO(E) launch_timed(conv3d_halo_kernel<BN, HC, E>, grid, block, s, a, tiles_m, tiles, splits, part)
+  if (splits > 1) {
+    FH_HALO(CONV_PART);
+    const int64_t M = (int64_t)a.T * a.H * a.W;
+    const dim3 rgrid((unsigned)((M * (a.cout / 4) + 255) / 256));
+    switch (epi) {
+      case CONV_PLAIN: conv_reduce_kernel<CONV_PLAIN><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_RES: conv_reduce_kernel<CONV_RES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_UP: conv_reduce_kernel<CONV_UP><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_FRAMES: conv_reduce_kernel<CONV_FRAMES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (epi) {
-    case CONV_PLAIN: launch_timed(conv3d_halo_kernel<BN, CONV_PLAIN>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_RES: launch_timed(conv3d_halo_kernel<BN, CONV_RES>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_UP: launch_timed(conv3d_halo_kernel<BN, CONV_UP>, grid, block, s, a, tiles_m, tiles); break;
-    case CONV_FRAMES: launch_timed(conv3d_halo_kernel<BN, CONV_FRAMES>, grid, block, s, a, tiles_m, tiles); break;
+    case CONV_PLAIN: FH_HALO(CONV_PLAIN); break;
+    case CONV_RES: FH_HALO(CONV_RES); break;
+    case CONV_UP: FH_HALO(CONV_UP); break;
+    case CONV_FRAMES: FH_HALO(CONV_FRAMES); break;
     default: return hipErrorInvalidValue;
   }
+#undef FH_HALO
   return hipGetLastError();
 }
 
@@ -478,11 +517,6 @@ hipError_t launch_conv(int epi, const ConvArgs& a, int splits, float* part, hipS
 
 }  // namespace
 
-bool halo_ok(const ConvArgs& a) {
-  const int64_t tiles = (int64_t)a.T * ((a.H + HR - 1) / HR) * (a.W / HC) * ((a.cout + 63) / 64);
-  return a.W % HC == 0 && a.cin_log2 >= 5 && tiles >= 128;
-}
-
 int conv_splits(int64_t M, int cin, int cout) {
   // split K where the output tiles cannot fill the chip: up to 256 workgroups,
   // at least 8 slabs of 32 per split
@@ -495,9 +529,34 @@ int conv_splits(int64_t M, int cin, int cout) {
   return sp < 1 ? 1 : sp;
 }
 
-size_t conv_part_elems(int64_t M, int cin, int cout) {
-  const int sp = conv_splits(M, cin, cout);
-  return sp > 1 ? (size_t)sp * M * cout : 0;
+// Which kernel a convolution takes. The halo-tiled one where the frames are a
+// whole number of 32- (else 16-) column tiles wide and the input has 32
+// channels or more: alone where its tiles fill half the chip, else split over
+// input chunks if that brings 128 workgroups or more; otherwise the per-tap
+// kernel with its own K split.
+struct ConvPlan {
+  int halo_hc;  // 32 or 16: halo-tiled with that many columns per tile; 0: per-tap kernel
+  int splits;
+};
+ConvPlan conv_plan(int T, int H, int W, int cin_log2, int cout) {
+  if (cin_log2 >= 5) {
+    const int hc = W % 32 == 0 ? 32 : W % 16 == 0 ? 16 : 0;
+    if (hc) {
+      const int hr = 128 / hc;
+      const int64_t tiles = (int64_t)T * ((H + hr - 1) / hr) * (W / hc) * ((cout + 63) / 64);
+      if (tiles >= 128) return {hc, 1};
+      const int64_t sp = std::min<int64_t>(1 << (cin_log2 - 5), 256 / tiles);
+      if (sp >= 2 && tiles * sp >= 128) return {hc, (int)sp};
+    }
+  }
+  return {0, conv_splits((int64_t)T * H * W, 1 << cin_log2, cout)};
+}
+
+size_t conv_part_elems(int T, int H, int W, int cin, int cout) {
+  int cl = 0;
+  while ((1 << cl) < cin) ++cl;
+  const ConvPlan pl = conv_plan(T, H, W, cl, cout);
+  return pl.splits > 1 ? (size_t)pl.splits * T * H * W * cout : 0;
 }
 
 hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems, hipStream_t s) {
@@ -509,11 +568,11 @@ hipError_t conv3d_f16(int epi, const ConvArgs& a, float* part, size_t part_elems
   if (epi == CONV_RES && !a.res) return hipErrorInvalidValue;
   if (epi == CONV_UP && (a.cout % 32)) return hipErrorInvalidValue;  // 8 sub-positions x a multiple of 4 channels
   if (epi == CONV_FRAMES && (!a.frames || a.cout % 16)) return hipErrorInvalidValue;
-  // frames a whole number of 32-column tiles wide, at least one 32-channel input chunk and
-  // tiles for half the CUs or more: the halo-tiled kernel
-  if (halo_ok(a)) return launch_halo<64>(epi, a, s);
-  const int splits = conv_splits(M, 1 << a.cin_log2, a.cout);
+  const ConvPlan pl = conv_plan(a.T, a.H, a.W, a.cin_log2, a.cout);
+  const int splits = pl.splits;
   if (splits > 1 && (!part || part_elems < (size_t)splits * M * a.cout)) return hipErrorInvalidValue;
+  if (pl.halo_hc == 32) return launch_halo<64, 32>(epi, a, splits, part, s);
+  if (pl.halo_hc == 16) return launch_halo<64, 16>(epi, a, splits, part, s);
   // 128 output channels per tile where there are that many, else 64
   return a.cout >= 128 ? launch_conv<128>(epi, a, splits, part, s) : launch_conv<64>(epi, a, splits, part, s);
 }
