@@ -96,11 +96,11 @@ __device__ __forceinline__ int swz(int row) { return BK == 64 ? ((row >> 1) & 7)
 // (i, j) of a wave holds row m = m0 + wm*BM/2 + j*32 + lr and columns
 // n = n0 + wn*BN/2 + i*32 + 8g + 4lh + {0..3} in acc[i][j][4g .. 4g+3]. The
 // slab buffers must be free (smem reused for staging).
-template <int EPI, int BM, int BN>
-__device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / 64][BM / 64], char* smem, const EpiArgs& ep,
+template <int EPI, int BM, int BN, int WN = 2>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[BN / (32 * WN)][BM / 64], char* smem, const EpiArgs& ep,
                                            int M, int N, int m0, int n0, int wm, int wn, int wave, int lane,
                                            int ks) {
-  constexpr int MI = BM / 64, NI = BN / 64, C = BN / 2;
+  constexpr int MI = BM / 64, NI = BN / (32 * WN), C = BN / WN;
   using ST = Stage<C>;
   const int lr = lane & 31, lh = lane >> 5;
   char* st = smem + wave * ST::BYTES;
@@ -355,24 +355,33 @@ __device__ __forceinline__ void prefetch_wave(const Prefetch& pf, char* lds, int
   wait_vm<0>();
 }
 
-template <int EPI, int BM, int BN, int BK, int NS, int KW, bool BATCH, bool PF>
-__global__ __launch_bounds__(256 * KW + (PF ? 64 : 0),
-                             (KW == 1 && !PF && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
+// WN = 4: one group of 2 x 4 waves (two waves per SIMD, each a (BM/2) x (BN/4)
+// sub-tile); the slab's 1 KB DMA groups may then not divide evenly among the
+// waves, and a wave's wait counts follow its own share.
+template <int EPI, int BM, int BN, int BK, int NS, int KW, bool BATCH, bool PF, int WN = 2>
+__global__ __launch_bounds__(128 * WN * KW + (PF ? 64 : 0),
+                             (KW == 1 && WN == 2 && !PF && smem_bytes<BM, BN, BK, NS>() <= 80 * 1024) ? 2 : 1)
 void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int ldw,
                   int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
-  constexpr int NW = 4 * KW;           // waves: KW groups of 2 x 2, group g takes k-steps g KK/KW ..
+  constexpr int NG = 2 * WN;           // waves per group (2 x WN)
+  constexpr int NW = NG * KW;          // waves: KW groups, group g takes k-steps g KK/KW ..
   constexpr int ROWB = BK * 2;         // bytes per LDS row of a slab
   constexpr int CH = BK / 8;           // 16-byte chunks per row
   constexpr int RG = 64 / CH;          // rows per 1 KB DMA group
   constexpr int MI = BM / 64;          // 32-row activation blocks per wave
-  constexpr int NI = BN / 64;          // 32-row weight blocks per wave
-  constexpr int GA = BM / RG / NW;     // 1 KB DMA groups per wave per slab, activations
-  constexpr int GW = BN / RG / NW;     // ... weights
+  constexpr int NI = BN / (32 * WN);   // 32-row weight blocks per wave
+  constexpr int TA = BM / RG, TW = BN / RG;   // 1 KB DMA groups per slab, activations / weights
+  constexpr int GA = (TA + NW - 1) / NW;      // ... at most per wave
+  constexpr int GW = (TW + NW - 1) / NW;
   constexpr int SLAB = (BM + BN) * ROWB;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && GA * RG * NW == BM && GW * RG * NW == BN, "tile shape");
+  static_assert(BM % 64 == 0 && BN % (32 * WN) == 0 && TA * RG == BM && TW * RG == BN, "tile shape");
+  static_assert(WN == 2 || (WN == 4 && KW == 1 && !BATCH), "2 x 4 waves: one group, plain launches");
+  static_assert(WN == 4 || (GA * NW == TA && GW * NW == TW), "2 x 2 waves share the DMA groups evenly");
+  static_assert(GW * NW == TW && (GA * NW == TA || GA * NW - TA < NW), "at most one group fewer per wave");
   static_assert(KW == 1 || KW == 2, "one or two wave groups along K");
   static_assert(NS >= 2 && (NS - 1) * (GA + GW) < 64, "DMA wait count must fit vmcnt");
   static_assert(!PF || !BATCH, "prefetch only in plain launches");
+  static_assert(!PF || WN == 2, "prefetch wave only beside 2 x 2 waves");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB + (PF ? 1024 : 0)];
 
   int bid = wg_x();
@@ -402,9 +411,12 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave >> 2;                    // wave group along K
-  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int kg = wave / NG;                    // wave group along K
+  const int wm = (wave / WN) & 1, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
+  // whether this wave takes GA activation DMA groups (wave + NW i < TA), or one fewer
+  constexpr bool EVEN = GA * NW == TA;
+  const bool a_full = EVEN || wave + NW * (GA - 1) < TA;
   if constexpr (PF) {
     if (wave == NW) {
       prefetch_wave<KW>(ep.pf, smem + NS * SLAB, tm + (int64_t)tiles_m * tn + (int64_t)ks * tiles,
@@ -433,8 +445,9 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   // one DMA instruction d of a slab: d < GA an activation group, else a weight group
   auto dma_one = [&](int d, int buf, int k0) {
     char* sa = smem + buf * SLAB;
-    if (d < GA) dma16(ga[d] + k0, sa + (wave + NW * d) * 1024);
-    else dma16(gw[d - GA] + k0, sa + BM * ROWB + (wave + NW * (d - GA)) * 1024);
+    if (d < GA) {
+      if (EVEN || d < GA - 1 || a_full) dma16(ga[d] + k0, sa + (wave + NW * d) * 1024);
+    } else dma16(gw[d - GA] + k0, sa + BM * ROWB + (wave + NW * (d - GA)) * 1024);
   };
 
   f32x16 acc[NI][MI];
@@ -448,13 +461,13 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   // Fragments of a whole slab are held in registers, in two sets: while the
   // MFMAs of slab kt run on one set, the fragments of slab kt + 1 are read
   // into the other. Rows: activations wm*BM/2 + 32 j + lr, weights
-  // wn*BN/2 + 32 i + lr; the wave's k-step kk covers the slab's k-columns
+  // wn*BN/WN + 32 i + lr; the wave's k-step kk covers the slab's k-columns
   // 16 (kg KK + kk) .. +15 (KK k-steps per wave group).
   constexpr int KK = BK / 16 / KW, P = NI * MI, NR = NI + MI, DPS = GA + GW;
   static_assert(KK * 16 * KW == BK, "slab splits evenly between the wave groups");
   constexpr int SLOTS = KK * P, READS = KK * NR;
   const int xr = swz<BK>(lr);
-  const int a_row = (wm * (BM / 2) + lr) * ROWB, w_row = BM * ROWB + (wn * (BN / 2) + lr) * ROWB;
+  const int a_row = (wm * (BM / 2) + lr) * ROWB, w_row = BM * ROWB + (wn * (BN / WN) + lr) * ROWB;
   bf16x8 wf[2][KK][NI], af[2][KK][MI];
   // fragment read r of a slab: k-step r / NR; r % NR < NI a weight block, else activations
   auto read_one = [&](int r, int set, int buf) {
@@ -500,12 +513,18 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int d = 0; d < DPS; ++d) dma_one(d, s, min(s, KT - 1) * BK);
-  wait_vm<(NS - 1) * DPS>();
+  // wait until at most n slabs' DMAs of this wave are in flight
+  auto wait_slabs = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    if (a_full) wait_vm<n * DPS>();
+    else wait_vm<n * (DPS - 1)>();
+  };
+  wait_slabs(std::integral_constant<int, NS - 1>{});
   barrier();
 #pragma unroll
   for (int r = 0; r < READS; ++r) read_one(r, 0, 0);
   auto iteration = [&](int kt, auto set_c) {
-    wait_vm<(NS - 2) * DPS>();  // this wave's DMAs of slab kt + 1 have landed
+    wait_slabs(std::integral_constant<int, NS - 2>{});  // this wave's DMAs of slab kt + 1 have landed
     wait_lgkm0();               // and its fragments of slab kt are in registers
     barrier();                  // so for every wave: slab kt + 1 is in, buffer kt % NS is free
     mma_slab(set_c, (kt + 1) % NS, kt % NS, min(kt + NS, KT - 1) * BK);
@@ -517,7 +536,7 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
   }
   wait_vm<0>();
 
-  static_assert(4 * Stage<BN / 2>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
+  static_assert(NG * Stage<BN / WN>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
   wait_lgkm0();
   barrier();  // every wave is done with the slab buffers (its DMAs landed above)
   if constexpr (KW == 2) {
@@ -551,7 +570,7 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
           acc[i][j][4 * q + 3] += v.w;
         }
   }
-  store_tile<EPI, BM, BN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
+  store_tile<EPI, BM, BN, WN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
 }
 
 // ---------------------------------------------------------------- MX-FP8
@@ -790,7 +809,7 @@ __global__ __launch_bounds__(256) void residual_from_parts_kernel(float* __restr
   *xp = apply_pending(r, *xp, m, n, M, N);
 }
 
-template <int BM, int BN, int BK, int NS, int KW = 1, bool BATCH = false, bool PF = false>
+template <int BM, int BN, int BK, int NS, int KW = 1, bool BATCH = false, bool PF = false, int WN = 2>
 hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
                   const EpiArgs& ep, hipStream_t s, int splits = 1) {
   if (N % BN || splits < 1 || K % (splits * BK)) return hipErrorInvalidValue;
@@ -812,9 +831,12 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   const int tiles = tiles_m * (N / BN);
   const int64_t wgs = (int64_t)tiles * splits * ep.batch_n;
   if (wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(256 * KW + (PF ? 64 : 0));
-#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH, PF>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
-  if constexpr (PF) {  // the forms that prefetch: the residual, query and split-K products
+  const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(128 * WN * KW + (PF ? 64 : 0));
+#define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH, PF, WN>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
+  if constexpr (WN == 4) {  // 2 x 4 waves: the GELU product alone
+    if (epi == EPI_GELU_BF16) FH_GEMM(EPI_GELU_BF16);
+    else return hipErrorInvalidValue;
+  } else if constexpr (PF) {  // the forms that prefetch: the residual, query and split-K products
     if (!ep.pf.any()) return hipErrorInvalidValue;
     if (epi == EPI_GATED_RES) FH_GEMM(EPI_GATED_RES);
     else if (epi == EPI_RES) FH_GEMM(EPI_RES);
@@ -1014,7 +1036,9 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
   if (epi == EPI_BF16_SSQ && !ep.ssq) return hipErrorInvalidValue;
   if (N % 128 || K % KALIGN || lda % 8 || ldw % 8 || epi == EPI_PARTIAL) return hipErrorInvalidValue;
   switch (gemm_tile_choice(M, N, K)) {
-    case 0: return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 0:
+      if (epi == EPI_GELU_BF16) return launch<192, 256, 32, 3, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+      return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 1: return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 2:
       // a fifth wave fits beside these tiles' registers (no spill), so they carry the prefetch
