@@ -110,24 +110,28 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   // V^T rows 8g + lane/8 (8 chunks per row), g = 4 wave + i
   const bf16_t* kbase = k + (int64_t)b * N * ldk + h * HD;
   const bf16_t* vbase = vt + ((int64_t)b * D + h * HD) * N;
-  auto issue = [&](int buf, int j) {
+  // DMA instruction d < 16 of a step: key half d >> 3, group i = (d >> 1) & 3,
+  // the K rows (d even) or the V^T rows (d odd)
+  auto issue_one = [&](int d, int buf, int j) {
     char* st = smem + buf * ASTAGE;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int kb = min(c == 0 ? j : nh0 + j, nkb - 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int g = 4 * wave + i;
-        const int krow = 4 * g + (lane >> 4);
-        const int kch = (lane & 15) ^ kswz(krow);
-        const int key = min(kb * KB + krow, N - 1);
-        dma16(kbase + (int64_t)key * ldk + kch * 8, st + c * 2 * KBLK + g * 1024);
-        const int vrow = 8 * g + (lane >> 3);
-        const int vch = (lane & 7) ^ vswz(vrow);
-        const int vkey = min(kb * KB + vch * 8, N - 8);
-        dma16(vbase + (int64_t)vrow * N + vkey, st + c * 2 * KBLK + KBLK + g * 1024);
-      }
+    const int c = d >> 3, i = (d >> 1) & 3;
+    const int kb = min(c == 0 ? j : nh0 + j, nkb - 1);
+    const int g = 4 * wave + i;
+    if ((d & 1) == 0) {
+      const int krow = 4 * g + (lane >> 4);
+      const int kch = (lane & 15) ^ kswz(krow);
+      const int key = min(kb * KB + krow, N - 1);
+      dma16(kbase + (int64_t)key * ldk + kch * 8, st + c * 2 * KBLK + g * 1024);
+    } else {
+      const int vrow = 8 * g + (lane >> 3);
+      const int vch = (lane & 7) ^ vswz(vrow);
+      const int vkey = min(kb * KB + vch * 8, N - 8);
+      dma16(vbase + (int64_t)vrow * N + vkey, st + c * 2 * KBLK + KBLK + g * 1024);
     }
+  };
+  auto issue = [&](int buf, int j) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) issue_one(d, buf, j);
   };
 
   f32x16 acc[4];
@@ -139,27 +143,39 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   const int krow_l = kperm(lr);
   const int kx = kswz(krow_l), vx = vswz(lr);
 
+  // Every step refills the other buffer (past the last step with the clamped
+  // last block, which nobody reads); the DMA instructions go out one after
+  // each score MFMA, so their address arithmetic runs under the matrix core.
   issue(0, 0);
   for (int j = 0; j < nh0; ++j) {
     wait_vm<0>();
     barrier();
-    if (j + 1 < nh0) issue((j + 1) & 1, j + 1);
     const int kb = kh == 0 ? j : nh0 + j;
-    if (kb >= nkb) continue;
+    if (kb >= nkb) {
+      issue((j + 1) & 1, j + 1);
+      continue;
+    }
     const char* kp = smem + (j & 1) * ASTAGE + kh * 2 * KBLK;
     const char* vp = kp + KBLK;
 
     f32x16 st[2];
+    bf16x8 kf[2][8];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
       const char* krow = kp + (32 * t + krow_l) * (HD * 2);
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(krow + (((2 * s + lh) ^ kx) << 4)), qf[s], st[t], 0, 0, 0);
+      for (int s = 0; s < 8; ++s) kf[t][s] = *reinterpret_cast<const bf16x8*>(krow + (((2 * s + lh) ^ kx) << 4));
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf[s], st[t], 0, 0, 0);
+        issue_one(2 * s + t, (j + 1) & 1, j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     // st[t][r] is the score of key kb*64 + 32t + 16(r>>3) + 8lh + (r&7)
     if ((kb + 1) * KB > N) {
 #pragma unroll
@@ -211,6 +227,7 @@ __global__ __launch_bounds__(256, 1) void flash_attn_kernel(
   l_run += __shfl_xor(l_run, 32, 64);
 
   // merge the key halves: wave (qg, 1) hands (m, l, acc) to wave (qg, 0)
+  wait_vm<0>();
   barrier();
   float* mg = reinterpret_cast<float*>(smem) + qg * (66 * 64);
   if (kh == 1) {
