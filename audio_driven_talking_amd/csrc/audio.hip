@@ -94,7 +94,7 @@ hipError_t audio_features(const float* states, int B, int L, int T, int C, int W
   const int64_t total = (int64_t)LF * B * W * L * C;
   if (total <= 0) return hipSuccess;
   if (T <= 0 || stride <= 0 || (V - 1) != stride * (LF - 1)) return hipErrorInvalidValue;
-  audio_features_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(states, B, L, T, C, W, V, stride, LF, X);
+  launch_timed(audio_features_kernel, (unsigned)((total + 255) / 256), 256, s, states, B, L, T, C, W, V, stride, LF, X);
   return hipGetLastError();
 }
 
@@ -105,11 +105,11 @@ hipError_t sum_parts(const float* part, int splits, int M, int N, const float* b
   if (splits < 1 || !bias || (!out_f && !out_b) || group <= 0 || ngroups <= 0 || (int64_t)group * ngroups != M)
     return hipErrorInvalidValue;
   if (splits >= 16 && total <= ((int64_t)1 << 24))
-    sum_parts_wide_kernel<<<(unsigned)((total * 64 + 255) / 256), 256, 0, s>>>(part, splits, M, N, bias, act, group,
-                                                                               ngroups, out_f, out_b);
+    launch_timed(sum_parts_wide_kernel, (unsigned)((total * 64 + 255) / 256), 256, s, part, splits, M, N, bias, act, group,
+                 ngroups, out_f, out_b);
   else
-    sum_parts_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, splits, M, N, bias, act, group, ngroups,
-                                                                     out_f, out_b);
+    launch_timed(sum_parts_kernel, (unsigned)((total + 255) / 256), 256, s, part, splits, M, N, bias, act, group, ngroups,
+                 out_f, out_b);
   return hipGetLastError();
 }
 

@@ -350,15 +350,15 @@ hipError_t color_match(const float* frames, int F, int64_t npix, const float* pi
   const int64_t groups = vec ? (int64_t)F * (npix / 4) : (int64_t)F * npix;
   const dim3 sgrid(nchunks, F + 1);
   if (vec)
-    color_stats_kernel<true><<<sgrid, 256, 0, s>>>(frames, npix, pic, npix_ref, F, T, partial);
+    launch_timed(color_stats_kernel<true>, sgrid, 256, s, frames, npix, pic, npix_ref, F, T, partial);
   else
-    color_stats_kernel<false><<<sgrid, 256, 0, s>>>(frames, npix, pic, npix_ref, F, T, partial);
-  color_finalize_kernel<<<F, 256, 0, s>>>(frames, npix, pic, npix_ref, partial, nchunks, F, T, coef);
+    launch_timed(color_stats_kernel<false>, sgrid, 256, s, frames, npix, pic, npix_ref, F, T, partial);
+  launch_timed(color_finalize_kernel, F, 256, s, frames, npix, pic, npix_ref, partial, nchunks, F, T, coef);
   const unsigned agrid = (unsigned)((groups + 255) / 256);
   if (vec)
-    color_apply_kernel<true><<<agrid, 256, 0, s>>>(frames, npix, F, coef, strength, T, out);
+    launch_timed(color_apply_kernel<true>, agrid, 256, s, frames, npix, F, coef, strength, T, out);
   else
-    color_apply_kernel<false><<<agrid, 256, 0, s>>>(frames, npix, F, coef, strength, T, out);
+    launch_timed(color_apply_kernel<false>, agrid, 256, s, frames, npix, F, coef, strength, T, out);
   return hipGetLastError();
 }
 

@@ -219,10 +219,10 @@ hipError_t gemm_f32(int epi, const float* A, int lda, const bf16_t* W, int ldw, 
   if (epi == F32_GATED_RES && (!ep.gate_tab || !ep.gate_e0 || ep.rows_per_lane <= 0)) return hipErrorInvalidValue;
   const dim3 grid(N / T, (M + T - 1) / T), block(256);
   switch (epi) {
-    case F32_OUT: gemm_f32_kernel<F32_OUT><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-    case F32_GELU: gemm_f32_kernel<F32_GELU><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-    case F32_RES: gemm_f32_kernel<F32_RES><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-    case F32_GATED_RES: gemm_f32_kernel<F32_GATED_RES><<<grid, block, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
+    case F32_OUT: launch_timed(gemm_f32_kernel<F32_OUT>, grid, block, s, A, lda, W, ldw, M, N, K, ep); break;
+    case F32_GELU: launch_timed(gemm_f32_kernel<F32_GELU>, grid, block, s, A, lda, W, ldw, M, N, K, ep); break;
+    case F32_RES: launch_timed(gemm_f32_kernel<F32_RES>, grid, block, s, A, lda, W, ldw, M, N, K, ep); break;
+    case F32_GATED_RES: launch_timed(gemm_f32_kernel<F32_GATED_RES>, grid, block, s, A, lda, W, ldw, M, N, K, ep); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -235,8 +235,8 @@ hipError_t layernorm_f32(const float* x, float* out, int rows, int D, int rows_p
   if (D <= 0 || rows_per_lane <= 0 || (!g && (!tab_shift || !tab_scale || !e_shift || !e_scale)) ||
       (g && !b))
     return hipErrorInvalidValue;
-  layernorm_f32_kernel<<<rows, 256, 0, s>>>(x, out, D, rows_per_lane, eps, tab_shift, tab_scale, e_shift,
-                                            e_scale, e_stride, g, b);
+  launch_timed(layernorm_f32_kernel, rows, 256, s, x, out, D, rows_per_lane, eps, tab_shift, tab_scale, e_shift,
+               e_scale, e_stride, g, b);
   return hipGetLastError();
 }
 
@@ -244,7 +244,7 @@ hipError_t rmsnorm_rope_f32(float* p, int ld, int rows, int D, const float* g, c
                             const float* sin_t, int rows_per_lane, int head_dim, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (D % 2 || !g || rows_per_lane <= 0 || head_dim % 2 || (cos_t && D % head_dim)) return hipErrorInvalidValue;
-  rmsnorm_rope_f32_kernel<<<rows, 256, 0, s>>>(p, ld, D, g, cos_t, sin_t, rows_per_lane, head_dim, eps);
+  launch_timed(rmsnorm_rope_f32_kernel, rows, 256, s, p, ld, D, g, cos_t, sin_t, rows_per_lane, head_dim, eps);
   return hipGetLastError();
 }
 
@@ -255,8 +255,8 @@ hipError_t attn_f32(const float* q, int ldq, const float* k, int ldk, const floa
   if (Nk <= 0 || n_heads <= 0 || n_heads > 65535 || B > 65535) return hipErrorInvalidValue;
   if (local ? (apf <= 0 || apf > MAXKEYS || hw <= 0 || (int64_t)((Nq - 1) / hw + 1) * apf > Nk) : Nk > MAXKEYS)
     return hipErrorInvalidValue;
-  attn_f32_kernel<<<dim3(Nq, n_heads, B), 128, 0, s>>>(q, ldq, k, ldk, v, ldv, o, ldo, Nq, Nk, scale, hw, apf,
-                                                      local);
+  launch_timed(attn_f32_kernel, dim3(Nq, n_heads, B), 128, s, q, ldq, k, ldk, v, ldv, o, ldo, Nq, Nk, scale, hw, apf,
+               local);
   return hipGetLastError();
 }
 

@@ -3,6 +3,10 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+#include <type_traits>
 
 #include "fh_common.h"
 
@@ -20,17 +24,46 @@ struct LaunchEvents {
 };
 LaunchEvents& armed_launch_events();  // this thread's
 
+// Launch trace: with FH_TRACE=1 in the environment (read once per process)
+// every kernel launch prints one line to stderr: the kernel's name, grid,
+// block, dynamic LDS bytes, stream and its scalar arguments (sizes, strides,
+// scale factors; pointers as addresses, structures as {}). Launches recorded
+// into a HIP graph print when the graph is captured, not when it replays.
+bool trace_on();
+void trace_line(const void* kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const std::string& args);
+template <typename T>
+void trace_arg(std::string& out, const T& v) {
+  char b[48];
+  if constexpr (std::is_same_v<T, bool>) snprintf(b, sizeof b, "%d", (int)v);
+  else if constexpr (std::is_integral_v<T> && std::is_signed_v<T>) snprintf(b, sizeof b, "%lld", (long long)v);
+  else if constexpr (std::is_integral_v<T>) snprintf(b, sizeof b, "%llu", (unsigned long long)v);
+  else if constexpr (std::is_floating_point_v<T>) snprintf(b, sizeof b, "%g", (double)v);
+  else if constexpr (std::is_pointer_v<T> || std::is_null_pointer_v<T>) snprintf(b, sizeof b, "%p", (const void*)v);
+  else snprintf(b, sizeof b, "{}");
+  if (!out.empty()) out += ", ";
+  out += b;
+}
+
 // a kernel launch that takes the armed events, if any
 template <typename Kern, typename... Args>
-void launch_timed(Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+void launch_timed_lds(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+  if (trace_on()) {
+    std::string a;
+    (trace_arg(a, args), ...);
+    trace_line(reinterpret_cast<const void*>(kern), grid, block, lds, s, a);
+  }
   LaunchEvents& e = armed_launch_events();
   if (e.start) {
-    hipExtLaunchKernelGGL(kern, grid, block, 0, s, e.start, e.stop, 0, args...);
+    hipExtLaunchKernelGGL(kern, grid, block, lds, s, e.start, e.stop, 0, args...);
     e.start = e.stop = nullptr;
     e.used = true;
   } else {
-    kern<<<grid, block, 0, s>>>(args...);
+    kern<<<grid, block, lds, s>>>(args...);
   }
+}
+template <typename Kern, typename... Args>
+void launch_timed(Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  launch_timed_lds(kern, grid, block, 0, s, args...);
 }
 
 // Epilogues of the bf16 GEMM C[M,N] = A[M,K] * W[N,K]^T (+ bias[N]).

@@ -28,6 +28,10 @@
 // head), weights chosen per group of rows (one weight matrix per latent
 // frame), and a launch over a table of weight pointers (one product per DiT
 // block). An MX-FP8 form on the block-scaled MFMA follows below.
+#include <cxxabi.h>
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "fh_common.h"
@@ -58,6 +62,31 @@ bool launch_events_used() {
   const bool u = t_launch_ev.used;
   t_launch_ev = LaunchEvents();
   return u;
+}
+
+bool trace_on() {
+  static const bool on = [] {
+    const char* v = getenv("FH_TRACE");
+    return v && v[0] == '1' && v[1] == 0;
+  }();
+  return on;
+}
+
+void trace_line(const void* kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const std::string& args) {
+  const char* mangled = hipKernelNameRefByPtr(kern, s);
+  int st = -1;
+  char* name = mangled ? abi::__cxa_demangle(mangled, nullptr, nullptr, &st) : nullptr;
+  std::string n = st == 0 && name ? name : mangled ? mangled : "?";
+  free(name);
+  // keep the name and template arguments: drop a return type, the namespaces and the parameter types
+  if (n.compare(0, 5, "void ") == 0) n.erase(0, 5);
+  for (const char* ns : {"(anonymous namespace)::", "fh::"})
+    for (size_t at; (at = n.find(ns)) != std::string::npos;) n.erase(at, strlen(ns));
+  const size_t paren = n.find('(');
+  if (paren != std::string::npos) n.resize(paren);
+  fprintf(stderr, "fh launch %s grid %ux%ux%u block %ux%ux%u lds %zu stream %p (%s)\n", n.c_str(), grid.x, grid.y,
+          grid.z, block.x, block.y, block.z, lds, (void*)s, args.c_str());
+  fflush(stderr);
 }
 namespace {
 
@@ -996,7 +1025,7 @@ __global__ void fill_batch_table_kernel(BatchEntry* dst, BatchTableArgs a) {
 
 hipError_t fill_batch_table(BatchEntry* dst, const BatchTableArgs& args, hipStream_t s) {
   if (!dst || args.n < 1 || args.n > MAX_BATCH_TABLE) return hipErrorInvalidValue;
-  fill_batch_table_kernel<<<1, MAX_BATCH_TABLE, 0, s>>>(dst, args);
+  launch_timed(fill_batch_table_kernel, 1, MAX_BATCH_TABLE, s, dst, args);
   return hipGetLastError();
 }
 
@@ -1021,7 +1050,7 @@ hipError_t gemm_bf16_grouped(int epi, const bf16_t* A, int lda, const bf16_t* W,
 hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, int N, hipStream_t s) {
   if (M <= 0 || !r.part) return hipSuccess;
   if (N % 4 || ldx % 4 || r.nparts < 1 || (r.gate_tab && r.rows_per_lane <= 0)) return hipErrorInvalidValue;
-  residual_from_parts_kernel<<<(unsigned)(((int64_t)M * N / 4 + 255) / 256), 256, 0, s>>>(x, ldx, r, M, N);
+  launch_timed(residual_from_parts_kernel, (unsigned)(((int64_t)M * N / 4 + 255) / 256), 256, s, x, ldx, r, M, N);
   return hipGetLastError();
 }
 
@@ -1077,8 +1106,8 @@ hipError_t mx_quantize(const float* in_f, const bf16_t* in_b, int64_t rows, int 
   if (rows <= 0) return hipSuccess;
   if (K % 64 || (!in_f == !in_b) || !codes || !scales) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((rows * (K / 32) + 255) / 256);
-  if (in_f) mx_quantize_kernel<float><<<grid, 256, 0, s>>>(in_f, rows, K, codes, scales);
-  else mx_quantize_kernel<bf16_t><<<grid, 256, 0, s>>>(in_b, rows, K, codes, scales);
+  if (in_f) launch_timed(mx_quantize_kernel<float>, grid, 256, s, in_f, rows, K, codes, scales);
+  else launch_timed(mx_quantize_kernel<bf16_t>, grid, 256, s, in_b, rows, K, codes, scales);
   return hipGetLastError();
 }
 

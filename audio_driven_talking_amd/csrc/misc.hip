@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void clock_probe_kernel(uint64_t* __restrict__
 
 hipError_t clock_probe(uint64_t* out, int n_wg, int iters, hipStream_t s) {
   if (!out || n_wg < 1 || iters < 1) return hipErrorInvalidValue;
-  clock_probe_kernel<<<n_wg, 256, 0, s>>>(out, iters, 0);
+  launch_timed(clock_probe_kernel, n_wg, 256, s, out, iters, 0);
   return hipGetLastError();
 }
 
@@ -370,8 +370,8 @@ hipError_t head_euler_f32(const float* h, int B, int N, int D, const bf16_t* Wh,
                           float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s) {
   const int64_t total = (int64_t)B * Co * N;
   if (total <= 0) return hipSuccess;
-  head_euler_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next,
-                                                                       motion, n_motion_tok, sigma, sigma_next, sa);
+  launch_timed(head_euler_f32_kernel, (unsigned)((total + 255) / 256), 256, s, h, B, N, D, Wh, bh, Co, lat_cur, lat_next,
+               motion, n_motion_tok, sigma, sigma_next, sa);
   return hipGetLastError();
 }
 
@@ -379,8 +379,8 @@ hipError_t rope_table(float* cos_t, float* sin_t, int F, int H, int W, int head_
                       hipStream_t s) {
   const int half = head_dim / 2, nr = head_dim / 6, nf = half - 2 * nr;
   const int64_t total = (int64_t)F * H * W * half;
-  rope_table_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(cos_t, sin_t, F, H, W, half, nf, nr,
-                                                                   theta);
+  launch_timed(rope_table_kernel, (unsigned)((total + 255) / 256), 256, s, cos_t, sin_t, F, H, W, half, nf, nr,
+               theta);
   return hipGetLastError();
 }
 
@@ -388,14 +388,14 @@ hipError_t sinusoid(float* out, const float* t_host, int R, int dim, hipStream_t
   if (R <= 0 || R > MAXR || dim % 2) return hipErrorInvalidValue;
   Times ts{};
   for (int r = 0; r < R; ++r) ts.t[r] = t_host[r];
-  sinusoid_kernel<<<(R * dim + 255) / 256, 256, 0, s>>>(out, ts, R, dim);
+  launch_timed(sinusoid_kernel, (R * dim + 255) / 256, 256, s, out, ts, R, dim);
   return hipGetLastError();
 }
 
 hipError_t gemv_bf16(const float* x, int R, int K, const bf16_t* W, const float* b, float* y, int N,
                      int act_in, int act_out, hipStream_t s) {
   if (R <= 0 || R > MAXR || K % 8 || (size_t)R * K * 4 > 65536) return hipErrorInvalidValue;
-  gemv_kernel<<<(N + 15) / 16, 256, (size_t)R * K * 4, s>>>(x, R, K, W, b, y, N, act_in, act_out);
+  launch_timed_lds(gemv_kernel, (N + 15) / 16, 256, (size_t)R * K * 4, s, x, R, K, W, b, y, N, act_in, act_out);
   return hipGetLastError();
 }
 
@@ -403,7 +403,7 @@ hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, 
                        float* x, int D, hipStream_t s) {
   if (C > MAXC || D % 4) return hipErrorInvalidValue;
   dim3 grid((N + PT - 1) / PT, B);
-  patch_embed_kernel<<<grid, 256, 0, s>>>(lat, C, N, Wp, bp, x, D);
+  launch_timed(patch_embed_kernel, grid, 256, s, lat, C, N, Wp, bp, x, D);
   return hipGetLastError();
 }
 
@@ -411,30 +411,30 @@ hipError_t head_euler(const bf16_t* h, int B, int N, int D, const bf16_t* Wh, co
                       const float* lat_cur, float* lat_next, const float* motion, int n_motion_tok,
                       float sigma, float sigma_next, const SamplerArgs& sa, hipStream_t s) {
   if (D % 128 || Co % 16) return hipErrorInvalidValue;
-  head_euler_kernel<<<(B * N + 15) / 16, 256, 0, s>>>(h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
-                                                      n_motion_tok, sigma, sigma_next, sa);
+  launch_timed(head_euler_kernel, (B * N + 15) / 16, 256, s, h, B, N, D, Wh, bh, Co, lat_cur, lat_next, motion,
+               n_motion_tok, sigma, sigma_next, sa);
   return hipGetLastError();
 }
 
 hipError_t philox_fill(uint32_t* out, int64_t n_groups, uint32_t first_group, uint32_t lane, uint32_t step,
                        uint64_t seed, hipStream_t s) {
   if (n_groups <= 0) return hipSuccess;
-  philox_fill_kernel<<<(unsigned)((n_groups + 255) / 256), 256, 0, s>>>(out, n_groups, first_group, lane, step,
-                                                                        (uint32_t)seed, (uint32_t)(seed >> 32));
+  launch_timed(philox_fill_kernel, (unsigned)((n_groups + 255) / 256), 256, s, out, n_groups, first_group, lane, step,
+               (uint32_t)seed, (uint32_t)(seed >> 32));
   return hipGetLastError();
 }
 
 hipError_t pin_motion(const float* lat, const float* motion, float* out, int BC, int N,
                       int n_motion_tok, hipStream_t s) {
   const int64_t total = (int64_t)BC * N;
-  pin_motion_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(lat, motion, out, total, N,
-                                                                   n_motion_tok);
+  launch_timed(pin_motion_kernel, (unsigned)((total + 255) / 256), 256, s, lat, motion, out, total, N,
+               n_motion_tok);
   return hipGetLastError();
 }
 
 hipError_t f32_to_bf16(const float* in, bf16_t* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  f32_to_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in, out, n);
+  launch_timed(f32_to_bf16_kernel, (unsigned)((n + 255) / 256), 256, s, in, out, n);
   return hipGetLastError();
 }
 

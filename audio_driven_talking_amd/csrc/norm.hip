@@ -180,8 +180,8 @@ hipError_t layernorm_bf16(float* x, bf16_t* out, int rows, int D, int rows_per_l
       return hipErrorInvalidValue;
     p = *pend;
   }
-  layernorm_kernel<<<rows, threads_for(D), 0, s>>>(x, out, rows, D, rows_per_lane, eps, tab_shift, tab_scale,
-                                                   e_shift, e_scale, e_stride, g, b, p, out_q, q_scale);
+  launch_timed(layernorm_kernel, rows, threads_for(D), s, x, out, rows, D, rows_per_lane, eps, tab_shift, tab_scale,
+               e_shift, e_scale, e_stride, g, b, p, out_q, q_scale);
   return hipGetLastError();
 }
 
@@ -194,8 +194,8 @@ hipError_t rmsnorm_rope_bf16(bf16_t* p, int ld, int rows, int D, int nparts, con
   if (D % 8 || ld % 8 || head_dim % 8 || nparts < 1 || nparts > 2 || tpp * nparts > 512)
     return hipErrorInvalidValue;
   if (out_q && (D % 32 || !q_scale || ldq % 32 || ldq < nparts * D)) return hipErrorInvalidValue;
-  rmsnorm_rope_kernel<<<rows, tpp * nparts, 0, s>>>(p, ld, D, tpp, g0, g1, cos_t, sin_t, rows_per_lane,
-                                                     head_dim, eps, out_q, q_scale, ldq, nullptr, 1);
+  launch_timed(rmsnorm_rope_kernel, rows, tpp * nparts, s, p, ld, D, tpp, g0, g1, cos_t, sin_t, rows_per_lane,
+               head_dim, eps, out_q, q_scale, ldq, nullptr, 1);
   return hipGetLastError();
 }
 
@@ -204,8 +204,8 @@ hipError_t rmsnorm_bf16_table(bf16_t* p, int ld, int rows, int D, const BatchEnt
   if (rows <= 0) return hipSuccess;
   const int tpp = threads_for(D);
   if (D % 8 || ld % 8 || ld < D || tpp > 512 || !tab || rows_per_entry <= 0) return hipErrorInvalidValue;
-  rmsnorm_rope_kernel<<<rows, tpp, 0, s>>>(p, ld, D, tpp, nullptr, nullptr, nullptr, nullptr, 1, 8, eps, nullptr,
-                                           nullptr, 0, tab, rows_per_entry);
+  launch_timed(rmsnorm_rope_kernel, rows, tpp, s, p, ld, D, tpp, nullptr, nullptr, nullptr, nullptr, 1, 8, eps, nullptr,
+               nullptr, 0, tab, rows_per_entry);
   return hipGetLastError();
 }
 

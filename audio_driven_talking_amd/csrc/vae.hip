@@ -468,10 +468,10 @@ hipError_t launch_halo(int epi, const ConvArgs& a, int splits, float* part, hipS
     const int64_t M = (int64_t)a.T * a.H * a.W;
     const dim3 rgrid((unsigned)((M * (a.cout / 4) + 255) / 256));
     switch (epi) {
-      case CONV_PLAIN: conv_reduce_kernel<CONV_PLAIN><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_RES: conv_reduce_kernel<CONV_RES><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_UP: conv_reduce_kernel<CONV_UP><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_FRAMES: conv_reduce_kernel<CONV_FRAMES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_PLAIN: launch_timed(conv_reduce_kernel<CONV_PLAIN>, rgrid, block, s, a, part, splits); break;
+      case CONV_RES: launch_timed(conv_reduce_kernel<CONV_RES>, rgrid, block, s, a, part, splits); break;
+      case CONV_UP: launch_timed(conv_reduce_kernel<CONV_UP>, rgrid, block, s, a, part, splits); break;
+      case CONV_FRAMES: launch_timed(conv_reduce_kernel<CONV_FRAMES>, rgrid, block, s, a, part, splits); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -497,10 +497,10 @@ hipError_t launch_conv(int epi, const ConvArgs& a, int splits, float* part, hipS
     launch_timed(conv3d_kernel<BN, CONV_PART>, grid, block, s, a, tiles_m, tiles, splits, part);
     const dim3 rgrid((unsigned)((M * (a.cout / 4) + 255) / 256));
     switch (epi) {
-      case CONV_PLAIN: conv_reduce_kernel<CONV_PLAIN><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_RES: conv_reduce_kernel<CONV_RES><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_UP: conv_reduce_kernel<CONV_UP><<<rgrid, block, 0, s>>>(a, part, splits); break;
-      case CONV_FRAMES: conv_reduce_kernel<CONV_FRAMES><<<rgrid, block, 0, s>>>(a, part, splits); break;
+      case CONV_PLAIN: launch_timed(conv_reduce_kernel<CONV_PLAIN>, rgrid, block, s, a, part, splits); break;
+      case CONV_RES: launch_timed(conv_reduce_kernel<CONV_RES>, rgrid, block, s, a, part, splits); break;
+      case CONV_UP: launch_timed(conv_reduce_kernel<CONV_UP>, rgrid, block, s, a, part, splits); break;
+      case CONV_FRAMES: launch_timed(conv_reduce_kernel<CONV_FRAMES>, rgrid, block, s, a, part, splits); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -581,14 +581,14 @@ hipError_t norm_silu_f16(const _Float16* x, const float* g, _Float16* y, int64_t
   if (M <= 0) return hipSuccess;
   if (C < 8 || C > 512 || (C & (C - 1))) return hipErrorInvalidValue;
   const int64_t threads = M * (C / 8);
-  norm_silu_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(x, g, y, M, C, eps);
+  launch_timed(norm_silu_kernel, (unsigned)((threads + 255) / 256), 256, s, x, g, y, M, C, eps);
   return hipGetLastError();
 }
 
 hipError_t latent_to_f16(const float* lat, int C, int64_t FHW, _Float16* out, _Float16* zero, hipStream_t s) {
   const int64_t n = (int64_t)C * FHW;
   const int64_t total = n > 128 ? n : 128;
-  latent_f16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(lat, C, FHW, out, zero);
+  launch_timed(latent_f16_kernel, (unsigned)((total + 255) / 256), 256, s, lat, C, FHW, out, zero);
   return hipGetLastError();
 }
 

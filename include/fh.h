@@ -25,6 +25,12 @@
  *  - Results are deterministic: the same inputs give the same bits.
  *  - On error a call returns an FH_E* code, enqueues nothing, and
  *    fh_last_error() describes the problem.
+ *  - Launch trace: with FH_TRACE=1 in the environment (read once per
+ *    process), every kernel launch prints one line to stderr -- kernel name
+ *    with its template arguments, grid, block, dynamic LDS bytes, stream and
+ *    the kernel's scalar arguments (sizes, strides, scales; pointers as
+ *    addresses). Work recorded into a HIP graph prints when the graph is
+ *    captured (a call's first run with FH_OPT_GRAPH on), not on replays.
  */
 #ifndef FH_H
 #define FH_H
