@@ -862,8 +862,9 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   if (wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(128 * WN * KW + (PF ? 64 : 0));
 #define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH, PF, WN>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
-  if constexpr (WN == 4) {  // 2 x 4 waves: the GELU product alone
+  if constexpr (WN == 4) {  // 2 x 4 waves: the GELU and QKV products
     if (epi == EPI_GELU_BF16) FH_GEMM(EPI_GELU_BF16);
+    else if (epi == EPI_SPLIT_T) FH_GEMM(EPI_SPLIT_T);
     else return hipErrorInvalidValue;
   } else if constexpr (PF) {  // the forms that prefetch: the residual, query and split-K products
     if (!ep.pf.any()) return hipErrorInvalidValue;
@@ -1075,7 +1076,9 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
         return launch<128, 64, 64, 4, 1, false, true>(epi, A, lda, W, ldw, M, N, K, ep, s);
       return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 3: return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    default: return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    default:
+      if (epi == EPI_SPLIT_T && M <= 1536) return launch<192, 128, 64, 3, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+      return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
 }
 

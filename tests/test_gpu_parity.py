@@ -282,15 +282,18 @@ def test_slice_two_blocks_full_width(fh):
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
 
 
-def test_slice_ragged_tiles(fh):
+@pytest.mark.parametrize("B", [1, 2])
+def test_slice_ragged_tiles(fh, B):
     """800 tokens (5 x 16 x 10): the GEMM M tail, the attention query tail and a
-    half key block; one block, one step."""
+    half key block; one block, one step. At B = 1 (M = 800) the FFN up-projection
+    runs its 2 x 4-wave 192-row tiles with a 32-row last tile (the waves of its
+    last 96 rows hold no valid row); at B = 2 (M = 1600) the 4-stage 2 x 2-wave form."""
     cfg = synth.CONFIGS["slice"].replace(n_blocks=1, width=10)
     W = synth.make_weights(cfg)
-    m = Model(fh, cfg, W, 2)
-    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    m = Model(fh, cfg, W, B)
+    lat, mot, aud = synth.slice_inputs(cfg, B)
     sig = [0.8, 0.3]
-    say("ragged slice 5x16x10, B=2")
+    say(f"ragged slice 5x16x10, B={B}")
     got = m.slice(lat, mot, aud, sig)
     ref = O.denoise_slice(lat, mot, aud, sig, synth.weights_f32(W), cfg)
     err = O.rel_err(got, ref, cfg.motion_frames)
