@@ -862,9 +862,13 @@ hipError_t launch(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, i
   if (wgs > (int64_t)1 << 30) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((wgs + 7) / 8 * 8)), block(128 * WN * KW + (PF ? 64 : 0));
 #define FH_GEMM(E) launch_gemm(gemm_bf16_nt<E, BM, BN, BK, NS, KW, BATCH, PF, WN>, grid, block, s, A, lda, W, ldw, M, N, K, tiles_m, tiles, splits, ep)
-  if constexpr (WN == 4) {  // 2 x 4 waves: the GELU and QKV products
+  if constexpr (WN == 4) {  // 2 x 4 waves
     if (epi == EPI_GELU_BF16) FH_GEMM(EPI_GELU_BF16);
     else if (epi == EPI_SPLIT_T) FH_GEMM(EPI_SPLIT_T);
+    else if (epi == EPI_GATED_RES) FH_GEMM(EPI_GATED_RES);
+    else if (epi == EPI_RES) FH_GEMM(EPI_RES);
+    else if (epi == EPI_BF16) FH_GEMM(EPI_BF16);
+    else if (epi == EPI_BF16_SSQ) FH_GEMM(EPI_BF16_SSQ);
     else return hipErrorInvalidValue;
   } else if constexpr (PF) {  // the forms that prefetch: the residual, query and split-K products
     if (!ep.pf.any()) return hipErrorInvalidValue;
@@ -1056,8 +1060,10 @@ hipError_t residual_from_parts(float* x, int ldx, const PendingRes& r, int M, in
 }
 
 int gemm_ssq_groups(int M, int N, int K) {
-  static const int bn[] = {256, 256, 64, 128, 128};  // BN of each gemm_tile_choice
-  return N / (bn[gemm_tile_choice(M, N, K)] / 2);
+  // columns per wave of each gemm_tile_choice's tiles: BN / 2, or BN / 4 where 2 x 4 waves run them
+  const int c = gemm_tile_choice(M, N, K);
+  static const int cols[] = {128, 128, 32, 64, 64};
+  return N / (c == 4 && M > 1536 ? 32 : cols[c]);
 }
 
 hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw, int M, int N, int K,
@@ -1069,7 +1075,9 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
     case 0:
       if (epi == EPI_GELU_BF16) return launch<192, 256, 32, 3, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
       return launch<192, 256, 32, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
-    case 1: return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+    case 1:
+      if (epi == EPI_GELU_BF16) return launch<192, 256, 32, 4, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+      return launch<192, 256, 32, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 2:
       // a fifth wave fits beside these tiles' registers (no spill), so they carry the prefetch
       if (ep.pf.any() && (epi == EPI_GATED_RES || epi == EPI_RES || epi == EPI_BF16_SSQ))
@@ -1077,7 +1085,9 @@ hipError_t gemm_bf16(int epi, const bf16_t* A, int lda, const bf16_t* W, int ldw
       return launch<128, 64, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     case 3: return launch<64, 128, 64, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
     default:
-      if (epi == EPI_SPLIT_T && M <= 1536) return launch<192, 128, 64, 3, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
+      if (epi == EPI_SPLIT_T ||
+          (M > 1536 && (epi == EPI_GATED_RES || epi == EPI_RES || epi == EPI_BF16 || epi == EPI_BF16_SSQ)))
+        return launch<192, 128, 64, 3, 1, false, false, 4>(epi, A, lda, W, ldw, M, N, K, ep, s);
       return launch<192, 128, 64, 3>(epi, A, lda, W, ldw, M, N, K, ep, s);
   }
 }
