@@ -620,20 +620,27 @@ constexpr int mx_slab_bytes() { return (BM + BN) * 64 + ((mx_arows<BM>() + BN) *
 
 __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }  // 64-byte rows
 
-template <int EPI, int BM, int BN, int NS>
-__global__ __launch_bounds__(256, 1)
+// WN = 4: 2 x 4 waves (two per SIMD), the activation DMA groups dealt as in
+// the bf16 kernel (a wave may take one fewer; its wait counts follow). FFN up
+// runs so (32.5 -> 30.3 us at 1280 tokens); the QKV tiles were slower.
+template <int EPI, int BM, int BN, int NS, int WN = 2>
+__global__ __launch_bounds__(128 * WN, 1)
 void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restrict__ As,
                 const uint8_t* __restrict__ W, int ldw, const uint16_t* __restrict__ Ws,
                 int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
   constexpr int ROWB = 64, CH = 4, RG = 16;   // bytes per LDS row, 16-byte chunks, rows per 1 KB DMA
-  constexpr int MI = BM / 64, NI = BN / 64;
-  constexpr int GA = BM / RG / 4, GW = BN / RG / 4;  // 1 KB code DMAs per wave per slab
+  constexpr int NW = 2 * WN;                  // waves, 2 x WN
+  constexpr int MI = BM / 64, NI = BN / (32 * WN);
+  constexpr int TA = BM / RG, TW = BN / RG;   // 1 KB code DMAs per slab, activations / weights
+  constexpr int GA = (TA + NW - 1) / NW, GW = (TW + NW - 1) / NW;  // ... at most per wave
   constexpr int SQA = mx_arows<BM>() / 128, SQ = SQA + BN / 128;  // 256-byte scale DMAs per slab
-  constexpr int SPW = (SQ + 3) / 4;                  // scale DMAs per wave (the last one repeated)
+  constexpr int SPW = (SQ + NW - 1) / NW;            // scale DMAs per wave (the last one repeated)
   constexpr int DPS = GA + GW + SPW;
   constexpr int SCB = (BM + BN) * ROWB;              // scale area of a slab
   constexpr int SLAB = mx_slab_bytes<BM, BN>();
-  static_assert(GA * RG * 4 == BM && GW * RG * 4 == BN && BN % 128 == 0, "tile shape");
+  static_assert(TA * RG == BM && TW * RG == BN && BN % 128 == 0 && BN % (32 * WN) == 0, "tile shape");
+  static_assert(WN == 2 || WN == 4, "2 x 2 or 2 x 4 waves");
+  static_assert(GW * NW == TW && (GA * NW == TA || GA * NW - TA < NW), "at most one group fewer per wave");
   static_assert(NS >= 2 && (NS - 1) * DPS < 64, "DMA wait count must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SLAB];
 
@@ -650,21 +657,24 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lh = lane >> 5;
   (void)slabs_all;
+  // whether this wave takes GA activation DMA groups (wave + NW i < TA), or one fewer
+  constexpr bool EVEN = GA * NW == TA;
+  const bool a_full = EVEN || wave + NW * (GA - 1) < TA;
 
   const int drow = lane / CH;
   const uint8_t* ga[GA];
   const uint8_t* gw[GW];
 #pragma unroll
   for (int i = 0; i < GA; ++i) {
-    const int r = RG * (wave + 4 * i) + drow;
+    const int r = RG * (wave + NW * i) + drow;
     ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
-    const int r = RG * (wave + 4 * i) + drow;
+    const int r = RG * (wave + NW * i) + drow;
     gw[i] = W + (int64_t)(n0 + r) * ldw + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
   }
   // scale DMA t of this wave (instruction q): rows 128 q + 2 lane and the next,
@@ -673,18 +683,18 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
   const uint16_t* gs[SPW];
 #pragma unroll
   for (int t = 0; t < SPW; ++t) {
-    const int q = min(wave + 4 * t, SQ - 1);
+    const int q = min(wave + NW * t, SQ - 1);
     gs[t] = q < SQA ? As + (int64_t)s_base * M + min(m0 + 128 * q + 2 * lane, M - 2)
                     : Ws + (int64_t)s_base * N + (n0 + 128 * (q - SQA) + 2 * lane);
   }
   auto dma_one = [&](int d, int buf, int slab) {
     char* sb = smem + buf * SLAB;
     if (d < GA) {
-      dma16(ga[d] + slab * 64, sb + (wave + 4 * d) * 1024);
+      if (EVEN || d < GA - 1 || a_full) dma16(ga[d] + slab * 64, sb + (wave + NW * d) * 1024);
     } else if (d < GA + GW) {
-      dma16(gw[d - GA] + slab * 64, sb + BM * ROWB + (wave + 4 * (d - GA)) * 1024);
+      dma16(gw[d - GA] + slab * 64, sb + BM * ROWB + (wave + NW * (d - GA)) * 1024);
     } else {
-      const int t = d - GA - GW, q = min(wave + 4 * t, SQ - 1);
+      const int t = d - GA - GW, q = min(wave + NW * t, SQ - 1);
       const int64_t step = q < SQA ? M : N;  // u16 elements per slab in this scale array
       __builtin_amdgcn_global_load_lds((gbl_void*)(gs[t] + slab * step), (lds_void*)(sb + SCB + q * 256), 4, 0, 0);
     }
@@ -700,7 +710,7 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
 
   typedef int v8i __attribute__((ext_vector_type(8)));
   constexpr int P = NI * MI, NR = NI + MI;
-  const int a_row = wm * (BM / 2) + lr, w_row = BM + wn * (BN / 2) + lr;  // slab rows (W after A)
+  const int a_row = wm * (BM / 2) + lr, w_row = BM + wn * (BN / WN) + lr;  // slab rows (W after A)
   v8i wf[2][NI], af[2][MI];
   int wsc[2][NI], asc[2][MI];
   // fragment read r of a slab (and its scale byte): r < NI weights, else activations
@@ -741,12 +751,18 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
   for (int s0 = 0; s0 < NS; ++s0)
 #pragma unroll
     for (int d = 0; d < DPS; ++d) dma_one(d, s0, min(s0, KT - 1));
-  wait_vm<(NS - 1) * DPS>();
+  // wait until at most n slabs' DMAs of this wave are in flight
+  auto wait_slabs = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    if (a_full) wait_vm<n * DPS>();
+    else wait_vm<n * (DPS - 1)>();
+  };
+  wait_slabs(std::integral_constant<int, NS - 1>{});
   barrier();
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_one(r, 0, 0);
   auto iteration = [&](int kt, auto set_c) {
-    wait_vm<(NS - 2) * DPS>();  // this wave's DMAs of slab kt + 1 have landed
+    wait_slabs(std::integral_constant<int, NS - 2>{});  // this wave's DMAs of slab kt + 1 have landed
     wait_lgkm0();               // and its fragments of slab kt are in registers
     barrier();                  // so for every wave: slab kt + 1 is in, buffer kt % NS is free
     mma_slab(set_c, (kt + 1) % NS, kt % NS, min(kt + NS, KT - 1));
@@ -756,10 +772,10 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
     if (kt + 1 < KT) iteration(kt + 1, std::integral_constant<int, 1>{});
   }
   wait_vm<0>();
-  static_assert(4 * Stage<BN / 2>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
+  static_assert(NW * Stage<BN / WN>::BYTES <= NS * SLAB, "epilogue staging must fit the slab buffers");
   wait_lgkm0();
   barrier();
-  store_tile<EPI, BM, BN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
+  store_tile<EPI, BM, BN, WN>(acc, smem, ep, M, N, m0, n0, wm, wn, wave, lane, ks);
 }
 
 // one thread per 32-element block: codes and the block's scale byte
@@ -795,7 +811,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ 
   reinterpret_cast<uint8_t*>(scales)[((int64_t)(kb / 2) * rows + row) * 2 + (kb & 1)] = (uint8_t)(ex + 127);
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WN = 2>
 hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
                      const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s,
                      int splits = 1) {
@@ -807,21 +823,26 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
   if ((epi == EPI_SPLIT_T || epi == EPI_SPLIT_T_MX) && (ep.split % BN || ep.rows_per_lane <= 0 || ep.rows_per_lane % 8))
     return hipErrorInvalidValue;
   if (epi == EPI_SPLIT_T_MX && (ep.rows_per_lane % 64 || M % ep.rows_per_lane || !ep.out_q || !ep.q_scale_b ||
-                                (BN / 2) % 64))
+                                (BN / WN) % 64))
     return hipErrorInvalidValue;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
-  const dim3 grid((tiles * splits + 7) / 8 * 8), block(256);
-#define FH_MX(E) launch_gemm(gemm_mx_nt<E, BM, BN, NS>, grid, block, s, A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
-  switch (epi) {
-    case EPI_BF16: FH_MX(EPI_BF16); break;
-    case EPI_GELU_MX: FH_MX(EPI_GELU_MX); break;
-    case EPI_GATED_RES: FH_MX(EPI_GATED_RES); break;
-    case EPI_RES: FH_MX(EPI_RES); break;
-    case EPI_PARTIAL: FH_MX(EPI_PARTIAL); break;
-    case EPI_SPLIT_T: FH_MX(EPI_SPLIT_T); break;
-    case EPI_SPLIT_T_MX: FH_MX(EPI_SPLIT_T_MX); break;
-    default: return hipErrorInvalidValue;
+  const dim3 grid((tiles * splits + 7) / 8 * 8), block(128 * WN);
+#define FH_MX(E) launch_gemm(gemm_mx_nt<E, BM, BN, NS, WN>, grid, block, s, A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
+  if constexpr (WN == 4) {  // 2 x 4 waves: the FFN up product
+    if (epi == EPI_GELU_MX) FH_MX(EPI_GELU_MX);
+    else return hipErrorInvalidValue;
+  } else {
+    switch (epi) {
+      case EPI_BF16: FH_MX(EPI_BF16); break;
+      case EPI_GELU_MX: FH_MX(EPI_GELU_MX); break;
+      case EPI_GATED_RES: FH_MX(EPI_GATED_RES); break;
+      case EPI_RES: FH_MX(EPI_RES); break;
+      case EPI_PARTIAL: FH_MX(EPI_PARTIAL); break;
+      case EPI_SPLIT_T: FH_MX(EPI_SPLIT_T); break;
+      case EPI_SPLIT_T_MX: FH_MX(EPI_SPLIT_T_MX); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef FH_MX
   return hipGetLastError();
@@ -1099,8 +1120,10 @@ hipError_t gemm_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const
   // stage counts from a same-process A/B of the FP8 slice (3 beat 4 and 5 here; 4 beat 3, 6 and 8 for split K);
   // 192 x 256 tiles only where they still give most CUs a tile (FFN up: 245 at 1280 tokens; QKV: 126 -> 192 x 128)
   const int64_t tiles_wide = (int64_t)((M + 191) / 192) * (N / 256);
-  if (N % 256 == 0 && N >= 4096 && tiles_wide >= 200)
+  if (N % 256 == 0 && N >= 4096 && tiles_wide >= 200) {
+    if (epi == EPI_GELU_MX) return launch_mx<192, 256, 3, 4>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
     return launch_mx<192, 256, 3>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
+  }
   return launch_mx<192, 128, 5>(epi, A, lda, As, W, ldw, Ws, M, N, K, ep, s);
 }
 
