@@ -184,12 +184,13 @@ int fh_dit_denoise_slice(fh_ctx* ctx, const fh_weights* w, int batch, const floa
  *       cos(2 pi u_b) for even i, sin(2 pi u_b) for odd i (Box-Muller).
  *       Motion frames are pinned after every step as with Euler; at s' = 0
  *       the two updates coincide.
- *   FH_OPT_PREFETCH: 1 (default): while a bf16 FFN up-projection runs, one
- *     extra wave per workgroup reads the block's down-projection weights,
- *     and while the down-projection runs, the next block's attention output
- *     and cross-attention query weights, so those GEMMs find them in the
- *     memory-side cache rather than in HBM; 0 turns it off. Results are
- *     bit-identical either way.                                            */
+ *   FH_OPT_PREFETCH: 1 (default): while the bf16 self-attention output and
+ *     cross-attention query projections run, one extra wave per workgroup
+ *     reads half each of the block's FFN down-projection weights, and while
+ *     the down-projection runs, the next block's attention-output and
+ *     cross-query weights, so those GEMMs find them in the memory-side cache
+ *     rather than in HBM; 0 turns it off. Results are bit-identical either
+ *     way.                                                                 */
 enum { FH_OPT_GRAPH = 1, FH_OPT_TIME_KERNEL = 2, FH_OPT_SAMPLER = 3, FH_OPT_PRECISION = 4, FH_OPT_PREFETCH = 5 };
 enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
 /*   FH_OPT_PRECISION: FH_PREC_BF16 (default): bf16 operands everywhere.
