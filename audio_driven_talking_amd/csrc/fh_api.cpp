@@ -369,6 +369,20 @@ fh::Prefetch ffn2_half(const WBlock& wb, int D, int Fd, int i) {
   return pf;
 }
 
+// The MX-FP8 form (FP8 FFN precisions): the codes (D Fd bytes) in two halves,
+// the scales ([Fd / 64][D] u16) with the second.
+fh::Prefetch ffn2_half_mx(const WBlock& wb, int D, int Fd, int i) {
+  const int64_t total = (int64_t)D * Fd, half = (total / 2) & ~(int64_t)1023;
+  fh::Prefetch pf;
+  pf.p[0] = reinterpret_cast<const char*>(wb.ffn2_q) + i * half;
+  pf.bytes[0] = i ? total - half : half;
+  if (i) {
+    pf.p[1] = wb.ffn2_s;
+    pf.bytes[1] = (int64_t)(Fd / 64) * D * 2;
+  }
+  return pf;
+}
+
 int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int e0_stride,
               const bf16_t* kc, const bf16_t* vct, const WS& ws, hipStream_t s,
               const fh::PendingRes* pend_in, fh::PendingRes* pend_out, const WBlock* next) {
@@ -426,7 +440,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.gate_e0 = e0 + 2 * D;
     ep.gate_stride = e0_stride;
     ep.rows_per_lane = N;
-    if (c->prefetch && !fp8) ep.pf = ffn2_half(wb, D, Fd, 0);
+    if (c->prefetch) ep.pf = fp8 ? ffn2_half_mx(wb, D, Fd, 0) : ffn2_half(wb, D, Fd, 0);
     FH_HIP(fh::gemm_bf16(fh::EPI_GATED_RES, ws.ao, D, wb.o_w, D, M, D, D, ep, s));
   }
   {
@@ -443,7 +457,7 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
     ep.out_bf = ws.qc;
     ep.ldo = D;
     ep.ssq = ws.ssq;
-    if (c->prefetch && !fp8) ep.pf = ffn2_half(wb, D, Fd, 1);
+    if (c->prefetch) ep.pf = fp8 ? ffn2_half_mx(wb, D, Fd, 1) : ffn2_half(wb, D, Fd, 1);
     FH_HIP(fh::gemm_bf16(fh::EPI_BF16_SSQ, ws.h, D, wb.cq_w, D, M, D, D, ep, s));
   }
   if (c->fold_co) {

@@ -328,16 +328,22 @@ def test_full_slice_against_stored_oracle(fh, case):
     np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
 
 
-def test_weight_prefetch_changes_nothing(fh):
+@pytest.mark.parametrize("precision", ["bf16", "fp8attn"])
+def test_weight_prefetch_changes_nothing(fh, precision):
     """FH_OPT_PREFETCH only adds loads of weights into the caches: a full slice
     at 1280 tokens, where the attention output, cross-attention query and
-    split-K FFN down-projection GEMMs carry the prefetch wave, is bit-identical
-    with it on (graph and direct launches) and off."""
+    (bf16) split-K FFN down-projection GEMMs carry the prefetch wave, is
+    bit-identical with it on (graph and direct launches) and off; with the MX-FP8
+    FFN the prefetched ranges are its codes and scales."""
     cfg = synth.CONFIGS["slice"]
-    m = Model(fh, cfg, synth.make_weights(cfg), 1)
+    if precision == "bf16":
+        m = Model(fh, cfg, synth.make_weights(cfg), 1)
+    else:
+        m = Model(fh, cfg, synth.make_weights(cfg), 1, precision=fh.FH_PREC_FP8_ATTN)
+        fh.fh_weights_quantize_fp8(m.ctx, m.w)
     lat, mot, aud = synth.slice_inputs(cfg, 1)
     sig = list(synth.SLICE_SIGMAS)
-    say("full slice B=1, prefetch on / off / on without the graph")
+    say(f"full slice B=1, {precision}, prefetch on / off / on without the graph")
     outs = []
     for pf, graph in ((1, True), (0, True), (1, False)):
         fh.fh_set_option(m.ctx, fh.FH_OPT_PREFETCH, pf)
