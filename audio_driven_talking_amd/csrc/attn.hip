@@ -485,48 +485,74 @@ constexpr int MAXG = 64;  // most column groups of the query sums of squares
 
 // The MFMA B-operand fragments of 32 query rows q0 .. q0+31 of head h (row
 // lr of lane half lh: dims 16 s + 8 lh .. +7 in qf[s]), with the query
-// RMSNorm over the full width applied when ssq is given.
+// RMSNorm over the full width applied when ssq is given. q_request issues
+// every load (the fragments, the row's column-group sums, the head's gains)
+// and q_finish waits for them and applies the norm, so a caller can put its
+// own independent loads in between.
+struct QReq {
+  bf16x8 qf[8];
+  f32x4 part[MAXG / 4];
+  f32x4 gv[16];
+};
+
+__device__ __forceinline__ void q_request(QReq& r, const bf16_t* __restrict__ q, int ldq, int b, int h, int q0,
+                                          int N, const float* __restrict__ ssq, int groups,
+                                          const float* __restrict__ g) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int qrow = min(q0 + lr, N - 1);
+  const bf16_t* qp = q + ((int64_t)b * N + qrow) * ldq + h * HD + 8 * lh;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r.qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  if (ssq) {
+    // all of the row's group sums requested at once (16-byte loads)
+    const f32x4* sp = reinterpret_cast<const f32x4*>(ssq + ((int64_t)b * N + qrow) * groups);
+#pragma unroll
+    for (int p = 0; p < MAXG / 4; ++p)
+      if (4 * p < groups) r.part[p] = sp[p];
+    const float* gp = g + h * HD + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.gv[2 * s] = *reinterpret_cast<const f32x4*>(gp + 16 * s);
+      r.gv[2 * s + 1] = *reinterpret_cast<const f32x4*>(gp + 16 * s + 4);
+    }
+  }
+}
+
+__device__ __forceinline__ void q_finish(QReq& r, bf16x8 (&qf)[8], int D, const float* __restrict__ ssq,
+                                         int groups, float eps) {
+  if (ssq) {
+    // RMSNorm of the query row over the full width: the group sums added in order
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAXG / 4; ++p)
+      if (4 * p < groups) ss = (((ss + r.part[p][0]) + r.part[p][1]) + r.part[p][2]) + r.part[p][3];
+    const float rs = rsqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f32x4 g0 = r.gv[2 * s], g1 = r.gv[2 * s + 1];
+      const u32x4 raw = __builtin_bit_cast(u32x4, r.qf[s]);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        w[e] = pack2bf(__uint_as_float(raw[e] << 16) * rs * g0[2 * e],
+                       __uint_as_float(raw[e] & 0xffff0000u) * rs * g0[2 * e + 1]);
+        w[e + 2] = pack2bf(__uint_as_float(raw[e + 2] << 16) * rs * g1[2 * e],
+                           __uint_as_float(raw[e + 2] & 0xffff0000u) * rs * g1[2 * e + 1]);
+      }
+      r.qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = r.qf[s];
+}
+
 __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[8], const bf16_t* __restrict__ q, int ldq, int b, int h,
                                              int q0, int N, int D, const float* __restrict__ ssq, int groups,
                                              const float* __restrict__ g, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lh = lane >> 5;
-  {
-    const int qrow = min(q0 + lr, N - 1);
-    const bf16_t* qp = q + ((int64_t)b * N + qrow) * ldq + h * HD + 8 * lh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-    if (ssq) {
-      // RMSNorm of the query row over the full width, from the column-group sums
-      // all of the row's group sums requested at once (16-byte loads), added in order
-      const f32x4* sp = reinterpret_cast<const f32x4*>(ssq + ((int64_t)b * N + qrow) * groups);
-      f32x4 part[MAXG / 4];
-#pragma unroll
-      for (int p = 0; p < MAXG / 4; ++p)
-        if (4 * p < groups) part[p] = sp[p];
-      float ss = 0.f;
-#pragma unroll
-      for (int p = 0; p < MAXG / 4; ++p)
-        if (4 * p < groups) ss = (((ss + part[p][0]) + part[p][1]) + part[p][2]) + part[p][3];
-      const float rs = rsqrtf(ss / (float)D + eps);
-      const float* gp = g + h * HD + 8 * lh;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp + 16 * s);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 16 * s + 4);
-        const u32x4 raw = __builtin_bit_cast(u32x4, qf[s]);
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          w[e] = pack2bf(__uint_as_float(raw[e] << 16) * rs * g0[2 * e],
-                         __uint_as_float(raw[e] & 0xffff0000u) * rs * g0[2 * e + 1]);
-          w[e + 2] = pack2bf(__uint_as_float(raw[e + 2] << 16) * rs * g1[2 * e],
-                             __uint_as_float(raw[e + 2] & 0xffff0000u) * rs * g1[2 * e + 1]);
-        }
-        qf[s] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-  }
+  QReq r;
+  q_request(r, q, ldq, b, h, q0, N, ssq, groups, g);
+  q_finish(r, qf, D, ssq, groups, eps);
 }
 
 __global__ __launch_bounds__(64) void cross_attn_kernel(
@@ -615,9 +641,18 @@ __global__ __launch_bounds__(64) void cross_probs_kernel(
   const int lr = lane & 31, lh = lane >> 5;
   const int q0 = blockIdx.x * 32;
 
-  bf16x8 qf[8];
-  load_q_frags(qf, q, ldq, b, h, q0, N, D, ssq, groups, g, eps);
+  // the query's loads and the first key block's go out together: one latency
   const int k_lo = (q0 / hw) * apf, nkb = apf / 32;
+  bf16x8 qf[8];
+  QReq qr;
+  q_request(qr, q, ldq, b, h, q0, N, ssq, groups, g);
+  bf16x8 kf0[8];
+  {
+    const bf16_t* kp = kc + ((int64_t)b * La + k_lo + lr) * ldk + h * HD + 8 * lh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+  }
+  q_finish(qr, qf, D, ssq, groups, eps);
 
   // S^T blocks: lane (lr, lh) holds query lr's scores of keys 8 (r/4) + 4 lh + r%4
   f32x16 st[MAXKB];
@@ -626,9 +661,14 @@ __global__ __launch_bounds__(64) void cross_probs_kernel(
   for (int kb = 0; kb < MAXKB; ++kb) {
     if (kb >= nkb) break;
     bf16x8 kf[8];
-    const bf16_t* kp = kc + ((int64_t)b * La + k_lo + 32 * kb + lr) * ldk + h * HD + 8 * lh;
+    if (kb == 0) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+      for (int s = 0; s < 8; ++s) kf[s] = kf0[s];
+    } else {
+      const bf16_t* kp = kc + ((int64_t)b * La + k_lo + 32 * kb + lr) * ldk + h * HD + 8 * lh;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
