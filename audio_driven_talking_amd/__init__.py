@@ -24,7 +24,7 @@ FH_OK, FH_EINVAL, FH_ESHAPE, FH_EUNSUPPORTED, FH_EWORKSPACE, FH_EHIP, FH_EWEIGHT
 FH_DTYPE_BF16, FH_DTYPE_F32, FH_DTYPE_F16 = 1, 2, 3
 FH_OPT_GRAPH, FH_OPT_TIME_KERNEL, FH_OPT_SAMPLER, FH_OPT_PRECISION, FH_OPT_PREFETCH = 1, 2, 3, 4, 5
 FH_SAMPLER_EULER, FH_SAMPLER_RENOISE = 0, 1
-FH_PREC_BF16, FH_PREC_FP8_FFN, FH_PREC_FP32, FH_PREC_FP8_ATTN = 0, 1, 2, 3
+FH_PREC_BF16, FH_PREC_FP8_FFN, FH_PREC_FP32, FH_PREC_FP8_ATTN, FH_PREC_FP8_QKV = 0, 1, 2, 3, 4
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_cq", "gemm_co", "gemm_ffn1", "gemm_ffn2", "attn",
                   "cross_attn", "layernorm", "rmsnorm_rope", "audio_kv"]
 FH_K = {n: i for i, n in enumerate(KERNEL_CLASSES)}

@@ -392,11 +392,12 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
   // FP8 self-attention: the QKV projection too runs on MX-FP8 operands (the
   // LayerNorm writes codes and scales for it)
   const bool mx_attn = c->precision == FH_PREC_FP8_ATTN;
-  const bool fp8 = c->precision == FH_PREC_FP8_FFN || mx_attn;
+  const bool mx_qkv = mx_attn || c->precision == FH_PREC_FP8_QKV;  // QKV projection on MX-FP8 operands
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN || mx_qkv;
   {
     Timed t(c, FH_K_LAYERNORM, s);
     FH_HIP(fh::layernorm_bf16(x, ws.h, M, D, N, g.eps, wb.mod, wb.mod + D, e0, e0 + D, e0_stride,
-                              nullptr, nullptr, pend_in, s, mx_attn ? ws.hq : nullptr, mx_attn ? ws.hs : nullptr));
+                              nullptr, nullptr, pend_in, s, mx_qkv ? ws.hq : nullptr, mx_qkv ? ws.hs : nullptr));
   }
   {
     Timed t(c, FH_K_GEMM_QKV, s);
@@ -412,6 +413,8 @@ int run_block(fh_ctx* c, const WBlock& wb, int B, float* x, const float* e0, int
       ep.out_q = ws.vq;
       ep.q_scale_b = ws.vs;
       FH_HIP(fh::gemm_mx(fh::EPI_SPLIT_T_MX, ws.hq, D, ws.hs, wb.qkv_q, D, wb.qkv_s, M, 3 * D, D, ep, s));
+    } else if (mx_qkv) {  // bf16 q, k and transposed values for the bf16 attention
+      FH_HIP(fh::gemm_mx(fh::EPI_SPLIT_T, ws.hq, D, ws.hs, wb.qkv_q, D, wb.qkv_s, M, 3 * D, D, ep, s));
     } else {
       FH_HIP(fh::gemm_bf16(fh::EPI_SPLIT_T, ws.h, D, wb.qkv_w, D, M, 3 * D, D, ep, s));
     }
@@ -881,7 +884,8 @@ int resolve_tensors(fh_ctx* c, const std::vector<Spec>& specs, const void* blob,
 int check_precision(fh_ctx* c, const fh_weights* w) {
   if (c->precision == FH_PREC_FP8_ATTN && c->N % 64)
     return fail(c, FH_EUNSUPPORTED, "FP8 self-attention needs tokens per lane a multiple of 64 (have %d)", c->N);
-  const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN;
+  const bool fp8 = c->precision == FH_PREC_FP8_FFN || c->precision == FH_PREC_FP8_ATTN ||
+                   c->precision == FH_PREC_FP8_QKV;
   if (fp8 && !w->fp8)
     return fail(c, FH_EINVAL, "FP8 precision needs fh_weights_quantize_fp8 on these weights");
   return FH_OK;
@@ -1232,7 +1236,8 @@ int fh_set_option(fh_ctx* c, int option, int value) {
     return FH_OK;
   }
   if (option == FH_OPT_PRECISION) {
-    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32 && value != FH_PREC_FP8_ATTN)
+    if (value != FH_PREC_BF16 && value != FH_PREC_FP8_FFN && value != FH_PREC_FP32 && value != FH_PREC_FP8_ATTN &&
+        value != FH_PREC_FP8_QKV)
       return fail(c, FH_EINVAL, "unknown precision %d", value);
     c->precision = value;
     return FH_OK;

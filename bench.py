@@ -1,7 +1,7 @@
 """Throughput of the FlashHead Lite slice denoiser on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload slice|slice_b3|slice768]
-                    [--sampler euler|renoise] [--precision bf16|fp8ffn]
+                    [--sampler euler|renoise] [--precision bf16|fp8ffn|fp8qkv|fp8attn]
 
 A step is one full slice denoise (30 blocks x 4 Euler steps, audio K/V, time
 embedding, head and motion pin) of a batch of synthetic inputs already in
@@ -386,10 +386,10 @@ def main():
     ap.add_argument("--workload", default="slice", choices=sorted(WORKLOADS))
     ap.add_argument("--sampler", default="euler", choices=["euler", "renoise"],
                     help="step update: Euler (the metric's configuration) or the re-noising variant")
-    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8ffn", "fp8attn"],
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8ffn", "fp8qkv", "fp8attn"],
                     help="bf16 everywhere (the metric's configuration); fp8ffn: the FFN's two GEMMs in "
-                         "block-scaled FP8 (MX e4m3, one power-of-two scale per 32 along K); fp8attn: "
-                         "those and the self-attention")
+                         "block-scaled FP8 (MX e4m3, one power-of-two scale per 32 along K); fp8qkv: "
+                         "those and the QKV projection; fp8attn: those and the self-attention")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every kernel class (slow)")
@@ -417,11 +417,12 @@ def main():
     W = synth.make_weights(cfg)
     ctx = fh.fh_create(cfg)
     w = fh.fh_weights_bind(ctx, W)
-    fp8 = args.precision in ("fp8ffn", "fp8attn")
+    fp8 = args.precision in ("fp8ffn", "fp8qkv", "fp8attn")
     if fp8:
         fh.fh_weights_quantize_fp8(ctx, w)
         fh.fh_set_option(ctx, fh.FH_OPT_PRECISION,
-                         fh.FH_PREC_FP8_ATTN if args.precision == "fp8attn" else fh.FH_PREC_FP8_FFN)
+                         {"fp8ffn": fh.FH_PREC_FP8_FFN, "fp8qkv": fh.FH_PREC_FP8_QKV,
+                          "fp8attn": fh.FH_PREC_FP8_ATTN}[args.precision])
     ws = fh.workspace(ctx, B)
     lat, mot, aud = synth.slice_inputs(cfg, B)
     L, Mo, A = (torch.from_numpy(a).cuda() for a in (lat, mot, aud))
@@ -522,6 +523,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8ffn": "bf16, FFN GEMMs mxfp8 (e4m3)",
+                  "fp8qkv": "bf16, FFN and QKV GEMMs mxfp8 (e4m3)",
                   "fp8attn": "bf16, FFN GEMMs and self-attention mxfp8 (e4m3)"}[args.precision],
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) latent/motion/audio)",
         "config": {"workload": desc, "batch": B, "tokens": cfg.tokens, "blocks": cfg.n_blocks,

@@ -219,7 +219,12 @@ enum { FH_SAMPLER_EULER = 0, FH_SAMPLER_RENOISE = 1 };
  *       (query fh_workspace_bytes after setting it). The gain over
  *       FH_PREC_FP8_FFN comes from the FP8 QKV projection: the attention
  *       kernel itself is softmax-bound and no faster than the bf16 one.    */
-enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2, FH_PREC_FP8_ATTN = 3 };
+/*     FH_PREC_FP8_QKV: FH_PREC_FP8_FFN and the QKV projection on MX-FP8
+ *       operands as in FH_PREC_FP8_ATTN (its LayerNorm writes codes and
+ *       scales), with q, k and v stored in bf16 and the bf16 self-attention:
+ *       the FP8 projection's time without the FP8 attention kernel's. Needs
+ *       fh_weights_quantize_fp8; the workspace is FH_PREC_FP8_FFN's.        */
+enum { FH_PREC_BF16 = 0, FH_PREC_FP8_FFN = 1, FH_PREC_FP32 = 2, FH_PREC_FP8_ATTN = 3, FH_PREC_FP8_QKV = 4 };
 /* Kernel classes of FH_OPT_TIME_KERNEL. FH_K_AUDIO_KV is the once-per-slice
  * audio keys and values of every block (all of its launches as one sample). */
 enum {

@@ -199,6 +199,12 @@ def test_fp8_precision_argument_errors():
     assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EINVAL
     assert "fh_weights_quantize_fp8" in fh.fh_last_error(ctx)
     assert L.fh_dit_block_forward(ctx, w, 0, 1, fake, fake, fake, fake, need, None) == fh.FH_EINVAL
+    # the FP8 QKV precision: FP8 FFN's workspace, and the same need for quantised weights
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_QKV) == fh.FH_OK
+    assert fh.fh_workspace_bytes(ctx, 1) == need
+    assert L.fh_dit_denoise_slice(ctx, w, 1, fake, fake, fake, sig, 1, fake, fake, need, None) == fh.FH_EINVAL
+    assert "fh_weights_quantize_fp8" in fh.fh_last_error(ctx)
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP8_FFN) == fh.FH_OK
     # quantisation buffer checks
     nb = fh.fh_fp8_weight_bytes(ctx)
     assert L.fh_weights_quantize_fp8(ctx, w, None, nb, None) == fh.FH_EINVAL
@@ -242,7 +248,7 @@ def test_fp32_precision_option_and_workspace():
     ctx = fh.fh_create(synth.CONFIGS["toy"])
     L = fh.lib
     base = fh.fh_workspace_bytes(ctx, 1)
-    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 4) == fh.FH_EINVAL
+    assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, 5) == fh.FH_EINVAL
     assert L.fh_set_option(ctx, fh.FH_OPT_PRECISION, fh.FH_PREC_FP32) == fh.FH_OK
     c = synth.CONFIGS["toy"]
     N, D, Fd, La = c.frames * c.height * c.width, c.dim, c.ffn_dim, c.frames * c.audio_per_frame

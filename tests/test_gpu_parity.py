@@ -965,8 +965,51 @@ def test_fp8_attn_block(fh):
     assert err_q <= TOL_MX and err <= TOL_FP8
 
 
+# FH_PREC_FP8_QKV: the FP8 FFN and the QKV projection on MX-FP8 operands, the
+# attention itself exact in bf16/float32 -- so its oracle is the MX-FP8 one with
+# the exact attention, at the same bars as the FP8 FFN.
+def _fp8_qkv_model(fh, cfg, W, B):
+    m = Model(fh, cfg, W, B, precision=fh.FH_PREC_FP8_QKV)
+    fh.fh_weights_quantize_fp8(m.ctx, m.w)
+    return m
+
+
+def test_fp8_qkv_toy_slice(fh):
+    cfg = synth.CONFIGS["toy"]
+    W = synth.make_weights(cfg)
+    m = _fp8_qkv_model(fh, cfg, W, 2)
+    lat, mot, aud = synth.slice_inputs(cfg, 2)
+    sig = [1.0, 0.75, 0.5, 0.25, 0.0]
+    say("toy slice, FP8 FFN and QKV projection, 4 steps")
+    got = m.slice(lat, mot, aud, sig)
+    Wf = synth.weights_f32(W)
+    ref_q = O.denoise_slice(lat, mot, aud, sig, Wf, cfg, ffn_linear=Q.mx_linear, qkv_linear=Q.mx_linear)
+    ref = O.denoise_slice(lat, mot, aud, sig, Wf, cfg)
+    err_q, err = O.rel_err(got, ref_q, cfg.motion_frames), O.rel_err(got, ref, cfg.motion_frames)
+    say(f"  rel err vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs the exact oracle {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL_MX and err <= TOL_FP8
+    np.testing.assert_array_equal(got[:, :, :cfg.motion_frames], mot)
+    np.testing.assert_array_equal(m.slice(lat, mot, aud, sig, graph=False), got)
+
+
+def test_fp8_qkv_block(fh):
+    cfg = synth.CONFIGS["block"]
+    W = synth.make_weights(cfg)
+    m = _fp8_qkv_model(fh, cfg, W, 1)
+    x, e, a = synth.block_inputs(cfg, 1)
+    say("full-width block, FP8 FFN and QKV projection")
+    got = m.block(0, x, e, a)
+    Wf = synth.weights_f32(W)
+    err_q = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg, ffn_linear=Q.mx_linear,
+                                                 qkv_linear=Q.mx_linear), x)
+    err = delta_err(got, O.dit_block_from_temb(x, e, a, Wf, 0, cfg), x)
+    say(f"  rel err of the update vs the MX-FP8 oracle {err_q:.3e} (bar {TOL_MX}), vs exact {err:.3e} (bar {TOL_FP8})")
+    assert err_q <= TOL_MX and err <= TOL_FP8
+
+
 @pytest.mark.parametrize("precision,case", [
     ("fp8attn", "slice_b1"), ("fp8attn", "slice_b3"), ("fp8attn", "slice768"),
+    ("fp8qkv", "slice_b1"), ("fp8qkv", "slice768"),
     ("fp8ffn", "slice_b3"), ("fp8ffn", "slice768"),
     ("fp32", "slice_b3"), ("fp32", "slice768")])
 def test_other_precisions_on_stored_full_slices(fh, precision, case):
@@ -983,6 +1026,8 @@ def test_other_precisions_on_stored_full_slices(fh, precision, case):
     assert synth.weights_digest(W) == str(g["digest"])
     if precision == "fp8attn":
         m = _fp8_attn_model(fh, cfg, W, B)
+    elif precision == "fp8qkv":
+        m = _fp8_qkv_model(fh, cfg, W, B)
     elif precision == "fp8ffn":
         m = _fp8_model(fh, cfg, W, B)
     else:
