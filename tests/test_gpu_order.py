@@ -69,6 +69,7 @@ def test_outputs_do_not_depend_on_workgroup_order(fh):
         "toy slice": _slice_runner(fh, synth.CONFIGS["toy"]),
         "full-width 2-block slice": _slice_runner(fh, synth.CONFIGS["slice"].replace(n_blocks=2)),
         "toy slice, FP8 FFN + attention": _slice_runner(fh, synth.CONFIGS["toy"], fh.FH_PREC_FP8_ATTN),
+        "toy slice, FP8 FFN + QKV": _slice_runner(fh, synth.CONFIGS["toy"], fh.FH_PREC_FP8_QKV),
         "video decoder (ragged)": _vae_runner(fh),
         "colour match": _color_runner(fh),
     }
