@@ -107,6 +107,39 @@ def test_graph_cache_eviction_while_graphs_run(fh):
         np.testing.assert_array_equal(o.cpu().numpy(), want, err_msg=f"call {i}")
 
 
+def test_graph_replays_between_eager_work(fh):
+    """One cached slice graph (full width, 2 blocks) replayed four times, with
+    direct-launch slices and unrelated torch work on the same stream and a
+    synchronisation between the replays: every replay equals the direct
+    (eager) result bitwise."""
+    cfg = synth.CONFIGS["slice"].replace(n_blocks=2)
+    W = synth.make_weights(cfg)
+    m = Model(fh, cfg, W, 1)
+    lat, mot, aud = synth.slice_inputs(cfg, 1)
+    sig = list(synth.SLICE_SIGMAS)
+    L, Mo, A = dev(lat), dev(mot), dev(aud)
+    out_g, out_e = torch.empty_like(L), torch.empty_like(L)
+    say("eager (direct launches) reference")
+    fh.fh_set_option(m.ctx, fh.FH_OPT_GRAPH, 0)
+    fh.fh_dit_denoise_slice(m.ctx, m.w, L, Mo, A, sig, out_e, m.ws)
+    want = out_e.cpu().numpy()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for r in range(4):
+        say(f"graph replay {r}")
+        fh.fh_set_option(m.ctx, fh.FH_OPT_GRAPH, 1)
+        out_g.fill_(float("nan"))
+        fh.fh_dit_denoise_slice(m.ctx, m.w, L, Mo, A, sig, out_g, m.ws)
+        got = out_g.cpu().numpy()
+        np.testing.assert_array_equal(got, want, err_msg=f"replay {r}")
+        # eager work between the replays: a direct-launch slice into another
+        # buffer, torch kernels, a synchronisation
+        fh.fh_set_option(m.ctx, fh.FH_OPT_GRAPH, 0)
+        fh.fh_dit_denoise_slice(m.ctx, m.w, L, Mo, A, sig, out_e, m.ws)
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out_e.cpu().numpy(), want, err_msg=f"eager {r}")
+
+
 def test_toy_multi_step_and_edge_cases(fh):
     cfg = synth.CONFIGS["toy"]
     W = synth.make_weights(cfg)
