@@ -732,7 +732,8 @@ hipError_t cross_probs(const bf16_t* q, int ldq, const bf16_t* kc, int ldk, bf16
                        int La, int hw, int apf, int n_heads, float scale, const float* ssq, int groups,
                        const float* g, float eps, hipStream_t s) {
   if (B <= 0 || N <= 0) return hipSuccess;
-  if (N % 32 || hw % 32 || apf % 32 || apf > 32 * MAXKB || La % 32 || ldq % 8 || ldk % 8 || ldp % 4 ||
+  // apf >= 32: the kernel reads the first key block of a frame before it knows the count
+  if (N % 32 || hw % 32 || apf % 32 || apf < 32 || apf > 32 * MAXKB || La % 32 || ldq % 8 || ldk % 8 || ldp % 4 ||
       ldp < n_heads * apf || (N / hw) * apf > La || !p)
     return hipErrorInvalidValue;
   if (ssq && (groups < 4 || groups > MAXG || groups % 4 || !g)) return hipErrorInvalidValue;
