@@ -615,29 +615,40 @@ void gemm_bf16_nt(const bf16_t* __restrict__ A, int lda, const bf16_t* __restric
 // rows' scales first (rounded up to 128 rows), then the weight rows'.
 template <int BM>
 constexpr int mx_arows() { return (BM + 127) / 128 * 128; }
-template <int BM, int BN>
-constexpr int mx_slab_bytes() { return (BM + BN) * 64 + ((mx_arows<BM>() + BN) * 2 + 1023) / 1024 * 1024; }
+// SB bytes of K per row and slab (64 or 128: one or two 64-deep MFMA k-steps),
+// then the scales of each k-step: (activation rows rounded to 128 + weight rows) u16
+template <int BM, int BN, int SB = 64>
+constexpr int mx_slab_bytes() { return (BM + BN) * SB + ((mx_arows<BM>() + BN) * 2 * (SB / 64) + 1023) / 1024 * 1024; }
 
 __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }  // 64-byte rows
+// 16-byte chunk swizzle of an SB-byte slab row (128-byte rows as the bf16 kernel's 64-deep slabs)
+template <int SB>
+__device__ __forceinline__ int swz_mx(int row) { return SB == 64 ? swz64(row) : (row >> 1) & 7; }
 
 // WN = 4: 2 x 4 waves (two per SIMD), the activation DMA groups dealt as in
 // the bf16 kernel (a wave may take one fewer; its wait counts follow). FFN up
 // runs so (32.5 -> 30.3 us at 1280 tokens); the QKV tiles were slower.
-template <int EPI, int BM, int BN, int NS, int WN = 2>
+// SB = 128: slabs of two 64-byte k-steps (half the slab iterations, barriers and
+// waits per FLOP; twice the fragment registers).
+template <int EPI, int BM, int BN, int NS, int WN = 2, int SB = 64>
 __global__ __launch_bounds__(128 * WN, 1)
 void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restrict__ As,
                 const uint8_t* __restrict__ W, int ldw, const uint16_t* __restrict__ Ws,
                 int M, int N, int K, int tiles_m, int tiles, int splits, EpiArgs ep) {
-  constexpr int ROWB = 64, CH = 4, RG = 16;   // bytes per LDS row, 16-byte chunks, rows per 1 KB DMA
+  constexpr int KK = SB / 64;                 // 64-byte k-steps per slab
+  constexpr int ROWB = SB, CH = SB / 16, RG = 1024 / SB;  // bytes per LDS row, 16-byte chunks, rows per 1 KB DMA
   constexpr int NW = 2 * WN;                  // waves, 2 x WN
   constexpr int MI = BM / 64, NI = BN / (32 * WN);
   constexpr int TA = BM / RG, TW = BN / RG;   // 1 KB code DMAs per slab, activations / weights
   constexpr int GA = (TA + NW - 1) / NW, GW = (TW + NW - 1) / NW;  // ... at most per wave
-  constexpr int SQA = mx_arows<BM>() / 128, SQ = SQA + BN / 128;  // 256-byte scale DMAs per slab
+  constexpr int SQA = mx_arows<BM>() / 128, SQ1 = SQA + BN / 128;  // 256-byte scale DMAs per k-step
+  constexpr int SQ = KK * SQ1;                       // ... per slab
   constexpr int SPW = (SQ + NW - 1) / NW;            // scale DMAs per wave (the last one repeated)
   constexpr int DPS = GA + GW + SPW;
   constexpr int SCB = (BM + BN) * ROWB;              // scale area of a slab
-  constexpr int SLAB = mx_slab_bytes<BM, BN>();
+  constexpr int SCK = (mx_arows<BM>() + BN) * 2;     // scale bytes of one k-step
+  constexpr int SLAB = mx_slab_bytes<BM, BN, SB>();
+  static_assert(SB == 64 || SB == 128, "slabs of one or two 64-byte k-steps");
   static_assert(TA * RG == BM && TW * RG == BN && BN % 128 == 0 && BN % (32 * WN) == 0, "tile shape");
   static_assert(WN == 2 || WN == 4, "2 x 2 or 2 x 4 waves");
   static_assert(GW * NW == TW && (GA * NW == TA || GA * NW - TA < NW), "at most one group fewer per wave");
@@ -670,33 +681,34 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < GA; ++i) {
     const int r = RG * (wave + NW * i) + drow;
-    ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
+    ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + (int64_t)s_base * 64 + ((lane % CH) ^ swz_mx<SB>(r)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < GW; ++i) {
     const int r = RG * (wave + NW * i) + drow;
-    gw[i] = W + (int64_t)(n0 + r) * ldw + (int64_t)s_base * 64 + ((lane % CH) ^ swz64(r)) * 16;
+    gw[i] = W + (int64_t)(n0 + r) * ldw + (int64_t)s_base * 64 + ((lane % CH) ^ swz_mx<SB>(r)) * 16;
   }
-  // scale DMA t of this wave (instruction q): rows 128 q + 2 lane and the next,
-  // of the activations for q < SQA (past M: the last row pair again), else of
-  // the weights
+  // scale DMA t of this wave (instruction q2 = SQ1 kk + q: k-step kk of the
+  // slab): rows 128 q + 2 lane and the next, of the activations for q < SQA
+  // (past M: the last row pair again), else of the weights
   const uint16_t* gs[SPW];
 #pragma unroll
   for (int t = 0; t < SPW; ++t) {
-    const int q = min(wave + NW * t, SQ - 1);
-    gs[t] = q < SQA ? As + (int64_t)s_base * M + min(m0 + 128 * q + 2 * lane, M - 2)
-                    : Ws + (int64_t)s_base * N + (n0 + 128 * (q - SQA) + 2 * lane);
+    const int q2 = min(wave + NW * t, SQ - 1), kk = q2 / SQ1, q = q2 % SQ1;
+    gs[t] = q < SQA ? As + (int64_t)(s_base + kk) * M + min(m0 + 128 * q + 2 * lane, M - 2)
+                    : Ws + (int64_t)(s_base + kk) * N + (n0 + 128 * (q - SQA) + 2 * lane);
   }
   auto dma_one = [&](int d, int buf, int slab) {
     char* sb = smem + buf * SLAB;
     if (d < GA) {
-      if (EVEN || d < GA - 1 || a_full) dma16(ga[d] + slab * 64, sb + (wave + NW * d) * 1024);
+      if (EVEN || d < GA - 1 || a_full) dma16(ga[d] + slab * SB, sb + (wave + NW * d) * 1024);
     } else if (d < GA + GW) {
-      dma16(gw[d - GA] + slab * 64, sb + BM * ROWB + (wave + NW * (d - GA)) * 1024);
+      dma16(gw[d - GA] + slab * SB, sb + BM * ROWB + (wave + NW * (d - GA)) * 1024);
     } else {
-      const int t = d - GA - GW, q = min(wave + NW * t, SQ - 1);
-      const int64_t step = q < SQA ? M : N;  // u16 elements per slab in this scale array
-      __builtin_amdgcn_global_load_lds((gbl_void*)(gs[t] + slab * step), (lds_void*)(sb + SCB + q * 256), 4, 0, 0);
+      const int t = d - GA - GW, q2 = min(wave + NW * t, SQ - 1), kk = q2 / SQ1, q = q2 % SQ1;
+      const int64_t step = q < SQA ? M : N;  // u16 elements per 64-byte k-step in this scale array
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gs[t] + (int64_t)slab * KK * step),
+                                       (lds_void*)(sb + SCB + kk * SCK + q * 256), 4, 0, 0);
     }
   };
 
@@ -711,42 +723,47 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
   typedef int v8i __attribute__((ext_vector_type(8)));
   constexpr int P = NI * MI, NR = NI + MI;
   const int a_row = wm * (BM / 2) + lr, w_row = BM + wn * (BN / WN) + lr;  // slab rows (W after A)
-  v8i wf[2][NI], af[2][MI];
-  int wsc[2][NI], asc[2][MI];
-  // fragment read r of a slab (and its scale byte): r < NI weights, else activations
+  v8i wf[2][KK][NI], af[2][KK][MI];
+  int wsc[2][KK][NI], asc[2][KK][MI];
+  // fragment read r of a slab (and its scale byte): k-step r / NR; r % NR < NI
+  // weights, else activations
   auto read_one = [&](int r, int set, int buf) {
+    const int kk = r / NR, q = r % NR;
     const char* sb = smem + buf * SLAB;
-    const int row = r < NI ? w_row + 32 * r : a_row + 32 * (r - NI);
+    const int row = q < NI ? w_row + 32 * q : a_row + 32 * (q - NI);
     const char* rp = sb + row * ROWB;
-    const int x = swz64(row);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + ((lh ^ x) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (((2 + lh) ^ x) << 4));
+    const int x = swz_mx<SB>(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + (((4 * kk + lh) ^ x) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + (((4 * kk + 2 + lh) ^ x) << 4));
     const v8i f = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    const int srow = r < NI ? mx_arows<BM>() + (row - BM) : row;  // row in the scale area
-    const int sc = (int)(*reinterpret_cast<const uint16_t*>(sb + SCB + srow * 2) >> (8 * lh));
-    if (r < NI) { wf[set][r] = f; wsc[set][r] = sc; }
-    else { af[set][r - NI] = f; asc[set][r - NI] = sc; }
+    const int srow = q < NI ? mx_arows<BM>() + (row - BM) : row;  // row in the scale area
+    const int sc = (int)(*reinterpret_cast<const uint16_t*>(sb + SCB + kk * SCK + srow * 2) >> (8 * lh));
+    if (q < NI) { wf[set][kk][q] = f; wsc[set][kk][q] = sc; }
+    else { af[set][kk][q - NI] = f; asc[set][kk][q - NI] = sc; }
   };
+  constexpr int SLOTS = KK * P, READS = KK * NR;
   auto mma_slab = [&](auto set_c, int rbuf, int dbuf, int dslab) {
     constexpr int set = decltype(set_c)::value;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int j = 0; j < MI; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[set][i], af[set][j], acc[i][j], 0, 0,
-                                                                    0, wsc[set][i], 0, asc[set][j]);
-        const int slot = i * MI + j;
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-          if (r * P / NR == slot) read_one(r, set ^ 1, rbuf);
+        for (int j = 0; j < MI; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[set][kk][i], af[set][kk][j], acc[i][j], 0,
+                                                                      0, 0, wsc[set][kk][i], 0, asc[set][kk][j]);
+          const int slot = kk * P + i * MI + j;
 #pragma unroll
-        for (int d = 0; d < DPS; ++d)
-          if (d * P / DPS == slot) dma_one(d, dbuf, dslab);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+          for (int r = 0; r < READS; ++r)
+            if (r * SLOTS / READS == slot) read_one(r, set ^ 1, rbuf);
+#pragma unroll
+          for (int d = 0; d < DPS; ++d)
+            if (d * SLOTS / DPS == slot) dma_one(d, dbuf, dslab);
+          __builtin_amdgcn_sched_barrier(0);
+        }
   };
 
-  const int KT = K / 64;
+  const int KT = K / SB;
 #pragma unroll
   for (int s0 = 0; s0 < NS; ++s0)
 #pragma unroll
@@ -760,7 +777,7 @@ void gemm_mx_nt(const uint8_t* __restrict__ A, int lda, const uint16_t* __restri
   wait_slabs(std::integral_constant<int, NS - 1>{});
   barrier();
 #pragma unroll
-  for (int r = 0; r < NR; ++r) read_one(r, 0, 0);
+  for (int r = 0; r < READS; ++r) read_one(r, 0, 0);
   auto iteration = [&](int kt, auto set_c) {
     wait_slabs(std::integral_constant<int, NS - 2>{});  // this wave's DMAs of slab kt + 1 have landed
     wait_lgkm0();               // and its fragments of slab kt are in registers
@@ -811,11 +828,11 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ 
   reinterpret_cast<uint8_t*>(scales)[((int64_t)(kb / 2) * rows + row) * 2 + (kb & 1)] = (uint8_t)(ex + 127);
 }
 
-template <int BM, int BN, int NS, int WN = 2>
+template <int BM, int BN, int NS, int WN = 2, int SB = 64>
 hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, const uint8_t* W, int ldw,
                      const uint16_t* Ws, int M, int N, int K, const EpiArgs& ep, hipStream_t s,
                      int splits = 1) {
-  if (N % BN || splits < 1 || K % (splits * 64) || lda % 16 || ldw % 16 || M % 2) return hipErrorInvalidValue;
+  if (N % BN || splits < 1 || K % (splits * SB) || lda % 16 || ldw % 16 || M % 2) return hipErrorInvalidValue;
   if (ep.w_group_rows || ep.ldt) return hipErrorInvalidValue;  // bf16 kernel only
   if (splits > 1 && (epi != EPI_PARTIAL || !ep.part || ep.part_elems < (size_t)splits * M * N))
     return hipErrorInvalidValue;
@@ -828,8 +845,11 @@ hipError_t launch_mx(int epi, const uint8_t* A, int lda, const uint16_t* As, con
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = tiles_m * (N / BN);
   const dim3 grid((tiles * splits + 7) / 8 * 8), block(128 * WN);
-#define FH_MX(E) launch_gemm(gemm_mx_nt<E, BM, BN, NS, WN>, grid, block, s, A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
-  if constexpr (WN == 4) {  // 2 x 4 waves: the FFN up product
+#define FH_MX(E) launch_gemm(gemm_mx_nt<E, BM, BN, NS, WN, SB>, grid, block, s, A, lda, As, W, ldw, Ws, M, N, K, tiles_m, tiles, splits, ep)
+  if constexpr (SB != 64) {  // 128-byte slabs: the split-K product
+    if (epi == EPI_PARTIAL) FH_MX(EPI_PARTIAL);
+    else return hipErrorInvalidValue;
+  } else if constexpr (WN == 4) {  // 2 x 4 waves: the FFN up product
     if (epi == EPI_GELU_MX) FH_MX(EPI_GELU_MX);
     else return hipErrorInvalidValue;
   } else {
@@ -1134,6 +1154,7 @@ hipError_t gemm_mx_splitk(const uint8_t* A, int lda, const uint16_t* As, const u
   EpiArgs ep;
   ep.part = part;
   ep.part_elems = part_elems;
+  if (K % 256 == 0) return launch_mx<128, 128, 4, 2, 128>(EPI_PARTIAL, A, lda, As, W, ldw, Ws, M, N, K, ep, s, 2);
   return launch_mx<128, 128, 4>(EPI_PARTIAL, A, lda, As, W, ldw, Ws, M, N, K, ep, s, 2);
 }
 
