@@ -527,10 +527,11 @@ def _mx_gemm_bound(a, w, extra, K):
 
 @pytest.mark.parametrize("M,N,K,split", [
     (1280, 8960, 1536, False),   # FFN-up shape
-    (1280, 1536, 8960, True),    # FFN-down shape, K in two halves
+    (1280, 1536, 8960, True),    # FFN-down shape, K in two halves (128-byte K slabs)
     (1280, 1536, 8960, False),   # FFN-down shape, one pass
     (1000, 384, 192, False),     # ragged M, fewer K slabs than pipeline stages
-    (1002, 256, 4096, True),     # ragged M, split
+    (1002, 256, 4096, True),     # ragged M, split (128-byte K slabs)
+    (1280, 256, 4224, True),     # split with K % 256 != 0 (64-byte K slabs)
     (2, 128, 64, False),         # smallest
 ])
 def test_mxfp8_gemm_exact_on_codes(fh, M, N, K, split):
