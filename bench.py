@@ -21,6 +21,8 @@ Extra objects on the line:
                 the clock every CU holds while it runs back-to-back MFMAs.
   workloads     batch 3 (three streams) and 768x768 (2880 tokens): frames/s,
                 ms per call and their own hot-kernel fractions.
+  fp8_options   the block-scaled FP8 precisions (FFN; FFN and QKV; FFN, QKV
+                and self-attention) on the batch-1 slice: frames/s, ms per call.
   cpu_baseline  the fp32 numpy oracle on this host: one real-shape block
                 (1280 tokens, its audio K/V and modulation) three times,
                 median, scaled to the slice's 120 block-steps.
@@ -302,6 +304,44 @@ def other_workload(fh, torch, synth, W, name, stream, steps, hot_passes, no_grap
     return res
 
 
+def fp8_options(fh, torch, synth, W, stream, steps, no_graph):
+    """frames/s and ms per call of the block-scaled FP8 precisions on the batch-1
+    slice and the same weights (quantised once): FFN; FFN and QKV; FFN, QKV and
+    self-attention. Options, not the metric's configuration."""
+    cfg = synth.CONFIGS["slice"]
+    sig = list(synth.SLICE_SIGMAS)
+    ctx = fh.fh_create(cfg)
+    w = fh.fh_weights_bind(ctx, W)
+    fh.fh_weights_quantize_fp8(ctx, w)
+    fh.fh_set_option(ctx, fh.FH_OPT_GRAPH, 0 if no_graph else 1)
+    L, Mo, A = (torch.from_numpy(a).cuda() for a in synth.slice_inputs(cfg, 1))
+    out = torch.empty_like(L)
+    total, _ = flops_per_slice(cfg, 1, len(sig) - 1)
+    res = {}
+    for name, prec in (("fp8ffn", fh.FH_PREC_FP8_FFN), ("fp8qkv", fh.FH_PREC_FP8_QKV),
+                       ("fp8attn", fh.FH_PREC_FP8_ATTN)):
+        fh.fh_set_option(ctx, fh.FH_OPT_PRECISION, prec)
+        ws = fh.workspace(ctx, 1)  # sized for the precision
+
+        def step():
+            fh.fh_dit_denoise_slice(ctx, w, L, Mo, A, sig, out, ws, stream)
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        T = time.perf_counter() - t0
+        res[name] = {"frames_per_s": round(FRAMES_PER_SLICE * steps / T, 2), "ms_per_call": round(1e3 * T / steps, 4),
+                     "tflops_end_to_end": round(total / (T / steps) / 1e12, 2), "steps": steps}
+        del ws
+    del w, L, Mo, A, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def vae_flops(vc):
     """Algorithmic FLOPs of one decode: 2 x 27 C_in C_out per output position of
     every convolution (the norms, SiLU and depth to space are bytes, not FLOPs)."""
@@ -495,10 +535,12 @@ def main():
 
     # the other workloads of the metric's configuration list, same weights
     extra = {}
+    fp8_opts = None
     if not args.no_extra and args.workload == "slice" and not fp8 and args.sampler == "euler":
         for name in ("slice_b3", "slice768"):
             extra[name] = other_workload(fh, torch, synth, W, name, stream, max(3, args.steps // 2),
                                          args.hot_passes, args.no_graph)
+        fp8_opts = fp8_options(fh, torch, synth, W, stream, args.steps, args.no_graph)
     del W
 
     front = audio_front_end(fh, torch, ctx, cfg, B, stream, args.steps) if cfg_name == "slice" else None
@@ -549,6 +591,8 @@ def main():
                        "peak_at_measured_clock_tflops": round(PEAK_BF16_TFLOPS * clock / 2400.0, 1)}
     if extra:
         line["workloads"] = extra
+    if fp8_opts is not None:
+        line["fp8_options"] = fp8_opts
     if front is not None:
         line["audio_front_end"] = front
     if vae is not None:

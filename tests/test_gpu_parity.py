@@ -1043,7 +1043,7 @@ def test_fp8_qkv_block(fh):
 
 @pytest.mark.parametrize("precision,case", [
     ("fp8attn", "slice_b1"), ("fp8attn", "slice_b3"), ("fp8attn", "slice768"),
-    ("fp8qkv", "slice_b1"), ("fp8qkv", "slice768"),
+    ("fp8qkv", "slice_b1"), ("fp8qkv", "slice_b3"), ("fp8qkv", "slice768"),
     ("fp8ffn", "slice_b3"), ("fp8ffn", "slice768"),
     ("fp32", "slice_b3"), ("fp32", "slice768")])
 def test_other_precisions_on_stored_full_slices(fh, precision, case):
