@@ -41,9 +41,11 @@ __global__ void sinusoid_kernel(float* __restrict__ out, Times ts, int R, int di
   out[i] = (float)(k < half ? cos(a) : sin(a));
 }
 
-// 16 outputs per 256-thread workgroup (4 per wave); the R input rows sit in LDS.
-// A wave requests the weights of its 4 rows for a 2048-deep chunk of K at once
-// (16 bytes per lane and row, 4 chunks of 512), then forms the products.
+// 16 outputs per 256-thread workgroup (4 per wave); the R input rows sit in LDS,
+// staged in 16-byte pieces whose loads are all in flight before the first
+// store (one scalar load-store round per element was the kernel's largest
+// cost). A wave requests the weights of its 4 rows for a 2048-deep chunk of K
+// at once (16 bytes per lane and row, 4 chunks of 512), then forms the products.
 constexpr int GV_OPW = 4, GV_KC = 4;
 
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int R, int K,
@@ -51,9 +53,33 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
                                                    const float* __restrict__ b, float* __restrict__ y,
                                                    int N, int act_in, int act_out) {
   extern __shared__ float sx[];
-  for (int i = threadIdx.x; i < R * K; i += 256) {
-    float v = x[i];
-    sx[i] = act_in ? silu(v) : v;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    // 16-byte pieces (R K is a multiple of 8), up to 8 per thread requested
+    // before the first is stored
+    const int n4 = R * K / 4;
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    f32x4* s4 = reinterpret_cast<f32x4*>(sx);
+    for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 256 * u < n4) v[u] = x4[i0 + 256 * u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 256 * u < n4) {
+          f32x4 t = v[u];
+          if (act_in) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = silu(t[e]);
+          }
+          s4[i0 + 256 * u] = t;
+        }
+    }
+  } else {
+    for (int i = threadIdx.x; i < R * K; i += 256) {
+      float v = x[i];
+      sx[i] = act_in ? silu(v) : v;
+    }
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

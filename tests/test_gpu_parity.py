@@ -270,6 +270,27 @@ def test_block_single_branch(fh, keep):
     assert err <= TOL
 
 
+def test_block_time_embedding_alignment(fh):
+    """The time-projection GEMV stages its input rows in 16-byte pieces when
+    they are 16-byte aligned and element by element otherwise: a time embedding
+    4 bytes off alignment gives the same bits as an aligned one."""
+    cfg = synth.CONFIGS["toy"]
+    m = Model(fh, cfg, synth.make_weights(cfg), 2)
+    x, e, a = synth.block_inputs(cfg, 2)
+    X0, X1 = dev(x), dev(x)
+    E0 = dev(e)
+    buf = torch.zeros(E0.numel() + 1, dtype=torch.float32, device="cuda")
+    E1 = buf[1:].view(E0.shape)
+    E1.copy_(E0)
+    assert E0.data_ptr() % 16 == 0 and E1.data_ptr() % 16 == 4
+    say("toy block B=2, aligned and misaligned time embedding")
+    fh.fh_dit_block_forward(m.ctx, m.w, 0, X0, E0, dev(a), m.ws)
+    fh.fh_dit_block_forward(m.ctx, m.w, 0, X1, E1, dev(a), m.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(X0, X1)
+    assert not torch.equal(X0, dev(x))
+
+
 # ------------------------------------------------------------------ self-attention kernels
 ATTN_SHAPES = {
     # 128 tokens: two 64-key blocks, one per key half
