@@ -141,11 +141,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
   }
 }
 
-constexpr int PT = 8;   // tokens per patch-embed workgroup
+constexpr int PT = 4;   // tokens per patch-embed workgroup (1280 tokens: 320 workgroups)
 constexpr int MAXC = 64;
 
-// Each thread owns 4 output columns and produces them for the workgroup's 8
-// tokens, so a weight row group is read once per 8 tokens.
+// Each thread owns 4 output columns and produces them for the workgroup's PT
+// tokens, so a weight row group is read once per PT tokens; the weights come
+// in 16-byte pieces of 8 channels (C a multiple of 8), one round of loads per
+// 8 channels rather than per channel.
 __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restrict__ lat, int C, int N,
                                                           const bf16_t* __restrict__ Wp,
                                                           const float* __restrict__ bp,
@@ -164,16 +166,18 @@ __global__ __launch_bounds__(256) void patch_embed_kernel(const float* __restric
     for (int tt = 0; tt < PT; ++tt) {
       acc[tt][0] = bias.x; acc[tt][1] = bias.y; acc[tt][2] = bias.z; acc[tt][3] = bias.w;
     }
-    for (int c = 0; c < C; ++c) {
-      float w[4];
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      u16x8 w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = bf2f(Wp[(int64_t)(d + e) * C + c]);
+      for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const u16x8*>(Wp + (int64_t)(d + e) * C + c0);
 #pragma unroll
-      for (int tt = 0; tt < PT; ++tt) {
-        const float l = sl[c * PT + tt];
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[tt][e] += w[e] * l;
-      }
+        for (int tt = 0; tt < PT; ++tt) {
+          const float l = sl[(c0 + j) * PT + tt];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tt][e] += bf2f(w[e][j]) * l;
+        }
     }
 #pragma unroll
     for (int tt = 0; tt < PT; ++tt)
@@ -427,7 +431,7 @@ hipError_t gemv_bf16(const float* x, int R, int K, const bf16_t* W, const float*
 
 hipError_t patch_embed(const float* lat, int B, int C, int N, const bf16_t* Wp, const float* bp,
                        float* x, int D, hipStream_t s) {
-  if (C > MAXC || D % 4) return hipErrorInvalidValue;
+  if (C > MAXC || C % 8 || D % 4 || ((uintptr_t)Wp & 15)) return hipErrorInvalidValue;
   dim3 grid((N + PT - 1) / PT, B);
   launch_timed(patch_embed_kernel, grid, 256, s, lat, C, N, Wp, bp, x, D);
   return hipGetLastError();
